@@ -1,0 +1,6 @@
+"""CPU oracle (float64 numpy) for the tiled MonarchAttention forward.
+
+Test infrastructure: only the tests, the smoke check and the benchmark's CPU
+baseline use it; the GPU library does not.
+"""
+from .monarch_oracle import *  # noqa: F401,F403

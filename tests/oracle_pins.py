@@ -1,0 +1,306 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each ``check_*`` takes an oracle module (the real one, or a copy with a
+planted mistake) and raises AssertionError when the fact does not hold.  The
+facts come from the mathematics of the method and from textbook attention,
+never from the oracle's own output:
+
+* row-stochastic attention rows, and the factored apply equal to the dense
+  Monarch matrix times V;
+* the one-tile case equal to the plain Monarch product P^T L P R written out
+  with an explicit permutation matrix;
+* degenerate block shapes and one-row tiles reduce to dense softmax attention
+  (computed by torch's scaled_dot_product_attention in float64);
+* Q = 0 gives the uniform matrix (every output row is the mean of V);
+* every half-step is the exact maximiser of the entropy-regularised objective
+  (checked by numerical optimisation with scipy), so the objective never
+  decreases, and the objective equals sum lse - sum KL to dense attention;
+* block rank at most the tile count, and the KKT (log-softmax) conditions;
+* an exactly separable positional input is reproduced exactly by aligned
+  blocks in one iteration.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOL = 1e-10
+
+
+def _rand(rng, *shape, scale=1.0):
+    return scale * rng.standard_normal(shape)
+
+
+def _sdpa(q, k, v):
+    """Dense softmax attention from torch (library routine), float64 on CPU."""
+    import torch
+    import torch.nn.functional as F
+    tq = torch.from_numpy(np.asarray(q, dtype=np.float64))[None, None]
+    tk = torch.from_numpy(np.asarray(k, dtype=np.float64))[None, None]
+    tv = torch.from_numpy(np.asarray(v, dtype=np.float64))[None, None]
+    return F.scaled_dot_product_attention(tq, tk, tv)[0, 0].numpy()
+
+
+def _dense_A(q, k):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    x = (q @ k.T) / math.sqrt(q.shape[1])
+    x = x - x.max(axis=1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _case(seed=0, b1=6, b2=5, d=8, scale=1.5):
+    rng = np.random.default_rng(seed)
+    N = b1 * b2
+    return (_rand(rng, N, d, scale=scale), _rand(rng, N, d, scale=scale),
+            _rand(rng, N, d))
+
+
+# ----------------------------------------------------------------- checks --
+
+def check_tile_bounds(orc):
+    for b1 in (1, 2, 7, 90, 630, 945):
+        for t in (1, 2, 3, 4, 8):
+            if t > b1:
+                continue
+            bd = orc.tile_bounds(b1, t)
+            assert bd[0] == 0 and bd[-1] == b1 and len(bd) == t + 1
+            sizes = np.diff(bd)
+            assert sizes.min() >= 1 and sizes.max() - sizes.min() <= 1
+            if 2 * t <= b1:
+                assert set(bd) <= set(orc.tile_bounds(b1, 2 * t))
+            g = orc.tile_of_rows(b1, t)
+            assert np.all(np.diff(g) >= 0) and g[0] == 0 and g[-1] == t - 1
+
+
+def check_row_stochastic_and_dense_apply(orc):
+    """O1 + O2: M >= 0, rows sum to one, factored apply == M @ V."""
+    for (b1, b2, t, T) in [(6, 5, 1, 1), (6, 5, 2, 2), (5, 6, 3, 1), (4, 4, 4, 2)]:
+        q, k, v = _case(1, b1, b2)
+        y, (L, R, _) = orc.monarch_head(q, k, v, b1, b2, t, T, return_factors=True)
+        M = orc.dense_monarch_matrix(L, R, orc.tile_bounds(b1, t))
+        assert M.min() >= 0.0
+        assert np.max(np.abs(M.sum(axis=1) - 1.0)) <= 1e-12
+        assert np.max(np.abs(M @ v - y)) <= 1e-12
+
+
+def check_plain_monarch_product(orc):
+    """O3 + O12: one tile equals P^T L P R with an explicit permutation."""
+    b1, b2 = 5, 3
+    P = orc.permutation_matrix(b1, b2)
+    assert np.array_equal(P @ P.T, np.eye(b1 * b2))
+    # P is the (b1,b2) -> (b2,b1) transpose of a row-major index grid
+    x = np.arange(b1 * b2, dtype=np.float64)
+    assert np.array_equal(P @ x, x.reshape(b1, b2).T.ravel())
+    for T in (1, 2):
+        q, k, v = _case(2, b1, b2)
+        y, (L, R, _) = orc.monarch_head(q, k, v, b1, b2, 1, T, return_factors=True)
+        M_plain = orc.explicit_monarch_matrix(L, R[0])
+        M = orc.dense_monarch_matrix(L, R, [0, b1])
+        assert np.max(np.abs(M - M_plain)) <= 1e-14
+        assert np.max(np.abs(M_plain @ v - y)) <= 1e-12
+
+
+def check_degenerate_blocks_are_dense_attention(orc):
+    """O4: (b1,b2) = (1,N) or (N,1) is exactly softmax attention."""
+    q, k, v = _case(3, 4, 6)
+    N = q.shape[0]
+    ref = _sdpa(q, k, v)
+    for (b1, b2) in [(1, N), (N, 1)]:
+        for T in (1, 2):
+            y = orc.monarch_head(q, k, v, b1, b2, 1, T)
+            assert np.max(np.abs(y - ref)) <= TOL, (b1, b2, T)
+
+
+def check_one_row_tiles(orc):
+    """O4: t = b1.  T >= 2 is exact dense attention; T = 1 has a closed form:
+    L = softmax over blocks of s*q.kbar_c1 (kbar = block mean of keys),
+    R = softmax within the block of s*q.k."""
+    b1, b2, d = 5, 4, 8
+    q, k, v = _case(4, b1, b2, d)
+    ref = _sdpa(q, k, v)
+    for T in (2, 3):
+        y = orc.monarch_head(q, k, v, b1, b2, b1, T)
+        assert np.max(np.abs(y - ref)) <= TOL, T
+    y1 = orc.monarch_head(q, k, v, b1, b2, b1, 1)
+    s = 1.0 / math.sqrt(d)
+    kb = k.reshape(b1, b2, d)
+    kbar = kb.mean(axis=1)
+    expect = np.empty_like(v)
+    vb = v.reshape(b1, b2, d)
+    for n in range(b1 * b2):
+        lw = np.exp(s * (kbar @ q[n]))
+        lw /= lw.sum()
+        acc = np.zeros(d)
+        for c1 in range(b1):
+            rw = np.exp(s * (kb[c1] @ q[n]))
+            rw /= rw.sum()
+            acc += lw[c1] * (rw @ vb[c1])
+        expect[n] = acc
+    assert np.max(np.abs(y1 - expect)) <= TOL
+
+
+def check_zero_queries_uniform(orc):
+    """O5: Q = 0 makes every logit equal, so M = 1/N and y_n = mean(V)."""
+    b1, b2, d = 6, 4, 8
+    _, k, v = _case(5, b1, b2, d)
+    q = np.zeros_like(k)
+    for t in (1, 3):
+        y = orc.monarch_head(q, k, v, b1, b2, t, 2)
+        assert np.max(np.abs(y - v.mean(axis=0))) <= 1e-12
+
+
+def check_objective_ascent_and_identity(orc):
+    """O6: F never decreases over the 2T half-steps, and
+    F(M) = sum_n logsumexp(s S_n) - sum_n KL(M_n || A_n)."""
+    b1, b2, d = 6, 5, 8
+    q, k, v = _case(6, b1, b2, d, scale=2.0)
+    s = 1.0 / math.sqrt(d)
+    A = _dense_A(q, k)
+    S = s * (q @ k.T)
+    lse = np.log(np.sum(np.exp(S - S.max(axis=1, keepdims=True)), axis=1)) + S.max(axis=1)
+    for t in (1, 2, 3):
+        bounds = orc.tile_bounds(b1, t)
+        _, (_, _, hist) = orc.monarch_head(q, k, v, b1, b2, t, 3, return_factors=True)
+        prev = -np.inf
+        for _, L, R in hist:
+            M = orc.dense_monarch_matrix(L, R, bounds)
+            F = orc.objective(M, q, k)
+            # independent evaluation of F for the identity
+            ent = -np.sum(np.where(M > 0, M * np.log(np.where(M > 0, M, 1)), 0))
+            F_direct = float(np.sum(M * S) + ent)
+            assert abs(F - F_direct) <= 1e-9 * max(1.0, abs(F))
+            kl = orc.row_kl(M, A)
+            assert np.all(kl >= -1e-12)
+            assert abs(F - (lse.sum() - kl.sum())) <= 1e-9 * max(1.0, abs(F))
+            assert F >= prev - 1e-10, (t, F, prev)
+            prev = F
+
+
+def check_steps_are_exact_maximisers(orc):
+    """Each half-step maximises F over its factor: compare the closed form with
+    a generic numerical maximisation (scipy L-BFGS over free logits)."""
+    from scipy.optimize import minimize
+    b1, b2, d = 3, 2, 4
+    N = b1 * b2
+    q, k, _ = _case(7, b1, b2, d)
+    s = 1.0 / math.sqrt(d)
+    S = s * (q @ k.T)
+    rng = np.random.default_rng(0)
+    t = 1
+    bounds = [0, b1]
+    R = orc.softmax(rng.standard_normal((t, b1, b2, b2)), axis=-1)
+    qb, kb = q.reshape(b1, b2, d), k.reshape(b1, b2, d)
+
+    def F_of(L, Rf):
+        M = np.empty((b1, b2, b1, b2))
+        for a1 in range(b1):
+            for a2 in range(b2):
+                for c1 in range(b1):
+                    M[a1, a2, c1] = L[a2, a1, c1] * Rf[0, c1, a2]
+        M = M.reshape(N, N)
+        ent = -np.sum(np.where(M > 0, M * np.log(np.where(M > 0, M, 1)), 0))
+        return float(np.sum(M * S) + ent)
+
+    def sm(z, shape):
+        z = z.reshape(shape)
+        z = z - z.max(axis=-1, keepdims=True)
+        e = np.exp(z)
+        return e / e.sum(axis=-1, keepdims=True)
+
+    L_closed, _ = orc.l_step(qb, kb, R, bounds, s)
+    res = minimize(lambda z: -F_of(sm(z, (b2, b1, b1)), R), np.zeros(b2 * b1 * b1),
+                   method="L-BFGS-B", options={"gtol": 1e-12, "ftol": 1e-15, "maxiter": 5000})
+    L_num = sm(res.x, (b2, b1, b1))
+    assert np.max(np.abs(L_num - L_closed)) <= 2e-5
+    assert F_of(L_closed, R) >= -res.fun - 1e-9
+
+    R_closed, _, _ = orc.r_step(qb, kb, L_closed, bounds, s)
+    res = minimize(lambda z: -F_of(L_closed, sm(z, (t, b1, b2, b2))), np.zeros(t * b1 * b2 * b2),
+                   method="L-BFGS-B", options={"gtol": 1e-12, "ftol": 1e-15, "maxiter": 5000})
+    R_num = sm(res.x, (t, b1, b2, b2))
+    assert np.max(np.abs(R_num - R_closed)) <= 2e-5
+    assert F_of(L_closed, R_closed) >= -res.fun - 1e-9
+
+
+def check_block_rank_at_most_tiles(orc):
+    """O7: block (a2, c1) of P M P^T has rank <= t; one tile's rows, rank 1."""
+    b1, b2, d = 8, 4, 8
+    q, k, v = _case(8, b1, b2, d)
+    for t in (1, 2, 4):
+        bounds = orc.tile_bounds(b1, t)
+        _, (L, R, _) = orc.monarch_head(q, k, v, b1, b2, t, 2, return_factors=True)
+        M = orc.dense_monarch_matrix(L, R, bounds).reshape(b1, b2, b1, b2)
+        for a2 in range(b2):
+            for c1 in range(b1):
+                blk = M[:, a2, c1, :]                     # rows a1, cols c2
+                sv = np.linalg.svd(blk, compute_uv=False)
+                assert np.sum(sv > 1e-12 * sv[0]) <= t
+                for g in range(t):
+                    sub = np.linalg.svd(blk[bounds[g]:bounds[g + 1]], compute_uv=False)
+                    assert np.sum(sub > 1e-12 * max(sub[0], 1e-300)) <= 1
+
+
+def check_kkt(orc):
+    """O11: log L - logits is constant along each L row; same for R."""
+    b1, b2, d = 6, 5, 8
+    q, k, _ = _case(9, b1, b2, d)
+    s = 1.0 / math.sqrt(d)
+    qb, kb = q.reshape(b1, b2, d), k.reshape(b1, b2, d)
+    bounds = orc.tile_bounds(b1, 2)
+    R = orc.uniform_R(b1, b2, 2)
+    for _ in range(2):
+        L, logits = orc.l_step(qb, kb, R, bounds, s)
+        gap = np.log(L) - logits
+        assert np.max(np.abs(gap - gap[..., :1])) <= 1e-12
+        assert np.max(np.abs(L.sum(-1) - 1)) <= 1e-12
+        R, q_hat, beta = orc.r_step(qb, kb, L, bounds, s)
+        rl = s * np.einsum("gcad,cpd->gcap", q_hat, kb)
+        gap = np.log(R) - rl
+        assert np.max(np.abs(gap - gap[..., :1])) <= 1e-12
+        # the aggregated query is the L-weighted mean of the tile's queries
+        g, c1, a2 = 1, 2, 3
+        lo, hi = bounds[g], bounds[g + 1]
+        w = L[a2, lo:hi, c1]
+        assert abs(beta[g, c1, a2] - w.sum()) <= 1e-14
+        assert np.max(np.abs(q_hat[g, c1, a2] - (w @ qb[lo:hi, a2]) / w.sum())) <= 1e-12
+
+
+def check_separable_positional_exact(orc):
+    """O8: logits that split into a (frame,row) part plus a column part are
+    reproduced exactly by aligned blocks in one iteration; a token shuffle
+    breaks it."""
+    from structured_attention_video_monarch_amd.inputs import positional_term
+    f, h, w, d = 2, 3, 4, 24
+    pos = positional_term(f, h, w, d, 1.0)
+    q = k = pos
+    rng = np.random.default_rng(10)
+    v = rng.standard_normal(pos.shape)
+    b1, b2 = f * h, w
+    dense = _sdpa(q, k, v)
+    y, (L, R, _) = orc.monarch_head(q, k, v, b1, b2, 1, 1, return_factors=True)
+    assert np.max(np.abs(y - dense)) <= 1e-10
+    M = orc.dense_monarch_matrix(L, R, [0, b1])
+    assert np.max(np.abs(orc.row_kl(M, _dense_A(q, k)))) <= 1e-10
+    perm = rng.permutation(q.shape[0])
+    qs, ks = q[perm], k[perm]
+    _, (L, R, _) = orc.monarch_head(qs, ks, v[perm], b1, b2, 1, 1, return_factors=True)
+    Ms = orc.dense_monarch_matrix(L, R, [0, b1])
+    assert orc.row_kl(Ms, _dense_A(qs, ks)).mean() >= 1e-4
+
+
+ALL_CHECKS = [
+    check_tile_bounds,
+    check_row_stochastic_and_dense_apply,
+    check_plain_monarch_product,
+    check_degenerate_blocks_are_dense_attention,
+    check_one_row_tiles,
+    check_zero_queries_uniform,
+    check_objective_ascent_and_identity,
+    check_steps_are_exact_maximisers,
+    check_block_rank_at_most_tiles,
+    check_kkt,
+    check_separable_positional_exact,
+]
