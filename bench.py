@@ -1,0 +1,230 @@
+"""Benchmark: MonarchAttention forward layer calls on one MI355X.
+
+One step = one full forward call (block-mean keys, T x (L-step, R-step),
+L-apply) over one batch of seeded synthetic Q/K/V already resident in HBM.
+Prints ONE JSON line with tokens/s (value), layer-calls/s, the roofline of the
+dominant kernel (timed with HIP events on the launch stream inside the timed
+region) and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload latent720p]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MonarchAttention fwd tokens/s & layer-calls/s at 1 MI355X; % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = ["structured_attention_video_monarch_amd/csrc/device_common.h",
+                  "structured_attention_video_monarch_amd/csrc/lside.h",
+                  "structured_attention_video_monarch_amd/csrc/rside.h",
+                  "structured_attention_video_monarch_amd/csrc/monarch_attn.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(wl, it_last=True):
+    """Per launch: (flops, bytes) each kernel must do by the method's definition.
+
+    Per (batch, head), e = element bytes, N = b1*b2:
+      k_kbar       0 flops;   bytes  N*d*e (read K) + b1*d*e (write means)
+      k_lse        2*N*b1*d   (L logits);          bytes N*d*e + 4N
+      k_aggregate  2*N*b1*d   (L^T q per tile);    bytes N*d*e + 4N + t*N*d*e
+      k_rstep      4*t*N*b2*d (R logits + R V);    bytes t*N*d*e (Qh) + 2*N*d*e (K,V) + t*N*d*e (U)
+      k_apply      2*N*b1*d   (L U);               bytes N*d*e + 4N + t*N*d*e + N*d*e
+    Logit recomputation in k_aggregate/k_apply is not counted (an
+    implementation choice, not part of the method).
+    """
+    e = 2 if wl.dtype == "bf16" else 4
+    BH, N, d, b1, b2, t = wl.B * wl.H, wl.N, wl.d, wl.b1, wl.b2, wl.tiles
+    nd = N * d * e
+    return {
+        "k_kbar": (0.0, BH * (nd + b1 * d * e)),
+        "k_lse": (BH * 2.0 * N * b1 * d, BH * (nd + 4 * N)),
+        "k_aggregate": (BH * 2.0 * N * b1 * d, BH * (nd + 4 * N + t * nd)),
+        "k_rstep": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 2 * nd)),
+        "k_apply": (BH * 2.0 * N * b1 * d, BH * (2 * nd + 4 * N + t * nd)),
+    }
+
+
+def roofline_entry(name, flops, nbytes, avg_s, dtype, traffic):
+    peak_f = (PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12
+    peak_b = PEAK_HBM_GBS * 1e9
+    if flops / peak_f >= nbytes / peak_b:
+        ach = flops / avg_s / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / (peak_f / 1e12), 4), "traffic": traffic}
+    ach = nbytes / avg_s / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seed, budget_s=30.0):
+    """The oracle as it is, on a bounded sample: whole heads, one at a time,
+    until about budget_s seconds have passed (at least one head)."""
+    import oracle
+    from structured_attention_video_monarch_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    done, spent = 0, 0.0
+    while done < wl.B * wl.H and (done == 0 or spent < budget_s):
+        b, h = divmod(done, wl.H)
+        x = I.make_inputs(wl.with_(B=1), seed, heads=[h], want_bits=False)
+        t0 = time.perf_counter()
+        oracle.monarch_head(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], wl.b1, wl.b2, wl.tiles, wl.iters)
+        spent += time.perf_counter() - t0
+        done += 1
+    per_call = spent / done * wl.B * wl.H
+    return {"value": round(wl.B * wl.N / per_call, 1), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} of {wl.B * wl.H} heads of one {wl.name} call, fp64 numpy oracle, "
+                      f"{spent:.1f} s; full call extrapolated as heads x per-head time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="latent720p")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the forward pass "
+              "has no multi-GPU path in this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import structured_attention_video_monarch_amd as M
+    from structured_attention_video_monarch_amd import inputs as I
+
+    wl = I.get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    x = I.make_inputs(wl, args.seed, want_f32=(wl.dtype == "f32"))
+    if wl.dtype == "bf16":
+        q, k, v = (torch.from_numpy(x[n + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+                   for n in "qkv")
+    else:
+        q, k, v = (torch.from_numpy(x[n]).to(dev) for n in "qkv")
+    del x
+    print(f"[bench] inputs {wl.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    out = torch.empty_like(q)
+    nb = M.monarch_attn_workspace_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2,
+                                        wl.tiles, wl.iters,
+                                        M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        M.monarch_attn_fwd_ws(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters,
+                              ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    M.monarch_attn_profile_collect()
+    M.monarch_attn_profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    M.monarch_attn_profile_enable(False)
+    per_kernel = M.monarch_attn_profile_collect()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    work = algorithmic_work(wl)
+    kernels = {}
+    for full, (ms, n) in per_kernel.items():
+        short = full.split(" ")[0]
+        if n:
+            kernels[short] = {"avg_ms": round(ms / n, 5), "launches_per_step": n / args.steps,
+                              "ms_per_step": round(ms / args.steps, 5)}
+    dom = max(kernels, key=lambda kname: kernels[kname]["ms_per_step"])
+    launches = kernels[dom]["launches_per_step"]
+    fl, by = work[dom]
+    # k_lse/k_aggregate/k_rstep run once per iteration: per-launch work is per iteration
+    roof = roofline_entry(dom, fl, by, kernels[dom]["avg_ms"] / 1e3, wl.dtype,
+                          read_traffic(dom, wl.name))
+    roof["launches_per_step"] = launches
+    for kname, rec in kernels.items():
+        f2, b2 = work[kname]
+        r = roofline_entry(kname, f2, b2, rec["avg_ms"] / 1e3, wl.dtype, None)
+        rec.update({"bound": r["bound"], "frac": r["frac"]})
+
+    total_flops = sum(work[kn][0] * kernels[kn]["launches_per_step"] for kn in kernels)
+    res = {
+        "metric": METRIC,
+        "value": round(wl.B * wl.N / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "f": wl.f, "h": wl.h, "w": wl.w,
+                   "N": wl.N, "d": wl.d, "b1": wl.b1, "b2": wl.b2, "tiles": wl.tiles,
+                   "iters": wl.iters, "spike_frac": wl.spike_frac},
+        "layer_calls_per_s": round(1e3 / ms_step, 2),
+        "path_alg_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
+        "path_frac_of_mfma_peak": round(total_flops / (ms_step / 1e3) / 1e12 /
+                                        (PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS), 4),
+        "roofline": roof,
+        "kernels": kernels,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

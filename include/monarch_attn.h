@@ -1,0 +1,118 @@
+/*
+ * monarch_attn.h -- C ABI of the MonarchAttention forward for AMD MI355X (gfx950).
+ *
+ * The operation (MonarchRT pages):
+ *   Video self-attention over N = f*h*w tokens is approximated by a Monarch
+ *   matrix M = P^T L P R: P is the fixed reshape-transpose permutation of the
+ *   token index, L and R are block-diagonal factors (yunpan.plus MonarchRT
+ *   article, section "Monarch matrices: a unified structured approximation
+ *   tool").  The factors are computed from Q and K by alternating block
+ *   softmax steps (MonarchAttention; same section, Fig. 3), with blocks
+ *   aligned to the video as (b1, b2) = (f*h, w) ("Innovation 1: block
+ *   alignment"), optionally split into independently factorised tiles along
+ *   the f*h axis ("Innovation 2: tiled Monarch parameterisation"), for a given
+ *   number of iterations ("Innovation 3: finetuning and efficient kernels").
+ *   The output is Y = M V, computed without forming the N x N matrix.
+ *
+ * Exact definition used (readings of points the pages leave open):
+ *   token n = a1*b2 + a2, key m = c1*b2 + c2, s = 1/sqrt(d);
+ *   tile g of a1: [floor(g*b1/t), floor((g+1)*b1/t));
+ *   R starts uniform; one iteration = L-step then R-step:
+ *     L-step: L[a2][a1,:] = softmax_c1( s<q_n, Kt[g,c1,a2]> + H(R[g,c1,a2,:]) ),
+ *             Kt[g,c1,a2] = sum_c2 R[g,c1,a2,c2] k_(c1,c2);
+ *     R-step: R[g,c1,a2,:] = softmax_c2( s<Qh[g,c1,a2], k_(c1,c2)> ),
+ *             Qh[g,c1,a2] = sum_(a1 in g) L[a2][a1,c1] q_(a1,a2) / sum_(a1 in g) L[a2][a1,c1]
+ *             (Qh = 0 when that sum is 0);
+ *   y_(a1,a2) = sum_c1 L[a2][a1,c1] sum_c2 R[g(a1),c1,a2,c2] v_(c1,c2).
+ *
+ * Layout: q, k, v, out are [B, H, N, d] contiguous, token order
+ *   n = (fi*h + hi)*w + wi (column fastest).  bf16 entry points take raw bf16
+ *   storage (2 bytes per element); f32 entry points take float.  All pointers
+ *   are DEVICE pointers owned by the caller; the library never frees or keeps
+ *   them past the call.  Everything is enqueued on `stream` (a hipStream_t;
+ *   NULL = the null stream) and the call returns without synchronising: the
+ *   caller keeps the buffers alive until the stream has run the work.
+ *
+ * Errors: every entry point returns a monarch_status.  Arguments are checked
+ *   before any GPU call; on MONARCH_EINVAL / MONARCH_EUNSUPPORTED nothing is
+ *   launched and `out` is untouched.  MONARCH_EHIP reports a HIP runtime
+ *   failure; monarch_attn_last_hip_error() gives its code.  The library never
+ *   prints or aborts.  NaN/Inf in the inputs propagate to the output.
+ *
+ * Supported envelope: d in {16, 32, 64, 128}; 1 <= b2 <= 128; any b1 >= 1;
+ *   b1*b2 == f*h*w; 1 <= tiles <= b1; iters >= 1; tiles*N*d < 2^31.
+ */
+#ifndef MONARCH_ATTN_H
+#define MONARCH_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MONARCH_OK = 0,
+    MONARCH_EINVAL = -1,        /* bad argument (NULL, aliasing, dims, blocks, tiles, iters) */
+    MONARCH_EUNSUPPORTED = -2,  /* valid but outside the kernels' envelope (d, b2, sizes) */
+    MONARCH_EHIP = -3,          /* a HIP runtime call failed */
+    MONARCH_ENOMEM = -4,        /* workspace allocation failed or workspace too small */
+} monarch_status;
+
+typedef enum {
+    MONARCH_BF16 = 0,           /* bf16 I/O; bf16 MFMA with fp32 accumulation and softmax */
+    MONARCH_F32 = 1,            /* fp32 I/O and fp32 arithmetic throughout */
+} monarch_dtype;
+
+/* Y = M V for bf16 q, k, v, out ([B,H,N,d], N = f*h*w).  (b1, b2) are the
+ * Monarch block sizes (b1*b2 == N; the aligned choice is (f*h, w)), `tiles`
+ * the number of tiles per aligned block along the f*h axis, `iters` the
+ * number of (L-step, R-step) iterations.  Allocates its workspace
+ * stream-ordered (hipMallocAsync/hipFreeAsync on `stream`). */
+int monarch_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                     int B, int H, int f, int h, int w, int d,
+                     int b1, int b2, int tiles, int iters, void* stream);
+
+/* Same operation with float I/O and float arithmetic. */
+int monarch_attn_fwd_f32(const float* q, const float* k, const float* v, float* out,
+                         int B, int H, int f, int h, int w, int d,
+                         int b1, int b2, int tiles, int iters, void* stream);
+
+/* Bytes of device workspace monarch_attn_fwd_ws needs for these arguments
+ * (0 if the arguments are invalid or unsupported). */
+size_t monarch_attn_workspace_bytes(int B, int H, int f, int h, int w, int d,
+                                    int b1, int b2, int tiles, int iters, int dtype);
+
+/* Same operation for either dtype with a caller-provided device workspace of
+ * at least monarch_attn_workspace_bytes(...) bytes (256-byte aligned).  The
+ * workspace must not overlap q, k, v or out; its contents on entry are
+ * ignored and on return are unspecified.  Returns MONARCH_ENOMEM when
+ * workspace_bytes is too small. */
+int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
+                        int B, int H, int f, int h, int w, int d,
+                        int b1, int b2, int tiles, int iters, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* monarch_attn_status_string(int status);
+
+/* hipError_t of the last MONARCH_EHIP on the calling thread (0 if none). */
+int monarch_attn_last_hip_error(void);
+
+/* ---- per-kernel timing (benchmarking aid; not thread-safe) ----
+ * While enabled, each kernel launch is bracketed by HIP events recorded on
+ * the launch stream.  monarch_attn_profile_collect waits for those events,
+ * adds each kernel's elapsed milliseconds and launch count into ms[i] and
+ * launches[i] for kernel id i < n, and forgets them.  Kernel ids:
+ * 0 block-mean keys, 1 L-row log-sum-exp, 2 R-side aggregation through L,
+ * 3 R-step block softmax (+ R V or next keys/entropy), 4 L-apply. */
+#define MONARCH_NUM_KERNELS 5
+int monarch_attn_profile_enable(int on);
+int monarch_attn_profile_collect(double* ms, long* launches, int n);
+const char* monarch_attn_kernel_name(int id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MONARCH_ATTN_H */

@@ -1,5 +1,177 @@
-"""MonarchAttention forward for MI355X (gfx950): Python binding.
+"""MonarchAttention forward for MI355X (gfx950): thin Python binding.
 
-The binding loads ``libmonarch_attn.so`` lazily, on first use, so that
-``structured_attention_video_monarch_amd.inputs`` can be imported without it.
+Every step of the computation runs in ``libmonarch_attn.so`` (HIP kernels for
+gfx950); this module only marshals arguments: device pointers of torch
+tensors, sizes, and the current HIP stream.  The C entry points are exposed
+under the same names.  If the library is missing or fails to load, every
+call raises: there is no fallback path.
+
+The library is loaded lazily, so ``structured_attention_video_monarch_amd.inputs``
+imports without it.
 """
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmonarch_attn.so")
+
+MONARCH_OK = 0
+MONARCH_EINVAL = -1
+MONARCH_EUNSUPPORTED = -2
+MONARCH_EHIP = -3
+MONARCH_ENOMEM = -4
+MONARCH_BF16 = 0
+MONARCH_F32 = 1
+MONARCH_NUM_KERNELS = 5
+
+_lib = None
+
+
+class MonarchError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _declare(lib):
+    c_int, c_void_p, c_size_t = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    dims = [c_int] * 10  # B, H, f, h, w, d, b1, b2, tiles, iters
+    lib.monarch_attn_fwd.argtypes = [c_void_p] * 4 + dims + [c_void_p]
+    lib.monarch_attn_fwd.restype = c_int
+    lib.monarch_attn_fwd_f32.argtypes = [c_void_p] * 4 + dims + [c_void_p]
+    lib.monarch_attn_fwd_f32.restype = c_int
+    lib.monarch_attn_workspace_bytes.argtypes = dims + [c_int]
+    lib.monarch_attn_workspace_bytes.restype = c_size_t
+    lib.monarch_attn_fwd_ws.argtypes = [c_void_p] * 4 + dims + [c_int, c_void_p, c_size_t, c_void_p]
+    lib.monarch_attn_fwd_ws.restype = c_int
+    lib.monarch_attn_status_string.argtypes = [c_int]
+    lib.monarch_attn_status_string.restype = ctypes.c_char_p
+    lib.monarch_attn_last_hip_error.argtypes = []
+    lib.monarch_attn_last_hip_error.restype = c_int
+    lib.monarch_attn_profile_enable.argtypes = [c_int]
+    lib.monarch_attn_profile_enable.restype = c_int
+    lib.monarch_attn_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                                 ctypes.POINTER(ctypes.c_long), c_int]
+    lib.monarch_attn_profile_collect.restype = c_int
+    lib.monarch_attn_kernel_name.argtypes = [c_int]
+    lib.monarch_attn_kernel_name.restype = ctypes.c_char_p
+    return lib
+
+
+def lib():
+    """The loaded C library (builds it first only if no built copy exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from .build import build_library
+            build_library()
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def monarch_attn_status_string(status: int) -> str:
+    return lib().monarch_attn_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != MONARCH_OK:
+        extra = ""
+        if rc == MONARCH_EHIP:
+            extra = f" (hipError {lib().monarch_attn_last_hip_error()})"
+        raise MonarchError(rc, f"{what}: {monarch_attn_status_string(rc)}{extra}")
+
+
+def _dims(q, f, h, w, b1, b2, tiles, iters):
+    if q.dim() != 4:
+        raise ValueError("q, k, v, out must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if f * h * w != N:
+        raise ValueError(f"f*h*w = {f * h * w} != N = {N}")
+    return [B, H, f, h, w, d, b1, b2, tiles, iters]
+
+
+def _tensors(q, k, v, out, dtype):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.shape != q.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
+    return [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def monarch_attn_fwd(q, k, v, out, f, h, w, b1, b2, tiles=1, iters=1, stream=None):
+    """bf16: out <- M V (in place), enqueued on ``stream`` (default: current)."""
+    import torch
+    ptrs = _tensors(q, k, v, out, torch.bfloat16)
+    _check(lib().monarch_attn_fwd(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, iters), _stream(stream)),
+           "monarch_attn_fwd")
+    return out
+
+
+def monarch_attn_fwd_f32(q, k, v, out, f, h, w, b1, b2, tiles=1, iters=1, stream=None):
+    """float32 variant of :func:`monarch_attn_fwd`."""
+    import torch
+    ptrs = _tensors(q, k, v, out, torch.float32)
+    _check(lib().monarch_attn_fwd_f32(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, iters), _stream(stream)),
+           "monarch_attn_fwd_f32")
+    return out
+
+
+def monarch_attn_workspace_bytes(B, H, f, h, w, d, b1, b2, tiles, iters, dtype=MONARCH_BF16) -> int:
+    return int(lib().monarch_attn_workspace_bytes(B, H, f, h, w, d, b1, b2, tiles, iters, dtype))
+
+
+def monarch_attn_fwd_ws(q, k, v, out, f, h, w, b1, b2, tiles, iters, workspace, stream=None):
+    """Either dtype, with a caller-provided workspace (a uint8 GPU tensor)."""
+    import torch
+    dtype = MONARCH_BF16 if q.dtype == torch.bfloat16 else MONARCH_F32
+    ptrs = _tensors(q, k, v, out, q.dtype)
+    if not workspace.is_cuda or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 GPU tensor")
+    nbytes = workspace.numel()
+    _check(lib().monarch_attn_fwd_ws(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, iters), dtype,
+                                     ctypes.c_void_p(workspace.data_ptr()), nbytes, _stream(stream)),
+           "monarch_attn_fwd_ws")
+    return out
+
+
+def monarch_attn(q, k, v, f, h, w, b1=None, b2=None, tiles=1, iters=1):
+    """Allocate the output and run the forward; aligned blocks by default."""
+    import torch
+    b1 = f * h if b1 is None else b1
+    b2 = w if b2 is None else b2
+    out = torch.empty_like(q)
+    if q.dtype == torch.bfloat16:
+        return monarch_attn_fwd(q, k, v, out, f, h, w, b1, b2, tiles, iters)
+    return monarch_attn_fwd_f32(q, k, v, out, f, h, w, b1, b2, tiles, iters)
+
+
+def monarch_attn_profile_enable(on: bool = True):
+    _check(lib().monarch_attn_profile_enable(1 if on else 0), "monarch_attn_profile_enable")
+
+
+def monarch_attn_profile_collect():
+    """{kernel name: (total ms, launches)} since the last collect."""
+    n = MONARCH_NUM_KERNELS
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_long * n)()
+    _check(lib().monarch_attn_profile_collect(ms, cnt, n), "monarch_attn_profile_collect")
+    return {monarch_attn_kernel_name(i): (ms[i], cnt[i]) for i in range(n)}
+
+
+def monarch_attn_kernel_name(i: int) -> str:
+    return lib().monarch_attn_kernel_name(int(i)).decode()

@@ -1,0 +1,200 @@
+// R-side kernel: everything indexed by a key block c1 (b2 consecutive tokens).
+//
+// For one (batch*head, c1) and every tile g the R block is
+//   R[g,c1,a2,:] = softmax_c2( s<Qh[g,c1,a2], k_(c1,c2)> ),   a2, c2 in [b2]
+// (the R-step of MonarchAttention; yunpan.plus MonarchRT article, section
+// "Monarch matrices", Fig. 3; one R per tile: "Innovation 2: tiled Monarch").
+// It is consumed at once and never stored:
+//   last iteration:  U[g,c1,a2,:]  = sum_c2 R v_(c1,c2)   (written over Qh)
+//   otherwise:       Kt[g,c1,a2,:] = sum_c2 R k_(c1,c2)   and the row entropy
+//                    H[g,c1,a2] = -sum_c2 R log R (in nats), the keys and bias
+//                    of the next L-step (the entropy computed alongside the
+//                    block softmax, as in the VMonarch abstract's fused
+//                    "online entropy").
+// The K and V blocks are contiguous (b2 x d) and staged in LDS once per
+// workgroup; each wave owns 16 rows a2 and all tiles are looped in-kernel.
+#pragma once
+
+#include "device_common.h"
+
+namespace monarch {
+
+struct RGeom {
+  int BH, b1, b2, t;
+  int b2p;    // b2 rounded up to 32
+  float c;    // log2(e) / sqrt(d)
+};
+
+template <typename T>
+__host__ __device__ constexpr int rside_pitch(int D) { return (D < 32 ? 32 : D) + Elem<T>::kPad; }
+
+template <typename T>
+__host__ __device__ constexpr int rside_pitcht(int b2p) { return b2p + Elem<T>::kPad; }
+
+// Dynamic LDS bytes: K row-major [b2p][pitch] + one transposed [D][pitcht]
+// (V^T for the last iteration, K^T otherwise).
+template <typename T>
+inline size_t rside_lds_bytes(int D, int b2p) {
+  return sizeof(T) * (static_cast<size_t>(b2p) * rside_pitch<T>(D) +
+                      static_cast<size_t>(D) * rside_pitcht<T>(b2p));
+}
+
+template <typename T, int D, bool LAST>
+__global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T* __restrict__ v,
+                                               T* qhat,   // [BH][t][b1][b2][D]; U written over it when LAST
+                                               T* __restrict__ ktil, float* __restrict__ hent,
+                                               RGeom p) {
+  using E = Elem<T>;
+  constexpr int DK = D < 32 ? 32 : D;
+  constexpr int KS = DK / 32;
+  constexpr int PITCH = DK + E::kPad;
+  constexpr int NDP = D / 32;
+  constexpr int NACC = NDP > 0 ? NDP : 1;
+  constexpr int MAXCP = 4;  // b2 <= 128
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* sK = reinterpret_cast<T*>(smem_raw);
+  T* sXT = sK + p.b2p * PITCH;
+  const int pitcht = p.b2p + E::kPad;
+  const int nt = blockDim.x;
+
+  const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
+  const int c1 = item % p.b1;
+  const int bh = item / p.b1;
+  const long long blk = static_cast<long long>(item) * p.b2 * D;  // first element of block c1
+
+  // stage K (row-major) and V^T or K^T
+  {
+    constexpr int V = E::kVec;
+    constexpr int VPR = DK / V;
+    for (int idx = threadIdx.x; idx < p.b2p * VPR; idx += nt) {
+      const int r = idx / VPR, col = (idx % VPR) * V;
+      uint4 val = {0u, 0u, 0u, 0u};
+      if (r < p.b2 && col < D) val = *reinterpret_cast<const uint4*>(k + blk + r * D + col);
+      *reinterpret_cast<uint4*>(sK + r * PITCH + col) = val;
+    }
+    const T* xs = LAST ? v : k;
+    constexpr int VPRT = D / V;
+    for (int idx = threadIdx.x; idx < p.b2p * VPRT; idx += nt) {
+      const int r = idx / VPRT, col = (idx % VPRT) * V;
+      uint4 val = {0u, 0u, 0u, 0u};
+      if (r < p.b2) val = *reinterpret_cast<const uint4*>(xs + blk + r * D + col);
+      const T* e = reinterpret_cast<const T*>(&val);
+#pragma unroll
+      for (int j = 0; j < V; ++j) sXT[(col + j) * pitcht + r] = e[j];
+    }
+  }
+  __syncthreads();
+
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int l16 = lane & 15, G = lane >> 4;
+  const int a2 = wave * 16 + l16;
+  const bool row_ok = a2 < p.b2;
+  const int ncp = p.b2p / 32;
+
+  for (int g = 0; g < p.t; ++g) {
+    const long long row = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
+    typename E::frag bq[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int col = s * 32 + 8 * G;
+      bq[s] = (row_ok && col < D) ? E::load(qhat + row * D + col) : E::zero();
+    }
+    // logits, transposed: rows c2 (permuted within 32-blocks), columns a2
+    f32x4 S[MAXCP][2];
+#pragma unroll
+    for (int cp = 0; cp < MAXCP; ++cp) {
+      S[cp][0] = f32x4{0, 0, 0, 0};
+      S[cp][1] = f32x4{0, 0, 0, 0};
+      if (cp < ncp) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const typename E::frag a = E::load(sK + (32 * cp + perm_row(ct, l16)) * PITCH + s * 32 + 8 * G);
+            S[cp][ct] = E::mma(a, bq[s], S[cp][ct]);
+          }
+      }
+    }
+    // softmax over c2 for column a2 = l16 (+16*wave): lane holds c2 = 32cp + 8G + j
+    float x[MAXCP][8];
+    float mx = -1e30f;
+#pragma unroll
+    for (int cp = 0; cp < MAXCP; ++cp)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c2 = 32 * cp + 8 * G + j;
+        x[cp][j] = (cp < ncp && c2 < p.b2) ? S[cp][j >> 2][j & 3] * p.c : kNegInf;
+        mx = fmaxf(mx, x[cp][j]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float sum = 0.0f;
+#pragma unroll
+    for (int cp = 0; cp < MAXCP; ++cp)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += fast_exp2(x[cp][j] - mx);
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    const float lse2 = mx + log2f(sum);
+    typename E::frag pf[MAXCP];
+    float rx = 0.0f;  // sum_c2 R * x (log2 units), for the entropy
+#pragma unroll
+    for (int cp = 0; cp < MAXCP; ++cp) {
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        w[j] = fast_exp2(x[cp][j] - lse2);
+        if (!LAST && w[j] > 0.0f) rx += w[j] * x[cp][j];
+      }
+      pf[cp] = E::pack(w);
+    }
+    // X^T P^T: rows d (permuted within 32-blocks), columns a2
+    f32x4 acc[NACC][2];
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp) {
+      acc[dp][0] = f32x4{0, 0, 0, 0};
+      acc[dp][1] = f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int cp = 0; cp < MAXCP; ++cp) {
+      if (cp >= ncp) break;
+      if (NDP > 0) {
+#pragma unroll
+        for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const typename E::frag a = E::load(sXT + (32 * dp + perm_row(dt, l16)) * pitcht + 32 * cp + 8 * G);
+            acc[dp][dt] = E::mma(a, pf[cp], acc[dp][dt]);
+          }
+      } else {
+        const typename E::frag a = E::load(sXT + l16 * pitcht + 32 * cp + 8 * G);
+        acc[0][0] = E::mma(a, pf[cp], acc[0][0]);
+      }
+    }
+    if (row_ok) {
+      T* dst = (LAST ? qhat : ktil) + row * D;
+      if (NDP > 0) {
+#pragma unroll
+        for (int dp = 0; dp < NACC; ++dp) {
+          float o[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[j] = acc[dp][j >> 2][j & 3];
+          E::store8(dst + 32 * dp + 8 * G, o);
+        }
+      } else {
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = acc[0][0][i];
+        E::store4(dst + 4 * G, o);
+      }
+    }
+    if (!LAST) {
+      rx += __shfl_xor(rx, 16);
+      rx += __shfl_xor(rx, 32);
+      // H = ln(sum e^x) - sum R x, here from log2 quantities: H = (lse2 - sum R x2) * ln 2
+      if (row_ok && G == 0) hent[row] = (lse2 - rx) * 0.69314718055994531f;
+    }
+  }
+}
+
+}  // namespace monarch

@@ -1,0 +1,156 @@
+"""GPU path against the CPU oracle, element by element (needs an MI355X).
+
+Inputs are the seeded workloads (the oracle reads the same bf16-rounded
+values the GPU reads).  Bars: bf16 I/O max-abs <= 2e-2 and mean-abs <= 2e-3,
+fp32 I/O max-abs <= 1e-5, on every output element of the heads compared.
+Large workloads run whole on the GPU, in the launch configuration the
+benchmark uses, and the oracle checks a subset of heads (heads are
+independent, so each compared head is exact parity for that head).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, errors, say, to_device, to_host
+from structured_attention_video_monarch_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_gpu(wl, x):
+    import structured_attention_video_monarch_amd as M
+    q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
+    out = torch.empty_like(q)
+    fn = M.monarch_attn_fwd if wl.dtype == "bf16" else M.monarch_attn_fwd_f32
+    fn(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def compare(wl, seed=0, heads=None, label=""):
+    say(f"[case] {label or wl.name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} blocks=({wl.b1},{wl.b2}) "
+        f"t={wl.tiles} T={wl.iters} {wl.dtype} seed={seed}")
+    x = I.make_inputs(wl, seed)
+    y = run_gpu(wl, x)
+    assert np.all(np.isfinite(y))
+    heads = range(wl.H) if heads is None else heads
+    worst = (0.0, 0.0)
+    for b in range(wl.B):
+        for h in heads:
+            ref = oracle.monarch_head(x["q"][b, h], x["k"][b, h], x["v"][b, h],
+                                      wl.b1, wl.b2, wl.tiles, wl.iters)
+            mx, mean = errors(y[b, h], ref)
+            worst = (max(worst[0], mx), max(worst[1], mean))
+            if wl.dtype == "bf16":
+                assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (b, h, mx, mean)
+            else:
+                assert mx <= F32_MAX_ABS, (b, h, mx)
+    say(f"[ok] {label or wl.name}: max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e}")
+    return worst
+
+
+def test_tiny_f32():
+    compare(I.get_workload("tiny"))
+
+
+def test_chunk480p_bf16_all_heads():
+    compare(I.get_workload("chunk480p"))
+
+
+def test_chunk480p_f32():
+    compare(I.get_workload("chunk480p").with_(H=3, dtype="f32"), label="chunk480p-f32")
+
+
+def test_clip480p_bf16():
+    compare(I.get_workload("clip480p"), heads=[0, 6, 11])
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+@pytest.mark.parametrize("T", [1, 2])
+def test_clip480p_spikes_sweep(t, T):
+    compare(I.get_workload(f"clip480p_spikes_t{t}_T{T}"), heads=[0, 11])
+
+
+def test_latent720p_bf16():
+    compare(I.get_workload("latent720p"), heads=[0, 19, 39])
+
+
+# ragged and degenerate shapes: partial 32-row chunks and 16-row tiles, odd
+# block sizes, one-row tiles, blocks that are not the aligned ones, B > 1.
+EDGE = [
+    # name, B, H, d, f, h, w, b1, b2, t, T, dtype
+    ("b2_1_dense_rows", 1, 2, 64, 2, 5, 7, 70, 1, 1, 1, "bf16"),
+    ("b1_1_dense_cols", 1, 2, 64, 1, 1, 100, 1, 100, 1, 2, "bf16"),
+    ("odd_blocks", 2, 3, 32, 3, 7, 13, 21, 13, 2, 1, "bf16"),
+    ("one_row_tiles", 1, 2, 128, 2, 3, 10, 6, 10, 6, 2, "bf16"),
+    ("misaligned_blocks", 1, 2, 128, 4, 6, 8, 48, 4, 3, 2, "bf16"),
+    ("b2_128", 1, 1, 128, 2, 2, 128, 4, 128, 1, 1, "bf16"),
+    ("b2_17_d16", 1, 3, 16, 5, 7, 17, 35, 17, 4, 3, "bf16"),
+    ("ragged_f32", 2, 2, 64, 3, 11, 9, 33, 9, 5, 2, "f32"),
+    ("d32_f32", 1, 2, 32, 2, 9, 20, 18, 20, 2, 1, "f32"),
+    ("d128_f32_T3", 1, 1, 128, 3, 5, 24, 15, 24, 3, 3, "f32"),
+    ("b1_big_ragged", 1, 1, 128, 7, 37, 3, 259, 3, 3, 1, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_shapes(case):
+    name, B, H, d, f, h, w, b1, b2, t, T, dt = case
+    wl = I.Workload(name, B, H, d, f, h, w, b1, b2, t, T, dt)
+    compare(wl, seed=3, label=name)
+
+
+def test_zero_queries_give_mean_of_values():
+    wl = I.get_workload("chunk480p").with_(H=2)
+    x = I.make_inputs(wl, 0)
+    x["q_bits"][:] = 0
+    y = run_gpu(wl, x)
+    ref = x["v"].astype(np.float64).mean(axis=2, keepdims=True)
+    assert np.max(np.abs(y - ref)) <= 4e-3
+
+
+def test_deterministic_and_ws_variant_matches():
+    import structured_attention_video_monarch_amd as M
+    wl = I.get_workload("clip480p").with_(H=2)
+    x = I.make_inputs(wl, 1)
+    q, k, v = (to_device(x, n, "bf16") for n in "qkv")
+    o1, o2, o3 = (torch.empty_like(q) for _ in range(3))
+    args = (wl.f, wl.h, wl.w, wl.b1, wl.b2, 2, 2)
+    M.monarch_attn_fwd(q, k, v, o1, *args)
+    M.monarch_attn_fwd(q, k, v, o2, *args)
+    nb = M.monarch_attn_workspace_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, 2, 2)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    M.monarch_attn_fwd_ws(q, k, v, o3, *args, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_errors_launch_nothing():
+    import structured_attention_video_monarch_amd as M
+    wl = I.get_workload("chunk480p").with_(H=1)
+    x = I.make_inputs(wl, 0)
+    q, k, v = (to_device(x, n, "bf16") for n in "qkv")
+    out = torch.full_like(q, 7.0)
+    with pytest.raises(M.MonarchError) as e:
+        M.monarch_attn_fwd(q, k, v, out, wl.f, wl.h, wl.w, 91, 52, 1, 1)   # b1*b2 != N
+    assert e.value.status == M.MONARCH_EINVAL
+    with pytest.raises(M.MonarchError) as e:
+        M.monarch_attn_fwd(q, k, v, out, wl.f, wl.h, wl.w, 90, 52, 91, 1)  # tiles > b1
+    assert e.value.status == M.MONARCH_EINVAL
+    with pytest.raises(M.MonarchError) as e:
+        M.monarch_attn_fwd(q, k, v, q, wl.f, wl.h, wl.w, 90, 52, 1, 1)     # out aliases q
+    assert e.value.status == M.MONARCH_EINVAL
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(M.MonarchError) as e:
+        M.monarch_attn_fwd_ws(q, k, v, out, wl.f, wl.h, wl.w, 90, 52, 1, 1, ws)
+    assert e.value.status == M.MONARCH_ENOMEM
+    torch.cuda.synchronize()
+    assert bool((out.float() == 7.0).all())
