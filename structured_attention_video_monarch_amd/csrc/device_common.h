@@ -70,6 +70,23 @@ template <> struct Elem<bf16_t> {
   }
   // the value a fragment slot holds, as float (for sums of rounded weights)
   __device__ static inline float slot(const frag& f, int j) { return static_cast<float>(f[j]); }
+  // Fragment whose contraction index runs down the rows of a row-major LDS
+  // tile: lane (G, i) gets tile[k0 + 8G + j][cbase + cstride*(i/4) + i%4],
+  // j = 0..7.  Two ds_read_b64_tr_b16: within each 16-lane block, output lane
+  // i, element j is element i%4 of the 8 bytes addressed by lane 4j + i/4.
+  __device__ static inline frag load_tr(const bf16_t* tile, int pitch, int k0, int cbase,
+                                        int cstride) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const int l = threadIdx.x & 63;
+    const int i = l & 15, G = l >> 4;
+    const bf16_t* p = tile + (k0 + 8 * G + (i >> 2)) * pitch + cbase + cstride * (i & 3);
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * pitch));
+    const v8i16 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(frag, r);
+  }
 };
 
 template <> struct Elem<float> {
@@ -106,6 +123,20 @@ template <> struct Elem<float> {
     *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
   }
   __device__ static inline float slot(const frag& f, int j) { return j < 4 ? f.lo[j] : f.hi[j - 4]; }
+  // Same contract as the bf16 version, with plain LDS reads.
+  __device__ static inline frag load_tr(const float* tile, int pitch, int k0, int cbase,
+                                        int cstride) {
+    const int l = threadIdx.x & 63;
+    const int i = l & 15, G = l >> 4;
+    const float* p = tile + (k0 + 8 * G) * pitch + cbase + cstride * (i >> 2) + (i & 3);
+    frag r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.lo[j] = p[j * pitch];
+      r.hi[j] = p[(4 + j) * pitch];
+    }
+    return r;
+  }
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -130,34 +161,37 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
-// Copy `rows` rows of D elements (global row stride `rstride` elements) into
-// LDS row-major with pitch `pitch`; rows >= nvalid and columns >= D (up to DK)
-// are zero.
+// Register-staged copy of a ROWS x DK tile (row stride `rstride` elements in
+// global memory) into an LDS tile of pitch `pitch`.  load() issues the global
+// reads; store() writes them to LDS, so a caller can compute on one LDS
+// buffer while the next tile is in flight.  Rows >= nvalid and columns >= D
+// (up to DK) are zero.
 template <typename T, int D, int DK, int ROWS, int NT>
-__device__ inline void stage_rows(T* lds, int pitch, const T* g, long long rstride, int nvalid) {
-  constexpr int V = Elem<T>::kVec;
-  constexpr int VPR = DK / V;
-  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
-    const int r = idx / VPR, c = (idx % VPR) * V;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (r < nvalid && c < D) val = *reinterpret_cast<const uint4*>(g + r * rstride + c);
-    *reinterpret_cast<uint4*>(lds + r * pitch + c) = val;
-  }
-}
-
-// Copy `rows` rows of D elements into LDS transposed: ldsT[d * pitchT + r].
-template <typename T, int D, int ROWS, int NT>
-__device__ inline void stage_rows_T(T* ldsT, int pitchT, const T* g, long long rstride, int nvalid) {
-  constexpr int V = Elem<T>::kVec;
-  constexpr int VPR = D / V;
-  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
-    const int r = idx / VPR, c = (idx % VPR) * V;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (r < nvalid) val = *reinterpret_cast<const uint4*>(g + r * rstride + c);
-    const T* e = reinterpret_cast<const T*>(&val);
+struct TileLoader {
+  static constexpr int V = Elem<T>::kVec;
+  static constexpr int VPR = DK / V;
+  static constexpr int TOTAL = ROWS * VPR;
+  static constexpr int PER = (TOTAL + NT - 1) / NT;
+  uint4 buf[PER];
+  __device__ inline void load(const T* g, long long rstride, int nvalid) {
 #pragma unroll
-    for (int j = 0; j < V; ++j) ldsT[(c + j) * pitchT + r] = e[j];
+    for (int u = 0; u < PER; ++u) {
+      const int idx = threadIdx.x + u * NT;
+      const int r = idx / VPR, c = (idx % VPR) * V;
+      buf[u] = uint4{0u, 0u, 0u, 0u};
+      if ((TOTAL % NT == 0 || idx < TOTAL) && r < nvalid && c < D)
+        buf[u] = *reinterpret_cast<const uint4*>(g + r * rstride + c);
+    }
   }
-}
+  __device__ inline void store(T* lds, int pitch) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = threadIdx.x + u * NT;
+      if (TOTAL % NT != 0 && idx >= TOTAL) break;
+      const int r = idx / VPR, c = (idx % VPR) * V;
+      *reinterpret_cast<uint4*>(lds + r * pitch + c) = buf[u];
+    }
+  }
+};
 
 }  // namespace monarch

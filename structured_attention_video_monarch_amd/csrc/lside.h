@@ -73,6 +73,37 @@ struct ColItem {
   }
 };
 
+// Fragment of the transposed tile for output columns of d-tile pair dp, half
+// dt (pair mode: 8 consecutive d per lane after the product) or the single
+// 16-wide d tile (D == 16).
+template <typename T, int D>
+__device__ inline typename Elem<T>::frag load_vals_tr(const T* tile, int pitch, int k0, int dp,
+                                                      int dt) {
+  if (D >= 32) return Elem<T>::load_tr(tile, pitch, k0, 32 * dp + 4 * dt, 8);
+  return Elem<T>::load_tr(tile, pitch, k0, 0, 4);
+}
+
+// Store 8 (pair mode) or 4 (D == 16) consecutive outputs of lane group G.
+template <typename T, int D, int NACC, int RW>
+__device__ inline void store_rows(T* dst, const f32x4 (&acc)[NACC][2][RW], int rt, float scale,
+                                  int G) {
+  using E = Elem<T>;
+  if (D >= 32) {
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = acc[dp][j >> 2][rt][j & 3] * scale;
+      E::store8(dst + 32 * dp + 8 * G, v);
+    }
+  } else {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = acc[0][0][rt][i] * scale;
+    E::store4(dst + 4 * G, v);
+  }
+}
+
 // ------------------------------------------------------------------ k_lse --
 // CONTIG: rows are consecutive tokens of a head (only with BCAST keys, where
 // the logits do not depend on the column or tile).
@@ -87,8 +118,8 @@ __global__ __launch_bounds__(NW * kWave) void k_lse(const T* __restrict__ q,
   constexpr int PITCH = DK + E::kPad;
   constexpr int RB = NW * RW * 16;
   constexpr int NT = NW * kWave;
-  __shared__ __align__(16) T sK[32 * PITCH];
-  __shared__ float sBias[32];
+  __shared__ __align__(16) T sK[2][32 * PITCH];
+  __shared__ float sBias[2][32];
 
   int bh, g = 0, a2 = 0, nrows;
   long long n0, nstride;
@@ -127,14 +158,22 @@ __global__ __launch_bounds__(NW * kWave) void k_lse(const T* __restrict__ q,
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) { m[rt] = -1e30f; l[rt] = 0.0f; }
 
+  TileLoader<T, D, DK, 32, NT> ld;
   const int nch = (p.b1 + 31) / 32;
+  float bpre = 0.0f;
+  ld.load(ks.k, ks.kstride, p.b1);
+  if (threadIdx.x < 32) bpre = ks.bias(threadIdx.x, p.b1);
+  ld.store(sK[0], PITCH);
+  if (threadIdx.x < 32) sBias[0][threadIdx.x] = bpre;
+  __syncthreads();
   for (int ch = 0; ch < nch; ++ch) {
-    const int c1_0 = ch * 32;
-    __syncthreads();
-    stage_rows<T, D, DK, 32, NT>(sK, PITCH, ks.k + c1_0 * ks.kstride, ks.kstride, p.b1 - c1_0);
-    if (threadIdx.x < 32) sBias[threadIdx.x] = ks.bias(c1_0 + threadIdx.x, p.b1);
-    __syncthreads();
-
+    const int cur = ch & 1;
+    const bool more = ch + 1 < nch;
+    if (more) {
+      const int c1n = (ch + 1) * 32;
+      ld.load(ks.k + c1n * ks.kstride, ks.kstride, p.b1 - c1n);
+      if (threadIdx.x < 32) bpre = ks.bias(c1n + threadIdx.x, p.b1);
+    }
     f32x4 S[2][RW];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
@@ -144,21 +183,21 @@ __global__ __launch_bounds__(NW * kWave) void k_lse(const T* __restrict__ q,
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const typename E::frag a = E::load(sK + perm_row(ct, l16) * PITCH + s * 32 + 8 * G);
+        const typename E::frag a = E::load(sK[cur] + perm_row(ct, l16) * PITCH + s * 32 + 8 * G);
 #pragma unroll
         for (int rt = 0; rt < RW; ++rt) S[ct][rt] = E::mma(a, bq[rt][s], S[ct][rt]);
       }
     }
     float bias[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bias[j] = sBias[8 * G + j];
+    for (int j = 0; j < 8; ++j) bias[j] = sBias[cur][8 * G + j];
 #pragma unroll
     for (int rt = 0; rt < RW; ++rt) {
       float x[8];
       float cm = -1e30f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        x[j] = S[j >> 2][rt][j & 3] * p.c + bias[j];
+        x[j] = __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
         cm = fmaxf(cm, x[j]);
       }
       const float mn = fmaxf(m[rt], cm);
@@ -168,6 +207,11 @@ __global__ __launch_bounds__(NW * kWave) void k_lse(const T* __restrict__ q,
       l[rt] = acc;
       m[rt] = mn;
     }
+    if (more) {
+      ld.store(sK[cur ^ 1], PITCH);
+      if (threadIdx.x < 32) sBias[cur ^ 1][threadIdx.x] = bpre;
+    }
+    __syncthreads();
   }
 
 #pragma unroll
@@ -189,8 +233,9 @@ __global__ __launch_bounds__(NW * kWave) void k_lse(const T* __restrict__ q,
 // ------------------------------------------------------------ k_aggregate --
 // One workgroup: (bh, g, a2) and a block of CB = NW*RW*16 key blocks c1.
 // Qh[c1,:] = sum_(a1 in g) L[a1,c1] q_a1 / sum_(a1 in g) L[a1,c1], computed as
-// Qh^T = q^T P over chunks of 32 rows a1 (q staged in LDS twice: row-major
-// for the logits and transposed for the weighted sum).
+// Qh^T = q^T P over chunks of 32 rows a1.  q is staged once, row-major: the
+// logits read it by rows, the weighted sum reads it by columns (transposing
+// LDS reads).
 template <typename T, int D, int RW, int NW, bool BCAST>
 __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ q,
                                                           const T* __restrict__ kt,
@@ -201,13 +246,12 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ 
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
   constexpr int PITCH = DK + E::kPad;
-  constexpr int PITCHT = 32 + E::kPad;
   constexpr int CB = NW * RW * 16;
   constexpr int NT = NW * kWave;
   constexpr int NDP = D / 32;  // pairs of 16-wide d tiles (0 when D == 16)
-  __shared__ __align__(16) T sQ[32 * PITCH];
-  __shared__ __align__(16) T sQT[D * PITCHT];
-  __shared__ float sL[32];
+  constexpr int NACC = NDP > 0 ? NDP : 1;
+  __shared__ __align__(16) T sQ[2][32 * PITCH];
+  __shared__ float sL[2][32];
 
   // decode (bh, g, a2, cb)
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -236,7 +280,6 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ 
     bias[rt] = ks.bias(c1, p.b1);
   }
 
-  constexpr int NACC = NDP > 0 ? NDP : 1;
   f32x4 acc[NACC][2][RW];
 #pragma unroll
   for (int dp = 0; dp < NACC; ++dp)
@@ -252,15 +295,25 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ 
   const float* lh = lse + static_cast<long long>(bh) * p.N;
   const long long qstride = static_cast<long long>(p.b2) * D;
   const int nrows = hi - lo;
-  for (int r0 = 0; r0 < nrows; r0 += 32) {
-    const long long n_first = static_cast<long long>(lo + r0) * p.b2 + a2;
-    const int nvalid = nrows - r0;
-    __syncthreads();
-    stage_rows<T, D, DK, 32, NT>(sQ, PITCH, qh + n_first * D, qstride, nvalid);
-    stage_rows_T<T, D, 32, NT>(sQT, PITCHT, qh + n_first * D, qstride, nvalid);
+  const int nch = (nrows + 31) / 32;
+  TileLoader<T, D, DK, 32, NT> ld;
+  float lpre = 0.0f;
+  auto fetch = [&](int ch) {
+    const long long n_first = static_cast<long long>(lo + ch * 32) * p.b2 + a2;
+    const int nvalid = nrows - ch * 32;
+    ld.load(qh + n_first * D, qstride, nvalid);
     if (threadIdx.x < 32)
-      sL[threadIdx.x] = threadIdx.x < nvalid ? lh[n_first + threadIdx.x * static_cast<long long>(p.b2)] : kPosInf;
-    __syncthreads();
+      lpre = static_cast<int>(threadIdx.x) < nvalid ? lh[n_first + threadIdx.x * static_cast<long long>(p.b2)]
+                                                    : kPosInf;
+  };
+  fetch(0);
+  ld.store(sQ[0], PITCH);
+  if (threadIdx.x < 32) sL[0][threadIdx.x] = lpre;
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int cur = ch & 1;
+    const bool more = ch + 1 < nch;
+    if (more) fetch(ch + 1);
 
     f32x4 S[2][RW];
 #pragma unroll
@@ -271,40 +324,39 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ 
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int at = 0; at < 2; ++at) {
-        const typename E::frag a = E::load(sQ + perm_row(at, l16) * PITCH + s * 32 + 8 * G);
+        const typename E::frag a = E::load(sQ[cur] + perm_row(at, l16) * PITCH + s * 32 + 8 * G);
 #pragma unroll
         for (int rt = 0; rt < RW; ++rt) S[at][rt] = E::mma(a, bk[rt][s], S[at][rt]);
       }
     }
     float lrow[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lrow[j] = sL[8 * G + j];
+    for (int j = 0; j < 8; ++j) lrow[j] = sL[cur][8 * G + j];
     typename E::frag pf[RW];
 #pragma unroll
     for (int rt = 0; rt < RW; ++rt) {
       float w[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = fast_exp2(S[j >> 2][rt][j & 3] * p.c + bias[rt] - lrow[j]);
+      for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[rt] - lrow[j]));
       pf[rt] = E::pack(w);
       float sb = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) sb += E::slot(pf[rt], j);
       beta[rt] += sb;
     }
-    if (NDP > 0) {
 #pragma unroll
-      for (int dp = 0; dp < NACC; ++dp)
+    for (int dp = 0; dp < NACC; ++dp)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const typename E::frag a = E::load(sQT + (32 * dp + perm_row(dt, l16)) * PITCHT + 8 * G);
+      for (int dt = 0; dt < (NDP > 0 ? 2 : 1); ++dt) {
+        const typename E::frag a = load_vals_tr<T, D>(sQ[cur], PITCH, 0, dp, dt);
 #pragma unroll
-          for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = E::mma(a, pf[rt], acc[dp][dt][rt]);
-        }
-    } else {
-      const typename E::frag a = E::load(sQT + l16 * PITCHT + 8 * G);
-#pragma unroll
-      for (int rt = 0; rt < RW; ++rt) acc[0][0][rt] = E::mma(a, pf[rt], acc[0][0][rt]);
+        for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = E::mma(a, pf[rt], acc[dp][dt][rt]);
+      }
+    if (more) {
+      ld.store(sQ[cur ^ 1], PITCH);
+      if (threadIdx.x < 32) sL[cur ^ 1][threadIdx.x] = lpre;
     }
+    __syncthreads();
   }
 
 #pragma unroll
@@ -316,20 +368,7 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ 
     const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
     if (c1 >= p.b1) continue;
     T* dst = qhat + ((((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2) * D);
-    if (NDP > 0) {
-#pragma unroll
-      for (int dp = 0; dp < NACC; ++dp) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = acc[dp][j >> 2][rt][j & 3] * inv;
-        E::store8(dst + 32 * dp + 8 * G, v);
-      }
-    } else {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[0][0][rt][i] * inv;
-      E::store4(dst + 4 * G, v);
-    }
+    store_rows<T, D, NACC, RW>(dst, acc, rt, inv, G);
   }
 }
 
@@ -348,13 +387,13 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
   constexpr int PITCH = DK + E::kPad;
-  constexpr int PITCHT = 32 + E::kPad;
   constexpr int RB = NW * RW * 16;
   constexpr int NT = NW * kWave;
   constexpr int NDP = D / 32;
-  __shared__ __align__(16) T sK[32 * PITCH];
-  __shared__ __align__(16) T sUT[D * PITCHT];
-  __shared__ float sBias[32];
+  constexpr int NACC = NDP > 0 ? NDP : 1;
+  __shared__ __align__(16) T sK[2][32 * PITCH];
+  __shared__ __align__(16) T sU[2][32 * PITCH];
+  __shared__ float sBias[2][32];
 
   ColItem it(p, RB);
   if (it.nrows <= 0) return;
@@ -384,7 +423,6 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
     lrow[rt] = ok ? lh[n0 + r * nstride] : 0.0f;
   }
 
-  constexpr int NACC = NDP > 0 ? NDP : 1;
   f32x4 acc[NACC][2][RW];
 #pragma unroll
   for (int dp = 0; dp < NACC; ++dp)
@@ -393,14 +431,28 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
 
+  TileLoader<T, D, DK, 32, NT> ldk;
+  TileLoader<T, D, D, 32, NT> ldu;
+  float bpre = 0.0f;
   const int nch = (p.b1 + 31) / 32;
-  for (int ch = 0; ch < nch; ++ch) {
+  auto fetch = [&](int ch) {
     const int c1_0 = ch * 32;
-    __syncthreads();
-    stage_rows<T, D, DK, 32, NT>(sK, PITCH, ks.k + c1_0 * ks.kstride, ks.kstride, p.b1 - c1_0);
-    stage_rows_T<T, D, 32, NT>(sUT, PITCHT, ucol + c1_0 * ustride, ustride, p.b1 - c1_0);
-    if (threadIdx.x < 32) sBias[threadIdx.x] = ks.bias(c1_0 + threadIdx.x, p.b1);
-    __syncthreads();
+    ldk.load(ks.k + c1_0 * ks.kstride, ks.kstride, p.b1 - c1_0);
+    ldu.load(ucol + c1_0 * ustride, ustride, p.b1 - c1_0);
+    if (threadIdx.x < 32) bpre = ks.bias(c1_0 + threadIdx.x, p.b1);
+  };
+  auto put = [&](int buf) {
+    ldk.store(sK[buf], PITCH);
+    ldu.store(sU[buf], PITCH);
+    if (threadIdx.x < 32) sBias[buf][threadIdx.x] = bpre;
+  };
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int cur = ch & 1;
+    const bool more = ch + 1 < nch;
+    if (more) fetch(ch + 1);
 
     f32x4 S[2][RW];
 #pragma unroll
@@ -411,36 +463,32 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const typename E::frag a = E::load(sK + perm_row(ct, l16) * PITCH + s * 32 + 8 * G);
+        const typename E::frag a = E::load(sK[cur] + perm_row(ct, l16) * PITCH + s * 32 + 8 * G);
 #pragma unroll
         for (int rt = 0; rt < RW; ++rt) S[ct][rt] = E::mma(a, bq[rt][s], S[ct][rt]);
       }
     }
     float bias[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bias[j] = sBias[8 * G + j];
+    for (int j = 0; j < 8; ++j) bias[j] = sBias[cur][8 * G + j];
     typename E::frag pf[RW];
 #pragma unroll
     for (int rt = 0; rt < RW; ++rt) {
       float w[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = fast_exp2(S[j >> 2][rt][j & 3] * p.c + bias[j] - lrow[rt]);
+      for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j] - lrow[rt]));
       pf[rt] = E::pack(w);
     }
-    if (NDP > 0) {
 #pragma unroll
-      for (int dp = 0; dp < NACC; ++dp)
+    for (int dp = 0; dp < NACC; ++dp)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const typename E::frag a = E::load(sUT + (32 * dp + perm_row(dt, l16)) * PITCHT + 8 * G);
+      for (int dt = 0; dt < (NDP > 0 ? 2 : 1); ++dt) {
+        const typename E::frag a = load_vals_tr<T, D>(sU[cur], PITCH, 0, dp, dt);
 #pragma unroll
-          for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = E::mma(a, pf[rt], acc[dp][dt][rt]);
-        }
-    } else {
-      const typename E::frag a = E::load(sUT + l16 * PITCHT + 8 * G);
-#pragma unroll
-      for (int rt = 0; rt < RW; ++rt) acc[0][0][rt] = E::mma(a, pf[rt], acc[0][0][rt]);
-    }
+        for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = E::mma(a, pf[rt], acc[dp][dt][rt]);
+      }
+    if (more) put(cur ^ 1);
+    __syncthreads();
   }
 
   T* oh = out + static_cast<long long>(bh) * p.N * D;
@@ -448,21 +496,7 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
   for (int rt = 0; rt < RW; ++rt) {
     const int r = (wave * RW + rt) * 16 + l16;
     if (r >= it.nrows) continue;
-    T* dst = oh + (n0 + r * nstride) * D;
-    if (NDP > 0) {
-#pragma unroll
-      for (int dp = 0; dp < NACC; ++dp) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = acc[dp][j >> 2][rt][j & 3];
-        E::store8(dst + 32 * dp + 8 * G, v);
-      }
-    } else {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[0][0][rt][i];
-      E::store4(dst + 4 * G, v);
-    }
+    store_rows<T, D, NACC, RW>(oh + (n0 + r * nstride) * D, acc, rt, 1.0f, G);
   }
 }
 

@@ -181,13 +181,14 @@ int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned cha
   RGeom rg{BH, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
   const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
-  const size_t r_lds = rside_lds_bytes<T>(D, rg.b2p);
-  if (r_lds > 65536) {
+  const size_t r_lds_last = rside_lds_bytes<T>(D, rg.b2p, true);
+  const size_t r_lds_mid = rside_lds_bytes<T>(D, rg.b2p, false);
+  if (r_lds_last > 65536)
     ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rstep<T, D, true>),
-                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds)));
+                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds_last)));
+  if (r_lds_mid > 65536)
     ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rstep<T, D, false>),
-                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds)));
-  }
+                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds_mid)));
 
   for (int it = 1; it <= s.T; ++it) {
     const bool first = it == 1, last = it == s.T;
@@ -208,11 +209,11 @@ int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned cha
     }
     if (last) {
       ok(timed(3, st, [&] {
-        k_rstep<T, D, true><<<r_grid, r_threads, r_lds, st>>>(k, v, qhat, nullptr, nullptr, rg);
+        k_rstep<T, D, true><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, nullptr, nullptr, rg);
       }));
     } else {
       ok(timed(3, st, [&] {
-        k_rstep<T, D, false><<<r_grid, r_threads, r_lds, st>>>(k, v, qhat, ktil, hent, rg);
+        k_rstep<T, D, false><<<r_grid, r_threads, r_lds_mid, st>>>(k, v, qhat, ktil, hent, rg);
       }));
     }
   }

@@ -28,15 +28,12 @@ struct RGeom {
 template <typename T>
 __host__ __device__ constexpr int rside_pitch(int D) { return (D < 32 ? 32 : D) + Elem<T>::kPad; }
 
+// Dynamic LDS bytes: the K block and the V block (last iteration only), both
+// row-major [b2p][pitch].  The products with R read them by columns through
+// transposing LDS reads; K serves both the logits and the next keys.
 template <typename T>
-__host__ __device__ constexpr int rside_pitcht(int b2p) { return b2p + Elem<T>::kPad; }
-
-// Dynamic LDS bytes: K row-major [b2p][pitch] + one transposed [D][pitcht]
-// (V^T for the last iteration, K^T otherwise).
-template <typename T>
-inline size_t rside_lds_bytes(int D, int b2p) {
-  return sizeof(T) * (static_cast<size_t>(b2p) * rside_pitch<T>(D) +
-                      static_cast<size_t>(D) * rside_pitcht<T>(b2p));
+inline size_t rside_lds_bytes(int D, int b2p, bool last) {
+  return sizeof(T) * static_cast<size_t>(b2p) * rside_pitch<T>(D) * (last ? 2 : 1);
 }
 
 template <typename T, int D, bool LAST>
@@ -53,8 +50,7 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
   constexpr int MAXCP = 4;  // b2 <= 128
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* sK = reinterpret_cast<T*>(smem_raw);
-  T* sXT = sK + p.b2p * PITCH;
-  const int pitcht = p.b2p + E::kPad;
+  T* sV = sK + p.b2p * PITCH;
   const int nt = blockDim.x;
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
@@ -62,43 +58,39 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
   const int bh = item / p.b1;
   const long long blk = static_cast<long long>(item) * p.b2 * D;  // first element of block c1
 
-  // stage K (row-major) and V^T or K^T
-  {
-    constexpr int V = E::kVec;
-    constexpr int VPR = DK / V;
-    for (int idx = threadIdx.x; idx < p.b2p * VPR; idx += nt) {
-      const int r = idx / VPR, col = (idx % VPR) * V;
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (r < p.b2 && col < D) val = *reinterpret_cast<const uint4*>(k + blk + r * D + col);
-      *reinterpret_cast<uint4*>(sK + r * PITCH + col) = val;
-    }
-    const T* xs = LAST ? v : k;
-    constexpr int VPRT = D / V;
-    for (int idx = threadIdx.x; idx < p.b2p * VPRT; idx += nt) {
-      const int r = idx / VPRT, col = (idx % VPRT) * V;
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (r < p.b2) val = *reinterpret_cast<const uint4*>(xs + blk + r * D + col);
-      const T* e = reinterpret_cast<const T*>(&val);
-#pragma unroll
-      for (int j = 0; j < V; ++j) sXT[(col + j) * pitcht + r] = e[j];
-    }
-  }
-  __syncthreads();
-
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
   const int a2 = wave * 16 + l16;
   const bool row_ok = a2 < p.b2;
   const int ncp = p.b2p / 32;
+  auto qrow = [&](int g) { return ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2; };
+
+  // first tile's aggregated queries in flight while K and V are staged
+  typename E::frag bq[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int col = s * 32 + 8 * G;
+    bq[s] = (row_ok && col < D) ? E::load(qhat + qrow(0) * D + col) : E::zero();
+  }
+  {
+    constexpr int V = E::kVec;
+    constexpr int VPR = DK / V;
+    for (int idx = threadIdx.x; idx < p.b2p * VPR; idx += nt) {
+      const int r = idx / VPR, col = (idx % VPR) * V;
+      uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (r < p.b2 && col < D) {
+        kv = *reinterpret_cast<const uint4*>(k + blk + r * D + col);
+        if (LAST) vv = *reinterpret_cast<const uint4*>(v + blk + r * D + col);
+      }
+      *reinterpret_cast<uint4*>(sK + r * PITCH + col) = kv;
+      if (LAST) *reinterpret_cast<uint4*>(sV + r * PITCH + col) = vv;
+    }
+  }
+  __syncthreads();
+  const T* sX = LAST ? sV : sK;
 
   for (int g = 0; g < p.t; ++g) {
-    const long long row = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
-    typename E::frag bq[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int col = s * 32 + 8 * G;
-      bq[s] = (row_ok && col < D) ? E::load(qhat + row * D + col) : E::zero();
-    }
+    const long long row = qrow(g);
     // logits, transposed: rows c2 (permuted within 32-blocks), columns a2
     f32x4 S[MAXCP][2];
 #pragma unroll
@@ -115,7 +107,16 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
           }
       }
     }
-    // softmax over c2 for column a2 = l16 (+16*wave): lane holds c2 = 32cp + 8G + j
+    // next tile's aggregated queries (their rows are not written by this g)
+    if (g + 1 < p.t) {
+      const long long nrow = qrow(g + 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int col = s * 32 + 8 * G;
+        bq[s] = (row_ok && col < D) ? E::load(qhat + nrow * D + col) : E::zero();
+      }
+    }
+    // softmax over c2 for column a2: lane holds c2 = 32cp + 8G + j
     float x[MAXCP][8];
     float mx = -1e30f;
 #pragma unroll
@@ -148,28 +149,24 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
       }
       pf[cp] = E::pack(w);
     }
-    // X^T P^T: rows d (permuted within 32-blocks), columns a2
-    f32x4 acc[NACC][2];
+    // X^T P^T (X = V, or K for the next keys): rows d, columns a2
+    f32x4 acc[NACC][2][1];
 #pragma unroll
     for (int dp = 0; dp < NACC; ++dp) {
-      acc[dp][0] = f32x4{0, 0, 0, 0};
-      acc[dp][1] = f32x4{0, 0, 0, 0};
+      acc[dp][0][0] = f32x4{0, 0, 0, 0};
+      acc[dp][1][0] = f32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int cp = 0; cp < MAXCP; ++cp) {
       if (cp >= ncp) break;
-      if (NDP > 0) {
 #pragma unroll
-        for (int dp = 0; dp < NACC; ++dp)
+      for (int dp = 0; dp < NACC; ++dp)
 #pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const typename E::frag a = E::load(sXT + (32 * dp + perm_row(dt, l16)) * pitcht + 32 * cp + 8 * G);
-            acc[dp][dt] = E::mma(a, pf[cp], acc[dp][dt]);
-          }
-      } else {
-        const typename E::frag a = E::load(sXT + l16 * pitcht + 32 * cp + 8 * G);
-        acc[0][0] = E::mma(a, pf[cp], acc[0][0]);
-      }
+        for (int dt = 0; dt < (NDP > 0 ? 2 : 1); ++dt) {
+          const typename E::frag a = D >= 32 ? E::load_tr(sX, PITCH, 32 * cp, 32 * dp + 4 * dt, 8)
+                                             : E::load_tr(sX, PITCH, 32 * cp, 0, 4);
+          acc[dp][dt][0] = E::mma(a, pf[cp], acc[dp][dt][0]);
+        }
     }
     if (row_ok) {
       T* dst = (LAST ? qhat : ktil) + row * D;
@@ -178,13 +175,13 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
         for (int dp = 0; dp < NACC; ++dp) {
           float o[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) o[j] = acc[dp][j >> 2][j & 3];
+          for (int j = 0; j < 8; ++j) o[j] = acc[dp][j >> 2][0][j & 3];
           E::store8(dst + 32 * dp + 8 * G, o);
         }
       } else {
         float o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = acc[0][0][i];
+        for (int i = 0; i < 4; ++i) o[i] = acc[0][0][0][i];
         E::store4(dst + 4 * G, o);
       }
     }
