@@ -15,6 +15,8 @@ HIPCC_FLAGS = [
     # packed fp32 vector ops off: plain fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # MFMA results in VGPRs: the softmax reads them without accvgpr moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -35,9 +35,14 @@ template <typename T> struct Elem;
 
 template <> struct Elem<bf16_t> {
   static constexpr int kVec = 8;  // elements per 16-byte access
-  static constexpr int kPad = 8;  // LDS row padding (elements)
   using frag = bf16x8;
   __device__ static inline frag zero() { return frag{}; }
+  __device__ static inline frag ones() {
+    frag r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = static_cast<__bf16>(1.0f);
+    return r;
+  }
   __device__ static inline frag load(const bf16_t* p) {
     return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
   }
@@ -70,30 +75,13 @@ template <> struct Elem<bf16_t> {
   }
   // the value a fragment slot holds, as float (for sums of rounded weights)
   __device__ static inline float slot(const frag& f, int j) { return static_cast<float>(f[j]); }
-  // Fragment whose contraction index runs down the rows of a row-major LDS
-  // tile: lane (G, i) gets tile[k0 + 8G + j][cbase + cstride*(i/4) + i%4],
-  // j = 0..7.  Two ds_read_b64_tr_b16: within each 16-lane block, output lane
-  // i, element j is element i%4 of the 8 bytes addressed by lane 4j + i/4.
-  __device__ static inline frag load_tr(const bf16_t* tile, int pitch, int k0, int cbase,
-                                        int cstride) {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    typedef short v8i16 __attribute__((ext_vector_type(8)));
-    const int l = threadIdx.x & 63;
-    const int i = l & 15, G = l >> 4;
-    const bf16_t* p = tile + (k0 + 8 * G + (i >> 2)) * pitch + cbase + cstride * (i & 3);
-    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * pitch));
-    const v8i16 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(frag, r);
-  }
 };
 
 template <> struct Elem<float> {
   static constexpr int kVec = 4;
-  static constexpr int kPad = 4;
   struct frag { f32x4 lo, hi; };
   __device__ static inline frag zero() { return frag{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}; }
+  __device__ static inline frag ones() { return frag{f32x4{1, 1, 1, 1}, f32x4{1, 1, 1, 1}}; }
   __device__ static inline frag load(const float* p) {
     frag r;
     r.lo = *reinterpret_cast<const f32x4*>(p);
@@ -123,19 +111,61 @@ template <> struct Elem<float> {
     *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
   }
   __device__ static inline float slot(const frag& f, int j) { return j < 4 ? f.lo[j] : f.hi[j - 4]; }
-  // Same contract as the bf16 version, with plain LDS reads.
-  __device__ static inline frag load_tr(const float* tile, int pitch, int k0, int cbase,
-                                        int cstride) {
+};
+
+
+// LDS tiles: rows of DK elements with no padding; the 16-byte chunks of row r
+// are stored XOR-permuted by swz(r) = 4*(r%4) + (r/8)%4 (masked to the row's
+// chunk count).  Both read patterns below then spread each 16-lane group over
+// all banks: row reads (16 rows that differ in bits 0,1,3,4, same chunk) and
+// transposing reads (4 consecutive rows x 4 consecutive chunks).
+template <typename T, int DK>
+struct Tile {
+  static constexpr int V = Elem<T>::kVec;
+  static constexpr int NCH = DK / V;
+  __device__ static inline int swz(int r) { return (4 * (r & 3) + ((r >> 3) & 3)) & (NCH - 1); }
+  // element offset of (row r, column col)
+  __device__ static inline int off(int r, int col) {
+    return r * DK + (((col / V) ^ swz(r)) * V) + (col % V);
+  }
+  // eight consecutive elements of row r from column col (col % 8 == 0)
+  __device__ static inline typename Elem<T>::frag load8(const T* t, int r, int col) {
+    if constexpr (V == 8) {
+      return Elem<T>::load(t + off(r, col));
+    } else {
+      typename Elem<T>::frag f;
+      f.lo = *reinterpret_cast<const f32x4*>(t + off(r, col));
+      f.hi = *reinterpret_cast<const f32x4*>(t + off(r, col + 4));
+      return f;
+    }
+  }
+  // Fragment whose contraction index runs down the rows: lane (G, i) gets
+  // t[k0 + 8G + j][cbase + cstride*(i/4) + i%4], j = 0..7.
+  __device__ static inline typename Elem<T>::frag load_tr(const T* t, int k0, int cbase, int cstride) {
     const int l = threadIdx.x & 63;
     const int i = l & 15, G = l >> 4;
-    const float* p = tile + (k0 + 8 * G) * pitch + cbase + cstride * (i >> 2) + (i & 3);
-    frag r;
+    if constexpr (V == 8) {
+      // two ds_read_b64_tr_b16: within each 16-lane block, output lane i,
+      // element j is element i%4 of the 8 bytes addressed by lane 4j + i/4
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef short v8i16 __attribute__((ext_vector_type(8)));
+      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+      const int r = k0 + 8 * G + (i >> 2);
+      const int col = cbase + cstride * (i & 3);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + off(r, col)));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + off(r + 4, col)));
+      const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(typename Elem<T>::frag, v);
+    } else {
+      const int col = cbase + cstride * (i >> 2) + (i & 3);
+      typename Elem<T>::frag f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      r.lo[j] = p[j * pitch];
-      r.hi[j] = p[(4 + j) * pitch];
+      for (int j = 0; j < 4; ++j) {
+        f.lo[j] = t[off(k0 + 8 * G + j, col)];
+        f.hi[j] = t[off(k0 + 8 * G + 4 + j, col)];
+      }
+      return f;
     }
-    return r;
   }
 };
 
@@ -162,10 +192,10 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
 }
 
 // Register-staged copy of a ROWS x DK tile (row stride `rstride` elements in
-// global memory) into an LDS tile of pitch `pitch`.  load() issues the global
-// reads; store() writes them to LDS, so a caller can compute on one LDS
-// buffer while the next tile is in flight.  Rows >= nvalid and columns >= D
-// (up to DK) are zero.
+// global memory) into a swizzled LDS Tile.  load() issues the global reads;
+// store() writes them to LDS, so a caller can compute on one LDS buffer while
+// the next tile is in flight.  Rows >= nvalid and columns >= D (up to DK) are
+// zero.
 template <typename T, int D, int DK, int ROWS, int NT>
 struct TileLoader {
   static constexpr int V = Elem<T>::kVec;
@@ -183,13 +213,13 @@ struct TileLoader {
         buf[u] = *reinterpret_cast<const uint4*>(g + r * rstride + c);
     }
   }
-  __device__ inline void store(T* lds, int pitch) const {
+  __device__ inline void store(T* lds) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = threadIdx.x + u * NT;
       if (TOTAL % NT != 0 && idx >= TOTAL) break;
       const int r = idx / VPR, c = (idx % VPR) * V;
-      *reinterpret_cast<uint4*>(lds + r * pitch + c) = buf[u];
+      *reinterpret_cast<uint4*>(lds + Tile<T, DK>::off(r, c)) = buf[u];
     }
   }
 };

@@ -73,14 +73,31 @@ struct ColItem {
   }
 };
 
-// Fragment of the transposed tile for output columns of d-tile pair dp, half
-// dt (pair mode: 8 consecutive d per lane after the product) or the single
-// 16-wide d tile (D == 16).
-template <typename T, int D>
-__device__ inline typename Elem<T>::frag load_vals_tr(const T* tile, int pitch, int k0, int dp,
-                                                      int dt) {
-  if (D >= 32) return Elem<T>::load_tr(tile, pitch, k0, 32 * dp + 4 * dt, 8);
-  return Elem<T>::load_tr(tile, pitch, k0, 0, 4);
+// Rows of K, q or U staged per pipeline step (32-row MFMA contraction
+// blocks); one barrier per step.
+#ifndef MONARCH_STEP
+#define MONARCH_STEP 64
+#endif
+constexpr int kStep = MONARCH_STEP;
+constexpr int kHalves = kStep / 32;
+// Minimum waves per SIMD the register allocator must allow (launch bounds).
+#ifndef MONARCH_LSE_MINW
+#define MONARCH_LSE_MINW 1
+#endif
+#ifndef MONARCH_AGG_MINW
+#define MONARCH_AGG_MINW 1
+#endif
+#ifndef MONARCH_APP_MINW
+#define MONARCH_APP_MINW 1
+#endif
+
+// Fragment of a transposed tile for output columns of d-tile pair dp, half dt
+// (pair mode: the product leaves 8 consecutive d per lane) or the single
+// 16-wide d tile (D == 16), contraction rows k0..k0+31.
+template <typename T, int D, int DK>
+__device__ inline typename Elem<T>::frag load_vals_tr(const T* tile, int k0, int dp, int dt) {
+  if (D >= 32) return Tile<T, DK>::load_tr(tile, k0, 32 * dp + 4 * dt, 8);
+  return Tile<T, DK>::load_tr(tile, k0, 0, 4);
 }
 
 // Store 8 (pair mode) or 4 (D == 16) consecutive outputs of lane group G.
@@ -104,22 +121,70 @@ __device__ inline void store_rows(T* dst, const f32x4 (&acc)[NACC][2][RW], int r
   }
 }
 
+// The 32-row block k0..k0+31 of a tile as A fragments by rows (permuted, see
+// perm_row), for logits: a[s][ct] covers contraction columns 32s..32s+31.
+template <typename T, int DK, int KS>
+__device__ inline void load_rows(typename Elem<T>::frag (&a)[KS][2], const T* tile, int k0, int l16,
+                                 int G) {
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) a[s][ct] = Tile<T, DK>::load8(tile, k0 + perm_row(ct, l16), s * 32 + 8 * G);
+}
+
+// The same block by columns, for the weighted sums: v[dp][dt] (see load_vals_tr).
+template <typename T, int D, int DK, int NACC>
+__device__ inline void load_cols(typename Elem<T>::frag (&v)[NACC][2], const T* tile, int k0) {
+#pragma unroll
+  for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+    for (int dt = 0; dt < (D >= 32 ? 2 : 1); ++dt) v[dp][dt] = load_vals_tr<T, D, DK>(tile, k0, dp, dt);
+}
+
+// S tiles with rows from `a` (a 32-row block) and columns from the wave's RW
+// tiles of B fragments.
+template <typename T, int KS, int RW>
+__device__ inline void logits(f32x4 (&S)[2][RW], const typename Elem<T>::frag (&a)[KS][2],
+                              const typename Elem<T>::frag (&b)[RW][KS]) {
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int rt = 0; rt < RW; ++rt) S[ct][rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) S[ct][rt] = Elem<T>::mma(a[s][ct], b[rt][s], S[ct][rt]);
+}
+
+// acc[dp][dt][rt] += v[dp][dt] * pf[rt]
+template <typename T, int D, int NACC, int RW>
+__device__ inline void weighted_sum(f32x4 (&acc)[NACC][2][RW], const typename Elem<T>::frag (&v)[NACC][2],
+                                    const typename Elem<T>::frag (&pf)[RW]) {
+#pragma unroll
+  for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+    for (int dt = 0; dt < (D >= 32 ? 2 : 1); ++dt)
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = Elem<T>::mma(v[dp][dt], pf[rt], acc[dp][dt][rt]);
+}
+
 // ------------------------------------------------------------------ k_lse --
 // CONTIG: rows are consecutive tokens of a head (only with BCAST keys, where
 // the logits do not depend on the column or tile).
 template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG>
-__global__ __launch_bounds__(NW * kWave) void k_lse(const T* __restrict__ q,
+__global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
                                                     const T* __restrict__ kt,
                                                     const float* __restrict__ h2,
                                                     float* __restrict__ lse, LGeom p) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
-  constexpr int PITCH = DK + E::kPad;
   constexpr int RB = NW * RW * 16;
   constexpr int NT = NW * kWave;
-  __shared__ __align__(16) T sK[2][32 * PITCH];
-  __shared__ float sBias[2][32];
+  __shared__ __align__(16) T sK[2][kStep * DK];
+  __shared__ float sBias[2][kStep];
 
   int bh, g = 0, a2 = 0, nrows;
   long long n0, nstride;
@@ -158,58 +223,62 @@ __global__ __launch_bounds__(NW * kWave) void k_lse(const T* __restrict__ q,
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) { m[rt] = -1e30f; l[rt] = 0.0f; }
 
-  TileLoader<T, D, DK, 32, NT> ld;
-  const int nch = (p.b1 + 31) / 32;
+  TileLoader<T, D, DK, kStep, NT> ld;
+  const int nst = (p.b1 + kStep - 1) / kStep;
   float bpre = 0.0f;
-  ld.load(ks.k, ks.kstride, p.b1);
-  if (threadIdx.x < 32) bpre = ks.bias(threadIdx.x, p.b1);
-  ld.store(sK[0], PITCH);
-  if (threadIdx.x < 32) sBias[0][threadIdx.x] = bpre;
+  auto fetch = [&](int st) {
+    const int c1 = st * kStep;
+    ld.load(ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
+    if (threadIdx.x < kStep) bpre = ks.bias(c1 + threadIdx.x, p.b1);
+  };
+  fetch(0);
+  ld.store(sK[0]);
+  if (threadIdx.x < kStep) sBias[0][threadIdx.x] = bpre;
   __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    const int cur = ch & 1;
-    const bool more = ch + 1 < nch;
-    if (more) {
-      const int c1n = (ch + 1) * 32;
-      ld.load(ks.k + c1n * ks.kstride, ks.kstride, p.b1 - c1n);
-      if (threadIdx.x < 32) bpre = ks.bias(c1n + threadIdx.x, p.b1);
-    }
-    f32x4 S[2][RW];
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < nst;
+    if (more) fetch(st + 1);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int half = 0; half < kHalves; ++half) {
+      const int k0 = 32 * half;
+      // keys past b1 only exist in the last step
+      if (st * kStep + k0 >= p.b1) break;
+      const bool masked = !BCAST || (st + 1) * kStep > p.b1;
+      typename E::frag a[KS][2];
+      load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
+      float bias[8];
+      if (masked) {
 #pragma unroll
-      for (int rt = 0; rt < RW; ++rt) S[ct][rt] = f32x4{0, 0, 0, 0};
+        for (int j = 0; j < 8; ++j) bias[j] = sBias[cur][k0 + 8 * G + j];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 S[2][RW];
+      logits<T, KS, RW>(S, a, bq);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+      for (int rt = 0; rt < RW; ++rt) {
+        float x[8];
+        if (masked) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const typename E::frag a = E::load(sK[cur] + perm_row(ct, l16) * PITCH + s * 32 + 8 * G);
+          for (int j = 0; j < 8; ++j) x[j] = __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
+        } else {
 #pragma unroll
-        for (int rt = 0; rt < RW; ++rt) S[ct][rt] = E::mma(a, bq[rt][s], S[ct][rt]);
+          for (int j = 0; j < 8; ++j) x[j] = S[j >> 2][rt][j & 3] * p.c;
+        }
+        float cm = x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
+        const float mn = fmaxf(m[rt], cm);
+        float acc = l[rt] * fast_exp2(m[rt] - mn);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += fast_exp2(x[j] - mn);
+        l[rt] = acc;
+        m[rt] = mn;
       }
     }
-    float bias[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bias[j] = sBias[cur][8 * G + j];
-#pragma unroll
-    for (int rt = 0; rt < RW; ++rt) {
-      float x[8];
-      float cm = -1e30f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        x[j] = __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
-        cm = fmaxf(cm, x[j]);
-      }
-      const float mn = fmaxf(m[rt], cm);
-      float acc = l[rt] * fast_exp2(m[rt] - mn);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc += fast_exp2(x[j] - mn);
-      l[rt] = acc;
-      m[rt] = mn;
-    }
     if (more) {
-      ld.store(sK[cur ^ 1], PITCH);
-      if (threadIdx.x < 32) sBias[cur ^ 1][threadIdx.x] = bpre;
+      ld.store(sK[cur ^ 1]);
+      if (threadIdx.x < kStep) sBias[cur ^ 1][threadIdx.x] = bpre;
     }
     __syncthreads();
   }
@@ -233,11 +302,12 @@ __global__ __launch_bounds__(NW * kWave) void k_lse(const T* __restrict__ q,
 // ------------------------------------------------------------ k_aggregate --
 // One workgroup: (bh, g, a2) and a block of CB = NW*RW*16 key blocks c1.
 // Qh[c1,:] = sum_(a1 in g) L[a1,c1] q_a1 / sum_(a1 in g) L[a1,c1], computed as
-// Qh^T = q^T P over chunks of 32 rows a1.  q is staged once, row-major: the
-// logits read it by rows, the weighted sum reads it by columns (transposing
-// LDS reads).
+// Qh^T = q^T P over steps of 64 rows a1.  q is staged once: the logits read
+// it by rows, the weighted sum by columns (transposing LDS reads); the mass
+// beta comes from one more product with a ones fragment, so it sums exactly
+// the rounded weights the weighted sum uses.
 template <typename T, int D, int RW, int NW, bool BCAST>
-__global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ q,
+__global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(const T* __restrict__ q,
                                                           const T* __restrict__ kt,
                                                           const float* __restrict__ h2,
                                                           const float* __restrict__ lse,
@@ -245,13 +315,12 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ 
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
-  constexpr int PITCH = DK + E::kPad;
   constexpr int CB = NW * RW * 16;
   constexpr int NT = NW * kWave;
   constexpr int NDP = D / 32;  // pairs of 16-wide d tiles (0 when D == 16)
   constexpr int NACC = NDP > 0 ? NDP : 1;
-  __shared__ __align__(16) T sQ[2][32 * PITCH];
-  __shared__ float sL[2][32];
+  __shared__ __align__(16) T sQ[2][kStep * DK];
+  __shared__ float sL[2][kStep];
 
   // decode (bh, g, a2, cb)
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -277,93 +346,86 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ 
       const int col = s * 32 + 8 * G;
       bk[rt][s] = (c1 < p.b1 && col < D) ? E::load(ks.k + c1 * ks.kstride + col) : E::zero();
     }
-    bias[rt] = ks.bias(c1, p.b1);
+    // rows c1 >= b1 (zero keys) are computed but never stored: no mask needed
+    bias[rt] = BCAST ? 0.0f : (c1 < p.b1 ? ks.bias(c1, p.b1) : 0.0f);
   }
 
   f32x4 acc[NACC][2][RW];
+  f32x4 accb[RW];  // column sums of the rounded weights (the mass beta)
 #pragma unroll
-  for (int dp = 0; dp < NACC; ++dp)
+  for (int rt = 0; rt < RW; ++rt) {
+    accb[rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int dp = 0; dp < NACC; ++dp)
 #pragma unroll
-      for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
-  float beta[RW];
-#pragma unroll
-  for (int rt = 0; rt < RW; ++rt) beta[rt] = 0.0f;
+      for (int dt = 0; dt < 2; ++dt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
+  }
+  const typename E::frag ones = E::ones();
 
   const T* qh = q + static_cast<long long>(bh) * p.N * D;
   const float* lh = lse + static_cast<long long>(bh) * p.N;
   const long long qstride = static_cast<long long>(p.b2) * D;
   const int nrows = hi - lo;
-  const int nch = (nrows + 31) / 32;
-  TileLoader<T, D, DK, 32, NT> ld;
+  const int nst = (nrows + kStep - 1) / kStep;
+  TileLoader<T, D, DK, kStep, NT> ld;
   float lpre = 0.0f;
-  auto fetch = [&](int ch) {
-    const long long n_first = static_cast<long long>(lo + ch * 32) * p.b2 + a2;
-    const int nvalid = nrows - ch * 32;
+  // sL holds -lse of each staged row (-inf past the tile: weight 0)
+  auto fetch = [&](int st) {
+    const long long n_first = static_cast<long long>(lo + st * kStep) * p.b2 + a2;
+    const int nvalid = nrows - st * kStep;
     ld.load(qh + n_first * D, qstride, nvalid);
-    if (threadIdx.x < 32)
-      lpre = static_cast<int>(threadIdx.x) < nvalid ? lh[n_first + threadIdx.x * static_cast<long long>(p.b2)]
-                                                    : kPosInf;
+    if (threadIdx.x < kStep)
+      lpre = static_cast<int>(threadIdx.x) < nvalid
+                 ? -lh[n_first + threadIdx.x * static_cast<long long>(p.b2)]
+                 : kNegInf;
   };
   fetch(0);
-  ld.store(sQ[0], PITCH);
-  if (threadIdx.x < 32) sL[0][threadIdx.x] = lpre;
+  ld.store(sQ[0]);
+  if (threadIdx.x < kStep) sL[0][threadIdx.x] = lpre;
   __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    const int cur = ch & 1;
-    const bool more = ch + 1 < nch;
-    if (more) fetch(ch + 1);
-
-    f32x4 S[2][RW];
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < nst;
+    if (more) fetch(st + 1);
 #pragma unroll
-    for (int at = 0; at < 2; ++at)
+    for (int half = 0; half < kHalves; ++half) {
+      const int k0 = 32 * half;
+      if (st * kStep + k0 >= nrows) break;
+      // all LDS operands of this 32-row block first: rows of q for the
+      // logits, columns of q for the weighted sum, and -lse
+      typename E::frag a[KS][2];
+      typename E::frag v[NACC][2];
+      load_rows<T, DK, KS>(a, sQ[cur], k0, l16, G);
+      load_cols<T, D, DK, NACC>(v, sQ[cur], k0);
+      float nl[8];
 #pragma unroll
-      for (int rt = 0; rt < RW; ++rt) S[at][rt] = f32x4{0, 0, 0, 0};
+      for (int j = 0; j < 8; ++j) nl[j] = sL[cur][k0 + 8 * G + j];
+      __builtin_amdgcn_sched_barrier(0);
+      // S tiles: rows a1 (permuted), columns c1 (the wave's key rows)
+      f32x4 S[2][RW];
+      logits<T, KS, RW>(S, a, bk);
+      typename E::frag pf[RW];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+      for (int rt = 0; rt < RW; ++rt) {
+        float w[8];
 #pragma unroll
-      for (int at = 0; at < 2; ++at) {
-        const typename E::frag a = E::load(sQ[cur] + perm_row(at, l16) * PITCH + s * 32 + 8 * G);
-#pragma unroll
-        for (int rt = 0; rt < RW; ++rt) S[at][rt] = E::mma(a, bk[rt][s], S[at][rt]);
+        for (int j = 0; j < 8; ++j)
+          w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? nl[j] : nl[j] + bias[rt]));
+        pf[rt] = E::pack(w);
+        accb[rt] = E::mma(ones, pf[rt], accb[rt]);
       }
+      weighted_sum<T, D, NACC, RW>(acc, v, pf);
     }
-    float lrow[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lrow[j] = sL[cur][8 * G + j];
-    typename E::frag pf[RW];
-#pragma unroll
-    for (int rt = 0; rt < RW; ++rt) {
-      float w[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[rt] - lrow[j]));
-      pf[rt] = E::pack(w);
-      float sb = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sb += E::slot(pf[rt], j);
-      beta[rt] += sb;
-    }
-#pragma unroll
-    for (int dp = 0; dp < NACC; ++dp)
-#pragma unroll
-      for (int dt = 0; dt < (NDP > 0 ? 2 : 1); ++dt) {
-        const typename E::frag a = load_vals_tr<T, D>(sQ[cur], PITCH, 0, dp, dt);
-#pragma unroll
-        for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = E::mma(a, pf[rt], acc[dp][dt][rt]);
-      }
     if (more) {
-      ld.store(sQ[cur ^ 1], PITCH);
-      if (threadIdx.x < 32) sL[cur ^ 1][threadIdx.x] = lpre;
+      ld.store(sQ[cur ^ 1]);
+      if (threadIdx.x < kStep) sL[cur ^ 1][threadIdx.x] = lpre;
     }
     __syncthreads();
   }
 
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
-    float b = beta[rt];
-    b += __shfl_xor(b, 16);
-    b += __shfl_xor(b, 32);
+    const float b = accb[rt][0];  // every element of column c1 = l16 holds beta[c1]
     const float inv = b > 0.0f ? 1.0f / b : 0.0f;
     const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
     if (c1 >= p.b1) continue;
@@ -377,7 +439,7 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate(const T* __restrict__ 
 // y[a1,:] = sum_c1 L[a1,c1] U[g,c1,a2,:], with L normalised by the stored
 // log-sum-exp (no running rescale), computed as y^T = U^T P^T.
 template <typename T, int D, int RW, int NW, bool BCAST>
-__global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
+__global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T* __restrict__ q,
                                                       const T* __restrict__ kt,
                                                       const float* __restrict__ h2,
                                                       const float* __restrict__ lse,
@@ -386,14 +448,13 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
-  constexpr int PITCH = DK + E::kPad;
   constexpr int RB = NW * RW * 16;
   constexpr int NT = NW * kWave;
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
-  __shared__ __align__(16) T sK[2][32 * PITCH];
-  __shared__ __align__(16) T sU[2][32 * PITCH];
-  __shared__ float sBias[2][32];
+  __shared__ __align__(16) T sK[2][kStep * DK];
+  __shared__ __align__(16) T sU[2][kStep * DK];
+  __shared__ float sBias[2][kStep];
 
   ColItem it(p, RB);
   if (it.nrows <= 0) return;
@@ -410,7 +471,7 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
   const long long ustride = static_cast<long long>(p.b2) * D;
 
   typename E::frag bq[RW][KS];
-  float lrow[RW];
+  float nlrow[RW];  // -lse of the lane's rows
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
     const int r = (wave * RW + rt) * 16 + l16;
@@ -420,7 +481,7 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
       const int col = s * 32 + 8 * G;
       bq[rt][s] = (ok && col < D) ? E::load(qh + (n0 + r * nstride) * D + col) : E::zero();
     }
-    lrow[rt] = ok ? lh[n0 + r * nstride] : 0.0f;
+    nlrow[rt] = ok ? -lh[n0 + r * nstride] : 0.0f;
   }
 
   f32x4 acc[NACC][2][RW];
@@ -431,62 +492,68 @@ __global__ __launch_bounds__(NW * kWave) void k_apply(const T* __restrict__ q,
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
 
-  TileLoader<T, D, DK, 32, NT> ldk;
-  TileLoader<T, D, D, 32, NT> ldu;
+  TileLoader<T, D, DK, kStep, NT> ldk;
+  TileLoader<T, D, DK, kStep, NT> ldu;
   float bpre = 0.0f;
-  const int nch = (p.b1 + 31) / 32;
-  auto fetch = [&](int ch) {
-    const int c1_0 = ch * 32;
-    ldk.load(ks.k + c1_0 * ks.kstride, ks.kstride, p.b1 - c1_0);
-    ldu.load(ucol + c1_0 * ustride, ustride, p.b1 - c1_0);
-    if (threadIdx.x < 32) bpre = ks.bias(c1_0 + threadIdx.x, p.b1);
+  const int nst = (p.b1 + kStep - 1) / kStep;
+  auto fetch = [&](int st) {
+    const int c1 = st * kStep;
+    ldk.load(ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
+    ldu.load(ucol + c1 * ustride, ustride, p.b1 - c1);
+    if (threadIdx.x < kStep) bpre = ks.bias(c1 + threadIdx.x, p.b1);
   };
   auto put = [&](int buf) {
-    ldk.store(sK[buf], PITCH);
-    ldu.store(sU[buf], PITCH);
-    if (threadIdx.x < 32) sBias[buf][threadIdx.x] = bpre;
+    ldk.store(sK[buf]);
+    ldu.store(sU[buf]);
+    if (threadIdx.x < kStep) sBias[buf][threadIdx.x] = bpre;
   };
   fetch(0);
   put(0);
   __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    const int cur = ch & 1;
-    const bool more = ch + 1 < nch;
-    if (more) fetch(ch + 1);
-
-    f32x4 S[2][RW];
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < nst;
+    if (more) fetch(st + 1);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int half = 0; half < kHalves; ++half) {
+      const int k0 = 32 * half;
+      if (st * kStep + k0 >= p.b1) break;
+      // keys past b1 only exist in the last step; their U rows are zero but
+      // their weights are masked as well
+      const bool masked = !BCAST || (st + 1) * kStep > p.b1;
+      typename E::frag a[KS][2];
+      typename E::frag v[NACC][2];
+      load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
+      load_cols<T, D, DK, NACC>(v, sU[cur], k0);
+      float bias[8];
+      if (masked) {
 #pragma unroll
-      for (int rt = 0; rt < RW; ++rt) S[ct][rt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const typename E::frag a = E::load(sK[cur] + perm_row(ct, l16) * PITCH + s * 32 + 8 * G);
-#pragma unroll
-        for (int rt = 0; rt < RW; ++rt) S[ct][rt] = E::mma(a, bq[rt][s], S[ct][rt]);
+        for (int j = 0; j < 8; ++j) bias[j] = sBias[cur][k0 + 8 * G + j];
       }
-    }
-    float bias[8];
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 S[2][RW];
+      logits<T, KS, RW>(S, a, bq);
+      typename E::frag pf[RW];
+      if (masked) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bias[j] = sBias[cur][8 * G + j];
-    typename E::frag pf[RW];
+        for (int rt = 0; rt < RW; ++rt) {
+          float w[8];
 #pragma unroll
-    for (int rt = 0; rt < RW; ++rt) {
-      float w[8];
+          for (int j = 0; j < 8; ++j)
+            w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j] + nlrow[rt]));
+          pf[rt] = E::pack(w);
+        }
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j] - lrow[rt]));
-      pf[rt] = E::pack(w);
-    }
+        for (int rt = 0; rt < RW; ++rt) {
+          float w[8];
 #pragma unroll
-    for (int dp = 0; dp < NACC; ++dp)
-#pragma unroll
-      for (int dt = 0; dt < (NDP > 0 ? 2 : 1); ++dt) {
-        const typename E::frag a = load_vals_tr<T, D>(sU[cur], PITCH, 0, dp, dt);
-#pragma unroll
-        for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = E::mma(a, pf[rt], acc[dp][dt][rt]);
+          for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, nlrow[rt]));
+          pf[rt] = E::pack(w);
+        }
       }
+      weighted_sum<T, D, NACC, RW>(acc, v, pf);
+    }
     if (more) put(cur ^ 1);
     __syncthreads();
   }

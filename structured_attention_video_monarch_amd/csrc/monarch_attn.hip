@@ -30,11 +30,29 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 // ----------------------------------------------------------- tuning knobs --
-// Rows per wave (in 16-row MFMA tiles) and waves per workgroup of the L-side
-// kernels.
-constexpr int kRW = 2;
-constexpr int kNW = 4;
-constexpr int kRowsPerBlock = kRW * kNW * 16;
+// Rows per wave (in 16-row MFMA tiles) and waves per workgroup of each
+// L-side kernel (overridable at build time for tuning sweeps).
+#ifndef MONARCH_LSE_RW
+#define MONARCH_LSE_RW 2
+#endif
+#ifndef MONARCH_LSE_NW
+#define MONARCH_LSE_NW 4
+#endif
+#ifndef MONARCH_AGG_RW
+#define MONARCH_AGG_RW 2
+#endif
+#ifndef MONARCH_AGG_NW
+#define MONARCH_AGG_NW 4
+#endif
+#ifndef MONARCH_APP_RW
+#define MONARCH_APP_RW 2
+#endif
+#ifndef MONARCH_APP_NW
+#define MONARCH_APP_NW 8
+#endif
+constexpr int kLseRW = MONARCH_LSE_RW, kLseNW = MONARCH_LSE_NW;
+constexpr int kAggRW = MONARCH_AGG_RW, kAggNW = MONARCH_AGG_NW;
+constexpr int kAppRW = MONARCH_APP_RW, kAppNW = MONARCH_APP_NW;
 
 // ------------------------------------------------------------------ checks --
 struct Shape {
@@ -78,24 +96,49 @@ Shape make_shape(int B, int H, int f, int h, int w, int d, int b1, int b2, int t
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Heads are processed in passes of `heads_per_pass` (b, h) pairs, all kernels
+// of a pass back to back, so that one pass's intermediates (the aggregated
+// queries, written over by R V) and its inputs stay in the 256 MB Infinity
+// Cache between the kernels that produce and consume them.
+// Measured on MI355X at the 720p latent shape: one pass over all heads is
+// faster than per-head passes (launch tails outweigh cache residency), so the
+// default budget is unlimited (0); a budget bounds the workspace instead.
+#ifndef MONARCH_PASS_BUDGET_MB
+#define MONARCH_PASS_BUDGET_MB 0
+#endif
+long long heads_per_pass(const Shape& s, size_t elem) {
+  if (MONARCH_PASS_BUDGET_MB <= 0) return s.BH;
+  const long long nd = s.N * s.d * static_cast<long long>(elem);
+  long long per_head = s.t * nd + 4 * nd + s.N * 4;
+  if (s.T > 1) per_head += s.t * nd + s.t * s.N * 4;
+  const long long budget = static_cast<long long>(MONARCH_PASS_BUDGET_MB) << 20;
+  long long hc = budget / per_head;
+  if (hc < 1) hc = 1;
+  if (hc > s.BH) hc = s.BH;
+  return hc;
+}
+
 struct Workspace {
+  long long hc;  // heads per pass
   size_t kbar, lse, qhat, ktil, hent, total;
 };
 
 Workspace layout(const Shape& s, size_t elem) {
   Workspace w{};
+  w.hc = heads_per_pass(s, elem);
+  const size_t hc = static_cast<size_t>(w.hc);
   size_t off = 0;
   w.kbar = off;
-  off += align_up(static_cast<size_t>(s.BH) * s.b1 * s.d * elem);
+  off += align_up(hc * s.b1 * s.d * elem);
   w.lse = off;
-  off += align_up(static_cast<size_t>(s.BH) * s.N * sizeof(float));
+  off += align_up(hc * s.N * sizeof(float));
   w.qhat = off;
-  off += align_up(static_cast<size_t>(s.BH) * s.t * s.N * s.d * elem);
+  off += align_up(hc * s.t * s.N * s.d * elem);
   if (s.T > 1) {
     w.ktil = off;
-    off += align_up(static_cast<size_t>(s.BH) * s.t * s.N * s.d * elem);
+    off += align_up(hc * s.t * s.N * s.d * elem);
     w.hent = off;
-    off += align_up(static_cast<size_t>(s.BH) * s.t * s.N * sizeof(float));
+    off += align_up(hc * s.t * s.N * sizeof(float));
   } else {
     w.ktil = w.hent = 0;
   }
@@ -146,9 +189,10 @@ hipError_t timed(int id, hipStream_t st, F&& launch) {
 }
 
 // ------------------------------------------------------------------ launch --
+// All kernels of one pass over `s.BH` heads starting at the given pointers.
 template <typename T, int D>
-int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned char* ws,
-        const Workspace& w, hipStream_t st) {
+hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned char* ws,
+                    const Workspace& w, hipStream_t st) {
   const float c = kLog2e / std::sqrt(static_cast<float>(D));
   T* kbar = reinterpret_cast<T*>(ws + w.kbar);
   float* lse = reinterpret_cast<float*>(ws + w.lse);
@@ -169,14 +213,18 @@ int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned cha
     ok(timed(0, st, [&] { k_kbar<T, D><<<grid, 256, 0, st>>>(k, kbar, BH, s.b1, s.b2); }));
   }
 
-  LGeom col{BH, N, s.b1, s.b2, s.t, (ngmax + kRowsPerBlock - 1) / kRowsPerBlock, c};
-  const unsigned col_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * col.nrb);
-  LGeom agg = col;
-  agg.nrb = (s.b1 + kRowsPerBlock - 1) / kRowsPerBlock;
+  constexpr int lse_rows = kLseRW * kLseNW * 16, agg_rows = kAggRW * kAggNW * 16,
+                app_rows = kAppRW * kAppNW * 16;
+  const LGeom base{BH, N, s.b1, s.b2, s.t, 0, c};
+  LGeom lse_col = base, lse_contig = base, agg = base, app = base;
+  lse_col.nrb = (ngmax + lse_rows - 1) / lse_rows;
+  lse_contig.nrb = (N + lse_rows - 1) / lse_rows;
+  agg.nrb = (s.b1 + agg_rows - 1) / agg_rows;
+  app.nrb = (ngmax + app_rows - 1) / app_rows;
+  const unsigned lse_col_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lse_col.nrb);
+  const unsigned lse_contig_grid = static_cast<unsigned>(s.BH * lse_contig.nrb);
   const unsigned agg_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * agg.nrb);
-  LGeom contig = col;
-  contig.nrb = (N + kRowsPerBlock - 1) / kRowsPerBlock;
-  const unsigned contig_grid = static_cast<unsigned>(s.BH * contig.nrb);
+  const unsigned app_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * app.nrb);
 
   RGeom rg{BH, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
@@ -194,17 +242,17 @@ int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned cha
     const bool first = it == 1, last = it == s.T;
     if (first) {
       ok(timed(1, st, [&] {
-        k_lse<T, D, kRW, kNW, true, true><<<contig_grid, kNW * kWave, 0, st>>>(q, kbar, nullptr, lse, contig);
+        k_lse<T, D, kLseRW, kLseNW, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(q, kbar, nullptr, lse, lse_contig);
       }));
       ok(timed(2, st, [&] {
-        k_aggregate<T, D, kRW, kNW, true><<<agg_grid, kNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, agg);
+        k_aggregate<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, agg);
       }));
     } else {
       ok(timed(1, st, [&] {
-        k_lse<T, D, kRW, kNW, false, false><<<col_grid, kNW * kWave, 0, st>>>(q, ktil, hent, lse, col);
+        k_lse<T, D, kLseRW, kLseNW, false, false><<<lse_col_grid, kLseNW * kWave, 0, st>>>(q, ktil, hent, lse, lse_col);
       }));
       ok(timed(2, st, [&] {
-        k_aggregate<T, D, kRW, kNW, false><<<agg_grid, kNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, agg);
+        k_aggregate<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, agg);
       }));
     }
     if (last) {
@@ -219,16 +267,29 @@ int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned cha
   }
   if (s.T == 1) {
     ok(timed(4, st, [&] {
-      k_apply<T, D, kRW, kNW, true><<<col_grid, kNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, out, col);
+      k_apply<T, D, kAppRW, kAppNW, true><<<app_grid, kAppNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, out, app);
     }));
   } else {
     ok(timed(4, st, [&] {
-      k_apply<T, D, kRW, kNW, false><<<col_grid, kNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, out, col);
+      k_apply<T, D, kAppRW, kAppNW, false><<<app_grid, kAppNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, out, app);
     }));
   }
-  if (err != hipSuccess) {
-    g_last_hip_error = static_cast<int>(err);
-    return MONARCH_EHIP;
+  return err;
+}
+
+template <typename T, int D>
+int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned char* ws,
+        const Workspace& w, hipStream_t st) {
+  const long long per = s.N * D;
+  for (long long h0 = 0; h0 < s.BH; h0 += w.hc) {
+    Shape ps = s;
+    ps.BH = s.BH - h0 < w.hc ? s.BH - h0 : w.hc;
+    const long long o = h0 * per;
+    const hipError_t err = run_pass<T, D>(q + o, k + o, v + o, out + o, ps, ws, w, st);
+    if (err != hipSuccess) {
+      g_last_hip_error = static_cast<int>(err);
+      return MONARCH_EHIP;
+    }
   }
   return MONARCH_OK;
 }

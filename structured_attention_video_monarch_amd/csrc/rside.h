@@ -25,15 +25,12 @@ struct RGeom {
   float c;    // log2(e) / sqrt(d)
 };
 
-template <typename T>
-__host__ __device__ constexpr int rside_pitch(int D) { return (D < 32 ? 32 : D) + Elem<T>::kPad; }
-
 // Dynamic LDS bytes: the K block and the V block (last iteration only), both
-// row-major [b2p][pitch].  The products with R read them by columns through
-// transposing LDS reads; K serves both the logits and the next keys.
+// swizzled tiles of b2p rows.  The products with R read them by columns
+// through transposing LDS reads; K serves both the logits and the next keys.
 template <typename T>
 inline size_t rside_lds_bytes(int D, int b2p, bool last) {
-  return sizeof(T) * static_cast<size_t>(b2p) * rside_pitch<T>(D) * (last ? 2 : 1);
+  return sizeof(T) * static_cast<size_t>(b2p) * (D < 32 ? 32 : D) * (last ? 2 : 1);
 }
 
 template <typename T, int D, bool LAST>
@@ -44,13 +41,13 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
-  constexpr int PITCH = DK + E::kPad;
+  using TL = Tile<T, DK>;
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
   constexpr int MAXCP = 4;  // b2 <= 128
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* sK = reinterpret_cast<T*>(smem_raw);
-  T* sV = sK + p.b2p * PITCH;
+  T* sV = sK + p.b2p * DK;
   const int nt = blockDim.x;
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
@@ -82,8 +79,8 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
         kv = *reinterpret_cast<const uint4*>(k + blk + r * D + col);
         if (LAST) vv = *reinterpret_cast<const uint4*>(v + blk + r * D + col);
       }
-      *reinterpret_cast<uint4*>(sK + r * PITCH + col) = kv;
-      if (LAST) *reinterpret_cast<uint4*>(sV + r * PITCH + col) = vv;
+      *reinterpret_cast<uint4*>(sK + TL::off(r, col)) = kv;
+      if (LAST) *reinterpret_cast<uint4*>(sV + TL::off(r, col)) = vv;
     }
   }
   __syncthreads();
@@ -102,7 +99,7 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
         for (int s = 0; s < KS; ++s)
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
-            const typename E::frag a = E::load(sK + (32 * cp + perm_row(ct, l16)) * PITCH + s * 32 + 8 * G);
+            const typename E::frag a = TL::load8(sK, 32 * cp + perm_row(ct, l16), s * 32 + 8 * G);
             S[cp][ct] = E::mma(a, bq[s], S[cp][ct]);
           }
       }
@@ -163,8 +160,8 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
       for (int dp = 0; dp < NACC; ++dp)
 #pragma unroll
         for (int dt = 0; dt < (NDP > 0 ? 2 : 1); ++dt) {
-          const typename E::frag a = D >= 32 ? E::load_tr(sX, PITCH, 32 * cp, 32 * dp + 4 * dt, 8)
-                                             : E::load_tr(sX, PITCH, 32 * cp, 0, 4);
+          const typename E::frag a = D >= 32 ? TL::load_tr(sX, 32 * cp, 32 * dp + 4 * dt, 8)
+                                             : TL::load_tr(sX, 32 * cp, 0, 4);
           acc[dp][dt][0] = E::mma(a, pf[cp], acc[dp][dt][0]);
         }
     }
