@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB (float32 read + write), "
+                         "to scale HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the forward pass "
@@ -132,6 +135,17 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                          "launches": 3}), flush=True)
+        return
+
     import structured_attention_video_monarch_amd as M
     from structured_attention_video_monarch_amd import inputs as I
 
