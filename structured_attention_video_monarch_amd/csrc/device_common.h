@@ -224,4 +224,49 @@ struct TileLoader {
   }
 };
 
+
+// Global -> LDS DMA of a ROWS x DK tile (row stride `rstride` elements) into a
+// swizzled Tile.  One wave instruction writes 1 KiB of consecutive LDS bytes,
+// lane l 16 bytes at base + 16*l (measured on gfx950), so each lane fetches
+// the global chunk that belongs at its LDS position.  Rows >= nvalid are read
+// from row nvalid-1 and columns >= D (only D = 16 with DK = 32) from column
+// col - D: finite data that callers give zero weight (rows) or multiply by
+// zero contraction slots (columns).  Completion is tracked by vmcnt; callers
+// wait (a __syncthreads waits for everything) before reading the tile.
+template <typename T, int D, int DK, int ROWS, int NW>
+struct TileDma {
+  static constexpr int V = Elem<T>::kVec;
+  static constexpr int ROWB = DK * static_cast<int>(sizeof(T));
+  static constexpr int NINS = ROWS * ROWB / 1024;
+  static_assert(NINS % NW == 0 && NINS >= NW, "tile must split evenly over the waves");
+  static constexpr int PERW = NINS / NW;
+  __device__ static inline void issue(T* tile, const T* g, long long rstride, int nvalid) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < PERW; ++j) {
+      const int ci = wave * PERW + j;
+      const int byte = ci * 1024 + 16 * lane;
+      const int r = byte / ROWB;
+      const int c = ((byte % ROWB) / 16) ^ Tile<T, DK>::swz(r);  // logical chunk at this position
+      int col = c * V;
+      if (col >= D) col -= D;
+      const int rr = r < nvalid ? r : nvalid - 1;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g + rr * rstride + col),
+                                       (__attribute__((address_space(3))) void*)(tile + ci * (1024 / static_cast<int>(sizeof(T)))),
+                                       16, 0, 0);
+    }
+  }
+};
+
+// Global -> LDS DMA of 64 floats, one per lane of the calling wave:
+// dst[l] = src[min(l, nvalid - 1) * stride].
+__device__ inline void dma_floats64(float* dst, const float* src, long long stride, int nvalid) {
+  const int lane = threadIdx.x & 63;
+  const int rr = lane < nvalid ? lane : nvalid - 1;
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + rr * stride),
+                                   (__attribute__((address_space(3))) void*)(dst), 4, 0, 0);
+}
+
+
+
 }  // namespace monarch

@@ -49,9 +49,10 @@ struct KeySrc {
       hstride = p.b2;
     }
   }
+  // entropy bias of key block c1 in log2 units (the R-step stores it in bits)
   __device__ float bias(int c1, int b1) const {
     if (c1 >= b1) return kNegInf;
-    return BCAST ? 0.0f : h[static_cast<long long>(c1) * hstride] * kLog2e;
+    return BCAST ? 0.0f : h[static_cast<long long>(c1) * hstride];
   }
 };
 
@@ -80,6 +81,7 @@ struct ColItem {
 #endif
 constexpr int kStep = MONARCH_STEP;
 constexpr int kHalves = kStep / 32;
+static_assert(kStep == 64, "one 64-lane float DMA stages the log-sum-exps / entropies of a step");
 // Minimum waves per SIMD the register allocator must allow (launch bounds).
 #ifndef MONARCH_LSE_MINW
 #define MONARCH_LSE_MINW 1
@@ -175,16 +177,16 @@ __device__ inline void weighted_sum(f32x4 (&acc)[NACC][2][RW], const typename El
 // the logits do not depend on the column or tile).
 template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG>
 __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
-                                                    const T* __restrict__ kt,
-                                                    const float* __restrict__ h2,
-                                                    float* __restrict__ lse, LGeom p) {
+                                                                      const T* __restrict__ kt,
+                                                                      const float* __restrict__ h2,
+                                                                      float* __restrict__ lse, LGeom p) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
   constexpr int RB = NW * RW * 16;
-  constexpr int NT = NW * kWave;
+  using Dma = TileDma<T, D, DK, kStep, NW>;
   __shared__ __align__(16) T sK[2][kStep * DK];
-  __shared__ float sBias[2][kStep];
+  __shared__ __align__(16) float sH[2][kStep];
 
   int bh, g = 0, a2 = 0, nrows;
   long long n0, nstride;
@@ -208,6 +210,14 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
   const int l16 = lane & 15, G = lane >> 4;
   const T* qh = q + static_cast<long long>(bh) * p.N * D;
 
+  const int nst = (p.b1 + kStep - 1) / kStep;
+  auto fetch = [&](int st, int buf) {
+    const int c1 = st * kStep;
+    Dma::issue(sK[buf], ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
+    if (!BCAST && wave == NW - 1) dma_floats64(sH[buf], ks.h + static_cast<long long>(c1) * ks.hstride, ks.hstride, p.b1 - c1);
+  };
+  fetch(0, 0);
+
   typename E::frag bq[RW][KS];
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
@@ -218,39 +228,27 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
       bq[rt][s] = (r < nrows && col < D) ? E::load(qh + (n0 + r * nstride) * D + col) : E::zero();
     }
   }
-
   float m[RW], l[RW];
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) { m[rt] = -1e30f; l[rt] = 0.0f; }
-
-  TileLoader<T, D, DK, kStep, NT> ld;
-  const int nst = (p.b1 + kStep - 1) / kStep;
-  float bpre = 0.0f;
-  auto fetch = [&](int st) {
-    const int c1 = st * kStep;
-    ld.load(ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
-    if (threadIdx.x < kStep) bpre = ks.bias(c1 + threadIdx.x, p.b1);
-  };
-  fetch(0);
-  ld.store(sK[0]);
-  if (threadIdx.x < kStep) sBias[0][threadIdx.x] = bpre;
   __syncthreads();
+
   for (int st = 0; st < nst; ++st) {
     const int cur = st & 1;
-    const bool more = st + 1 < nst;
-    if (more) fetch(st + 1);
+    if (st + 1 < nst) fetch(st + 1, cur ^ 1);
 #pragma unroll
     for (int half = 0; half < kHalves; ++half) {
       const int k0 = 32 * half;
-      // keys past b1 only exist in the last step
-      if (st * kStep + k0 >= p.b1) break;
-      const bool masked = !BCAST || (st + 1) * kStep > p.b1;
+      const int c1_0 = st * kStep + k0;  // first key of this 32-key block
+      if (c1_0 >= p.b1) break;
+      // keys past b1 only exist in the last block
+      const bool tail = c1_0 + 32 > p.b1;
       typename E::frag a[KS][2];
       load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
       float bias[8];
-      if (masked) {
+      if (!BCAST) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bias[j] = sBias[cur][k0 + 8 * G + j];
+        for (int j = 0; j < 8; ++j) bias[j] = sH[cur][k0 + 8 * G + j];
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x4 S[2][RW];
@@ -258,12 +256,11 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         float x[8];
-        if (masked) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
-        } else {
+        for (int j = 0; j < 8; ++j) x[j] = BCAST ? S[j >> 2][rt][j & 3] * p.c : __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
+        if (tail) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = S[j >> 2][rt][j & 3] * p.c;
+          for (int j = 0; j < 8; ++j) x[j] = c1_0 + 8 * G + j < p.b1 ? x[j] : kNegInf;
         }
         float cm = x[0];
 #pragma unroll
@@ -275,10 +272,6 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
         l[rt] = acc;
         m[rt] = mn;
       }
-    }
-    if (more) {
-      ld.store(sK[cur ^ 1]);
-      if (threadIdx.x < kStep) sBias[cur ^ 1][threadIdx.x] = bpre;
     }
     __syncthreads();
   }
@@ -440,21 +433,21 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
 // log-sum-exp (no running rescale), computed as y^T = U^T P^T.
 template <typename T, int D, int RW, int NW, bool BCAST>
 __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T* __restrict__ q,
-                                                      const T* __restrict__ kt,
-                                                      const float* __restrict__ h2,
-                                                      const float* __restrict__ lse,
-                                                      const T* __restrict__ u,
-                                                      T* __restrict__ out, LGeom p) {
+                                                                        const T* __restrict__ kt,
+                                                                        const float* __restrict__ h2,
+                                                                        const float* __restrict__ lse,
+                                                                        const T* __restrict__ u,
+                                                                        T* __restrict__ out, LGeom p) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
   constexpr int RB = NW * RW * 16;
-  constexpr int NT = NW * kWave;
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
+  using Dma = TileDma<T, D, DK, kStep, NW>;
   __shared__ __align__(16) T sK[2][kStep * DK];
   __shared__ __align__(16) T sU[2][kStep * DK];
-  __shared__ float sBias[2][kStep];
+  __shared__ __align__(16) float sH[2][kStep];
 
   ColItem it(p, RB);
   if (it.nrows <= 0) return;
@@ -470,6 +463,15 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
   const T* ucol = u + ((static_cast<long long>(bh) * p.t + g) * p.b1 * p.b2 + a2) * D;
   const long long ustride = static_cast<long long>(p.b2) * D;
 
+  const int nst = (p.b1 + kStep - 1) / kStep;
+  auto fetch = [&](int st, int buf) {
+    const int c1 = st * kStep;
+    Dma::issue(sK[buf], ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
+    Dma::issue(sU[buf], ucol + c1 * ustride, ustride, p.b1 - c1);
+    if (!BCAST && wave == NW - 1) dma_floats64(sH[buf], ks.h + static_cast<long long>(c1) * ks.hstride, ks.hstride, p.b1 - c1);
+  };
+  fetch(0, 0);
+
   typename E::frag bq[RW][KS];
   float nlrow[RW];  // -lse of the lane's rows
 #pragma unroll
@@ -483,7 +485,6 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
     }
     nlrow[rt] = ok ? -lh[n0 + r * nstride] : 0.0f;
   }
-
   f32x4 acc[NACC][2][RW];
 #pragma unroll
   for (int dp = 0; dp < NACC; ++dp)
@@ -491,70 +492,45 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
-
-  TileLoader<T, D, DK, kStep, NT> ldk;
-  TileLoader<T, D, DK, kStep, NT> ldu;
-  float bpre = 0.0f;
-  const int nst = (p.b1 + kStep - 1) / kStep;
-  auto fetch = [&](int st) {
-    const int c1 = st * kStep;
-    ldk.load(ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
-    ldu.load(ucol + c1 * ustride, ustride, p.b1 - c1);
-    if (threadIdx.x < kStep) bpre = ks.bias(c1 + threadIdx.x, p.b1);
-  };
-  auto put = [&](int buf) {
-    ldk.store(sK[buf]);
-    ldu.store(sU[buf]);
-    if (threadIdx.x < kStep) sBias[buf][threadIdx.x] = bpre;
-  };
-  fetch(0);
-  put(0);
   __syncthreads();
+
   for (int st = 0; st < nst; ++st) {
     const int cur = st & 1;
-    const bool more = st + 1 < nst;
-    if (more) fetch(st + 1);
+    if (st + 1 < nst) fetch(st + 1, cur ^ 1);
 #pragma unroll
     for (int half = 0; half < kHalves; ++half) {
       const int k0 = 32 * half;
-      if (st * kStep + k0 >= p.b1) break;
-      // keys past b1 only exist in the last step; their U rows are zero but
-      // their weights are masked as well
-      const bool masked = !BCAST || (st + 1) * kStep > p.b1;
+      const int c1_0 = st * kStep + k0;
+      if (c1_0 >= p.b1) break;
+      // keys past b1 only exist in the last block: weight 0
+      const bool tail = c1_0 + 32 > p.b1;
       typename E::frag a[KS][2];
       typename E::frag v[NACC][2];
       load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
       load_cols<T, D, DK, NACC>(v, sU[cur], k0);
       float bias[8];
-      if (masked) {
+      if (!BCAST) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bias[j] = sBias[cur][k0 + 8 * G + j];
+        for (int j = 0; j < 8; ++j) bias[j] = sH[cur][k0 + 8 * G + j];
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x4 S[2][RW];
       logits<T, KS, RW>(S, a, bq);
       typename E::frag pf[RW];
-      if (masked) {
 #pragma unroll
-        for (int rt = 0; rt < RW; ++rt) {
-          float w[8];
+      for (int rt = 0; rt < RW; ++rt) {
+        float w[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j] + nlrow[rt]));
-          pf[rt] = E::pack(w);
+        for (int j = 0; j < 8; ++j)
+          w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? nlrow[rt] : bias[j] + nlrow[rt]));
+        if (tail) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = c1_0 + 8 * G + j < p.b1 ? w[j] : 0.0f;
         }
-      } else {
-#pragma unroll
-        for (int rt = 0; rt < RW; ++rt) {
-          float w[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, nlrow[rt]));
-          pf[rt] = E::pack(w);
-        }
+        pf[rt] = E::pack(w);
       }
       weighted_sum<T, D, NACC, RW>(acc, v, pf);
     }
-    if (more) put(cur ^ 1);
     __syncthreads();
   }
 

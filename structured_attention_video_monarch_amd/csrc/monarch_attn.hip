@@ -48,7 +48,7 @@ thread_local int g_last_hip_error = 0;
 #define MONARCH_APP_RW 2
 #endif
 #ifndef MONARCH_APP_NW
-#define MONARCH_APP_NW 8
+#define MONARCH_APP_NW 4
 #endif
 constexpr int kLseRW = MONARCH_LSE_RW, kLseNW = MONARCH_LSE_NW;
 constexpr int kAggRW = MONARCH_AGG_RW, kAggNW = MONARCH_AGG_NW;
@@ -223,8 +223,8 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
   app.nrb = (ngmax + app_rows - 1) / app_rows;
   const unsigned lse_col_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lse_col.nrb);
   const unsigned lse_contig_grid = static_cast<unsigned>(s.BH * lse_contig.nrb);
-  const unsigned agg_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * agg.nrb);
   const unsigned app_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * app.nrb);
+  const unsigned agg_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * agg.nrb);
 
   RGeom rg{BH, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);

@@ -7,7 +7,7 @@
 // It is consumed at once and never stored:
 //   last iteration:  U[g,c1,a2,:]  = sum_c2 R v_(c1,c2)   (written over Qh)
 //   otherwise:       Kt[g,c1,a2,:] = sum_c2 R k_(c1,c2)   and the row entropy
-//                    H[g,c1,a2] = -sum_c2 R log R (in nats), the keys and bias
+//                    H[g,c1,a2] = -sum_c2 R log2 R (in bits), the keys and bias
 //                    of the next L-step (the entropy computed alongside the
 //                    block softmax, as in the VMonarch abstract's fused
 //                    "online entropy").
@@ -185,8 +185,9 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
     if (!LAST) {
       rx += __shfl_xor(rx, 16);
       rx += __shfl_xor(rx, 32);
-      // H = ln(sum e^x) - sum R x, here from log2 quantities: H = (lse2 - sum R x2) * ln 2
-      if (row_ok && G == 0) hent[row] = (lse2 - rx) * 0.69314718055994531f;
+      // entropy in bits (the unit of the L-step's log2 logits):
+      // H2 = log2(sum 2^x) - sum R x = H / ln 2
+      if (row_ok && G == 0) hent[row] = lse2 - rx;
     }
   }
 }
