@@ -33,6 +33,11 @@ inline size_t rside_lds_bytes(int D, int b2p, bool last) {
   return sizeof(T) * static_cast<size_t>(b2p) * (D < 32 ? 32 : D) * (last ? 2 : 1);
 }
 
+// Tiles whose aggregated queries one wave loads together (bf16).
+#ifndef MONARCH_RSTEP_TB
+#define MONARCH_RSTEP_TB 2
+#endif
+
 template <typename T, int D, bool LAST>
 __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T* __restrict__ v,
                                                T* qhat,   // [BH][t][b1][b2][D]; U written over it when LAST
@@ -48,7 +53,6 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* sK = reinterpret_cast<T*>(smem_raw);
   T* sV = sK + p.b2p * DK;
-  const int nt = blockDim.x;
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
   const int c1 = item % p.b1;
@@ -62,31 +66,50 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
   const int ncp = p.b2p / 32;
   auto qrow = [&](int g) { return ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2; };
 
-  // first tile's aggregated queries in flight while K and V are staged
-  typename E::frag bq[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const int col = s * 32 + 8 * G;
-    bq[s] = (row_ok && col < D) ? E::load(qhat + qrow(0) * D + col) : E::zero();
-  }
+  // K (and V) blocks by global->LDS DMA: rows past b2 are copies of row b2-1,
+  // whose logits are masked below (weight 0)
   {
-    constexpr int V = E::kVec;
-    constexpr int VPR = DK / V;
-    for (int idx = threadIdx.x; idx < p.b2p * VPR; idx += nt) {
-      const int r = idx / VPR, col = (idx % VPR) * V;
-      uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (r < p.b2 && col < D) {
-        kv = *reinterpret_cast<const uint4*>(k + blk + r * D + col);
-        if (LAST) vv = *reinterpret_cast<const uint4*>(v + blk + r * D + col);
-      }
-      *reinterpret_cast<uint4*>(sK + TL::off(r, col)) = kv;
-      if (LAST) *reinterpret_cast<uint4*>(sV + TL::off(r, col)) = vv;
+    constexpr int ROWB = DK * static_cast<int>(sizeof(T));
+    const int nins = p.b2p * ROWB / 1024;
+    const int nw = blockDim.x / kWave;
+    for (int ci = wave; ci < nins; ci += nw) {
+      const int byte = ci * 1024 + 16 * lane;
+      const int r = byte / ROWB;
+      const int c = ((byte % ROWB) / 16) ^ TL::swz(r);
+      int col = c * E::kVec;
+      if (col >= D) col -= D;
+      const long long src = blk + static_cast<long long>(r < p.b2 ? r : p.b2 - 1) * D + col;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(k + src),
+                                       (__attribute__((address_space(3))) void*)(sK + ci * (1024 / static_cast<int>(sizeof(T)))),
+                                       16, 0, 0);
+      if (LAST)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(v + src),
+                                         (__attribute__((address_space(3))) void*)(sV + ci * (1024 / static_cast<int>(sizeof(T)))),
+                                         16, 0, 0);
     }
   }
+  // aggregated queries of up to TB tiles in flight at once
+  constexpr int TB = sizeof(T) == 2 ? MONARCH_RSTEP_TB : 1;
+  typename E::frag bq[TB][KS];
+  auto load_queries = [&](int g0) {
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int col = s * 32 + 8 * G;
+        bq[i][s] = (g0 + i < p.t && row_ok && col < D) ? E::load(qhat + qrow(g0 + i) * D + col) : E::zero();
+      }
+  };
+  load_queries(0);
   __syncthreads();
   const T* sX = LAST ? sV : sK;
 
-  for (int g = 0; g < p.t; ++g) {
+  for (int g0 = 0; g0 < p.t; g0 += TB) {
+    if (g0 > 0) load_queries(g0);
+#pragma unroll
+  for (int gi = 0; gi < TB; ++gi) {
+    const int g = g0 + gi;
+    if (g >= p.t) break;
     const long long row = qrow(g);
     // logits, transposed: rows c2 (permuted within 32-blocks), columns a2
     f32x4 S[MAXCP][2];
@@ -100,17 +123,8 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             const typename E::frag a = TL::load8(sK, 32 * cp + perm_row(ct, l16), s * 32 + 8 * G);
-            S[cp][ct] = E::mma(a, bq[s], S[cp][ct]);
+            S[cp][ct] = E::mma(a, bq[gi][s], S[cp][ct]);
           }
-      }
-    }
-    // next tile's aggregated queries (their rows are not written by this g)
-    if (g + 1 < p.t) {
-      const long long nrow = qrow(g + 1);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int col = s * 32 + 8 * G;
-        bq[s] = (row_ok && col < D) ? E::load(qhat + nrow * D + col) : E::zero();
       }
     }
     // softmax over c2 for column a2: lane holds c2 = 32cp + 8G + j
@@ -189,6 +203,7 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
       // H2 = log2(sum 2^x) - sum R x = H / ln 2
       if (row_ok && G == 0) hent[row] = lse2 - rx;
     }
+  }
   }
 }
 
