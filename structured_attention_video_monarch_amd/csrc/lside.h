@@ -427,6 +427,121 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
   }
 }
 
+// ------------------------------------------------------- k_aggregate_col --
+// Same result as k_aggregate for tiles of at most kColRows rows: the whole q
+// column of the tile and its log-sum-exps are copied to LDS once (DMA), then
+// all its 32-row blocks run with no further barrier or wait.
+constexpr int kColRows = 256;
+
+template <typename T, int D, int RW, int NW, bool BCAST>
+__global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(const T* __restrict__ q,
+                                                                                const T* __restrict__ kt,
+                                                                                const float* __restrict__ h2,
+                                                                                const float* __restrict__ lse,
+                                                                                T* __restrict__ qhat, LGeom p) {
+  using E = Elem<T>;
+  constexpr int DK = D < 32 ? 32 : D;
+  constexpr int KS = DK / 32;
+  constexpr int CB = NW * RW * 16;
+  constexpr int NDP = D / 32;
+  constexpr int NACC = NDP > 0 ? NDP : 1;
+  using Dma = TileDma<T, D, DK, kStep, NW>;
+  constexpr int NSTEP = kColRows / kStep;
+  __shared__ __align__(16) T sQ[NSTEP][kStep * DK];
+  __shared__ __align__(16) float sL[NSTEP][kStep];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int cb = logical % p.nrb;
+  int rest = logical / p.nrb;
+  const int a2 = rest % p.b2;
+  rest /= p.b2;
+  const int g = rest % p.t;
+  const int bh = rest / p.t;
+  const int lo = tile_lo(g, p.b1, p.t), hi = tile_lo(g + 1, p.b1, p.t);
+  const int nrows = hi - lo;
+  const int nst = (nrows + kStep - 1) / kStep;
+  const KeySrc<T, D, BCAST> ks(kt, h2, p, bh, g, a2);
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int l16 = lane & 15, G = lane >> 4;
+
+  const T* qh = q + static_cast<long long>(bh) * p.N * D;
+  const float* lh = lse + static_cast<long long>(bh) * p.N;
+  const long long qstride = static_cast<long long>(p.b2) * D;
+  for (int st = 0; st < nst; ++st) {
+    const long long n_first = static_cast<long long>(lo + st * kStep) * p.b2 + a2;
+    const int nvalid = nrows - st * kStep;
+    Dma::issue(sQ[st], qh + n_first * D, qstride, nvalid);
+    if (wave == NW - 1) dma_floats64(sL[st], lh + n_first, p.b2, nvalid);
+  }
+
+  typename E::frag bk[RW][KS];
+  float bias[RW];
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int col = s * 32 + 8 * G;
+      bk[rt][s] = (c1 < p.b1 && col < D) ? E::load(ks.k + c1 * ks.kstride + col) : E::zero();
+    }
+    bias[rt] = BCAST ? 0.0f : (c1 < p.b1 ? ks.bias(c1, p.b1) : 0.0f);
+  }
+  f32x4 acc[NACC][2][RW];
+  f32x4 accb[RW];
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    accb[rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
+  }
+  const typename E::frag ones = E::ones();
+  __syncthreads();
+
+  const int nblk = (nrows + 31) / 32;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int st = blk / kHalves, k0 = 32 * (blk % kHalves);
+    const int r0 = 32 * blk;
+    const bool tail = r0 + 32 > nrows;
+    typename E::frag a[KS][2];
+    typename E::frag v[NACC][2];
+    load_rows<T, DK, KS>(a, sQ[st], k0, l16, G);
+    load_cols<T, D, DK, NACC>(v, sQ[st], k0);
+    float lr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lr[j] = sL[st][k0 + 8 * G + j];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 S[2][RW];
+    logits<T, KS, RW>(S, a, bk);
+    typename E::frag pf[RW];
+#pragma unroll
+    for (int rt = 0; rt < RW; ++rt) {
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? -lr[j] : bias[rt] - lr[j]));
+      if (tail) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = r0 + 8 * G + j < nrows ? w[j] : 0.0f;
+      }
+      pf[rt] = E::pack(w);
+      accb[rt] = E::mma(ones, pf[rt], accb[rt]);
+    }
+    weighted_sum<T, D, NACC, RW>(acc, v, pf);
+  }
+
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    const float b = accb[rt][0];
+    const float inv = b > 0.0f ? 1.0f / b : 0.0f;
+    const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
+    if (c1 >= p.b1) continue;
+    T* dst = qhat + ((((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2) * D);
+    store_rows<T, D, NACC, RW>(dst, acc, rt, inv, G);
+  }
+}
+
 // ---------------------------------------------------------------- k_apply --
 // One workgroup: (bh, g, a2) and a block of RB = NW*RW*16 rows a1 of tile g.
 // y[a1,:] = sum_c1 L[a1,c1] U[g,c1,a2,:], with L normalised by the stored

@@ -225,6 +225,12 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
   const unsigned lse_contig_grid = static_cast<unsigned>(s.BH * lse_contig.nrb);
   const unsigned app_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * app.nrb);
   const unsigned agg_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * agg.nrb);
+  // whole tile column resident in LDS when it is short enough (bf16 only:
+  // the f32 column would not fit)
+#ifndef MONARCH_AGG_COL
+#define MONARCH_AGG_COL 1
+#endif
+  const bool col_fits = MONARCH_AGG_COL && sizeof(T) == 2 && ngmax <= kColRows;
 
   RGeom rg{BH, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
@@ -245,14 +251,20 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
         k_lse<T, D, kLseRW, kLseNW, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(q, kbar, nullptr, lse, lse_contig);
       }));
       ok(timed(2, st, [&] {
-        k_aggregate<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, agg);
+        if (col_fits)
+          k_aggregate_col<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, agg);
+        else
+          k_aggregate<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, agg);
       }));
     } else {
       ok(timed(1, st, [&] {
         k_lse<T, D, kLseRW, kLseNW, false, false><<<lse_col_grid, kLseNW * kWave, 0, st>>>(q, ktil, hent, lse, lse_col);
       }));
       ok(timed(2, st, [&] {
-        k_aggregate<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, agg);
+        if (col_fits)
+          k_aggregate_col<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, agg);
+        else
+          k_aggregate<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, agg);
       }));
     }
     if (last) {
