@@ -238,13 +238,11 @@ struct TileDma {
   static constexpr int V = Elem<T>::kVec;
   static constexpr int ROWB = DK * static_cast<int>(sizeof(T));
   static constexpr int NINS = ROWS * ROWB / 1024;
-  static_assert(NINS % NW == 0 && NINS >= NW, "tile must split evenly over the waves");
-  static constexpr int PERW = NINS / NW;
+  static_assert(NINS * 1024 == ROWS * ROWB, "tile must be a whole number of KiB");
   __device__ static inline void issue(T* tile, const T* g, long long rstride, int nvalid) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < PERW; ++j) {
-      const int ci = wave * PERW + j;
+    for (int ci = wave; ci < NINS; ci += NW) {
       const int byte = ci * 1024 + 16 * lane;
       const int r = byte / ROWB;
       const int c = ((byte % ROWB) / 16) ^ Tile<T, DK>::swz(r);  // logical chunk at this position
