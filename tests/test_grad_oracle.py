@@ -1,0 +1,57 @@
+"""The gradient oracle against facts it does not compute itself, and planted
+mistakes in it that those facts must catch (CPU only)."""
+import os
+import types
+
+import pytest
+
+import oracle.monarch_grad as grad_oracle
+from grad_pins import ALL_CHECKS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "monarch_grad.py")
+
+MUTANTS = {
+    "dL_apply_missing": ("dL[:, lo:hi, :] = dy_cols @ Ug.transpose(0, 2, 1)",
+                         "dL[:, lo:hi, :] = 0.0 * (dy_cols @ Ug.transpose(0, 2, 1))"),
+    "dU_unweighted": ("dU = (Lg.transpose(0, 2, 1) @ dy_cols)", "dU = (np.ones_like(Lg).transpose(0, 2, 1) @ dy_cols)"),
+    "dv_R_not_transposed": ("dvb += R[g].transpose(0, 2, 1) @ dU", "dvb += R[g] @ dU"),
+    "dz_no_centering": ("dz = R[g] * (dR - np.sum(R[g] * dR, axis=-1, keepdims=True))", "dz = R[g] * dR"),
+    "dqhat_no_scale": ("dq_hat = s * (dz @ kb)", "dq_hat = (dz @ kb)"),
+    "dk_r_missing": ("dkb += s * (dz.transpose(0, 2, 1) @ q_hat[g])", "pass"),
+    "G_no_beta": ("dq_hat / np.where(mass > 0, mass, 1.0)[:, :, None]", "dq_hat"),
+    "dL_agg_no_qhat_term": ("- np.sum(Gc * qh_c, axis=-1)[:, None, :]", "- 0.0"),
+    "dL_agg_sign": ("dL[:, lo:hi, :] += q_cols @ Gc.transpose(0, 2, 1)", "dL[:, lo:hi, :] -= q_cols @ Gc.transpose(0, 2, 1)"),
+    "dq_agg_missing": ("dqb[lo:hi] += (Lg @ Gc).transpose(1, 0, 2)", "pass"),
+    "dl_no_centering": ("dl = L * (dL - np.sum(L * dL, axis=-1, keepdims=True))", "dl = L * dL"),
+    "dq_l_missing": ("dqb += (s * (dl @ kbar)).transpose(1, 0, 2)", "pass"),
+    "dkbar_not_mean": ("dkb += dkbar[:, None, :] / b2", "dkb += dkbar[:, None, :]"),
+    "dkbar_wrong_axis": ('np.einsum("pac,pad->cd", dl, q_perm)', 'np.einsum("pca,pad->cd", dl, q_perm)'),
+    "tile0_U": ("Ug = U[g].transpose(1, 0, 2)", "Ug = U[0].transpose(1, 0, 2)"),
+}
+
+
+def _mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    mod = types.ModuleType("oracle.monarch_grad_mutant")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), SRC + ":mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
+def test_pin(check):
+    check(grad_oracle)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant(*MUTANTS[name])
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception as e:  # an assertion, or a crash the mistake causes
+            failed.append((check.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"
