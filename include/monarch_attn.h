@@ -93,6 +93,45 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
                         int b1, int b2, int tiles, int iters, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- training: the one-iteration form and its gradient ----
+ * The pages' deployed regime is one iteration after finetuning the video
+ * model with this attention in place (yunpan.plus MonarchRT article,
+ * "Innovation 3: finetuning and efficient kernels", Fig. 4 right), which
+ * needs the gradient of the layer.  These calls fix iters = 1.
+ *
+ * monarch_attn_fwd_train computes the same out as monarch_attn_fwd_ws with
+ * iters = 1 and also leaves in `state` (a caller-owned device buffer of at
+ * least monarch_attn_train_state_bytes(...) bytes, 256-byte aligned, not
+ * overlapping q, k, v or out) what the backward pass reads: the block-mean
+ * keys, the L-row log-sum-exps, the column masses beta, the aggregated
+ * queries Qh and U = R V of every tile.  Its size is
+ *   B*H*(b1*d*e + 4*N + 4*t*N + 2*t*N*d*e)  (+ alignment), e = element bytes.
+ *
+ * monarch_attn_bwd takes the same q, k, v, the out and state of a
+ * monarch_attn_fwd_train call with the same arguments, and dout = dLoss/dout,
+ * and writes dq, dk, dv = dLoss/dq, dLoss/dk, dLoss/dv ([B,H,N,d], same
+ * dtype).  Definition: with R starting uniform the L-step keys are the block
+ * means Kbar[c1] = mean_c2 k_(c1,c2), and the gradient is the chain rule
+ * through L = softmax(s q Kbar^T), Qh = sum L q / beta (0 where beta == 0),
+ * R = softmax(s Qh k^T), U = R V and y = L U on the permuted index.
+ * dq, dk, dv must not overlap each other or any input (state included).
+ * It allocates a workspace stream-ordered (about t*N*d*(2e + 4/d) + N*d*4
+ * bytes per head).  Returns MONARCH_EUNSUPPORTED where the key-block pass
+ * does not fit in LDS (4 * roundup(b2, 32) * max(d, 32) * e bytes must stay
+ * below 160 KiB: f32 needs b2 <= 64 at d = 128).  State from another shape
+ * or dtype gives undefined results. */
+size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d,
+                                      int b1, int b2, int tiles, int dtype);
+int monarch_attn_fwd_train(const void* q, const void* k, const void* v, void* out,
+                           int B, int H, int f, int h, int w, int d,
+                           int b1, int b2, int tiles, int dtype,
+                           void* state, size_t state_bytes, void* stream);
+int monarch_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const void* dout, void* dq, void* dk, void* dv,
+                     int B, int H, int f, int h, int w, int d,
+                     int b1, int b2, int tiles, int dtype,
+                     void* state, size_t state_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* monarch_attn_status_string(int status);
 
@@ -105,8 +144,10 @@ int monarch_attn_last_hip_error(void);
  * adds each kernel's elapsed milliseconds and launch count into ms[i] and
  * launches[i] for kernel id i < n, and forgets them.  Kernel ids:
  * 0 block-mean keys, 1 L-row log-sum-exp, 2 R-side aggregation through L,
- * 3 R-step block softmax (+ R V or next keys/entropy), 4 L-apply. */
-#define MONARCH_NUM_KERNELS 5
+ * 3 R-step block softmax (+ R V or next keys/entropy), 4 L-apply;
+ * backward: 5 dU per tile column, 6 R-step per key block, 7 row pass (dq),
+ * 8 block-mean key gradient, 9 dk assembly. */
+#define MONARCH_NUM_KERNELS 10
 int monarch_attn_profile_enable(int on);
 int monarch_attn_profile_collect(double* ms, long* launches, int n);
 const char* monarch_attn_kernel_name(int id);

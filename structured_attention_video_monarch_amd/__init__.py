@@ -1,4 +1,4 @@
-"""MonarchAttention forward for MI355X (gfx950): thin Python binding.
+"""MonarchAttention for MI355X (gfx950): thin Python binding.
 
 Every step of the computation runs in ``libmonarch_attn.so`` (HIP kernels for
 gfx950); this module only marshals arguments: device pointers of torch
@@ -24,7 +24,7 @@ MONARCH_EHIP = -3
 MONARCH_ENOMEM = -4
 MONARCH_BF16 = 0
 MONARCH_F32 = 1
-MONARCH_NUM_KERNELS = 5
+MONARCH_NUM_KERNELS = 10
 
 _lib = None
 
@@ -46,6 +46,13 @@ def _declare(lib):
     lib.monarch_attn_workspace_bytes.restype = c_size_t
     lib.monarch_attn_fwd_ws.argtypes = [c_void_p] * 4 + dims + [c_int, c_void_p, c_size_t, c_void_p]
     lib.monarch_attn_fwd_ws.restype = c_int
+    tdims = [c_int] * 9  # B, H, f, h, w, d, b1, b2, tiles
+    lib.monarch_attn_train_state_bytes.argtypes = tdims + [c_int]
+    lib.monarch_attn_train_state_bytes.restype = c_size_t
+    lib.monarch_attn_fwd_train.argtypes = [c_void_p] * 4 + tdims + [c_int, c_void_p, c_size_t, c_void_p]
+    lib.monarch_attn_fwd_train.restype = c_int
+    lib.monarch_attn_bwd.argtypes = [c_void_p] * 8 + tdims + [c_int, c_void_p, c_size_t, c_void_p]
+    lib.monarch_attn_bwd.restype = c_int
     lib.monarch_attn_status_string.argtypes = [c_int]
     lib.monarch_attn_status_string.restype = ctypes.c_char_p
     lib.monarch_attn_last_hip_error.argtypes = []
@@ -158,6 +165,46 @@ def monarch_attn(q, k, v, f, h, w, b1=None, b2=None, tiles=1, iters=1):
     if q.dtype == torch.bfloat16:
         return monarch_attn_fwd(q, k, v, out, f, h, w, b1, b2, tiles, iters)
     return monarch_attn_fwd_f32(q, k, v, out, f, h, w, b1, b2, tiles, iters)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MONARCH_BF16
+    if t.dtype == torch.float32:
+        return MONARCH_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, tiles, dtype=MONARCH_BF16) -> int:
+    return int(lib().monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, tiles, dtype))
+
+
+def _state(state):
+    import torch
+    if not state.is_cuda or state.dtype != torch.uint8:
+        raise ValueError("state must be a uint8 GPU tensor")
+    return ctypes.c_void_p(state.data_ptr()), state.numel()
+
+
+def monarch_attn_fwd_train(q, k, v, out, f, h, w, b1, b2, tiles, state, stream=None):
+    """One-iteration forward that also fills ``state`` for the backward."""
+    ptrs = _tensors(q, k, v, out, q.dtype)
+    sp, sn = _state(state)
+    dims = _dims(q, f, h, w, b1, b2, tiles, 1)[:9]
+    _check(lib().monarch_attn_fwd_train(*ptrs, *dims, _dtype_code(q), sp, sn, _stream(stream)),
+           "monarch_attn_fwd_train")
+    return out
+
+
+def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, f, h, w, b1, b2, tiles, state, stream=None):
+    """dq, dk, dv <- gradients of sum(dout * out) (state from monarch_attn_fwd_train)."""
+    ptrs = _tensors(q, k, v, out, q.dtype) + _tensors(dout, dq, dk, dv, q.dtype)
+    sp, sn = _state(state)
+    dims = _dims(q, f, h, w, b1, b2, tiles, 1)[:9]
+    _check(lib().monarch_attn_bwd(*ptrs, *dims, _dtype_code(q), sp, sn, _stream(stream)),
+           "monarch_attn_bwd")
+    return dq, dk, dv
 
 
 def monarch_attn_profile_enable(on: bool = True):

@@ -304,7 +304,8 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
                                                           const T* __restrict__ kt,
                                                           const float* __restrict__ h2,
                                                           const float* __restrict__ lse,
-                                                          T* __restrict__ qhat, LGeom p) {
+                                                          T* __restrict__ qhat, float* __restrict__ beta_out,
+                                                          LGeom p) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -422,8 +423,9 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
     const float inv = b > 0.0f ? 1.0f / b : 0.0f;
     const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
     if (c1 >= p.b1) continue;
-    T* dst = qhat + ((((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2) * D);
-    store_rows<T, D, NACC, RW>(dst, acc, rt, inv, G);
+    const long long row = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
+    store_rows<T, D, NACC, RW>(qhat + row * D, acc, rt, inv, G);
+    if (beta_out && G == 0) beta_out[row] = b;
   }
 }
 
@@ -438,7 +440,8 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
                                                                                 const T* __restrict__ kt,
                                                                                 const float* __restrict__ h2,
                                                                                 const float* __restrict__ lse,
-                                                                                T* __restrict__ qhat, LGeom p) {
+                                                                                T* __restrict__ qhat,
+                                                                                float* __restrict__ beta_out, LGeom p) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -537,8 +540,9 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
     const float inv = b > 0.0f ? 1.0f / b : 0.0f;
     const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
     if (c1 >= p.b1) continue;
-    T* dst = qhat + ((((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2) * D);
-    store_rows<T, D, NACC, RW>(dst, acc, rt, inv, G);
+    const long long row = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
+    store_rows<T, D, NACC, RW>(qhat + row * D, acc, rt, inv, G);
+    if (beta_out && G == 0) beta_out[row] = b;
   }
 }
 

@@ -19,6 +19,7 @@
 #include <mutex>
 #include <vector>
 
+#include "backward.h"
 #include "lside.h"
 #include "rside.h"
 #include "../../include/monarch_attn.h"
@@ -168,7 +169,10 @@ Profiler g_prof;
 
 const char* const kKernelNames[MONARCH_NUM_KERNELS] = {
     "k_kbar (block-mean keys)", "k_lse (L-row log-sum-exp)", "k_aggregate (R-side aggregation through L)",
-    "k_rstep (R block softmax + R V / next keys)", "k_apply (L-apply on the permuted index)"};
+    "k_rstep (R block softmax + R V / next keys)", "k_apply (L-apply on the permuted index)",
+    "kb_du (backward: dU = L^T dy per tile column)", "kb_rside (backward: R-step per key block)",
+    "kb_dq (backward: row pass, dq)", "kb_dkbar (backward: block-mean key gradient)",
+    "kb_dk_finish (backward: dk = dk_R + dKbar / b2)"};
 
 // Launch wrapper: records events around the launch when profiling is on.
 template <typename F>
@@ -190,15 +194,44 @@ hipError_t timed(int id, hipStream_t st, F&& launch) {
 
 // ------------------------------------------------------------------ launch --
 // All kernels of one pass over `s.BH` heads starting at the given pointers.
+// Intermediates of one pass.  `u` receives R V (== qhat: written over the
+// aggregated queries); `beta` receives the column masses when not NULL (both
+// kept for the backward pass by the training forward).
+template <typename T>
+struct Bufs {
+  T* kbar;
+  float* lse;
+  T* qhat;
+  T* ktil;
+  float* hent;
+  T* u;
+  float* beta;
+};
+
+template <typename T>
+Bufs<T> bufs_of(const Shape& s, unsigned char* ws, const Workspace& w) {
+  Bufs<T> b{};
+  b.kbar = reinterpret_cast<T*>(ws + w.kbar);
+  b.lse = reinterpret_cast<float*>(ws + w.lse);
+  b.qhat = reinterpret_cast<T*>(ws + w.qhat);
+  b.ktil = s.T > 1 ? reinterpret_cast<T*>(ws + w.ktil) : nullptr;
+  b.hent = s.T > 1 ? reinterpret_cast<float*>(ws + w.hent) : nullptr;
+  b.u = b.qhat;
+  b.beta = nullptr;
+  return b;
+}
+
 template <typename T, int D>
-hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned char* ws,
-                    const Workspace& w, hipStream_t st) {
+hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, const Bufs<T>& bf,
+                    hipStream_t st) {
   const float c = kLog2e / std::sqrt(static_cast<float>(D));
-  T* kbar = reinterpret_cast<T*>(ws + w.kbar);
-  float* lse = reinterpret_cast<float*>(ws + w.lse);
-  T* qhat = reinterpret_cast<T*>(ws + w.qhat);
-  T* ktil = s.T > 1 ? reinterpret_cast<T*>(ws + w.ktil) : nullptr;
-  float* hent = s.T > 1 ? reinterpret_cast<float*>(ws + w.hent) : nullptr;
+  T* kbar = bf.kbar;
+  float* lse = bf.lse;
+  T* qhat = bf.qhat;
+  T* ktil = bf.ktil;
+  float* hent = bf.hent;
+  T* uout = bf.u == bf.qhat ? nullptr : bf.u;
+  float* beta = bf.beta;
   const int BH = static_cast<int>(s.BH), N = static_cast<int>(s.N);
   const int ngmax = (s.b1 + s.t - 1) / s.t;
   hipError_t err = hipSuccess;
@@ -252,9 +285,9 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
       }));
       ok(timed(2, st, [&] {
         if (col_fits)
-          k_aggregate_col<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, agg);
+          k_aggregate_col<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
         else
-          k_aggregate<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, agg);
+          k_aggregate<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
       }));
     } else {
       ok(timed(1, st, [&] {
@@ -262,28 +295,28 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
       }));
       ok(timed(2, st, [&] {
         if (col_fits)
-          k_aggregate_col<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, agg);
+          k_aggregate_col<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg);
         else
-          k_aggregate<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, agg);
+          k_aggregate<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg);
       }));
     }
     if (last) {
       ok(timed(3, st, [&] {
-        k_rstep<T, D, true><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, nullptr, nullptr, rg);
+        k_rstep<T, D, true><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, nullptr, nullptr, uout, rg);
       }));
     } else {
       ok(timed(3, st, [&] {
-        k_rstep<T, D, false><<<r_grid, r_threads, r_lds_mid, st>>>(k, v, qhat, ktil, hent, rg);
+        k_rstep<T, D, false><<<r_grid, r_threads, r_lds_mid, st>>>(k, v, qhat, ktil, hent, nullptr, rg);
       }));
     }
   }
   if (s.T == 1) {
     ok(timed(4, st, [&] {
-      k_apply<T, D, kAppRW, kAppNW, true><<<app_grid, kAppNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, out, app);
+      k_apply<T, D, kAppRW, kAppNW, true><<<app_grid, kAppNW * kWave, 0, st>>>(q, kbar, nullptr, lse, bf.u, out, app);
     }));
   } else {
     ok(timed(4, st, [&] {
-      k_apply<T, D, kAppRW, kAppNW, false><<<app_grid, kAppNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, out, app);
+      k_apply<T, D, kAppRW, kAppNW, false><<<app_grid, kAppNW * kWave, 0, st>>>(q, ktil, hent, lse, bf.u, out, app);
     }));
   }
   return err;
@@ -297,7 +330,7 @@ int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned cha
     Shape ps = s;
     ps.BH = s.BH - h0 < w.hc ? s.BH - h0 : w.hc;
     const long long o = h0 * per;
-    const hipError_t err = run_pass<T, D>(q + o, k + o, v + o, out + o, ps, ws, w, st);
+    const hipError_t err = run_pass<T, D>(q + o, k + o, v + o, out + o, ps, bufs_of<T>(ps, ws, w), st);
     if (err != hipSuccess) {
       g_last_hip_error = static_cast<int>(err);
       return MONARCH_EHIP;
@@ -362,6 +395,267 @@ int fwd_alloc(const void* q, const void* k, const void* v, void* out, const Shap
   return rc;
 }
 
+// ------------------------------------------------------------ training --
+// Training state: what the backward pass reads from the one-iteration
+// forward, for all heads of the call.
+struct TrainState {
+  size_t kbar, lse, beta, qhat, u, total;
+};
+
+TrainState train_layout(const Shape& s, size_t elem) {
+  TrainState t{};
+  const size_t BH = static_cast<size_t>(s.BH), N = static_cast<size_t>(s.N), d = static_cast<size_t>(s.d);
+  const size_t tN = static_cast<size_t>(s.t) * N;
+  size_t off = 0;
+  t.kbar = off;
+  off += align_up(BH * s.b1 * d * elem);
+  t.lse = off;
+  off += align_up(BH * N * sizeof(float));
+  t.beta = off;
+  off += align_up(BH * tN * sizeof(float));
+  t.qhat = off;
+  off += align_up(BH * tN * d * elem);
+  t.u = off;
+  off += align_up(BH * tN * d * elem);
+  t.total = off;
+  return t;
+}
+
+template <typename T>
+Bufs<T> train_bufs(unsigned char* st, const TrainState& t) {
+  Bufs<T> b{};
+  b.kbar = reinterpret_cast<T*>(st + t.kbar);
+  b.lse = reinterpret_cast<float*>(st + t.lse);
+  b.qhat = reinterpret_cast<T*>(st + t.qhat);
+  b.ktil = nullptr;
+  b.hent = nullptr;
+  b.u = reinterpret_cast<T*>(st + t.u);
+  b.beta = reinterpret_cast<float*>(st + t.beta);
+  return b;
+}
+
+// Backward workspace (allocated per call, stream-ordered).
+struct BwdWorkspace {
+  int na2g, a2per;
+  size_t du, gq, ev, delta, dkr, part, total;
+};
+
+// Column groups of the key-mean pass: 4 per tile (at least one column each).
+constexpr int kBwdColGroups = 4;
+
+BwdWorkspace bwd_layout(const Shape& s, size_t elem) {
+  BwdWorkspace w{};
+  w.a2per = (s.b2 + kBwdColGroups - 1) / kBwdColGroups;
+  w.na2g = (s.b2 + w.a2per - 1) / w.a2per;
+  const size_t BH = static_cast<size_t>(s.BH), N = static_cast<size_t>(s.N), d = static_cast<size_t>(s.d);
+  const size_t tN = static_cast<size_t>(s.t) * N;
+  size_t off = 0;
+  w.du = off;
+  off += align_up(BH * tN * d * elem);
+  w.gq = off;
+  off += align_up(BH * tN * d * elem);
+  w.ev = off;
+  off += align_up(BH * tN * sizeof(float));
+  w.delta = off;
+  off += align_up(BH * N * sizeof(float));
+  w.dkr = off;
+  off += align_up(BH * N * d * sizeof(float));
+  w.part = off;
+  off += align_up(BH * static_cast<size_t>(s.t) * w.na2g * s.b1 * d * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+constexpr size_t kLdsBytes = 160 * 1024;
+
+// Backward tuning: rows/columns per wave (16-wide tiles) and waves.
+template <typename T> struct BwdCfg;
+template <> struct BwdCfg<bf16_t> {
+  static constexpr int kLcolRW = 2, kLcolNW = 4, kDqRW = 1, kDqNW = 8;
+};
+template <> struct BwdCfg<float> {
+  static constexpr int kLcolRW = 1, kLcolNW = 4, kDqRW = 1, kDqNW = 4;
+};
+
+template <typename T, int D>
+hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* dout, T* dq, T* dk,
+                   T* dv, const Shape& s, const Bufs<T>& bf, unsigned char* ws, const BwdWorkspace& w,
+                   hipStream_t st) {
+  using C = BwdCfg<T>;
+  const float c = kLog2e / std::sqrt(static_cast<float>(D));
+  const float sc = 1.0f / std::sqrt(static_cast<float>(D));
+  T* du = reinterpret_cast<T*>(ws + w.du);
+  T* gq = reinterpret_cast<T*>(ws + w.gq);
+  float* ev = reinterpret_cast<float*>(ws + w.ev);
+  float* delta = reinterpret_cast<float*>(ws + w.delta);
+  float* dkr = reinterpret_cast<float*>(ws + w.dkr);
+  float* part = reinterpret_cast<float*>(ws + w.part);
+  const int BH = static_cast<int>(s.BH), N = static_cast<int>(s.N);
+  const int ngmax = (s.b1 + s.t - 1) / s.t;
+  hipError_t err = hipSuccess;
+  auto ok = [&](hipError_t e) {
+    if (e != hipSuccess && err == hipSuccess) err = e;
+  };
+  constexpr int lcb = C::kLcolRW * C::kLcolNW * 16;
+  BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b1 + lcb - 1) / lcb, s.b2, 1, (s.b2 + 31) / 32 * 32, c, sc};
+
+  // dU = L^T dy per tile column
+  {
+    const unsigned grid = static_cast<unsigned>(s.BH * s.t * bg.na2g * bg.ncb);
+    ok(timed(5, st, [&] {
+      kb_lcol<T, D, C::kLcolRW, C::kLcolNW, kLcolDU><<<grid, C::kLcolNW * kWave, 0, st>>>(
+          q, dout, bf.kbar, bf.lse, nullptr, nullptr, nullptr, nullptr, du, nullptr, bg);
+    }));
+  }
+  // R-step backward per key block
+  {
+    const size_t lds = rside_bwd_lds_bytes<T, D>(bg.b2p);
+    if (lds > 65536)
+      ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&kb_rside<T, D>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)));
+    const unsigned grid = static_cast<unsigned>(s.BH * s.b1);
+    const unsigned threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
+    ok(timed(6, st, [&] {
+      kb_rside<T, D><<<grid, threads, lds, st>>>(k, v, bf.qhat, du, bf.beta, gq, ev, dv, dkr, bg);
+    }));
+  }
+  // row pass: delta and dq
+  {
+    constexpr int rows = C::kDqRW * C::kDqNW * 16;
+    LGeom lg{BH, N, s.b1, s.b2, s.t, (ngmax + rows - 1) / rows, c};
+    const unsigned grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lg.nrb);
+    ok(timed(7, st, [&] {
+      kb_dq<T, D, C::kDqRW, C::kDqNW><<<grid, C::kDqNW * kWave, 0, st>>>(
+          q, dout, out, bf.kbar, bf.lse, bf.u, gq, ev, delta, dq, lg, sc);
+    }));
+  }
+  // block-mean key gradient, partial sums per tile and column group
+  {
+    BGeom bk = bg;
+    bk.na2g = w.na2g;
+    bk.a2per = w.a2per;
+    const unsigned grid = static_cast<unsigned>(s.BH * s.t * bk.na2g * bk.ncb);
+    ok(timed(8, st, [&] {
+      kb_lcol<T, D, C::kLcolRW, C::kLcolNW, kLcolDKbar><<<grid, C::kLcolNW * kWave, 0, st>>>(
+          q, dout, bf.kbar, bf.lse, delta, bf.u, gq, ev, nullptr, part, bk);
+    }));
+  }
+  // dk = dk_R + dKbar / b2
+  {
+    const long long threads = s.BH * s.b1 * (D / 4);
+    const unsigned grid = static_cast<unsigned>((threads + 255) / 256);
+    ok(timed(9, st, [&] {
+      kb_dk_finish<T, D><<<grid, 256, 0, st>>>(dkr, part, dk, BH, s.b1, s.b2, s.t * w.na2g);
+    }));
+  }
+  return err;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_train(const Shape& s, size_t elem, const void* state, size_t state_bytes) {
+  if (elem == 0) return MONARCH_EINVAL;
+  if (s.T != 1) return MONARCH_EINVAL;
+  const TrainState t = train_layout(s, elem);
+  if (!state || state_bytes < t.total) return MONARCH_ENOMEM;
+  if (reinterpret_cast<uintptr_t>(state) % kAlign != 0) return MONARCH_EINVAL;
+  return MONARCH_OK;
+}
+
+int fwd_train(const void* q, const void* k, const void* v, void* out, const Shape& s, int dtype,
+              void* state, size_t state_bytes, hipStream_t st) {
+  const size_t elem = elem_size(dtype);
+  int rc = check_args(q, k, v, out, s, elem);
+  if (rc != MONARCH_OK) return rc;
+  rc = check_train(s, elem, state, state_bytes);
+  if (rc != MONARCH_OK) return rc;
+  const size_t io = static_cast<size_t>(s.BH * s.N * s.d) * elem;
+  for (const void* p : {q, k, v, static_cast<const void*>(out)})
+    if (overlaps(p, io, state, state_bytes)) return MONARCH_EINVAL;
+  const TrainState t = train_layout(s, elem);
+  unsigned char* sp = static_cast<unsigned char*>(state);
+  hipError_t e = hipSuccess;
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    const Bufs<T> b = train_bufs<T>(sp, t);
+    const T* tq = static_cast<const T*>(q);
+    const T* tk = static_cast<const T*>(k);
+    const T* tv = static_cast<const T*>(v);
+    T* to = static_cast<T*>(out);
+    switch (s.d) {
+      case 16: e = run_pass<T, 16>(tq, tk, tv, to, s, b, st); break;
+      case 32: e = run_pass<T, 32>(tq, tk, tv, to, s, b, st); break;
+      case 64: e = run_pass<T, 64>(tq, tk, tv, to, s, b, st); break;
+      default: e = run_pass<T, 128>(tq, tk, tv, to, s, b, st); break;
+    }
+  };
+  if (dtype == MONARCH_BF16) go(bf16_t{}); else go(float{});
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return MONARCH_EHIP;
+  }
+  return MONARCH_OK;
+}
+
+int bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, void* dq,
+        void* dk, void* dv, const Shape& s, int dtype, void* state, size_t state_bytes, hipStream_t st) {
+  const size_t elem = elem_size(dtype);
+  int rc = check_args(q, k, v, out, s, elem);
+  if (rc != MONARCH_OK) return rc;
+  if (!dout || !dq || !dk || !dv) return MONARCH_EINVAL;
+  rc = check_train(s, elem, state, state_bytes);
+  if (rc != MONARCH_OK) return rc;
+  const size_t io = static_cast<size_t>(s.BH * s.N * s.d) * elem;
+  const void* ins[] = {q, k, v, out, dout, state};
+  const size_t insz[] = {io, io, io, io, io, state_bytes};
+  void* outs[] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], io, ins[j], insz[j])) return MONARCH_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], io, outs[j], io)) return MONARCH_EINVAL;
+  }
+  const int b2p = (s.b2 + 31) / 32 * 32;
+  const int DK = s.d < 32 ? 32 : s.d;
+  if (static_cast<size_t>(b2p) * DK * elem * 4 + 8 * b2p > kLdsBytes) return MONARCH_EUNSUPPORTED;
+
+  const TrainState t = train_layout(s, elem);
+  const BwdWorkspace w = bwd_layout(s, elem);
+  void* wsp = nullptr;
+  hipError_t e = hipMallocAsync(&wsp, w.total, st);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    (void)hipGetLastError();
+    return e == hipErrorOutOfMemory ? MONARCH_ENOMEM : MONARCH_EHIP;
+  }
+  unsigned char* ws = static_cast<unsigned char*>(wsp);
+  unsigned char* sp = static_cast<unsigned char*>(state);
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    const Bufs<T> b = train_bufs<T>(sp, t);
+    const T* a[5] = {static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                     static_cast<const T*>(out), static_cast<const T*>(dout)};
+    T* g3[3] = {static_cast<T*>(dq), static_cast<T*>(dk), static_cast<T*>(dv)};
+    switch (s.d) {
+      case 16: e = run_bwd<T, 16>(a[0], a[1], a[2], a[3], a[4], g3[0], g3[1], g3[2], s, b, ws, w, st); break;
+      case 32: e = run_bwd<T, 32>(a[0], a[1], a[2], a[3], a[4], g3[0], g3[1], g3[2], s, b, ws, w, st); break;
+      case 64: e = run_bwd<T, 64>(a[0], a[1], a[2], a[3], a[4], g3[0], g3[1], g3[2], s, b, ws, w, st); break;
+      default: e = run_bwd<T, 128>(a[0], a[1], a[2], a[3], a[4], g3[0], g3[1], g3[2], s, b, ws, w, st); break;
+    }
+  };
+  if (dtype == MONARCH_BF16) go(bf16_t{}); else go(float{});
+  const hipError_t ef = hipFreeAsync(wsp, st);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return MONARCH_EHIP;
+  }
+  return MONARCH_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------- C ABI --
@@ -398,6 +692,31 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, 
   const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   return fwd_ws(q, k, v, out, s, dtype, workspace, workspace_bytes,
                 static_cast<hipStream_t>(stream));
+}
+
+size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d, int b1, int b2,
+                                      int tiles, int dtype) {
+  const size_t elem = elem_size(dtype);
+  if (elem == 0) return 0;
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, 1);
+  static const char dummy[4] = {0};
+  if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
+  return train_layout(s, elem).total;
+}
+
+int monarch_attn_fwd_train(const void* q, const void* k, const void* v, void* out, int B, int H,
+                           int f, int h, int w, int d, int b1, int b2, int tiles, int dtype,
+                           void* state, size_t state_bytes, void* stream) {
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, 1);
+  return fwd_train(q, k, v, out, s, dtype, state, state_bytes, static_cast<hipStream_t>(stream));
+}
+
+int monarch_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     void* dq, void* dk, void* dv, int B, int H, int f, int h, int w, int d, int b1,
+                     int b2, int tiles, int dtype, void* state, size_t state_bytes, void* stream) {
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, 1);
+  return bwd(q, k, v, out, dout, dq, dk, dv, s, dtype, state, state_bytes,
+             static_cast<hipStream_t>(stream));
 }
 
 const char* monarch_attn_status_string(int status) {

@@ -42,6 +42,7 @@ template <typename T, int D, bool LAST>
 __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T* __restrict__ v,
                                                T* qhat,   // [BH][t][b1][b2][D]; U written over it when LAST
                                                T* __restrict__ ktil, float* __restrict__ hent,
+                                               T* uout,   // U goes here instead when not NULL
                                                RGeom p) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
         }
     }
     if (row_ok) {
-      T* dst = (LAST ? qhat : ktil) + row * D;
+      T* dst = (LAST ? (uout ? uout : qhat) : ktil) + row * D;
       if (NDP > 0) {
 #pragma unroll
         for (int dp = 0; dp < NACC; ++dp) {

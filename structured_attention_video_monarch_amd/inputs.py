@@ -194,3 +194,30 @@ def make_inputs(wl: Workload, seed: int = 0, heads=None, want_f32: bool = True,
                 elif want_f32:
                     out[name][b, j] = x
     return out
+
+
+def make_cotangent(wl: Workload, seed: int = 0, heads=None, want_f32: bool = True,
+                   want_bits: bool = True):
+    """Seeded upstream gradient dLoss/dout for the backward pass: standard
+    normal per (batch, head), from its own stream (``[seed, b, h, 1]``), in
+    the same dict format as :func:`make_inputs` under the key ``dy``."""
+    heads = list(range(wl.H)) if heads is None else list(heads)
+    shape = (wl.B, len(heads), wl.N, wl.d)
+    bf16 = wl.dtype == "bf16"
+    out = {}
+    if want_f32:
+        out["dy"] = np.empty(shape, dtype=np.float32)
+    if bf16 and want_bits:
+        out["dy_bits"] = np.empty(shape, dtype=np.uint16)
+    for b in range(wl.B):
+        for j, hh in enumerate(heads):
+            x = np.random.default_rng([seed, b, hh, 1]).standard_normal((wl.N, wl.d), dtype=np.float32)
+            if bf16:
+                bits = round_to_bf16_bits(x)
+                if want_bits:
+                    out["dy_bits"][b, j] = bits
+                if want_f32:
+                    out["dy"][b, j] = bf16_bits_to_f32(bits)
+            elif want_f32:
+                out["dy"][b, j] = x
+    return out

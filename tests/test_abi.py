@@ -91,3 +91,55 @@ def test_workspace_bytes(shape):
 def test_workspace_bytes_zero_when_invalid():
     assert M.monarch_attn_workspace_bytes(1, 1, 2, 4, 4, 16, 8, 5, 1, 1, 1) == 0
     assert M.monarch_attn_workspace_bytes(1, 1, 2, 4, 4, 16, 8, 4, 1, 1, 7) == 0
+
+
+# ---- training entry points (fake, widely spaced pointers: checks only)
+_GAP = 1 << 40
+
+
+def _train_ptrs(n):
+    return [ctypes.c_void_p((i + 1) * _GAP) for i in range(n)]
+
+
+def _bwd(state_bytes=None, B=1, H=2, f=3, h=30, w=52, d=128, b1=90, b2=52, t=1, dtype=0, null=None,
+         alias=None):
+    p = _train_ptrs(9)  # q k v out dout dq dk dv state
+    if null is not None:
+        p[null] = ctypes.c_void_p(0)
+    if alias is not None:
+        p[alias[0]] = p[alias[1]]
+    if state_bytes is None:
+        state_bytes = M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, dtype)
+    return M.lib().monarch_attn_bwd(*p[:8], B, H, f, h, w, d, b1, b2, t, dtype, p[8], state_bytes, None)
+
+
+def test_train_state_bytes_formula():
+    B, H, f, h, w, d, b1, b2, t = 1, 40, 21, 45, 80, 128, 945, 80, 4
+    N, BH, e = f * h * w, B * H, 2
+    expect = (_align(BH * b1 * d * e) + _align(BH * N * 4) + _align(BH * t * N * 4)
+              + 2 * _align(BH * t * N * d * e))
+    assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, 0) == expect
+    assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1 + 1, b2, t, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(null=4), M.MONARCH_EINVAL),                     # dout NULL
+    (dict(null=5), M.MONARCH_EINVAL),                     # dq NULL
+    (dict(null=8), M.MONARCH_ENOMEM),                     # state NULL
+    (dict(state_bytes=1024), M.MONARCH_ENOMEM),           # state too small
+    (dict(alias=(5, 0)), M.MONARCH_EINVAL),               # dq aliases q
+    (dict(alias=(7, 6)), M.MONARCH_EINVAL),               # dv aliases dk
+    (dict(alias=(6, 8)), M.MONARCH_EINVAL),               # dk aliases the state
+    (dict(b1=91), M.MONARCH_EINVAL),
+    (dict(d=48), M.MONARCH_EUNSUPPORTED),
+    # f32 key-block pass: 4 * 96 * 128 * 4 bytes of LDS does not fit
+    (dict(dtype=1, f=2, h=3, w=96, b1=6, b2=96), M.MONARCH_EUNSUPPORTED),
+])
+def test_bwd_bad_arguments_rejected_before_any_gpu_call(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_fwd_train_rejects_small_state():
+    p = _train_ptrs(5)
+    rc = M.lib().monarch_attn_fwd_train(*p[:4], 1, 2, 3, 30, 52, 128, 90, 52, 1, 0, p[4], 256, None)
+    assert rc == M.MONARCH_ENOMEM

@@ -1,0 +1,149 @@
+"""Backward pass on the GPU against the CPU gradient oracle (needs an MI355X).
+
+The upstream gradient dy is seeded (inputs.make_cotangent); the oracle reads
+the same bf16-rounded q, k, v, dy.  Gradients have no natural scale, so the
+bars are relative to the reference tensor of each head:
+  fp32 I/O:  max |g - ref| <= 2e-5 * max |ref|
+  bf16 I/O:  max |g - ref| <= 4e-2 * max |ref|  and  mean |g - ref| <= 1.5e-2 * mean |ref|
+(the bf16 path rounds the weights L, R, dl and dz to bf16 as MFMA operands and
+stores Qh, U, dU and G in bf16: a few relative errors of 2^-9 on every term).
+Large workloads run whole on the GPU; the oracle checks a subset of heads.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import say, to_device, to_host
+from structured_attention_video_monarch_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+F32_REL_MAX = 2e-5
+BF16_REL_MAX = 4e-2
+BF16_REL_MEAN = 1.5e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_train(wl, x, dyx):
+    import structured_attention_video_monarch_amd as M
+    q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
+    dy = to_device(dyx, "dy", wl.dtype)
+    dt = M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32
+    nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles, dt)
+    state = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    M.monarch_attn_fwd_train(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, state)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, state)
+    torch.cuda.synchronize()
+    return [to_host(t) for t in (out, dq, dk, dv)]
+
+
+def rel_errors(got, ref):
+    d = np.abs(got - ref)
+    return float(d.max() / max(np.abs(ref).max(), 1e-30)), float(d.mean() / max(np.abs(ref).mean(), 1e-30))
+
+
+def compare_grad(wl, seed=0, heads=None, label=""):
+    wl = wl.with_(iters=1)
+    say(f"[case] bwd {label or wl.name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} blocks=({wl.b1},{wl.b2}) "
+        f"t={wl.tiles} {wl.dtype} seed={seed}")
+    x = I.make_inputs(wl, seed)
+    dyx = I.make_cotangent(wl, seed)
+    y, dq, dk, dv = run_train(wl, x, dyx)
+    for t in (y, dq, dk, dv):
+        assert np.all(np.isfinite(t))
+    heads = range(wl.H) if heads is None else heads
+    worst = {}
+    for b in range(wl.B):
+        for h in heads:
+            refs = oracle.monarch_head_grad(x["q"][b, h], x["k"][b, h], x["v"][b, h], dyx["dy"][b, h],
+                                            wl.b1, wl.b2, wl.tiles)
+            for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+                mx, mean = rel_errors(got[b, h], ref)
+                w = worst.get(name, (0.0, 0.0))
+                worst[name] = (max(w[0], mx), max(w[1], mean))
+                if wl.dtype == "bf16":
+                    assert mx <= BF16_REL_MAX and mean <= BF16_REL_MEAN, (name, b, h, mx, mean)
+                else:
+                    assert mx <= F32_REL_MAX, (name, b, h, mx)
+    say(f"[ok] bwd {label or wl.name}: " + ", ".join(
+        f"{n} rel-max {w[0]:.2e} rel-mean {w[1]:.2e}" for n, w in worst.items()))
+    return worst
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_bwd_tiny_f32(t):
+    compare_grad(I.get_workload("tiny").with_(tiles=t), label=f"tiny-t{t}")
+
+
+def test_bwd_chunk480p_f32():
+    compare_grad(I.get_workload("chunk480p").with_(H=2, dtype="f32"), label="chunk480p-f32")
+
+
+def test_bwd_chunk480p_bf16():
+    compare_grad(I.get_workload("chunk480p"), heads=[0, 5, 11])
+
+
+@pytest.mark.parametrize("t", [1, 4])
+def test_bwd_clip480p_spikes_bf16(t):
+    compare_grad(I.get_workload(f"clip480p_spikes_t{t}_T1"), heads=[0, 11])
+
+
+def test_bwd_latent720p_bf16():
+    compare_grad(I.get_workload("latent720p"), heads=[0, 39])
+
+
+# ragged and degenerate shapes (one iteration): partial tiles of rows and
+# keys, odd block sizes, one-row tiles, non-aligned blocks, B > 1
+EDGE = [
+    # name, B, H, d, f, h, w, b1, b2, t, dtype
+    ("b2_1_dense_rows", 1, 2, 64, 2, 5, 7, 70, 1, 1, "bf16"),
+    ("b1_1_dense_cols", 1, 2, 64, 1, 1, 100, 1, 100, 1, "bf16"),
+    ("odd_blocks", 2, 3, 32, 3, 7, 13, 21, 13, 2, "bf16"),
+    ("one_row_tiles", 1, 2, 128, 2, 3, 10, 6, 10, 6, "bf16"),
+    ("misaligned_blocks", 1, 2, 128, 4, 6, 8, 48, 4, 3, "bf16"),
+    ("b2_128", 1, 1, 128, 2, 2, 128, 4, 128, 1, "bf16"),
+    ("b2_17_d16", 1, 3, 16, 5, 7, 17, 35, 17, 4, "bf16"),
+    ("ragged_f32", 2, 2, 64, 3, 11, 9, 33, 9, 5, "f32"),
+    ("d32_f32", 1, 2, 32, 2, 9, 20, 18, 20, 2, "f32"),
+    ("d128_f32", 1, 1, 128, 3, 5, 24, 15, 24, 3, "f32"),
+    ("b1_big_ragged", 1, 1, 128, 7, 37, 3, 259, 3, 3, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_bwd_edge_shapes(case):
+    name, B, H, d, f, h, w, b1, b2, t, dt = case
+    compare_grad(I.Workload(name, B, H, d, f, h, w, b1, b2, t, 1, dt), seed=3, label=name)
+
+
+def test_train_forward_equals_forward_and_bwd_is_deterministic():
+    import structured_attention_video_monarch_amd as M
+    wl = I.get_workload("clip480p_spikes_t4_T1").with_(H=2)
+    x = I.make_inputs(wl, 1)
+    dyx = I.make_cotangent(wl, 1)
+    q, k, v = (to_device(x, n, "bf16") for n in "qkv")
+    dy = to_device(dyx, "dy", "bf16")
+    args = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles)
+    ref = torch.empty_like(q)
+    M.monarch_attn_fwd(q, k, v, ref, *args, 1)
+    nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles)
+    state = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    M.monarch_attn_fwd_train(q, k, v, out, *args, state)
+    g1 = [torch.empty_like(q) for _ in range(3)]
+    g2 = [torch.empty_like(q) for _ in range(3)]
+    M.monarch_attn_bwd(q, k, v, out, dy, *g1, *args, state)
+    M.monarch_attn_bwd(q, k, v, out, dy, *g2, *args, state)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
