@@ -115,11 +115,9 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
  * through L = softmax(s q Kbar^T), Qh = sum L q / beta (0 where beta == 0),
  * R = softmax(s Qh k^T), U = R V and y = L U on the permuted index.
  * dq, dk, dv must not overlap each other or any input (state included).
- * It allocates a workspace stream-ordered (about t*N*d*(2e + 4/d) + N*d*4
- * bytes per head).  Returns MONARCH_EUNSUPPORTED where the key-block pass
- * does not fit in LDS (4 * roundup(b2, 32) * max(d, 32) * e bytes must stay
- * below 160 KiB: f32 needs b2 <= 64 at d = 128).  State from another shape
- * or dtype gives undefined results. */
+ * It allocates a workspace stream-ordered (about 2*t*N*d*e + 16*t*N +
+ * N*roundup(b1, 256)*e bytes per head).  The supported envelope is the
+ * forward's.  State from another shape or dtype gives undefined results. */
 size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d,
                                       int b1, int b2, int tiles, int dtype);
 int monarch_attn_fwd_train(const void* q, const void* k, const void* v, void* out,
@@ -145,9 +143,10 @@ int monarch_attn_last_hip_error(void);
  * launches[i] for kernel id i < n, and forgets them.  Kernel ids:
  * 0 block-mean keys, 1 L-row log-sum-exp, 2 R-side aggregation through L,
  * 3 R-step block softmax (+ R V or next keys/entropy), 4 L-apply;
- * backward: 5 dU per tile column, 6 R-step per key block, 7 row pass (dq),
- * 8 block-mean key gradient, 9 dk assembly. */
-#define MONARCH_NUM_KERNELS 10
+ * backward: 5 dU per tile column, 6 R-step per key block (G, statistics),
+ * 7 row pass (dq), 8 block-mean key gradient (product over tokens),
+ * 9 its reduction, 10 dv and dk per key block. */
+#define MONARCH_NUM_KERNELS 11
 int monarch_attn_profile_enable(int on);
 int monarch_attn_profile_collect(double* ms, long* launches, int n);
 const char* monarch_attn_kernel_name(int id);

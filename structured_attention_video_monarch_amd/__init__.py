@@ -24,7 +24,7 @@ MONARCH_EHIP = -3
 MONARCH_ENOMEM = -4
 MONARCH_BF16 = 0
 MONARCH_F32 = 1
-MONARCH_NUM_KERNELS = 10
+MONARCH_NUM_KERNELS = 11
 
 _lib = None
 

@@ -170,9 +170,11 @@ Profiler g_prof;
 const char* const kKernelNames[MONARCH_NUM_KERNELS] = {
     "k_kbar (block-mean keys)", "k_lse (L-row log-sum-exp)", "k_aggregate (R-side aggregation through L)",
     "k_rstep (R block softmax + R V / next keys)", "k_apply (L-apply on the permuted index)",
-    "kb_du (backward: dU = L^T dy per tile column)", "kb_rside (backward: R-step per key block)",
-    "kb_dq (backward: row pass, dq)", "kb_dkbar (backward: block-mean key gradient)",
-    "kb_dk_finish (backward: dk = dk_R + dKbar / b2)"};
+    "kb_du (backward: dU = L^T dy per tile column)",
+    "kb_rside_a (backward: R-step per key block, G and row statistics)",
+    "kb_dq (backward: row pass, dq)", "kb_dkbar (backward: block-mean key gradient over tokens)",
+    "kb_dkbar_reduce (backward: sum of the token-chunk partials)",
+    "kb_rside_b (backward: dv and dk per key block)"};
 
 // Launch wrapper: records events around the launch when profiling is on.
 template <typename F>
@@ -434,19 +436,60 @@ Bufs<T> train_bufs(unsigned char* st, const TrainState& t) {
   return b;
 }
 
-// Backward workspace (allocated per call, stream-ordered).
-struct BwdWorkspace {
-  int na2g, a2per;
-  size_t du, gq, ev, delta, dkr, part, total;
+// Backward tuning: rows/keys per wave (16-wide tiles) and waves per
+// workgroup of each backward kernel.
+template <typename T> struct BwdCfg;
+#ifndef MONARCH_BDQ_RW
+#define MONARCH_BDQ_RW 2
+#endif
+#ifndef MONARCH_BDQ_NW
+#define MONARCH_BDQ_NW 8
+#endif
+#ifndef MONARCH_BDU_RW
+#define MONARCH_BDU_RW 1
+#endif
+#ifndef MONARCH_BDU_NW
+#define MONARCH_BDU_NW 8
+#endif
+#ifndef MONARCH_BGM_RW
+#define MONARCH_BGM_RW 4
+#endif
+#ifndef MONARCH_BGM_NW
+#define MONARCH_BGM_NW 4
+#endif
+template <> struct BwdCfg<bf16_t> {
+  static constexpr int kDuRW = MONARCH_BDU_RW, kDuNW = MONARCH_BDU_NW;
+  static constexpr int kDqRW = MONARCH_BDQ_RW, kDqNW = MONARCH_BDQ_NW;
+  static constexpr int kGmRW = MONARCH_BGM_RW, kGmNW = MONARCH_BGM_NW;
+};
+template <> struct BwdCfg<float> {
+  static constexpr int kDuRW = 1, kDuNW = 4, kDqRW = 1, kDqNW = 4, kGmRW = 2, kGmNW = 4;
 };
 
-// Column groups of the key-mean pass: 4 per tile (at least one column each).
-constexpr int kBwdColGroups = 4;
+// Backward workspace (allocated per call, stream-ordered).
+struct BwdWorkspace {
+  int ldl;          // row stride of the stored s*dl (keys padded to the product's key block)
+  int nsplit, chunk;  // split of the tokens in the key-mean product
+  size_t du, gq, ev, lser, rho, delta, dl, part, dkbar, total;
+};
 
-BwdWorkspace bwd_layout(const Shape& s, size_t elem) {
+template <typename T>
+BwdWorkspace bwd_layout_t(const Shape& s) {
+  using C = BwdCfg<T>;
+  constexpr int cb = C::kGmRW * C::kGmNW * 16;
   BwdWorkspace w{};
-  w.a2per = (s.b2 + kBwdColGroups - 1) / kBwdColGroups;
-  w.na2g = (s.b2 + w.a2per - 1) / w.a2per;
+  const size_t elem = sizeof(T);
+  const long long ncb = (s.b1 + cb - 1) / cb;
+  w.ldl = static_cast<int>(ncb * cb);
+  // enough workgroups to fill the chip, chunks of at least 512 tokens
+  long long ns = (2048 + s.BH * ncb - 1) / (s.BH * ncb);
+  const long long ns_max = (s.N + 511) / 512;
+  if (ns > ns_max) ns = ns_max;
+  if (ns < 1) ns = 1;
+  long long chunk = (s.N + ns - 1) / ns;
+  chunk = (chunk + 31) / 32 * 32;
+  w.nsplit = static_cast<int>((s.N + chunk - 1) / chunk);
+  w.chunk = static_cast<int>(chunk);
   const size_t BH = static_cast<size_t>(s.BH), N = static_cast<size_t>(s.N), d = static_cast<size_t>(s.d);
   const size_t tN = static_cast<size_t>(s.t) * N;
   size_t off = 0;
@@ -456,26 +499,27 @@ BwdWorkspace bwd_layout(const Shape& s, size_t elem) {
   off += align_up(BH * tN * d * elem);
   w.ev = off;
   off += align_up(BH * tN * sizeof(float));
+  w.lser = off;
+  off += align_up(BH * tN * sizeof(float));
+  w.rho = off;
+  off += align_up(BH * tN * sizeof(float));
   w.delta = off;
   off += align_up(BH * N * sizeof(float));
-  w.dkr = off;
-  off += align_up(BH * N * d * sizeof(float));
+  w.dl = off;
+  off += align_up(BH * N * static_cast<size_t>(w.ldl) * elem);
   w.part = off;
-  off += align_up(BH * static_cast<size_t>(s.t) * w.na2g * s.b1 * d * sizeof(float));
+  off += align_up(BH * static_cast<size_t>(w.nsplit) * s.b1 * d * sizeof(float));
+  w.dkbar = off;
+  off += align_up(BH * static_cast<size_t>(s.b1) * d * sizeof(float));
   w.total = off;
   return w;
 }
 
-constexpr size_t kLdsBytes = 160 * 1024;
+BwdWorkspace bwd_layout(const Shape& s, size_t elem) {
+  return elem == 2 ? bwd_layout_t<bf16_t>(s) : bwd_layout_t<float>(s);
+}
 
-// Backward tuning: rows/columns per wave (16-wide tiles) and waves.
-template <typename T> struct BwdCfg;
-template <> struct BwdCfg<bf16_t> {
-  static constexpr int kLcolRW = 2, kLcolNW = 4, kDqRW = 1, kDqNW = 8;
-};
-template <> struct BwdCfg<float> {
-  static constexpr int kLcolRW = 1, kLcolNW = 4, kDqRW = 1, kDqNW = 4;
-};
+constexpr size_t kLdsBytes = 160 * 1024;
 
 template <typename T, int D>
 hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* dout, T* dq, T* dk,
@@ -487,67 +531,79 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   T* du = reinterpret_cast<T*>(ws + w.du);
   T* gq = reinterpret_cast<T*>(ws + w.gq);
   float* ev = reinterpret_cast<float*>(ws + w.ev);
+  float* lser = reinterpret_cast<float*>(ws + w.lser);
+  float* rho = reinterpret_cast<float*>(ws + w.rho);
   float* delta = reinterpret_cast<float*>(ws + w.delta);
-  float* dkr = reinterpret_cast<float*>(ws + w.dkr);
+  T* dl = reinterpret_cast<T*>(ws + w.dl);
   float* part = reinterpret_cast<float*>(ws + w.part);
+  float* dkbar = reinterpret_cast<float*>(ws + w.dkbar);
   const int BH = static_cast<int>(s.BH), N = static_cast<int>(s.N);
   const int ngmax = (s.b1 + s.t - 1) / s.t;
   hipError_t err = hipSuccess;
   auto ok = [&](hipError_t e) {
     if (e != hipSuccess && err == hipSuccess) err = e;
   };
-  constexpr int lcb = C::kLcolRW * C::kLcolNW * 16;
-  BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b1 + lcb - 1) / lcb, s.b2, 1, (s.b2 + 31) / 32 * 32, c, sc};
 
   // dU = L^T dy per tile column
   {
-    const unsigned grid = static_cast<unsigned>(s.BH * s.t * bg.na2g * bg.ncb);
+    constexpr int cb = C::kDuRW * C::kDuNW * 16;
+    LGeom lg{BH, N, s.b1, s.b2, s.t, (s.b1 + cb - 1) / cb, c};
+    const unsigned grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lg.nrb);
     ok(timed(5, st, [&] {
-      kb_lcol<T, D, C::kLcolRW, C::kLcolNW, kLcolDU><<<grid, C::kLcolNW * kWave, 0, st>>>(
-          q, dout, bf.kbar, bf.lse, nullptr, nullptr, nullptr, nullptr, du, nullptr, bg);
+      kb_du<T, D, C::kDuRW, C::kDuNW><<<grid, C::kDuNW * kWave, 0, st>>>(q, dout, bf.kbar, bf.lse, du, lg);
     }));
   }
-  // R-step backward per key block
+  // R-step backward per key block, part 1: G, e and the R row statistics
+  const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc};
+  const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
+  const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
   {
     const size_t lds = rside_bwd_lds_bytes<T, D>(bg.b2p);
-    if (lds > 65536)
-      ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&kb_rside<T, D>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)));
-    const unsigned grid = static_cast<unsigned>(s.BH * s.b1);
-    const unsigned threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
-    ok(timed(6, st, [&] {
-      kb_rside<T, D><<<grid, threads, lds, st>>>(k, v, bf.qhat, du, bf.beta, gq, ev, dv, dkr, bg);
-    }));
+    auto launch = [&](auto kern) {
+      if (lds > 65536)
+        ok(hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(lds)));
+      ok(timed(6, st, [&] {
+        kern<<<r_grid, r_threads, lds, st>>>(k, v, bf.qhat, du, bf.beta, gq, ev, lser, rho, bg);
+      }));
+    };
+    switch (bg.b2p / 32) {
+      case 1: launch(&kb_rside_a<T, D, 1>); break;
+      case 2: launch(&kb_rside_a<T, D, 2>); break;
+      case 3: launch(&kb_rside_a<T, D, 3>); break;
+      default: launch(&kb_rside_a<T, D, 4>); break;
+    }
   }
-  // row pass: delta and dq
+  // row pass: delta, dq and the stored s*dl
   {
     constexpr int rows = C::kDqRW * C::kDqNW * 16;
     LGeom lg{BH, N, s.b1, s.b2, s.t, (ngmax + rows - 1) / rows, c};
     const unsigned grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lg.nrb);
     ok(timed(7, st, [&] {
       kb_dq<T, D, C::kDqRW, C::kDqNW><<<grid, C::kDqNW * kWave, 0, st>>>(
-          q, dout, out, bf.kbar, bf.lse, bf.u, gq, ev, delta, dq, lg, sc);
+          q, dout, out, bf.kbar, bf.lse, bf.u, gq, ev, delta, dq, dl, w.ldl, lg, sc);
     }));
   }
-  // block-mean key gradient, partial sums per tile and column group
+  // block-mean key gradient: partial sums over chunks of tokens
   {
-    BGeom bk = bg;
-    bk.na2g = w.na2g;
-    bk.a2per = w.a2per;
-    const unsigned grid = static_cast<unsigned>(s.BH * s.t * bk.na2g * bk.ncb);
+    constexpr int cb = C::kGmRW * C::kGmNW * 16;
+    const int ncb = w.ldl / cb;
+    const unsigned grid = static_cast<unsigned>(s.BH * ncb * w.nsplit);
     ok(timed(8, st, [&] {
-      kb_lcol<T, D, C::kLcolRW, C::kLcolNW, kLcolDKbar><<<grid, C::kLcolNW * kWave, 0, st>>>(
-          q, dout, bf.kbar, bf.lse, delta, bf.u, gq, ev, nullptr, part, bk);
+      kb_dkbar<T, D, C::kGmRW, C::kGmNW><<<grid, C::kGmNW * kWave, 0, st>>>(q, dl, w.ldl, part, BH, N, s.b1, ncb,
+                                                                           w.nsplit, w.chunk);
     }));
   }
-  // dk = dk_R + dKbar / b2
+  // sum of the partials, spread over the b2 keys of each block
   {
     const long long threads = s.BH * s.b1 * (D / 4);
     const unsigned grid = static_cast<unsigned>((threads + 255) / 256);
-    ok(timed(9, st, [&] {
-      kb_dk_finish<T, D><<<grid, 256, 0, st>>>(dkr, part, dk, BH, s.b1, s.b2, s.t * w.na2g);
-    }));
+    ok(timed(9, st, [&] { kb_dkbar_reduce<D><<<grid, 256, 0, st>>>(part, dkbar, BH, s.b1, s.b2, w.nsplit); }));
   }
+  // R-step backward per key block, part 2: dv and dk
+  ok(timed(10, st, [&] {
+    kb_rside_b<T, D><<<r_grid, r_threads, 0, st>>>(k, v, bf.qhat, du, lser, rho, dkbar, dk, dv, bg);
+  }));
   return err;
 }
 
@@ -620,7 +676,7 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
   }
   const int b2p = (s.b2 + 31) / 32 * 32;
   const int DK = s.d < 32 ? 32 : s.d;
-  if (static_cast<size_t>(b2p) * DK * elem * 4 + 8 * b2p > kLdsBytes) return MONARCH_EUNSUPPORTED;
+  if (static_cast<size_t>(b2p) * DK * elem * 2 > kLdsBytes) return MONARCH_EUNSUPPORTED;
 
   const TrainState t = train_layout(s, elem);
   const BwdWorkspace w = bwd_layout(s, elem);

@@ -132,8 +132,7 @@ def test_train_state_bytes_formula():
     (dict(alias=(6, 8)), M.MONARCH_EINVAL),               # dk aliases the state
     (dict(b1=91), M.MONARCH_EINVAL),
     (dict(d=48), M.MONARCH_EUNSUPPORTED),
-    # f32 key-block pass: 4 * 96 * 128 * 4 bytes of LDS does not fit
-    (dict(dtype=1, f=2, h=3, w=96, b1=6, b2=96), M.MONARCH_EUNSUPPORTED),
+    (dict(f=2, h=3, w=130, b1=6, b2=130), M.MONARCH_EUNSUPPORTED),
 ])
 def test_bwd_bad_arguments_rejected_before_any_gpu_call(kw, status):
     assert _bwd(**kw) == status
