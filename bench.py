@@ -1,12 +1,15 @@
-"""Benchmark: MonarchAttention forward layer calls on one MI355X.
+"""Benchmark: MonarchAttention layer calls on one MI355X.
 
-One step = one full forward call (block-mean keys, T x (L-step, R-step),
-L-apply) over one batch of seeded synthetic Q/K/V already resident in HBM.
-Prints ONE JSON line with tokens/s (value), layer-calls/s, the roofline of the
-dominant kernel (timed with HIP events on the launch stream inside the timed
-region) and the CPU oracle timed on a bounded sample of the same workload.
+Default (--mode fwd): one step = one full forward call (block-mean keys,
+T x (L-step, R-step), L-apply) over one batch of seeded synthetic Q/K/V
+already resident in HBM.  --mode train: one step = the one-iteration training
+forward (which keeps its state) plus the backward pass for a seeded upstream
+gradient (dq, dk, dv).  Prints ONE JSON line with tokens/s (value),
+layer-calls/s, the roofline of the dominant kernel (timed with HIP events on
+the launch stream inside the timed region) and the CPU oracle timed on a
+bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload latent720p]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload latent720p] [--mode fwd|train]
 """
 from __future__ import annotations
 
@@ -24,12 +27,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MonarchAttention fwd tokens/s & layer-calls/s at 1 MI355X; % MFMA/HBM roofline"
+METRIC_TRAIN = ("MonarchAttention one-iteration training step (fwd + bwd) tokens/s at 1 MI355X; "
+                "% MFMA/HBM roofline")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = ["structured_attention_video_monarch_amd/csrc/device_common.h",
                   "structured_attention_video_monarch_amd/csrc/lside.h",
                   "structured_attention_video_monarch_amd/csrc/rside.h",
+                  "structured_attention_video_monarch_amd/csrc/backward.h",
                   "structured_attention_video_monarch_amd/csrc/monarch_attn.hip"]
 
 
@@ -62,6 +68,19 @@ def algorithmic_work(wl, it_last=True):
         "k_aggregate": (BH * 2.0 * N * b1 * d, BH * (nd + 4 * N + t * nd)),
         "k_rstep": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 2 * nd)),
         "k_apply": (BH * 2.0 * N * b1 * d, BH * (2 * nd + 4 * N + t * nd)),
+        # backward (one iteration), chain-rule products only (no logit
+        # recomputation, no stored s*dl), per (batch, head):
+        #   kb_du       dU = L^T dy                      2 N b1 d;  q, dy, lse in, dU out
+        #   kb_rside_a  dR = dU v^T, dQh = dz k          4 t N b2 d; Qh, dU, K, V, beta in, G out
+        #   kb_dq       <dy,U>, <q,G>, L G, dl Kbar      8 N b1 d;  q, dy, y, U, G, lse, e in, dq out
+        #   kb_dkbar    dKbar = dl^T q                   2 N b1 d;  q in
+        #   kb_rside_b  dv = R^T dU, dk_R = dz^T Qh      4 t N b2 d; Qh, dU, K, V in, dk, dv out
+        "kb_du": (BH * 2.0 * N * b1 * d, BH * (2 * nd + 4 * N + t * nd)),
+        "kb_rside_a": (BH * 4.0 * t * N * b2 * d, BH * (3 * t * nd + 2 * nd + 16 * t * N)),
+        "kb_dq": (BH * 8.0 * N * b1 * d, BH * (4 * nd + 2 * t * nd + 8 * N + 4 * t * N)),
+        "kb_dkbar": (BH * 2.0 * N * b1 * d, BH * nd),
+        "kb_dkbar_reduce": (0.0, BH * b1 * d * 4.0),
+        "kb_rside_b": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 4 * nd + 8 * t * N)),
     }
 
 
@@ -116,6 +135,33 @@ def cpu_baseline(wl, seed, budget_s=30.0):
                       f"{spent:.1f} s; full call extrapolated as heads x per-head time"}
 
 
+def cpu_baseline_train(wl, seed, budget_s=30.0):
+    """The forward and gradient oracles on a bounded sample: whole heads."""
+    import oracle
+    from structured_attention_video_monarch_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    done, spent = 0, 0.0
+    while done < wl.B * wl.H and (done == 0 or spent < budget_s):
+        b, h = divmod(done, wl.H)
+        x = I.make_inputs(wl.with_(B=1), seed, heads=[h], want_bits=False)
+        dy = I.make_cotangent(wl.with_(B=1), seed, heads=[h], want_bits=False)["dy"][0, 0]
+        t0 = time.perf_counter()
+        oracle.monarch_head(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], wl.b1, wl.b2, wl.tiles, 1)
+        oracle.monarch_head_grad(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], dy, wl.b1, wl.b2, wl.tiles)
+        spent += time.perf_counter() - t0
+        done += 1
+    per_call = spent / done * wl.B * wl.H
+    return {"value": round(wl.B * wl.N / per_call, 1), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} of {wl.B * wl.H} heads of one {wl.name} training step (forward and "
+                      f"gradient oracles, fp64 numpy), {spent:.1f} s; full step extrapolated as "
+                      f"heads x per-head time"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +171,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--mode", choices=["fwd", "train"], default="fwd",
+                    help="fwd: forward layer call; train: one-iteration training forward + backward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (float32 read + write), "
                          "to scale HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
@@ -150,6 +198,8 @@ def main():
     from structured_attention_video_monarch_amd import inputs as I
 
     wl = I.get_workload(args.workload)
+    if args.mode == "train":
+        wl = wl.with_(iters=1)
     dev = torch.device("cuda:0")
     t0 = time.time()
     x = I.make_inputs(wl, args.seed, want_f32=(wl.dtype == "f32"))
@@ -170,6 +220,24 @@ def main():
     def step():
         M.monarch_attn_fwd_ws(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters,
                               ws, stream)
+
+    if args.mode == "train":
+        del ws
+        dyx = I.make_cotangent(wl, args.seed, want_f32=(wl.dtype == "f32"))
+        if wl.dtype == "bf16":
+            dy = torch.from_numpy(dyx["dy_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            dy = torch.from_numpy(dyx["dy"]).to(dev)
+        del dyx
+        sb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles,
+                                              M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32)
+        state = torch.empty(sb, dtype=torch.uint8, device=dev)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        targs = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles)
+
+        def step():
+            M.monarch_attn_fwd_train(q, k, v, out, *targs, state, stream)
+            M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, *targs, state, stream)
 
     for _ in range(args.warmup):
         step()
@@ -209,7 +277,7 @@ def main():
 
     total_flops = sum(work[kn][0] * kernels[kn]["launches_per_step"] for kn in kernels)
     res = {
-        "metric": METRIC,
+        "metric": METRIC if args.mode == "fwd" else METRIC_TRAIN,
         "value": round(wl.B * wl.N / (ms_step / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -223,7 +291,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "f": wl.f, "h": wl.h, "w": wl.w,
                    "N": wl.N, "d": wl.d, "b1": wl.b1, "b2": wl.b2, "tiles": wl.tiles,
-                   "iters": wl.iters, "spike_frac": wl.spike_frac},
+                   "iters": wl.iters, "spike_frac": wl.spike_frac, "mode": args.mode},
         "layer_calls_per_s": round(1e3 / ms_step, 2),
         "path_alg_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
         "path_frac_of_mfma_peak": round(total_flops / (ms_step / 1e3) / 1e12 /
@@ -234,7 +302,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_budget)
+        res["cpu_baseline"] = (cpu_baseline(wl, args.seed, args.cpu_budget) if args.mode == "fwd"
+                               else cpu_baseline_train(wl, args.seed, args.cpu_budget))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
