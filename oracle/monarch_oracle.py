@@ -47,6 +47,14 @@ Readings fixed here (the pages leave them open):
 * Tiles split the a1 (frame*row) index into t contiguous ranges with bounds
   floor(g*b1/t); each tile has its own R; 1 <= t <= b1.
 * Natural logarithm, entropy coefficient 1, 0*log(0) = 0.
+* Chunked queries against cached keys (the autoregressive, KV-cached use of
+  the layer: a chunk of frames attends to the cache plus itself; yunpan.plus
+  article, section on why real-time generation is hard: autoregressive,
+  frame-by-frame generation with few steps).  The queries then span fewer
+  blocks than the keys: queries (a1, a2) with a1 in [b1q], keys (c1, c2) with
+  c1 in [b1k], the same b2.  Every formula above holds with a1 ranging over
+  b1q and c1 over b1k; tiles split the query index a1.  For b1q = b1k this is
+  the square layer.
 
 Parity unpinned: whether these readings match the MonarchRT authors' own
 kernels (initialisation, order, the beta temperature, the entropy term); the
@@ -111,14 +119,15 @@ def uniform_R(b1: int, b2: int, t: int) -> np.ndarray:
 def l_step(qb: np.ndarray, kb: np.ndarray, R: np.ndarray, bounds, s: float):
     """Exact maximiser of F over L for fixed R.
 
-    qb, kb: [b1, b2, d]; R: [t, b1(c1), b2(a2), b2(c2)].
-    Returns L [b2(a2), b1(a1), b1(c1)] (rows sum to 1 over c1) and the logits.
+    qb: [b1q, b2, d]; kb: [b1k, b2, d]; R: [t, b1k(c1), b2(a2), b2(c2)].
+    Returns L [b2(a2), b1q(a1), b1k(c1)] (rows sum to 1 over c1) and the logits.
     """
-    b1, b2, _ = qb.shape
+    b1q, b2, _ = qb.shape
+    b1k = kb.shape[0]
     # keys aggregated through R, one per (tile, block c1, column a2)
     k_til = np.einsum("gcap,cpd->gcad", R, kb)          # [t, c1, a2, d]
     h_r = entropy(R, axis=-1)                            # [t, c1, a2]
-    logits = np.empty((b2, b1, b1))
+    logits = np.empty((b2, b1q, b1k))
     for g in range(len(bounds) - 1):
         lo, hi = bounds[g], bounds[g + 1]
         q_cols = qb[lo:hi].transpose(1, 0, 2)            # [a2, a1 in g, d]
@@ -131,14 +140,15 @@ def l_step(qb: np.ndarray, kb: np.ndarray, R: np.ndarray, bounds, s: float):
 def r_step(qb: np.ndarray, kb: np.ndarray, L: np.ndarray, bounds, s: float):
     """Exact maximiser of F over R for fixed L.
 
-    L: [b2(a2), b1(a1), b1(c1)].  Returns R [t, c1, a2, c2], the aggregated
+    L: [b2(a2), b1q(a1), b1k(c1)].  Returns R [t, c1, a2, c2], the aggregated
     queries Qhat [t, c1, a2, d] and the column masses beta [t, c1, a2].
     """
-    b1, b2, d = qb.shape
+    _, b2, d = qb.shape
+    b1k = kb.shape[0]
     t = len(bounds) - 1
-    R = np.empty((t, b1, b2, b2))
-    q_hat = np.zeros((t, b1, b2, d))
-    beta = np.empty((t, b1, b2))
+    R = np.empty((t, b1k, b2, b2))
+    q_hat = np.zeros((t, b1k, b2, d))
+    beta = np.empty((t, b1k, b2))
     for g in range(t):
         lo, hi = bounds[g], bounds[g + 1]
         Lg = L[:, lo:hi, :]                               # [a2, a1 in g, c1]
@@ -157,10 +167,10 @@ def r_step(qb: np.ndarray, kb: np.ndarray, L: np.ndarray, bounds, s: float):
 def apply_factors(L: np.ndarray, R: np.ndarray, vb: np.ndarray, bounds) -> np.ndarray:
     """Y = M V without forming M: U = R V per block, then L on the permuted index.
 
-    Returns y [b1, b2, d] (token a1*b2 + a2 at [a1, a2]).
+    Returns y [b1q, b2, d] (token a1*b2 + a2 at [a1, a2]), b1q = L.shape[1].
     """
-    b1, b2, d = vb.shape
-    y = np.empty((b1, b2, d))
+    _, b2, d = vb.shape
+    y = np.empty((L.shape[1], b2, d))
     for g in range(len(bounds) - 1):
         lo, hi = bounds[g], bounds[g + 1]
         U = R[g] @ vb                                     # [c1, a2, d]
@@ -171,19 +181,26 @@ def apply_factors(L: np.ndarray, R: np.ndarray, vb: np.ndarray, bounds) -> np.nd
 
 def monarch_head(q, k, v, b1: int, b2: int, tiles: int = 1, iters: int = 1,
                  return_factors: bool = False):
-    """One (batch, head): q, k, v [N, d] -> y [N, d] (float64).
+    """One (batch, head): q [Nq, d], k, v [N, d] -> y [Nq, d] (float64).
 
+    ``b1`` counts the key blocks (b1*b2 == N); the queries span
+    b1q = Nq / b2 blocks (b1q == b1 for the square layer, fewer for a chunk
+    of frames against cached keys).  Tiles split the query blocks.
     With ``return_factors`` also returns (L, R, history) where history holds
     the factors after every half-step (for the objective pins).
     """
-    N, d = np.shape(q)
+    N, d = np.shape(k)
+    Nq = np.shape(q)[0]
     if b1 * b2 != N:
         raise ValueError(f"b1*b2 = {b1 * b2} != N = {N}")
+    if Nq % b2 != 0 or Nq == 0:
+        raise ValueError(f"query count {Nq} is not a positive multiple of b2 = {b2}")
     if iters < 1:
         raise ValueError("iters must be >= 1")
-    bounds = tile_bounds(b1, tiles)
+    b1q = Nq // b2
+    bounds = tile_bounds(b1q, tiles)
     s = 1.0 / math.sqrt(d)
-    qb, kb, vb = _blocks(q, b1, b2), _blocks(k, b1, b2), _blocks(v, b1, b2)
+    qb, kb, vb = _blocks(q, b1q, b2), _blocks(k, b1, b2), _blocks(v, b1, b2)
     R = uniform_R(b1, b2, tiles)
     history = []
     L = None
@@ -192,14 +209,14 @@ def monarch_head(q, k, v, b1: int, b2: int, tiles: int = 1, iters: int = 1,
         history.append(("L", L, R))
         R, _, _ = r_step(qb, kb, L, bounds, s)
         history.append(("R", L, R))
-    y = apply_factors(L, R, vb, bounds).reshape(N, d)
+    y = apply_factors(L, R, vb, bounds).reshape(Nq, d)
     if return_factors:
         return y, (L, R, history)
     return y
 
 
 def monarch_attention(q, k, v, b1: int, b2: int, tiles: int = 1, iters: int = 1):
-    """q, k, v [B, H, N, d] -> y [B, H, N, d] float64, head by head."""
+    """q [B, H, Nq, d], k, v [B, H, N, d] -> y [B, H, Nq, d] float64, head by head."""
     q = np.asarray(q)
     B, H, N, d = q.shape
     y = np.empty((B, H, N, d))
@@ -212,15 +229,15 @@ def monarch_attention(q, k, v, b1: int, b2: int, tiles: int = 1, iters: int = 1)
 # ----------------------------------------------- dense forms and objective --
 
 def dense_monarch_matrix(L: np.ndarray, R: np.ndarray, bounds) -> np.ndarray:
-    """M[(a1,a2),(c1,c2)] = L[a2][a1,c1] * R[g(a1)][c1][a2,c2], as [N, N]."""
-    b2, b1, _ = L.shape
-    g_of = tile_of_rows(b1, len(bounds) - 1)
-    M = np.empty((b1, b2, b1, b2))
-    for a1 in range(b1):
+    """M[(a1,a2),(c1,c2)] = L[a2][a1,c1] * R[g(a1)][c1][a2,c2], as [Nq, N]."""
+    b2, b1q, b1k = L.shape
+    g_of = tile_of_rows(b1q, len(bounds) - 1)
+    M = np.empty((b1q, b2, b1k, b2))
+    for a1 in range(b1q):
         Rg = R[g_of[a1]]                                  # [c1, a2, c2]
         # M[a1, a2, c1, c2] = L[a2, a1, c1] * Rg[c1, a2, c2]
         M[a1] = L[:, a1, :][:, :, None] * Rg.transpose(1, 0, 2)
-    return M.reshape(b1 * b2, b1 * b2)
+    return M.reshape(b1q * b2, b1k * b2)
 
 
 def permutation_matrix(b1: int, b2: int) -> np.ndarray:

@@ -17,7 +17,10 @@ never from the oracle's own output:
   decreases, and the objective equals sum lse - sum KL to dense attention;
 * block rank at most the tile count, and the KKT (log-softmax) conditions;
 * an exactly separable positional input is reproduced exactly by aligned
-  blocks in one iteration.
+  blocks in one iteration;
+* chunked queries against cached keys: row-stochastic non-square M equal to
+  the factored apply, exact attention where the blocks degenerate, and a chunk
+  equal to the matching rows of the square layer over all frames.
 """
 from __future__ import annotations
 
@@ -291,6 +294,64 @@ def check_separable_positional_exact(orc):
     assert orc.row_kl(Ms, _dense_A(qs, ks)).mean() >= 1e-4
 
 
+# --------------------------------------- chunked queries, cached keys (KV) --
+
+def check_kv_row_stochastic_and_dense_apply(orc):
+    """Chunk of query blocks against more key blocks: M is [Nq, N] row-stochastic
+    and the factored apply equals the dense product."""
+    rng = np.random.default_rng(50)
+    for (b1q, b1k, b2, t, T) in [(4, 10, 3, 1, 1), (4, 10, 3, 2, 2), (3, 7, 5, 3, 1)]:
+        q = 1.5 * rng.standard_normal((b1q * b2, 8))
+        k = 1.5 * rng.standard_normal((b1k * b2, 8))
+        v = rng.standard_normal((b1k * b2, 8))
+        y, (L, R, _) = orc.monarch_head(q, k, v, b1k, b2, t, T, return_factors=True)
+        assert y.shape == (b1q * b2, 8)
+        M = orc.dense_monarch_matrix(L, R, orc.tile_bounds(b1q, t))
+        assert M.shape == (b1q * b2, b1k * b2)
+        assert M.min() >= 0.0
+        assert np.max(np.abs(M.sum(axis=1) - 1.0)) <= 1e-12
+        assert np.max(np.abs(M @ v - y)) <= 1e-12
+
+
+def check_kv_exact_cases(orc):
+    """b2 = 1 (any tiles, iterations) and one key block with one-row tiles are
+    exact softmax attention of the chunk's queries over all keys."""
+    rng = np.random.default_rng(51)
+    Nq, Nk, d = 12, 30, 8
+    q = 1.5 * rng.standard_normal((Nq, d))
+    k = 1.5 * rng.standard_normal((Nk, d))
+    v = rng.standard_normal((Nk, d))
+    ref = _sdpa(q, k, v)
+    for t, T in [(1, 1), (4, 2), (12, 1)]:
+        y = orc.monarch_head(q, k, v, Nk, 1, t, T)
+        assert np.max(np.abs(y - ref)) <= TOL, ("b2=1", t, T)
+    # one key block (b1k = 1, b2 = Nk): queries must come in whole blocks of b2
+    q2 = 1.5 * rng.standard_normal((3 * Nk, d))
+    ref2 = _sdpa(q2, k, v)
+    for T in (1, 3):
+        y = orc.monarch_head(q2, k, v, 1, Nk, 3, T)
+        assert np.max(np.abs(y - ref2)) <= TOL, ("b1k=1", T)
+
+
+def check_kv_chunk_is_last_tiles_of_full_layer(orc):
+    """A chunk of the last fq frames against all fk frames equals the rows of
+    the square layer over all frames whose tiles cover exactly the chunk with
+    the same bounds (t_full = t * fk / fq): tiles are independent query-row
+    groups, and the chunk's rows see the same keys."""
+    rng = np.random.default_rng(52)
+    fk, fq, h, w, d = 6, 2, 3, 4, 8
+    b1k, b2 = fk * h, w
+    N, Nq = b1k * b2, fq * h * w
+    q = 1.5 * rng.standard_normal((N, d))
+    k = 1.5 * rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    for t in (1, 2, 3):
+        for T in (1, 2):
+            full = orc.monarch_head(q, k, v, b1k, b2, t * fk // fq, T)
+            chunk = orc.monarch_head(q[N - Nq:], k, v, b1k, b2, t, T)
+            assert np.max(np.abs(chunk - full[N - Nq:])) <= 1e-12, (t, T)
+
+
 ALL_CHECKS = [
     check_tile_bounds,
     check_row_stochastic_and_dense_apply,
@@ -302,5 +363,8 @@ ALL_CHECKS = [
     check_steps_are_exact_maximisers,
     check_block_rank_at_most_tiles,
     check_kkt,
+    check_kv_row_stochastic_and_dense_apply,
+    check_kv_exact_cases,
+    check_kv_chunk_is_last_tiles_of_full_layer,
     check_separable_positional_exact,
 ]

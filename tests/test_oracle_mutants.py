@@ -44,6 +44,8 @@ MUTANTS = {
     "kbar_from_values": ("L, _ = l_step(qb, kb, R, bounds, s)", "L, _ = l_step(qb, vb, R, bounds, s)"),
     "apply_values_are_keys": ("y = apply_factors(L, R, vb, bounds)", "y = apply_factors(L, R, kb, bounds)"),
     "dense_M_wrong_tile": ("Rg = R[g_of[a1]]", "Rg = R[0]"),
+    "kv_tiles_over_key_blocks": ("bounds = tile_bounds(b1q, tiles)", "bounds = tile_bounds(b1, tiles)"),
+    "kv_apply_rows_from_keys": ("y = np.empty((L.shape[1], b2, d))", "y = np.zeros((vb.shape[0], b2, d))"),
     "stale_L_in_apply": ("        R, _, _ = r_step(qb, kb, L, bounds, s)\n        history",
                          "        R, _, _ = r_step(qb, kb, L, bounds, s)\n        L = L[:, ::-1, :]\n        history"),
 }
