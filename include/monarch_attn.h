@@ -93,6 +93,31 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
                         int b1, int b2, int tiles, int iters, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- chunked queries against cached keys ----
+ * Autoregressive video generation produces a chunk of frames at a time; the
+ * chunk's queries attend to the cached keys and values of earlier frames plus
+ * the chunk's own (yunpan.plus MonarchRT article, on autoregressive,
+ * frame-by-frame real-time generation).  Here q and out are [B, H, Nq, d]
+ * with Nq = fq*h*w (the chunk: fq frames), k and v are [B, H, N, d] with
+ * N = f*h*w (all f frames the chunk attends to, its own included).  (b1, b2)
+ * block the keys (b1*b2 == N); the queries form b1q = Nq/b2 blocks of the same
+ * b2 (Nq must be a multiple of b2).  The definition is the one above with the
+ * query block index a1 in [b1q] and the key block index c1 in [b1]; tiles
+ * split the query blocks (1 <= tiles <= b1q).  With fq == f this is exactly
+ * monarch_attn_fwd_ws; a chunk of the last fq frames gives the rows of the
+ * full layer over all frames whose tiles cover the chunk with the same bounds.
+ * Errors and workspace rules as for monarch_attn_fwd_ws (out must not overlap
+ * q, k or v). */
+size_t monarch_attn_kv_workspace_bytes(int B, int H, int fq, int f, int h, int w, int d,
+                                       int b1, int b2, int tiles, int iters, int dtype);
+int monarch_attn_fwd_kv(const void* q, const void* k, const void* v, void* out,
+                        int B, int H, int fq, int f, int h, int w, int d,
+                        int b1, int b2, int tiles, int iters, int dtype, void* stream);
+int monarch_attn_fwd_kv_ws(const void* q, const void* k, const void* v, void* out,
+                           int B, int H, int fq, int f, int h, int w, int d,
+                           int b1, int b2, int tiles, int iters, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- training: the one-iteration form and its gradient ----
  * The pages' deployed regime is one iteration after finetuning the video
  * model with this attention in place (yunpan.plus MonarchRT article,

@@ -46,6 +46,13 @@ def _declare(lib):
     lib.monarch_attn_workspace_bytes.restype = c_size_t
     lib.monarch_attn_fwd_ws.argtypes = [c_void_p] * 4 + dims + [c_int, c_void_p, c_size_t, c_void_p]
     lib.monarch_attn_fwd_ws.restype = c_int
+    kdims = [c_int] * 11  # B, H, fq, f, h, w, d, b1, b2, tiles, iters
+    lib.monarch_attn_kv_workspace_bytes.argtypes = kdims + [c_int]
+    lib.monarch_attn_kv_workspace_bytes.restype = c_size_t
+    lib.monarch_attn_fwd_kv.argtypes = [c_void_p] * 4 + kdims + [c_int, c_void_p]
+    lib.monarch_attn_fwd_kv.restype = c_int
+    lib.monarch_attn_fwd_kv_ws.argtypes = [c_void_p] * 4 + kdims + [c_int, c_void_p, c_size_t, c_void_p]
+    lib.monarch_attn_fwd_kv_ws.restype = c_int
     tdims = [c_int] * 9  # B, H, f, h, w, d, b1, b2, tiles
     lib.monarch_attn_train_state_bytes.argtypes = tdims + [c_int]
     lib.monarch_attn_train_state_bytes.restype = c_size_t
@@ -165,6 +172,36 @@ def monarch_attn(q, k, v, f, h, w, b1=None, b2=None, tiles=1, iters=1):
     if q.dtype == torch.bfloat16:
         return monarch_attn_fwd(q, k, v, out, f, h, w, b1, b2, tiles, iters)
     return monarch_attn_fwd_f32(q, k, v, out, f, h, w, b1, b2, tiles, iters)
+
+
+def monarch_attn_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, iters, dtype=MONARCH_BF16) -> int:
+    return int(lib().monarch_attn_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, iters, dtype))
+
+
+def monarch_attn_fwd_kv(q, k, v, out, fq, f, h, w, b1, b2, tiles=1, iters=1, workspace=None,
+                        stream=None):
+    """Chunk of fq frames (q, out [B,H,fq*h*w,d]) against all f frames (k, v
+    [B,H,f*h*w,d]); (b1, b2) block the keys.  Either dtype; with ``workspace``
+    (a uint8 GPU tensor) nothing is allocated."""
+    import torch
+    for name, t, rows in (("q", q, fq * h * w), ("out", out, fq * h * w), ("k", k, f * h * w),
+                          ("v", v, f * h * w)):
+        if not t.is_cuda or t.dtype != q.dtype or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d GPU tensor of q's dtype")
+        if t.shape[0] != q.shape[0] or t.shape[1] != q.shape[1] or t.shape[3] != q.shape[3] \
+                or t.shape[2] != rows:
+            raise ValueError(f"{name} shape {tuple(t.shape)} does not match the chunk/frame sizes")
+    B, H, _, d = q.shape
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
+    dims = [B, H, fq, f, h, w, d, b1, b2, tiles, iters]
+    if workspace is None:
+        _check(lib().monarch_attn_fwd_kv(*ptrs, *dims, _dtype_code(q), _stream(stream)), "monarch_attn_fwd_kv")
+    else:
+        if not workspace.is_cuda or workspace.dtype != torch.uint8:
+            raise ValueError("workspace must be a uint8 GPU tensor")
+        _check(lib().monarch_attn_fwd_kv_ws(*ptrs, *dims, _dtype_code(q), ctypes.c_void_p(workspace.data_ptr()),
+                                            workspace.numel(), _stream(stream)), "monarch_attn_fwd_kv_ws")
+    return out
 
 
 def _dtype_code(t):

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
   rest /= p.b2;
   const int g = rest % p.t;
   const int bh = rest / p.t;
-  const int lo = tile_lo(g, p.b1, p.t), hi = tile_lo(g + 1, p.b1, p.t);
+  const int lo = tile_lo(g, p.b1r, p.t), hi = tile_lo(g + 1, p.b1r, p.t);
   const int nrows = hi - lo;
   const int nst = (nrows + kStep - 1) / kStep;
 

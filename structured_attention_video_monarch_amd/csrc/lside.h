@@ -23,7 +23,11 @@
 namespace monarch {
 
 struct LGeom {
-  int BH, N, b1, b2, t;
+  int BH;
+  int N;       // query tokens per head (rows of q, lse, out)
+  int b1;      // key blocks c1
+  int b1r;     // query blocks a1 (== b1 for the square layer; fewer for a chunk of frames)
+  int b2, t;
   int nrb;     // row blocks per (tile, column) or per head (contiguous mode)
   float c;     // log2(e) / sqrt(d)
 };
@@ -67,8 +71,8 @@ struct ColItem {
     rest /= p.b2;
     g = rest % p.t;
     bh = rest / p.t;
-    lo = tile_lo(g, p.b1, p.t);
-    hi = tile_lo(g + 1, p.b1, p.t);
+    lo = tile_lo(g, p.b1r, p.t);
+    hi = tile_lo(g + 1, p.b1r, p.t);
     a1_0 = lo + rb * rb_rows;
     nrows = hi - a1_0 < rb_rows ? hi - a1_0 : rb_rows;
   }
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
   rest /= p.b2;
   const int g = rest % p.t;
   const int bh = rest / p.t;
-  const int lo = tile_lo(g, p.b1, p.t), hi = tile_lo(g + 1, p.b1, p.t);
+  const int lo = tile_lo(g, p.b1r, p.t), hi = tile_lo(g + 1, p.b1r, p.t);
   const KeySrc<T, D, BCAST> ks(kt, h2, p, bh, g, a2);
 
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -460,7 +464,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
   rest /= p.b2;
   const int g = rest % p.t;
   const int bh = rest / p.t;
-  const int lo = tile_lo(g, p.b1, p.t), hi = tile_lo(g + 1, p.b1, p.t);
+  const int lo = tile_lo(g, p.b1r, p.t), hi = tile_lo(g + 1, p.b1r, p.t);
   const int nrows = hi - lo;
   const int nst = (nrows + kStep - 1) / kStep;
   const KeySrc<T, D, BCAST> ks(kt, h2, p, bh, g, a2);

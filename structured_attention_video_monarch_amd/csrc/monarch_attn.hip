@@ -56,41 +56,60 @@ constexpr int kAggRW = MONARCH_AGG_RW, kAggNW = MONARCH_AGG_NW;
 constexpr int kAppRW = MONARCH_APP_RW, kAppNW = MONARCH_APP_NW;
 
 // ------------------------------------------------------------------ checks --
+// Shapes of one call.  Keys and values: f frames, N = f*h*w tokens in b1
+// blocks of b2.  Queries: fq frames, Nq = fq*h*w tokens in b1q blocks of b2
+// (fq == f for the square layer; a chunk of frames against cached keys has
+// fewer).  Tiles split the query blocks.
 struct Shape {
   int B, H, f, h, w, d, b1, b2, t, T;
   long long N, BH;
+  int fq, b1q;
+  long long Nq;
 };
 
 int check_args(const void* q, const void* k, const void* v, const void* out, const Shape& s,
                size_t elem) {
   if (!q || !k || !v || !out) return MONARCH_EINVAL;
-  if (s.B <= 0 || s.H <= 0 || s.f <= 0 || s.h <= 0 || s.w <= 0 || s.d <= 0 || s.b1 <= 0 ||
-      s.b2 <= 0)
+  if (s.B <= 0 || s.H <= 0 || s.f <= 0 || s.fq <= 0 || s.h <= 0 || s.w <= 0 || s.d <= 0 ||
+      s.b1 <= 0 || s.b2 <= 0)
     return MONARCH_EINVAL;
   const long long N = static_cast<long long>(s.f) * s.h * s.w;
+  const long long Nq = static_cast<long long>(s.fq) * s.h * s.w;
   if (static_cast<long long>(s.b1) * s.b2 != N) return MONARCH_EINVAL;
-  if (s.t < 1 || s.t > s.b1) return MONARCH_EINVAL;
+  if (Nq % s.b2 != 0) return MONARCH_EINVAL;
+  const long long b1q = Nq / s.b2;
+  if (s.t < 1 || s.t > b1q) return MONARCH_EINVAL;
   if (s.T < 1) return MONARCH_EINVAL;
   if (s.d != 16 && s.d != 32 && s.d != 64 && s.d != 128) return MONARCH_EUNSUPPORTED;
   if (s.b2 > 128) return MONARCH_EUNSUPPORTED;
   if (static_cast<long long>(s.t) * N * s.d >= (1LL << 31)) return MONARCH_EUNSUPPORTED;
+  if (Nq * s.d >= (1LL << 31)) return MONARCH_EUNSUPPORTED;
   const long long BH = static_cast<long long>(s.B) * s.H;
   if (BH * s.b1 >= (1LL << 31)) return MONARCH_EUNSUPPORTED;
   // out must not overlap any input
-  const uintptr_t bytes = static_cast<uintptr_t>(BH * N * s.d) * elem;
+  const uintptr_t qbytes = static_cast<uintptr_t>(BH * Nq * s.d) * elem;
+  const uintptr_t kbytes = static_cast<uintptr_t>(BH * N * s.d) * elem;
   const uintptr_t o = reinterpret_cast<uintptr_t>(out);
-  for (const void* in : {q, k, v}) {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(in);
-    if (o < a + bytes && a < o + bytes) return MONARCH_EINVAL;
+  const void* ins[3] = {q, k, v};
+  const uintptr_t sizes[3] = {qbytes, kbytes, kbytes};
+  for (int i = 0; i < 3; ++i) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(ins[i]);
+    if (o < a + sizes[i] && a < o + qbytes) return MONARCH_EINVAL;
   }
   return MONARCH_OK;
 }
 
-Shape make_shape(int B, int H, int f, int h, int w, int d, int b1, int b2, int t, int T) {
-  Shape s{B, H, f, h, w, d, b1, b2, t, T, 0, 0};
+Shape make_shape_kv(int B, int H, int fq, int f, int h, int w, int d, int b1, int b2, int t, int T) {
+  Shape s{B, H, f, h, w, d, b1, b2, t, T, 0, 0, fq, 0, 0};
   s.N = static_cast<long long>(f) * h * w;
   s.BH = static_cast<long long>(B) * H;
+  s.Nq = static_cast<long long>(fq) * h * w;
+  s.b1q = b2 > 0 && s.Nq % b2 == 0 ? static_cast<int>(s.Nq / b2) : 0;
   return s;
+}
+
+Shape make_shape(int B, int H, int f, int h, int w, int d, int b1, int b2, int t, int T) {
+  return make_shape_kv(B, H, f, f, h, w, d, b1, b2, t, T);
 }
 
 // --------------------------------------------------------------- workspace --
@@ -132,7 +151,7 @@ Workspace layout(const Shape& s, size_t elem) {
   w.kbar = off;
   off += align_up(hc * s.b1 * s.d * elem);
   w.lse = off;
-  off += align_up(hc * s.N * sizeof(float));
+  off += align_up(hc * s.Nq * sizeof(float));
   w.qhat = off;
   off += align_up(hc * s.t * s.N * s.d * elem);
   if (s.T > 1) {
@@ -234,8 +253,8 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
   float* hent = bf.hent;
   T* uout = bf.u == bf.qhat ? nullptr : bf.u;
   float* beta = bf.beta;
-  const int BH = static_cast<int>(s.BH), N = static_cast<int>(s.N);
-  const int ngmax = (s.b1 + s.t - 1) / s.t;
+  const int BH = static_cast<int>(s.BH), Nq = static_cast<int>(s.Nq);
+  const int ngmax = (s.b1q + s.t - 1) / s.t;  // rows of the largest tile
   hipError_t err = hipSuccess;
   auto ok = [&](hipError_t e) {
     if (e != hipSuccess && err == hipSuccess) err = e;
@@ -250,10 +269,10 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
 
   constexpr int lse_rows = kLseRW * kLseNW * 16, agg_rows = kAggRW * kAggNW * 16,
                 app_rows = kAppRW * kAppNW * 16;
-  const LGeom base{BH, N, s.b1, s.b2, s.t, 0, c};
+  const LGeom base{BH, Nq, s.b1, s.b1q, s.b2, s.t, 0, c};
   LGeom lse_col = base, lse_contig = base, agg = base, app = base;
   lse_col.nrb = (ngmax + lse_rows - 1) / lse_rows;
-  lse_contig.nrb = (N + lse_rows - 1) / lse_rows;
+  lse_contig.nrb = (Nq + lse_rows - 1) / lse_rows;
   agg.nrb = (s.b1 + agg_rows - 1) / agg_rows;
   app.nrb = (ngmax + app_rows - 1) / app_rows;
   const unsigned lse_col_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lse_col.nrb);
@@ -327,12 +346,12 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
 template <typename T, int D>
 int run(const T* q, const T* k, const T* v, T* out, const Shape& s, unsigned char* ws,
         const Workspace& w, hipStream_t st) {
-  const long long per = s.N * D;
   for (long long h0 = 0; h0 < s.BH; h0 += w.hc) {
     Shape ps = s;
     ps.BH = s.BH - h0 < w.hc ? s.BH - h0 : w.hc;
-    const long long o = h0 * per;
-    const hipError_t err = run_pass<T, D>(q + o, k + o, v + o, out + o, ps, bufs_of<T>(ps, ws, w), st);
+    const long long oq = h0 * s.Nq * D, ok = h0 * s.N * D;
+    const hipError_t err =
+        run_pass<T, D>(q + oq, k + ok, v + ok, out + oq, ps, bufs_of<T>(ps, ws, w), st);
     if (err != hipSuccess) {
       g_last_hip_error = static_cast<int>(err);
       return MONARCH_EHIP;
@@ -547,7 +566,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   // dU = L^T dy per tile column
   {
     constexpr int cb = C::kDuRW * C::kDuNW * 16;
-    LGeom lg{BH, N, s.b1, s.b2, s.t, (s.b1 + cb - 1) / cb, c};
+    LGeom lg{BH, N, s.b1, s.b1, s.b2, s.t, (s.b1 + cb - 1) / cb, c};
     const unsigned grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lg.nrb);
     ok(timed(5, st, [&] {
       kb_du<T, D, C::kDuRW, C::kDuNW><<<grid, C::kDuNW * kWave, 0, st>>>(q, dout, bf.kbar, bf.lse, du, lg);
@@ -577,7 +596,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   // row pass: delta, dq and the stored s*dl
   {
     constexpr int rows = C::kDqRW * C::kDqNW * 16;
-    LGeom lg{BH, N, s.b1, s.b2, s.t, (ngmax + rows - 1) / rows, c};
+    LGeom lg{BH, N, s.b1, s.b1, s.b2, s.t, (ngmax + rows - 1) / rows, c};
     const unsigned grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lg.nrb);
     ok(timed(7, st, [&] {
       kb_dq<T, D, C::kDqRW, C::kDqNW><<<grid, C::kDqNW * kWave, 0, st>>>(
@@ -748,6 +767,31 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, 
   const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   return fwd_ws(q, k, v, out, s, dtype, workspace, workspace_bytes,
                 static_cast<hipStream_t>(stream));
+}
+
+size_t monarch_attn_kv_workspace_bytes(int B, int H, int fq, int f, int h, int w, int d, int b1, int b2,
+                                       int tiles, int iters, int dtype) {
+  const size_t elem = elem_size(dtype);
+  if (elem == 0) return 0;
+  const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
+  static const char dummy[4] = {0};
+  if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
+  return layout(s, elem).total;
+}
+
+int monarch_attn_fwd_kv(const void* q, const void* k, const void* v, void* out, int B, int H, int fq,
+                        int f, int h, int w, int d, int b1, int b2, int tiles, int iters, int dtype,
+                        void* stream) {
+  const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
+  if (elem_size(dtype) == 0) return MONARCH_EINVAL;
+  return fwd_alloc(q, k, v, out, s, dtype, static_cast<hipStream_t>(stream));
+}
+
+int monarch_attn_fwd_kv_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
+                           int fq, int f, int h, int w, int d, int b1, int b2, int tiles, int iters,
+                           int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
+  return fwd_ws(q, k, v, out, s, dtype, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d, int b1, int b2,

@@ -58,10 +58,27 @@ class Workload:
     dtype: str                # "f32" or "bf16": the I/O and compute type
     spike_frac: float = 0.0   # fraction of query rows with a planted match
     pos_amp: float = 0.5
+    fq: int = 0               # query frames: 0 = all f frames (the square layer);
+                              # else the last fq frames attend to all f (cached keys)
 
     @property
     def N(self) -> int:
+        """Key (and value) tokens: all f frames."""
         return self.f * self.h * self.w
+
+    @property
+    def Nq(self) -> int:
+        """Query (and output) tokens."""
+        return (self.fq or self.f) * self.h * self.w
+
+    @property
+    def b1q(self) -> int:
+        """Query blocks of b2 tokens."""
+        return self.Nq // self.b2
+
+    @property
+    def kv(self) -> bool:
+        return bool(self.fq) and self.fq != self.f
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -76,6 +93,10 @@ WORKLOADS = {
     "chunk480p": Workload("chunk480p", 1, 12, 128, 3, 30, 52, 90, 52, 1, 1, "bf16"),
     "clip480p": Workload("clip480p", 1, 12, 128, 21, 30, 52, 630, 52, 1, 1, "bf16"),
     "latent720p": Workload("latent720p", 1, 40, 128, 21, 45, 80, 945, 80, 4, 1, "bf16"),
+    # a 3-frame chunk (Self-Forcing's unit of generation) attending to 18
+    # cached frames plus itself, at the 480p and 720p latent sizes
+    "chunk480p_kv": Workload("chunk480p_kv", 1, 12, 128, 21, 30, 52, 630, 52, 1, 1, "bf16", fq=3),
+    "chunk720p_kv": Workload("chunk720p_kv", 1, 40, 128, 21, 45, 80, 945, 80, 1, 1, "bf16", fq=3),
 }
 for _t in (1, 2, 4, 8):
     for _T in (1, 2):
@@ -168,22 +189,27 @@ def make_inputs(wl: Workload, seed: int = 0, heads=None, want_f32: bool = True,
       ``<x>_bits`` uint16 bf16 bit patterns, same shape (bf16 workloads, if
                    ``want_bits``).
     ``heads`` selects a subset of head indices (default: all); each head's
-    values do not depend on which other heads are generated.
+    values do not depend on which other heads are generated.  For a chunk
+    against cached keys (``wl.fq``), q holds the last fq frames' queries of
+    the same draw (``[B, heads, Nq, d]``); k and v hold all frames.
     """
     heads = list(range(wl.H)) if heads is None else list(heads)
     N, d = wl.N, wl.d
     shape = (wl.B, len(heads), N, d)
+    qshape = (wl.B, len(heads), wl.Nq, d)
     bf16 = wl.dtype == "bf16"
     out = {}
     for name in "qkv":
+        shp = qshape if name == "q" else shape
         if want_f32:
-            out[name] = np.empty(shape, dtype=np.float32)
+            out[name] = np.empty(shp, dtype=np.float32)
         if bf16 and want_bits:
-            out[name + "_bits"] = np.empty(shape, dtype=np.uint16)
+            out[name + "_bits"] = np.empty(shp, dtype=np.uint16)
     pos = positional_term(wl.f, wl.h, wl.w, d, wl.pos_amp) if wl.pos_amp else None
     for b in range(wl.B):
         for j, hh in enumerate(heads):
-            tensors = make_head(wl, seed, b, hh, pos)
+            tensors = list(make_head(wl, seed, b, hh, pos))
+            tensors[0] = tensors[0][N - wl.Nq:]
             for name, x in zip("qkv", tensors):
                 if bf16:
                     bits = round_to_bf16_bits(x)
@@ -202,7 +228,7 @@ def make_cotangent(wl: Workload, seed: int = 0, heads=None, want_f32: bool = Tru
     normal per (batch, head), from its own stream (``[seed, b, h, 1]``), in
     the same dict format as :func:`make_inputs` under the key ``dy``."""
     heads = list(range(wl.H)) if heads is None else list(heads)
-    shape = (wl.B, len(heads), wl.N, wl.d)
+    shape = (wl.B, len(heads), wl.Nq, wl.d)
     bf16 = wl.dtype == "bf16"
     out = {}
     if want_f32:
@@ -211,7 +237,7 @@ def make_cotangent(wl: Workload, seed: int = 0, heads=None, want_f32: bool = Tru
         out["dy_bits"] = np.empty(shape, dtype=np.uint16)
     for b in range(wl.B):
         for j, hh in enumerate(heads):
-            x = np.random.default_rng([seed, b, hh, 1]).standard_normal((wl.N, wl.d), dtype=np.float32)
+            x = np.random.default_rng([seed, b, hh, 1]).standard_normal((wl.Nq, wl.d), dtype=np.float32)
             if bf16:
                 bits = round_to_bf16_bits(x)
                 if want_bits:

@@ -142,3 +142,38 @@ def test_fwd_train_rejects_small_state():
     p = _train_ptrs(5)
     rc = M.lib().monarch_attn_fwd_train(*p[:4], 1, 2, 3, 30, 52, 128, 90, 52, 1, 0, p[4], 256, None)
     assert rc == M.MONARCH_ENOMEM
+
+
+# ---- chunked queries against cached keys
+def _kv(B=1, H=2, fq=3, f=21, h=30, w=52, d=128, b1=630, b2=52, t=1, T=1, dtype=0, out=None):
+    p = _train_ptrs(4)
+    if out is not None:
+        p[3] = p[out]
+    return M.lib().monarch_attn_fwd_kv(*p, B, H, fq, f, h, w, d, b1, b2, t, T, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(b1=629), M.MONARCH_EINVAL),                  # b1*b2 != f*h*w
+    (dict(fq=0), M.MONARCH_EINVAL),
+    (dict(t=91), M.MONARCH_EINVAL),                    # tiles > query blocks (90)
+    (dict(fq=1, h=3, w=5, f=4, b1=12, b2=5, t=1, d=64), None),  # valid shape: checked below
+    (dict(fq=1, h=3, w=5, f=4, b1=6, b2=10, t=1, d=64), M.MONARCH_EINVAL),  # Nq = 15 not a multiple of b2
+    (dict(out=0), M.MONARCH_EINVAL),                   # out aliases q
+    (dict(d=48), M.MONARCH_EUNSUPPORTED),
+])
+def test_kv_bad_arguments_rejected_before_any_gpu_call(kw, status):
+    if status is None:
+        assert M.monarch_attn_kv_workspace_bytes(1, 2, 1, 4, 3, 5, 64, 12, 5, 1, 1, 0) > 0
+        return
+    assert _kv(**kw) == status
+
+
+def test_kv_workspace_bytes():
+    B, H, fq, f, h, w, d, b1, b2, t, T = 1, 40, 3, 21, 45, 80, 128, 945, 80, 1, 2
+    N, Nq, BH, e = f * h * w, fq * h * w, B * H, 2
+    expect = (_align(BH * b1 * d * e) + _align(BH * Nq * 4) + _align(BH * t * N * d * e)
+              + _align(BH * t * N * d * e) + _align(BH * t * N * 4))
+    assert M.monarch_attn_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, t, T, 0) == expect
+    # fq == f is the square layer
+    assert (M.monarch_attn_kv_workspace_bytes(B, H, f, f, h, w, d, b1, b2, 4, 1, 0)
+            == M.monarch_attn_workspace_bytes(B, H, f, h, w, d, b1, b2, 4, 1, 0))

@@ -107,3 +107,13 @@ def test_more_tiles_more_accuracy():
     for T in (1, 2):
         kls = [_kl_to_dense(q, k, v, wl.b1, wl.b2, t, T) for t in (1, 2, 4, 8)]
         assert all(b <= a + 1e-12 for a, b in zip(kls, kls[1:])), (T, kls)
+
+
+def test_chunk_queries_are_the_tail_of_the_full_draw():
+    from structured_attention_video_monarch_amd import inputs as I
+    wl = I.Workload("kvsmall", 1, 2, 16, 6, 3, 4, 18, 4, 1, 1, "bf16", fq=2)
+    x = I.make_inputs(wl, 5)
+    full = I.make_inputs(wl.with_(fq=0), 5)
+    assert x["q"].shape == (1, 2, 2 * 3 * 4, 16) and x["k"].shape == (1, 2, 6 * 3 * 4, 16)
+    assert np.array_equal(x["q_bits"], full["q_bits"][:, :, -24:])
+    assert np.array_equal(x["k_bits"], full["k_bits"]) and np.array_equal(x["v_bits"], full["v_bits"])
