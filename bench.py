@@ -50,7 +50,8 @@ def kernel_source_hash() -> str:
 def algorithmic_work(wl, it_last=True):
     """Per launch: (flops, bytes) each kernel must do by the method's definition.
 
-    Per (batch, head), e = element bytes, N = b1*b2:
+    Per (batch, head), e = element bytes, N = b1*b2 (for a chunk against
+    cached keys the query terms below use Nq, the chunk's tokens):
       k_kbar       0 flops;   bytes  N*d*e (read K) + b1*d*e (write means)
       k_lse        2*N*b1*d   (L logits);          bytes N*d*e + 4N
       k_aggregate  2*N*b1*d   (L^T q per tile);    bytes N*d*e + 4N + t*N*d*e
@@ -61,13 +62,14 @@ def algorithmic_work(wl, it_last=True):
     """
     e = 2 if wl.dtype == "bf16" else 4
     BH, N, d, b1, b2, t = wl.B * wl.H, wl.N, wl.d, wl.b1, wl.b2, wl.tiles
-    nd = N * d * e
+    Nq = wl.Nq   # query tokens (== N for the square layer; a chunk against cached keys has fewer)
+    nd, nqd = N * d * e, Nq * d * e
     return {
         "k_kbar": (0.0, BH * (nd + b1 * d * e)),
-        "k_lse": (BH * 2.0 * N * b1 * d, BH * (nd + 4 * N)),
-        "k_aggregate": (BH * 2.0 * N * b1 * d, BH * (nd + 4 * N + t * nd)),
+        "k_lse": (BH * 2.0 * Nq * b1 * d, BH * (nqd + 4 * Nq)),
+        "k_aggregate": (BH * 2.0 * Nq * b1 * d, BH * (nqd + 4 * Nq + t * nd)),
         "k_rstep": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 2 * nd)),
-        "k_apply": (BH * 2.0 * N * b1 * d, BH * (2 * nd + 4 * N + t * nd)),
+        "k_apply": (BH * 2.0 * Nq * b1 * d, BH * (2 * nqd + 4 * Nq + t * nd)),
         # backward (one iteration), chain-rule products only (no logit
         # recomputation, no stored s*dl), per (batch, head):
         #   kb_du       dU = L^T dy                      2 N b1 d;  q, dy, lse in, dU out
@@ -129,7 +131,7 @@ def cpu_baseline(wl, seed, budget_s=30.0):
         spent += time.perf_counter() - t0
         done += 1
     per_call = spent / done * wl.B * wl.H
-    return {"value": round(wl.B * wl.N / per_call, 1), "unit": "tokens/s", "cores": int(cores),
+    return {"value": round(wl.B * wl.Nq / per_call, 1), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{done} of {wl.B * wl.H} heads of one {wl.name} call, fp64 numpy oracle, "
                       f"{spent:.1f} s; full call extrapolated as heads x per-head time"}
@@ -211,15 +213,24 @@ def main():
     del x
     print(f"[bench] inputs {wl.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     out = torch.empty_like(q)
-    nb = M.monarch_attn_workspace_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2,
-                                        wl.tiles, wl.iters,
-                                        M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32)
+    dtc = M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32
+    nb = M.monarch_attn_kv_workspace_bytes(wl.B, wl.H, wl.fq or wl.f, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2,
+                                           wl.tiles, wl.iters, dtc)
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
         M.monarch_attn_fwd_ws(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters,
                               ws, stream)
+
+    if wl.kv:
+        if args.mode == "train":
+            print("bench.py: the training step is defined for the square layer only", file=sys.stderr)
+            sys.exit(2)
+
+        def step():
+            M.monarch_attn_fwd_kv(q, k, v, out, wl.fq, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles,
+                                  wl.iters, workspace=ws, stream=stream)
 
     if args.mode == "train":
         del ws
@@ -278,7 +289,7 @@ def main():
     total_flops = sum(work[kn][0] * kernels[kn]["launches_per_step"] for kn in kernels)
     res = {
         "metric": METRIC if args.mode == "fwd" else METRIC_TRAIN,
-        "value": round(wl.B * wl.N / (ms_step / 1e3), 1),
+        "value": round(wl.B * wl.Nq / (ms_step / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -290,7 +301,8 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "f": wl.f, "h": wl.h, "w": wl.w,
-                   "N": wl.N, "d": wl.d, "b1": wl.b1, "b2": wl.b2, "tiles": wl.tiles,
+                   "N": wl.N, "Nq": wl.Nq, "fq": wl.fq or wl.f, "d": wl.d, "b1": wl.b1, "b2": wl.b2,
+                   "tiles": wl.tiles,
                    "iters": wl.iters, "spike_frac": wl.spike_frac, "mode": args.mode},
         "layer_calls_per_s": round(1e3 / ms_step, 2),
         "path_alg_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
