@@ -68,7 +68,7 @@ import numpy as np
 
 __all__ = [
     "tile_bounds", "tile_of_rows", "softmax", "entropy", "uniform_R",
-    "l_step", "r_step", "apply_factors", "monarch_head", "monarch_attention",
+    "l_step", "r_step", "apply_factors", "monarch_head", "monarch_head_adaptive", "monarch_attention",
     "dense_monarch_matrix", "explicit_monarch_matrix", "permutation_matrix",
     "softmax_attention_head", "objective", "row_kl",
 ]
@@ -213,6 +213,43 @@ def monarch_head(q, k, v, b1: int, b2: int, tiles: int = 1, iters: int = 1,
     if return_factors:
         return y, (L, R, history)
     return y
+
+
+def monarch_head_adaptive(q, k, v, b1: int, b2: int, tiles: int, max_iters: int, tol: float):
+    """Iterate until the objective stops improving (training-free regime).
+
+    The pages run about ten iterations without finetuning (yunpan.plus
+    article, "Innovation 3", Fig. 4 right) and give no stopping rule.  Reading
+    used here: after the L-step of iteration i the factors (L_i, R_(i-1))
+    have objective F_i = sum_n logsumexp of that L-step's logits (L_i is the
+    exact maximiser for R_(i-1)); stop after iteration i when i == max_iters,
+    or when i >= 2 and (F_i - F_(i-1)) / Nq <= tol (gain per query token, in
+    nats).  Iteration i's R-step is then the last and the apply uses L_i, R_i.
+    Returns (y, iterations used, [F_1, F_2, ...]).
+    """
+    N, d = np.shape(k)
+    Nq = np.shape(q)[0]
+    if b1 * b2 != N or Nq % b2 != 0 or Nq == 0:
+        raise ValueError("bad block sizes")
+    if max_iters < 1:
+        raise ValueError("max_iters must be >= 1")
+    b1q = Nq // b2
+    tb = tile_bounds(b1q, tiles)
+    s = 1.0 / math.sqrt(d)
+    qb, kb, vb = _blocks(q, b1q, b2), _blocks(k, b1, b2), _blocks(v, b1, b2)
+    R = uniform_R(b1, b2, tiles)
+    F = []
+    it = 0
+    while True:
+        it += 1
+        L, logits = l_step(qb, kb, R, tb, s)
+        m = np.max(logits, axis=-1, keepdims=True)
+        F.append(float(np.sum(m[..., 0] + np.log(np.sum(np.exp(logits - m), axis=-1)))))
+        R, _, _ = r_step(qb, kb, L, tb, s)
+        if it >= max_iters or (it >= 2 and (F[-1] - F[-2]) / Nq <= tol):
+            break
+    out = apply_factors(L, R, vb, tb).reshape(Nq, d)
+    return out, it, F
 
 
 def monarch_attention(q, k, v, b1: int, b2: int, tiles: int = 1, iters: int = 1):

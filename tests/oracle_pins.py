@@ -352,6 +352,36 @@ def check_kv_chunk_is_last_tiles_of_full_layer(orc):
             assert np.max(np.abs(chunk - full[N - Nq:])) <= 1e-12, (t, T)
 
 
+# ------------------------------------------------ iterating to convergence --
+
+def check_adaptive_iterations(orc):
+    """Early stopping: F_i equals the dense objective of (L_i, R_(i-1)); the
+    stop is the first i >= 2 whose gain per token is <= tol (computed from the
+    dense objectives); never stopping early equals max_iters iterations, and
+    stopping at once equals two."""
+    b1, b2, t, d = 6, 5, 2, 8
+    q, k, v = _case(60, b1, b2, d)
+    N = b1 * b2
+    # dense objectives after each L-step, from the factors of a long run
+    _, (_, _, hist) = orc.monarch_head(q, k, v, b1, b2, t, 6, return_factors=True)
+    bounds = orc.tile_bounds(b1, t)
+    F_dense = [orc.objective(orc.dense_monarch_matrix(L, R, bounds), q, k)
+               for (kind, L, R) in hist if kind == "L"]
+    y, used, F = orc.monarch_head_adaptive(q, k, v, b1, b2, t, 6, -1.0)
+    assert used == 6
+    assert np.max(np.abs(np.array(F) - np.array(F_dense))) <= 1e-9 * max(1.0, abs(F_dense[0]))
+    assert np.max(np.abs(y - orc.monarch_head(q, k, v, b1, b2, t, 6))) <= 1e-12
+    gains = np.diff(F_dense) / N
+    assert np.all(gains >= -1e-12)
+    for tol in (1e30, float(gains[1]) * 1.0001, float(gains[2]) * 1.0001, 0.0):
+        want = next((i + 2 for i, g in enumerate(gains) if g <= tol), 6)
+        y, used, _ = orc.monarch_head_adaptive(q, k, v, b1, b2, t, 6, tol)
+        assert used == want, (tol, used, want)
+        assert np.max(np.abs(y - orc.monarch_head(q, k, v, b1, b2, t, want))) <= 1e-12
+    y1, used1, _ = orc.monarch_head_adaptive(q, k, v, b1, b2, t, 1, 1e30)
+    assert used1 == 1 and np.max(np.abs(y1 - orc.monarch_head(q, k, v, b1, b2, t, 1))) <= 1e-12
+
+
 ALL_CHECKS = [
     check_tile_bounds,
     check_row_stochastic_and_dense_apply,
@@ -366,5 +396,6 @@ ALL_CHECKS = [
     check_kv_row_stochastic_and_dense_apply,
     check_kv_exact_cases,
     check_kv_chunk_is_last_tiles_of_full_layer,
+    check_adaptive_iterations,
     check_separable_positional_exact,
 ]

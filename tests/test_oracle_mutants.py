@@ -46,6 +46,9 @@ MUTANTS = {
     "dense_M_wrong_tile": ("Rg = R[g_of[a1]]", "Rg = R[0]"),
     "kv_tiles_over_key_blocks": ("bounds = tile_bounds(b1q, tiles)", "bounds = tile_bounds(b1, tiles)"),
     "kv_apply_rows_from_keys": ("y = np.empty((L.shape[1], b2, d))", "y = np.zeros((vb.shape[0], b2, d))"),
+    "adaptive_gain_not_per_token": ("(F[-1] - F[-2]) / Nq <= tol", "(F[-1] - F[-2]) <= tol"),
+    "adaptive_stops_after_one": ("(it >= 2 and (F[-1] - F[-2]) / Nq <= tol)", "(it >= 1 and (F[-1] - F[-2 if it > 1 else -1]) / Nq <= tol)"),
+    "adaptive_objective_without_max": ("F.append(float(np.sum(m[..., 0] + np.log(", "F.append(float(np.sum(0 * m[..., 0] + np.log("),
     "stale_L_in_apply": ("        R, _, _ = r_step(qb, kb, L, bounds, s)\n        history",
                          "        R, _, _ = r_step(qb, kb, L, bounds, s)\n        L = L[:, ::-1, :]\n        history"),
 }
