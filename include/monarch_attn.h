@@ -93,6 +93,29 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
                         int b1, int b2, int tiles, int iters, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- iterating until the factors converge ----
+ * Without finetuning the pages run about ten iterations (yunpan.plus
+ * MonarchRT article, "Innovation 3: finetuning and efficient kernels",
+ * Fig. 4 right) and give no stopping rule.  monarch_attn_fwd_adaptive_ws runs
+ * up to max_iters iterations and stops each (batch, head) on its own: after
+ * the L-step of iteration i the objective of the current factors is
+ * F_i = sum_n log-sum-exp of that L-step's logits (nats; the L-step is the
+ * exact maximiser), and the head stops after iteration i when i == max_iters
+ * or when i >= 2 and (F_i - F_(i-1)) / N <= tol (gain per token).  Its last
+ * R-step then gives U = R V and the apply uses that iteration's L and R: the
+ * output equals monarch_attn_fwd_ws with iters = iters_used[head].
+ * iters_used is a DEVICE array of B*H ints written on `stream` (the count of
+ * iterations each head ran, 1..max_iters).  The workspace
+ * (monarch_attn_adaptive_workspace_bytes) holds every head at once.  tol NaN or
+ * iters_used NULL: MONARCH_EINVAL; otherwise errors as monarch_attn_fwd_ws. */
+size_t monarch_attn_adaptive_workspace_bytes(int B, int H, int f, int h, int w, int d,
+                                             int b1, int b2, int tiles, int max_iters, int dtype);
+int monarch_attn_fwd_adaptive_ws(const void* q, const void* k, const void* v, void* out,
+                                 int B, int H, int f, int h, int w, int d,
+                                 int b1, int b2, int tiles, int max_iters, float tol, int dtype,
+                                 int* iters_used, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* ---- chunked queries against cached keys ----
  * Autoregressive video generation produces a chunk of frames at a time; the
  * chunk's queries attend to the cached keys and values of earlier frames plus
@@ -170,8 +193,9 @@ int monarch_attn_last_hip_error(void);
  * 3 R-step block softmax (+ R V or next keys/entropy), 4 L-apply;
  * backward: 5 dU per tile column, 6 R-step per key block (G, statistics),
  * 7 row pass (dq), 8 block-mean key gradient (product over tokens),
- * 9 its reduction, 10 dv and dk per key block. */
-#define MONARCH_NUM_KERNELS 11
+ * 9 its reduction, 10 dv and dk per key block; 11 objective and early-stop
+ * decision per head. */
+#define MONARCH_NUM_KERNELS 12
 int monarch_attn_profile_enable(int on);
 int monarch_attn_profile_collect(double* ms, long* launches, int n);
 const char* monarch_attn_kernel_name(int id);

@@ -24,7 +24,7 @@ MONARCH_EHIP = -3
 MONARCH_ENOMEM = -4
 MONARCH_BF16 = 0
 MONARCH_F32 = 1
-MONARCH_NUM_KERNELS = 11
+MONARCH_NUM_KERNELS = 12
 
 _lib = None
 
@@ -46,6 +46,11 @@ def _declare(lib):
     lib.monarch_attn_workspace_bytes.restype = c_size_t
     lib.monarch_attn_fwd_ws.argtypes = [c_void_p] * 4 + dims + [c_int, c_void_p, c_size_t, c_void_p]
     lib.monarch_attn_fwd_ws.restype = c_int
+    lib.monarch_attn_adaptive_workspace_bytes.argtypes = dims + [c_int]
+    lib.monarch_attn_adaptive_workspace_bytes.restype = c_size_t
+    lib.monarch_attn_fwd_adaptive_ws.argtypes = ([c_void_p] * 4 + dims + [ctypes.c_float, c_int, c_void_p,
+                                                 c_void_p, c_size_t, c_void_p])
+    lib.monarch_attn_fwd_adaptive_ws.restype = c_int
     kdims = [c_int] * 11  # B, H, fq, f, h, w, d, b1, b2, tiles, iters
     lib.monarch_attn_kv_workspace_bytes.argtypes = kdims + [c_int]
     lib.monarch_attn_kv_workspace_bytes.restype = c_size_t
@@ -172,6 +177,33 @@ def monarch_attn(q, k, v, f, h, w, b1=None, b2=None, tiles=1, iters=1):
     if q.dtype == torch.bfloat16:
         return monarch_attn_fwd(q, k, v, out, f, h, w, b1, b2, tiles, iters)
     return monarch_attn_fwd_f32(q, k, v, out, f, h, w, b1, b2, tiles, iters)
+
+
+def monarch_attn_adaptive_workspace_bytes(B, H, f, h, w, d, b1, b2, tiles, max_iters, dtype=MONARCH_BF16) -> int:
+    return int(lib().monarch_attn_adaptive_workspace_bytes(B, H, f, h, w, d, b1, b2, tiles, max_iters, dtype))
+
+
+def monarch_attn_fwd_adaptive(q, k, v, out, f, h, w, b1, b2, tiles, max_iters, tol, iters_used=None,
+                              workspace=None, stream=None):
+    """Up to max_iters iterations, each head stopping when its objective gain
+    per token is <= tol.  Returns (out, iters_used) with iters_used an int32
+    GPU tensor [B, H] (allocated if not given)."""
+    import torch
+    ptrs = _tensors(q, k, v, out, q.dtype)
+    B, H, _, d = q.shape
+    dt = _dtype_code(q)
+    if iters_used is None:
+        iters_used = torch.empty((B, H), dtype=torch.int32, device=q.device)
+    if not iters_used.is_cuda or iters_used.dtype != torch.int32 or iters_used.numel() != B * H:
+        raise ValueError("iters_used must be an int32 GPU tensor of B*H elements")
+    if workspace is None:
+        nb = monarch_attn_adaptive_workspace_bytes(B, H, f, h, w, d, b1, b2, tiles, max_iters, dt)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().monarch_attn_fwd_adaptive_ws(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, max_iters), float(tol), dt,
+                                              ctypes.c_void_p(iters_used.data_ptr()),
+                                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                              _stream(stream)), "monarch_attn_fwd_adaptive_ws")
+    return out, iters_used
 
 
 def monarch_attn_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, iters, dtype=MONARCH_BF16) -> int:

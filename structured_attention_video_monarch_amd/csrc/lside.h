@@ -183,7 +183,9 @@ template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG>
 __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
                                                                       const T* __restrict__ kt,
                                                                       const float* __restrict__ h2,
-                                                                      float* __restrict__ lse, LGeom p) {
+                                                                      float* __restrict__ lse, LGeom p,
+                                                                      const int* __restrict__ stop_at = nullptr,
+                                                                      int it = 0) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -208,6 +210,8 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
     nrows = it.nrows;
   }
   if (nrows <= 0) return;
+  // heads that stopped iterating earlier keep their last log-sum-exps
+  if (stop_at && stop_at[bh] != 0 && stop_at[bh] < it) return;
   const KeySrc<T, D, BCAST> ks(kt, h2, p, bh, g, a2);
 
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -309,7 +313,8 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
                                                           const float* __restrict__ h2,
                                                           const float* __restrict__ lse,
                                                           T* __restrict__ qhat, float* __restrict__ beta_out,
-                                                          LGeom p) {
+                                                          LGeom p, const int* __restrict__ stop_at = nullptr,
+                                                          int it = 0) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -329,6 +334,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
   const int g = rest % p.t;
   const int bh = rest / p.t;
   const int lo = tile_lo(g, p.b1r, p.t), hi = tile_lo(g + 1, p.b1r, p.t);
+  if (stop_at && stop_at[bh] != 0 && stop_at[bh] < it) return;  // head done iterating
   const KeySrc<T, D, BCAST> ks(kt, h2, p, bh, g, a2);
 
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -445,7 +451,9 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
                                                                                 const float* __restrict__ h2,
                                                                                 const float* __restrict__ lse,
                                                                                 T* __restrict__ qhat,
-                                                                                float* __restrict__ beta_out, LGeom p) {
+                                                                                float* __restrict__ beta_out, LGeom p,
+                                                                                const int* __restrict__ stop_at = nullptr,
+                                                                                int it = 0) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -467,6 +475,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
   const int lo = tile_lo(g, p.b1r, p.t), hi = tile_lo(g + 1, p.b1r, p.t);
   const int nrows = hi - lo;
   const int nst = (nrows + kStep - 1) / kStep;
+  if (stop_at && stop_at[bh] != 0 && stop_at[bh] < it) return;  // head done iterating
   const KeySrc<T, D, BCAST> ks(kt, h2, p, bh, g, a2);
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
@@ -701,6 +710,44 @@ __global__ __launch_bounds__(256) void k_kbar(const T* __restrict__ k, T* __rest
 #pragma unroll
     for (int j = 0; j < V; ++j) dst[j] = E::from_f32(acc[j] * inv);
   }
+}
+
+// ------------------------------------------------------------- k_objective --
+// After the L-step of iteration `it`: F = sum_n lse_n (nats) is the objective
+// of the current factors (the L-step is the exact maximiser).  Per head, one
+// workgroup: stop after this iteration when it == max_it, or when it >= 2 and
+// the gain over the previous L-step per query token is <= tol.  Heads that
+// already stopped are left alone.  The sum runs in double in a fixed order.
+// The first L-step leaves out the entropy of the uniform R, log(b2), which is
+// the same for every key block (it cancels in the softmax); it is added back
+// here so that F_1 is the objective proper.
+__global__ __launch_bounds__(256) void k_objective(const float* __restrict__ lse, int N, int b2,
+                                                   double* __restrict__ fprev, int* __restrict__ stop_at, int it,
+                                                   int max_it, float tol) {
+  const int bh = blockIdx.x;
+  if (stop_at[bh] != 0) return;
+  __shared__ double red[256];
+  double acc = 0.0;
+  const float* l = lse + static_cast<long long>(bh) * N;
+  for (int n = threadIdx.x; n < N; n += 256) acc += static_cast<double>(l[n]);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (static_cast<int>(threadIdx.x) < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double F = red[0] * 0.69314718055994530942;  // log2 units -> nats
+    if (it == 1) F += static_cast<double>(N) * log(static_cast<double>(b2));
+    const bool stop = it >= max_it || (it >= 2 && F - fprev[bh] <= static_cast<double>(tol) * N);
+    fprev[bh] = F;
+    if (stop) stop_at[bh] = it;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_int(int* __restrict__ p, int n, int value) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = value;
 }
 
 }  // namespace monarch

@@ -143,9 +143,9 @@ struct Workspace {
   size_t kbar, lse, qhat, ktil, hent, total;
 };
 
-Workspace layout(const Shape& s, size_t elem) {
+Workspace layout(const Shape& s, size_t elem, bool all_heads = false) {
   Workspace w{};
-  w.hc = heads_per_pass(s, elem);
+  w.hc = all_heads ? s.BH : heads_per_pass(s, elem);
   const size_t hc = static_cast<size_t>(w.hc);
   size_t off = 0;
   w.kbar = off;
@@ -193,7 +193,8 @@ const char* const kKernelNames[MONARCH_NUM_KERNELS] = {
     "kb_rside_a (backward: R-step per key block, G and row statistics)",
     "kb_dq (backward: row pass, dq)", "kb_dkbar (backward: block-mean key gradient over tokens)",
     "kb_dkbar_reduce (backward: sum of the token-chunk partials)",
-    "kb_rside_b (backward: dv and dk per key block)"};
+    "kb_rside_b (backward: dv and dk per key block)",
+    "k_objective (objective per head and the early-stop decision)"};
 
 // Launch wrapper: records events around the launch when profiling is on.
 template <typename F>
@@ -242,9 +243,17 @@ Bufs<T> bufs_of(const Shape& s, unsigned char* ws, const Workspace& w) {
   return b;
 }
 
+// Early stopping (iterations until the objective stops improving): per-head
+// stop iterations (zeroed before the call) and the previous objectives.
+struct Adaptive {
+  int* stop_at;
+  double* fprev;
+  float tol;
+};
+
 template <typename T, int D>
 hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, const Bufs<T>& bf,
-                    hipStream_t st) {
+                    hipStream_t st, const Adaptive* ad = nullptr) {
   const float c = kLog2e / std::sqrt(static_cast<float>(D));
   T* kbar = bf.kbar;
   float* lse = bf.lse;
@@ -298,12 +307,29 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rstep<T, D, false>),
                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds_mid)));
 
+  const int* sa = ad ? ad->stop_at : nullptr;
+  if (ad && r_lds_last > 65536)
+    ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rstep_adaptive<T, D>),
+                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds_last)));
   for (int it = 1; it <= s.T; ++it) {
     const bool first = it == 1, last = it == s.T;
     if (first) {
       ok(timed(1, st, [&] {
         k_lse<T, D, kLseRW, kLseNW, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(q, kbar, nullptr, lse, lse_contig);
       }));
+    } else {
+      ok(timed(1, st, [&] {
+        k_lse<T, D, kLseRW, kLseNW, false, false><<<lse_col_grid, kLseNW * kWave, 0, st>>>(q, ktil, hent, lse, lse_col,
+                                                                                            sa, it);
+      }));
+    }
+    if (ad) {
+      ok(timed(11, st, [&] {
+        k_objective<<<static_cast<unsigned>(s.BH), 256, 0, st>>>(lse, Nq, s.b2, ad->fprev, ad->stop_at, it, s.T,
+                                                                  ad->tol);
+      }));
+    }
+    if (first) {
       ok(timed(2, st, [&] {
         if (col_fits)
           k_aggregate_col<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
@@ -311,17 +337,20 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
           k_aggregate<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
       }));
     } else {
-      ok(timed(1, st, [&] {
-        k_lse<T, D, kLseRW, kLseNW, false, false><<<lse_col_grid, kLseNW * kWave, 0, st>>>(q, ktil, hent, lse, lse_col);
-      }));
       ok(timed(2, st, [&] {
         if (col_fits)
-          k_aggregate_col<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg);
+          k_aggregate_col<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg,
+                                                                                          sa, it);
         else
-          k_aggregate<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg);
+          k_aggregate<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg,
+                                                                                      sa, it);
       }));
     }
-    if (last) {
+    if (ad) {
+      ok(timed(3, st, [&] {
+        k_rstep_adaptive<T, D><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, ktil, hent, ad->stop_at, it, rg);
+      }));
+    } else if (last) {
       ok(timed(3, st, [&] {
         k_rstep<T, D, true><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, nullptr, nullptr, uout, rg);
       }));
@@ -414,6 +443,56 @@ int fwd_alloc(const void* q, const void* k, const void* v, void* out, const Shap
     rc = MONARCH_EHIP;
   }
   return rc;
+}
+
+// --------------------------------------------------- iterate to converge --
+// Workspace of the early-stopping call: the forward's for max_iters
+// iterations over all heads at once, then the previous objective per head.
+size_t adaptive_bytes(const Shape& s, size_t elem, size_t* fprev_off) {
+  const Workspace w = layout(s, elem, true);
+  if (fprev_off) *fprev_off = w.total;
+  return w.total + align_up(static_cast<size_t>(s.BH) * sizeof(double));
+}
+
+int fwd_adaptive(const void* q, const void* k, const void* v, void* out, const Shape& s, int dtype,
+                 float tol, int* iters_used, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  const size_t elem = elem_size(dtype);
+  if (elem == 0) return MONARCH_EINVAL;
+  int rc = check_args(q, k, v, out, s, elem);
+  if (rc != MONARCH_OK) return rc;
+  if (!iters_used || std::isnan(tol)) return MONARCH_EINVAL;
+  size_t fprev_off = 0;
+  const size_t need = adaptive_bytes(s, elem, &fprev_off);
+  if (!workspace || workspace_bytes < need) return MONARCH_ENOMEM;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return MONARCH_EINVAL;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const Workspace w = layout(s, elem, true);
+  Adaptive ad{iters_used, reinterpret_cast<double*>(ws + fprev_off), tol};
+  hipError_t e = hipSuccess;
+  k_fill_int<<<static_cast<unsigned>((s.BH + 255) / 256), 256, 0, st>>>(iters_used, static_cast<int>(s.BH), 0);
+  e = hipGetLastError();
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    const Bufs<T> b = bufs_of<T>(s, ws, w);
+    const T* tq = static_cast<const T*>(q);
+    const T* tk = static_cast<const T*>(k);
+    const T* tv = static_cast<const T*>(v);
+    T* to = static_cast<T*>(out);
+    switch (s.d) {
+      case 16: e = run_pass<T, 16>(tq, tk, tv, to, s, b, st, &ad); break;
+      case 32: e = run_pass<T, 32>(tq, tk, tv, to, s, b, st, &ad); break;
+      case 64: e = run_pass<T, 64>(tq, tk, tv, to, s, b, st, &ad); break;
+      default: e = run_pass<T, 128>(tq, tk, tv, to, s, b, st, &ad); break;
+    }
+  };
+  if (e == hipSuccess) {
+    if (dtype == MONARCH_BF16) go(bf16_t{}); else go(float{});
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return MONARCH_EHIP;
+  }
+  return MONARCH_OK;
 }
 
 // ------------------------------------------------------------ training --
@@ -767,6 +846,25 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, 
   const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   return fwd_ws(q, k, v, out, s, dtype, workspace, workspace_bytes,
                 static_cast<hipStream_t>(stream));
+}
+
+size_t monarch_attn_adaptive_workspace_bytes(int B, int H, int f, int h, int w, int d, int b1, int b2,
+                                             int tiles, int max_iters, int dtype) {
+  const size_t elem = elem_size(dtype);
+  if (elem == 0) return 0;
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, max_iters);
+  static const char dummy[4] = {0};
+  if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
+  return adaptive_bytes(s, elem, nullptr);
+}
+
+int monarch_attn_fwd_adaptive_ws(const void* q, const void* k, const void* v, void* out, int B, int H,
+                                 int f, int h, int w, int d, int b1, int b2, int tiles, int max_iters,
+                                 float tol, int dtype, int* iters_used, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, max_iters);
+  return fwd_adaptive(q, k, v, out, s, dtype, tol, iters_used, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream));
 }
 
 size_t monarch_attn_kv_workspace_bytes(int B, int H, int fq, int f, int h, int w, int d, int b1, int b2,

@@ -39,11 +39,11 @@ inline size_t rside_lds_bytes(int D, int b2p, bool last) {
 #endif
 
 template <typename T, int D, bool LAST>
-__global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T* __restrict__ v,
-                                               T* qhat,   // [BH][t][b1][b2][D]; U written over it when LAST
-                                               T* __restrict__ ktil, float* __restrict__ hent,
-                                               T* uout,   // U goes here instead when not NULL
-                                               RGeom p) {
+__device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __restrict__ v,
+                                           T* qhat,   // [BH][t][b1][b2][D]; U written over it when LAST
+                                           T* __restrict__ ktil, float* __restrict__ hent,
+                                           T* uout,   // U goes here instead when not NULL
+                                           const RGeom& p) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -206,6 +206,31 @@ __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T*
     }
   }
   }
+}
+
+template <typename T, int D, bool LAST>
+__global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T* __restrict__ v, T* qhat,
+                                               T* __restrict__ ktil, float* __restrict__ hent, T* uout,
+                                               RGeom p) {
+  rstep_body<T, D, LAST>(k, v, qhat, ktil, hent, uout, p);
+}
+
+// Iteration `it` of a run that stops each head on its own: stop_at[bh] is the
+// iteration after which head bh stops (0 = not decided).  Heads that stopped
+// earlier are skipped; a head that stops now gets R V (the last R-step), the
+// others the next L-step's keys and entropies.  Dynamic LDS as for the last
+// R-step.
+template <typename T, int D>
+__global__ __launch_bounds__(512) void k_rstep_adaptive(const T* __restrict__ k, const T* __restrict__ v,
+                                                        T* qhat, T* __restrict__ ktil, float* __restrict__ hent,
+                                                        const int* __restrict__ stop_at, int it, RGeom p) {
+  const int bh = xcd_remap(blockIdx.x, gridDim.x) / p.b1;
+  const int sa = stop_at[bh];
+  if (sa != 0 && sa < it) return;
+  if (sa == it)
+    rstep_body<T, D, true>(k, v, qhat, nullptr, nullptr, nullptr, p);
+  else
+    rstep_body<T, D, false>(k, v, qhat, ktil, hent, nullptr, p);
 }
 
 }  // namespace monarch

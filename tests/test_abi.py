@@ -177,3 +177,19 @@ def test_kv_workspace_bytes():
     # fq == f is the square layer
     assert (M.monarch_attn_kv_workspace_bytes(B, H, f, f, h, w, d, b1, b2, 4, 1, 0)
             == M.monarch_attn_workspace_bytes(B, H, f, h, w, d, b1, b2, 4, 1, 0))
+
+
+def test_adaptive_workspace_and_bad_arguments():
+    shape = (1, 40, 21, 45, 80, 128, 945, 80, 4, 10, 0)
+    nb = M.monarch_attn_adaptive_workspace_bytes(*shape)
+    assert nb == M.monarch_attn_workspace_bytes(*shape) + _align(40 * 8)
+    p = _train_ptrs(6)  # q k v out iters_used workspace
+    base = (1, 2, 3, 30, 52, 128, 90, 52, 1, 10)
+    lib = M.lib()
+    need = M.monarch_attn_adaptive_workspace_bytes(*base, 0)
+    rc = lib.monarch_attn_fwd_adaptive_ws(*p[:4], *base, float("nan"), 0, p[4], p[5], need, None)
+    assert rc == M.MONARCH_EINVAL
+    rc = lib.monarch_attn_fwd_adaptive_ws(*p[:4], *base, 1e-3, 0, None, p[5], need, None)
+    assert rc == M.MONARCH_EINVAL
+    rc = lib.monarch_attn_fwd_adaptive_ws(*p[:4], *base, 1e-3, 0, p[4], p[5], need - 256, None)
+    assert rc == M.MONARCH_ENOMEM

@@ -1,0 +1,116 @@
+"""Iterating until the objective stops improving, on the GPU, against the CPU
+oracle (needs an MI355X).
+
+Each head stops on its own after the first iteration i >= 2 whose objective
+gain per token is <= tol (or at max_iters).  On these inputs the gains fall by
+about three orders of magnitude per iteration (6e-2, 6e-5, 3e-7 nats per
+token), so the tolerances below sit far from any gain and the GPU, which sums
+fp32 log-sum-exps of bf16 logits, must take the same decision as the float64
+oracle; the outputs are then compared with the usual bars.  Calls that never
+stop early, stop at the first chance, or run one iteration must equal the
+fixed-iteration forward bit for bit (same kernels).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, errors, say, to_device, to_host
+from structured_attention_video_monarch_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_adaptive(wl, x, max_iters, tol):
+    import structured_attention_video_monarch_amd as M
+    q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
+    out = torch.empty_like(q)
+    _, used = M.monarch_attn_fwd_adaptive(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, max_iters, tol)
+    torch.cuda.synchronize()
+    return out, used.cpu().numpy()
+
+
+def check_against_oracle(wl, x, y, used, max_iters, tol, heads):
+    worst = (0.0, 0.0)
+    for b in range(wl.B):
+        for h in heads:
+            ref, used_o, F = oracle.monarch_head_adaptive(x["q"][b, h], x["k"][b, h], x["v"][b, h], wl.b1, wl.b2,
+                                                          wl.tiles, max_iters, tol)
+            assert int(used[b, h]) == used_o, (b, h, int(used[b, h]), used_o, np.diff(F) / wl.N)
+            mx, mean = errors(to_host(y)[b, h], ref)
+            worst = (max(worst[0], mx), max(worst[1], mean))
+            if wl.dtype == "bf16":
+                assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (b, h, mx, mean)
+            else:
+                assert mx <= F32_MAX_ABS, (b, h, mx)
+    return worst
+
+
+@pytest.mark.parametrize("tol,expect", [(1e-3, 3), (1e-1, 2)])
+def test_adaptive_chunk480p(tol, expect):
+    wl = I.get_workload("chunk480p")
+    say(f"[case] adaptive chunk480p max_iters=10 tol={tol}")
+    x = I.make_inputs(wl, 0)
+    y, used = run_adaptive(wl, x, 10, tol)
+    assert np.all(used == expect), used
+    worst = check_against_oracle(wl, x, y, used, 10, tol, heads=[0, 6, 11])
+    say(f"[ok] adaptive chunk480p tol={tol}: iterations {expect}, max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e}")
+
+
+def test_adaptive_heads_stop_independently():
+    """Head 0 has zero queries (uniform attention: no gain, stops at 2), head 1
+    ordinary inputs (stops at 3 for tol 1e-3)."""
+    wl = I.get_workload("clip480p_spikes_t4_T1").with_(H=2)
+    say("[case] adaptive per-head stops, clip480p t=4")
+    x = I.make_inputs(wl, 1)
+    x["q_bits"][0, 0] = 0
+    x["q"][0, 0] = 0.0
+    y, used = run_adaptive(wl, x, 10, 1e-3)
+    assert used.tolist() == [[2, 3]], used
+    worst = check_against_oracle(wl, x, y, used, 10, 1e-3, heads=[0, 1])
+    say(f"[ok] adaptive per-head: {used.tolist()}, max-abs {worst[0]:.3e}")
+
+
+@pytest.mark.parametrize("max_iters,tol,fixed", [(4, -1.0, 4), (6, 1e30, 2), (1, -1.0, 1), (3, 1e-3, 3)])
+def test_adaptive_equals_fixed_iterations(max_iters, tol, fixed):
+    import structured_attention_video_monarch_amd as M
+    wl = I.get_workload("clip480p").with_(H=3)
+    say(f"[case] adaptive == fixed: max_iters={max_iters} tol={tol} -> {fixed}")
+    x = I.make_inputs(wl, 2)
+    y, used = run_adaptive(wl, x, max_iters, tol)
+    assert np.all(used == fixed), used
+    q, k, v = (to_device(x, n, "bf16") for n in "qkv")
+    ref = torch.empty_like(q)
+    M.monarch_attn_fwd(q, k, v, ref, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, fixed)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+
+
+def test_ten_iterations_latent720p_head():
+    """The training-free regime: ten iterations at the 720p shape (tol -1:
+    no early stop), head 0 against the oracle."""
+    wl = I.get_workload("latent720p").with_(H=2)
+    say("[case] 10 iterations latent720p (2 heads)")
+    x = I.make_inputs(wl, 0)
+    y, used = run_adaptive(wl, x, 10, -1.0)
+    assert np.all(used == 10)
+    ref = oracle.monarch_head(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], wl.b1, wl.b2, wl.tiles, 10)
+    mx, mean = errors(to_host(y)[0, 0], ref)
+    say(f"[ok] 10 iterations latent720p: max-abs {mx:.3e} mean-abs {mean:.3e}")
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS
+
+
+def test_adaptive_f32_small():
+    wl = I.Workload("adaptive_f32", 1, 2, 64, 3, 11, 9, 33, 9, 5, 1, "f32")
+    say("[case] adaptive f32 small")
+    x = I.make_inputs(wl, 3)
+    y, used = run_adaptive(wl, x, 8, 1e-4)
+    worst = check_against_oracle(wl, x, y, used, 8, 1e-4, heads=[0, 1])
+    say(f"[ok] adaptive f32: {used.tolist()} max-abs {worst[0]:.3e}")
