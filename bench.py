@@ -83,6 +83,8 @@ def algorithmic_work(wl, it_last=True):
         "kb_dkbar": (BH * 2.0 * N * b1 * d, BH * nd),
         "kb_dkbar_reduce": (0.0, BH * b1 * d * 4.0),
         "kb_rside_b": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 4 * nd + 8 * t * N)),
+        # early stopping: the objective per head reads the log-sum-exps once
+        "k_objective": (0.0, BH * 4.0 * Nq),
     }
 
 
@@ -175,6 +177,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--mode", choices=["fwd", "train"], default="fwd",
                     help="fwd: forward layer call; train: one-iteration training forward + backward")
+    ap.add_argument("--iters", type=int, default=0,
+                    help="override the workload's iteration count (0: keep it)")
+    ap.add_argument("--tol", type=float, default=None,
+                    help="iterate until the objective gain per token is <= tol (at most --iters or the "
+                         "workload's count; each head stops on its own)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (float32 read + write), "
                          "to scale HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
@@ -200,6 +207,8 @@ def main():
     from structured_attention_video_monarch_amd import inputs as I
 
     wl = I.get_workload(args.workload)
+    if args.iters:
+        wl = wl.with_(iters=args.iters)
     if args.mode == "train":
         wl = wl.with_(iters=1)
     dev = torch.device("cuda:0")
@@ -222,6 +231,21 @@ def main():
     def step():
         M.monarch_attn_fwd_ws(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters,
                               ws, stream)
+
+    iters_used = None
+    if args.tol is not None:
+        if wl.kv or args.mode == "train":
+            print("bench.py: --tol applies to the square forward only", file=sys.stderr)
+            sys.exit(2)
+        del ws
+        nb = M.monarch_attn_adaptive_workspace_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2,
+                                                     wl.tiles, wl.iters, dtc)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        iters_used = torch.empty((wl.B, wl.H), dtype=torch.int32, device=dev)
+
+        def step():
+            M.monarch_attn_fwd_adaptive(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters,
+                                        args.tol, iters_used=iters_used, workspace=ws, stream=stream)
 
     if wl.kv:
         if args.mode == "train":
@@ -281,6 +305,9 @@ def main():
     roof = roofline_entry(dom, fl, by, kernels[dom]["avg_ms"] / 1e3, wl.dtype,
                           read_traffic(dom, wl.name))
     roof["launches_per_step"] = launches
+    if iters_used is not None:
+        roof["note"] = ("early stopping: launches after every head has stopped return at once and are "
+                        "counted in the per-launch average")
     for kname, rec in kernels.items():
         f2, b2 = work[kname]
         r = roofline_entry(kname, f2, b2, rec["avg_ms"] / 1e3, wl.dtype, None)
@@ -304,6 +331,10 @@ def main():
                    "N": wl.N, "Nq": wl.Nq, "fq": wl.fq or wl.f, "d": wl.d, "b1": wl.b1, "b2": wl.b2,
                    "tiles": wl.tiles,
                    "iters": wl.iters, "spike_frac": wl.spike_frac, "mode": args.mode},
+        "early_stop": (None if iters_used is None else
+                       {"tol": args.tol, "max_iters": wl.iters,
+                        "iters_used_mean": round(float(iters_used.float().mean().item()), 3),
+                        "iters_used_max": int(iters_used.max().item())}),
         "layer_calls_per_s": round(1e3 / ms_step, 2),
         "path_alg_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
         "path_frac_of_mfma_peak": round(total_flops / (ms_step / 1e3) / 1e12 /
