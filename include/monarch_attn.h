@@ -153,7 +153,7 @@ int monarch_attn_fwd_kv_ws(const void* q, const void* k, const void* v, void* ou
  * overlapping q, k, v or out) what the backward pass reads: the block-mean
  * keys, the L-row log-sum-exps, the column masses beta, the aggregated
  * queries Qh and U = R V of every tile.  Its size is
- *   B*H*(b1*d*e + 4*N + 4*t*N + 2*t*N*d*e)  (+ alignment), e = element bytes.
+ *   B*H*(b1*d*e + 4*b1 + 4*N + 4*t*N + 2*t*N*d*e)  (+ alignment), e = element bytes.
  *
  * monarch_attn_bwd takes the same q, k, v, the out and state of a
  * monarch_attn_fwd_train call with the same arguments, and dout = dLoss/dout,

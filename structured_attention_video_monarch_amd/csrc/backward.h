@@ -364,11 +364,16 @@ __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const
 // ------------------------------------------------------------- kb_rside_b --
 // Key-block pass, part 2: one workgroup per (bh, c1), each wave owning 16
 // keys c2 (K and V rows as B operands); Qh and dU stream through LDS in
-// blocks of 32 rows a2, tile after tile, double-buffered by DMA.  R and dz
+// blocks of 32 rows a2, tile after tile, BPS blocks per double-buffered DMA
+// stage.  R and dz
 // are recomputed from the stored row statistics with a2 as the contraction
 // index, and
 //   dv[c1,c2] = sum_(g,a2) R dU,
 //   dk[c1,c2] = s sum_(g,a2) dz Qh + dKbar[c1] / b2   (dKbar already reduced).
+#ifndef MONARCH_BRB_BPS
+#define MONARCH_BRB_BPS 2
+#endif
+
 template <typename T, int D>
 __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ qhat, const T* __restrict__ du,
@@ -380,10 +385,12 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
   constexpr int KS = DK / 32;
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
-  __shared__ __align__(16) T sQ[2][32 * DK];
-  __shared__ __align__(16) T sU[2][32 * DK];
-  __shared__ __align__(16) float sLR[2][64];
-  __shared__ __align__(16) float sRh[2][64];
+  // 32-row blocks per pipeline stage (f32 tiles are twice as large: one)
+  constexpr int BPS = sizeof(T) == 2 ? MONARCH_BRB_BPS : 1;
+  __shared__ __align__(16) T sQ[2][BPS][32 * DK];
+  __shared__ __align__(16) T sU[2][BPS][32 * DK];
+  __shared__ __align__(16) float sLR[2][BPS][64];
+  __shared__ __align__(16) float sRh[2][BPS][64];
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
   const int c1 = item % p.b1;
@@ -395,16 +402,22 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
   const int c2 = wave * 16 + l16;
   const int c2c = c2 < p.b2 ? c2 : p.b2 - 1;
   const int ncp = p.b2p / 32;
-  const int nst = p.t * ncp;
+  const int nblk = p.t * ncp;                 // (tile, 32-row block) pairs, in order
+  const int nst = (nblk + BPS - 1) / BPS;
 
   auto fetch = [&](int st, int buf) {
-    const int g = st / ncp, a0 = 32 * (st % ncp);
-    const long long rb = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a0;
-    const int nvalid = p.b2 - a0;
-    dma_block<T, D, DK>(sQ[buf], qhat + rb * D, 32, nvalid, nw);
-    dma_block<T, D, DK>(sU[buf], du + rb * D, 32, nvalid, nw);
-    if (wave == 0) dma_floats64(sLR[buf], lser + rb, 1, nvalid);
-    if (wave == nw - 1) dma_floats64(sRh[buf], rho + rb, 1, nvalid);
+#pragma unroll
+    for (int j = 0; j < BPS; ++j) {
+      const int b = st * BPS + j;
+      if (b >= nblk) break;
+      const int g = b / ncp, a0 = 32 * (b % ncp);
+      const long long rb = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a0;
+      const int nvalid = p.b2 - a0;
+      dma_block<T, D, DK>(sQ[buf][j], qhat + rb * D, 32, nvalid, nw);
+      dma_block<T, D, DK>(sU[buf][j], du + rb * D, 32, nvalid, nw);
+      if (wave == 0) dma_floats64(sLR[buf][j], lser + rb, 1, nvalid);
+      if (wave == nw - 1) dma_floats64(sRh[buf][j], rho + rb, 1, nvalid);
+    }
   };
   fetch(0, 0);
 
@@ -425,27 +438,34 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
   for (int st = 0; st < nst; ++st) {
     const int cur = st & 1;
     if (st + 1 < nst) fetch(st + 1, cur ^ 1);
-    const int a0 = 32 * (st % ncp);
-    typename E::frag a[KS][2];
-    f32x4 Z[2][1], DR[2][1];
-    load_rows<T, DK, KS>(a, sQ[cur], 0, l16, G);
-    logits<T, KS, 1>(Z, a, bk2);
-    load_rows<T, DK, KS>(a, sU[cur], 0, l16, G);
-    logits<T, KS, 1>(DR, a, bv2);
-    float r[8], z[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = a0 + 8 * G + j < p.b2;  // rows past b2 repeat the last row: weight 0
-      const float rr = fast_exp2(Z[j >> 2][0][j & 3] * p.c - sLR[cur][8 * G + j]);
-      r[j] = ok ? rr : 0.0f;
-      z[j] = ok ? rr * (DR[j >> 2][0][j & 3] - sRh[cur][8 * G + j]) : 0.0f;
+    for (int j = 0; j < BPS; ++j) {
+      const int b = st * BPS + j;
+      if (b >= nblk) break;
+      const int a0 = 32 * (b % ncp);
+      const T* tq = sQ[cur][j];
+      const T* tu = sU[cur][j];
+      typename E::frag a[KS][2];
+      f32x4 Z[2][1], DR[2][1];
+      load_rows<T, DK, KS>(a, tq, 0, l16, G);
+      logits<T, KS, 1>(Z, a, bk2);
+      load_rows<T, DK, KS>(a, tu, 0, l16, G);
+      logits<T, KS, 1>(DR, a, bv2);
+      float r[8], z[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const bool ok = a0 + 8 * G + jj < p.b2;  // rows past b2 repeat the last row: weight 0
+        const float rr = fast_exp2(Z[jj >> 2][0][jj & 3] * p.c - sLR[cur][j][8 * G + jj]);
+        r[jj] = ok ? rr : 0.0f;
+        z[jj] = ok ? rr * (DR[jj >> 2][0][jj & 3] - sRh[cur][j][8 * G + jj]) : 0.0f;
+      }
+      const typename E::frag rf[1] = {E::pack(r)}, zf[1] = {E::pack(z)};
+      typename E::frag vv[NACC][2];
+      load_cols<T, D, DK, NACC>(vv, tu, 0);
+      weighted_sum<T, D, NACC, 1>(accv, vv, rf);
+      load_cols<T, D, DK, NACC>(vv, tq, 0);
+      weighted_sum<T, D, NACC, 1>(acck, vv, zf);
     }
-    const typename E::frag rf[1] = {E::pack(r)}, zf[1] = {E::pack(z)};
-    typename E::frag vv[NACC][2];
-    load_cols<T, D, DK, NACC>(vv, sU[cur], 0);
-    weighted_sum<T, D, NACC, 1>(accv, vv, rf);
-    load_cols<T, D, DK, NACC>(vv, sQ[cur], 0);
-    weighted_sum<T, D, NACC, 1>(acck, vv, zf);
     __syncthreads();
   }
 

@@ -18,6 +18,8 @@
 // previous R-step ([BH][t][b1][b2][d] with entropies h2 [BH][t][b1][b2]).
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace monarch {
@@ -179,13 +181,23 @@ __device__ inline void weighted_sum(f32x4 (&acc)[NACC][2][RW], const typename El
 // ------------------------------------------------------------------ k_lse --
 // CONTIG: rows are consecutive tokens of a head (only with BCAST keys, where
 // the logits do not depend on the column or tile).
+//
+// With BCAST keys (the first L-step) the log-sum-exp is taken against a fixed
+// offset per row instead of a running maximum: m_n = c |q_n| max_c1 |Kbar_c1|
+// bounds every logit of row n (Cauchy-Schwarz; knorm holds |Kbar_c1| of the
+// rounded keys), so no term exceeds 1 and lse = m_n + log2(sum 2^(x - m_n)).
+// That saves the maximum, the rescaling and their dependency chain.  If the
+// bound is so loose that a row's sum falls below 2^-60 (very large norms
+// with nearly orthogonal q and keys), the workgroup recomputes with the
+// running maximum.
 template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG>
 __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
                                                                       const T* __restrict__ kt,
                                                                       const float* __restrict__ h2,
                                                                       float* __restrict__ lse, LGeom p,
                                                                       const int* __restrict__ stop_at = nullptr,
-                                                                      int it = 0) {
+                                                                      int it = 0,
+                                                                      const float* __restrict__ knorm = nullptr) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -193,6 +205,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
   using Dma = TileDma<T, D, DK, kStep, NW>;
   __shared__ __align__(16) T sK[2][kStep * DK];
   __shared__ __align__(16) float sH[2][kStep];
+  __shared__ float sRed[NW];
 
   int bh, g = 0, a2 = 0, nrows;
   long long n0, nstride;
@@ -236,6 +249,88 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
       bq[rt][s] = (r < nrows && col < D) ? E::load(qh + (n0 + r * nstride) * D + col) : E::zero();
     }
   }
+
+  if constexpr (BCAST && CONTIG) {
+    if (knorm) {
+      // max_c1 |Kbar_c1| over the head
+      float km = 0.0f;
+      for (int i = threadIdx.x; i < p.b1; i += NW * kWave) km = fmaxf(km, knorm[static_cast<long long>(bh) * p.b1 + i]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) km = fmaxf(km, __shfl_xor(km, off));
+      if (lane == 0) sRed[wave] = km;
+      __syncthreads();
+      km = sRed[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) km = fmaxf(km, sRed[w]);
+      float mrow[RW], ls[RW];
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        float sq = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = E::slot(bq[rt][s], j);
+            sq = __builtin_fmaf(x, x, sq);
+          }
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        // a little above the bound: the MFMA sums in fp32
+        mrow[rt] = p.c * sqrtf(sq) * km * 1.00390625f + 0.00390625f;
+        ls[rt] = 0.0f;
+      }
+      // one 32-key block: masked only where keys run past b1
+      auto block = [&](const T* tile, int k0, int c1_0, auto masked) {
+        typename E::frag a[KS][2];
+        load_rows<T, DK, KS>(a, tile, k0, l16, G);
+        f32x4 S[2][RW];
+        logits<T, KS, RW>(S, a, bq);
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float w = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, -mrow[rt]));
+            if constexpr (decltype(masked)::value)
+              ls[rt] += c1_0 + 8 * G + j < p.b1 ? w : 0.0f;
+            else
+              ls[rt] += w;
+          }
+      };
+      for (int st = 0; st < nst; ++st) {
+        const int cur = st & 1;
+        if (st + 1 < nst) fetch(st + 1, cur ^ 1);
+#pragma unroll
+        for (int half = 0; half < kHalves; ++half) {
+          const int k0 = 32 * half;
+          const int c1_0 = st * kStep + k0;
+          if (c1_0 >= p.b1) break;
+          if (c1_0 + 32 > p.b1)
+            block(sK[cur], k0, c1_0, std::true_type{});
+          else
+            block(sK[cur], k0, c1_0, std::false_type{});
+        }
+        __syncthreads();
+      }
+      bool loose = false;
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        ls[rt] += __shfl_xor(ls[rt], 16);
+        ls[rt] += __shfl_xor(ls[rt], 32);
+        const int r = (wave * RW + rt) * 16 + l16;
+        if (r < nrows && !(ls[rt] >= 8.673617379884035e-19f)) loose = true;  // 2^-60 (or NaN)
+      }
+      if (!__syncthreads_or(loose)) {
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) {
+          const int r = (wave * RW + rt) * 16 + l16;
+          if (G == 0 && r < nrows) lse[static_cast<long long>(bh) * p.N + n0 + r * nstride] = mrow[rt] + log2f(ls[rt]);
+        }
+        return;
+      }
+      fetch(0, 0);  // the buffers are free: start over with the running maximum
+    }
+  }
+
   float m[RW], l[RW];
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) { m[rt] = -1e30f; l[rt] = 0.0f; }
@@ -681,7 +776,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
 // entropy term log(b2) is the same for every c1, so it cancels in the softmax).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_kbar(const T* __restrict__ k, T* __restrict__ kbar,
-                                              int BH, int b1, int b2) {
+                                              float* __restrict__ knorm, int BH, int b1, int b2) {
   using E = Elem<T>;
   constexpr int V = E::kVec;
   constexpr int LPR = D / V;        // lanes per row
@@ -704,11 +799,24 @@ __global__ __launch_bounds__(256) void k_kbar(const T* __restrict__ k, T* __rest
   for (int off = LPR; off < kWave; off <<= 1)
 #pragma unroll
     for (int j = 0; j < V; ++j) acc[j] += __shfl_xor(acc[j], off);
+  // every lane now holds the sums of its columns; round the means as they
+  // are stored and take |Kbar| of the rounded row (the bound k_lse uses)
+  const float inv = 1.0f / static_cast<float>(b2);
+  T mean[V];
+  float sq = 0.0f;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    mean[j] = E::from_f32(acc[j] * inv);
+    const float x = E::to_f32(mean[j]);
+    sq = __builtin_fmaf(x, x, sq);
+  }
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) sq += __shfl_xor(sq, off);
   if (ro == 0) {
-    const float inv = 1.0f / static_cast<float>(b2);
     T* dst = kbar + item * D + col;
 #pragma unroll
-    for (int j = 0; j < V; ++j) dst[j] = E::from_f32(acc[j] * inv);
+    for (int j = 0; j < V; ++j) dst[j] = mean[j];
+    if (knorm && lane == 0) knorm[item] = sqrtf(sq);
   }
 }
 

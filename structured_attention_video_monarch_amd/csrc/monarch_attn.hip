@@ -140,7 +140,7 @@ long long heads_per_pass(const Shape& s, size_t elem) {
 
 struct Workspace {
   long long hc;  // heads per pass
-  size_t kbar, lse, qhat, ktil, hent, total;
+  size_t kbar, knorm, lse, qhat, ktil, hent, total;
 };
 
 Workspace layout(const Shape& s, size_t elem, bool all_heads = false) {
@@ -150,6 +150,8 @@ Workspace layout(const Shape& s, size_t elem, bool all_heads = false) {
   size_t off = 0;
   w.kbar = off;
   off += align_up(hc * s.b1 * s.d * elem);
+  w.knorm = off;
+  off += align_up(hc * s.b1 * sizeof(float));
   w.lse = off;
   off += align_up(hc * s.Nq * sizeof(float));
   w.qhat = off;
@@ -222,6 +224,7 @@ hipError_t timed(int id, hipStream_t st, F&& launch) {
 template <typename T>
 struct Bufs {
   T* kbar;
+  float* knorm;  // |Kbar| per key block (offsets of the first L-step's log-sum-exp)
   float* lse;
   T* qhat;
   T* ktil;
@@ -234,6 +237,7 @@ template <typename T>
 Bufs<T> bufs_of(const Shape& s, unsigned char* ws, const Workspace& w) {
   Bufs<T> b{};
   b.kbar = reinterpret_cast<T*>(ws + w.kbar);
+  b.knorm = reinterpret_cast<float*>(ws + w.knorm);
   b.lse = reinterpret_cast<float*>(ws + w.lse);
   b.qhat = reinterpret_cast<T*>(ws + w.qhat);
   b.ktil = s.T > 1 ? reinterpret_cast<T*>(ws + w.ktil) : nullptr;
@@ -273,7 +277,7 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
   {
     const long long items = s.BH * s.b1;
     const unsigned grid = static_cast<unsigned>((items + 3) / 4);
-    ok(timed(0, st, [&] { k_kbar<T, D><<<grid, 256, 0, st>>>(k, kbar, BH, s.b1, s.b2); }));
+    ok(timed(0, st, [&] { k_kbar<T, D><<<grid, 256, 0, st>>>(k, kbar, bf.knorm, BH, s.b1, s.b2); }));
   }
 
   constexpr int lse_rows = kLseRW * kLseNW * 16, agg_rows = kAggRW * kAggNW * 16,
@@ -315,7 +319,8 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     const bool first = it == 1, last = it == s.T;
     if (first) {
       ok(timed(1, st, [&] {
-        k_lse<T, D, kLseRW, kLseNW, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(q, kbar, nullptr, lse, lse_contig);
+        k_lse<T, D, kLseRW, kLseNW, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(q, kbar, nullptr, lse, lse_contig,
+                                                                                          nullptr, 0, bf.knorm);
       }));
     } else {
       ok(timed(1, st, [&] {
@@ -499,7 +504,7 @@ int fwd_adaptive(const void* q, const void* k, const void* v, void* out, const S
 // Training state: what the backward pass reads from the one-iteration
 // forward, for all heads of the call.
 struct TrainState {
-  size_t kbar, lse, beta, qhat, u, total;
+  size_t kbar, knorm, lse, beta, qhat, u, total;
 };
 
 TrainState train_layout(const Shape& s, size_t elem) {
@@ -509,6 +514,8 @@ TrainState train_layout(const Shape& s, size_t elem) {
   size_t off = 0;
   t.kbar = off;
   off += align_up(BH * s.b1 * d * elem);
+  t.knorm = off;
+  off += align_up(BH * s.b1 * sizeof(float));
   t.lse = off;
   off += align_up(BH * N * sizeof(float));
   t.beta = off;
@@ -525,6 +532,7 @@ template <typename T>
 Bufs<T> train_bufs(unsigned char* st, const TrainState& t) {
   Bufs<T> b{};
   b.kbar = reinterpret_cast<T*>(st + t.kbar);
+  b.knorm = reinterpret_cast<float*>(st + t.knorm);
   b.lse = reinterpret_cast<float*>(st + t.lse);
   b.qhat = reinterpret_cast<T*>(st + t.qhat);
   b.ktil = nullptr;

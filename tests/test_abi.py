@@ -82,7 +82,7 @@ def test_workspace_bytes(shape):
     B, H, f, h, w, d, b1, b2, t, T, dt = shape
     e = 2 if dt == 0 else 4
     N, BH = f * h * w, B * H
-    expect = _align(BH * b1 * d * e) + _align(BH * N * 4) + _align(BH * t * N * d * e)
+    expect = _align(BH * b1 * d * e) + _align(BH * b1 * 4) + _align(BH * N * 4) + _align(BH * t * N * d * e)
     if T > 1:
         expect += _align(BH * t * N * d * e) + _align(BH * t * N * 4)
     assert M.monarch_attn_workspace_bytes(*shape) == expect
@@ -116,7 +116,7 @@ def _bwd(state_bytes=None, B=1, H=2, f=3, h=30, w=52, d=128, b1=90, b2=52, t=1, 
 def test_train_state_bytes_formula():
     B, H, f, h, w, d, b1, b2, t = 1, 40, 21, 45, 80, 128, 945, 80, 4
     N, BH, e = f * h * w, B * H, 2
-    expect = (_align(BH * b1 * d * e) + _align(BH * N * 4) + _align(BH * t * N * 4)
+    expect = (_align(BH * b1 * d * e) + _align(BH * b1 * 4) + _align(BH * N * 4) + _align(BH * t * N * 4)
               + 2 * _align(BH * t * N * d * e))
     assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, 0) == expect
     assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1 + 1, b2, t, 0) == 0
@@ -171,7 +171,7 @@ def test_kv_bad_arguments_rejected_before_any_gpu_call(kw, status):
 def test_kv_workspace_bytes():
     B, H, fq, f, h, w, d, b1, b2, t, T = 1, 40, 3, 21, 45, 80, 128, 945, 80, 1, 2
     N, Nq, BH, e = f * h * w, fq * h * w, B * H, 2
-    expect = (_align(BH * b1 * d * e) + _align(BH * Nq * 4) + _align(BH * t * N * d * e)
+    expect = (_align(BH * b1 * d * e) + _align(BH * b1 * 4) + _align(BH * Nq * 4) + _align(BH * t * N * d * e)
               + _align(BH * t * N * d * e) + _align(BH * t * N * 4))
     assert M.monarch_attn_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, t, T, 0) == expect
     # fq == f is the square layer

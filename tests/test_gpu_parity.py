@@ -154,3 +154,32 @@ def test_errors_launch_nothing():
     assert e.value.status == M.MONARCH_ENOMEM
     torch.cuda.synchronize()
     assert bool((out.float() == 7.0).all())
+
+
+def test_loose_logit_bound_falls_back_to_running_max():
+    """One key block with a large mean (100 along one channel) makes the first
+    L-step's per-row bound c|q| max|Kbar| lie more than 60 bits above most
+    rows' largest logit, so those workgroups take the running-maximum path;
+    the logits themselves stay moderate and the result must match the oracle."""
+    import math
+    wl = I.get_workload("chunk480p").with_(H=2)
+    x = I.make_inputs(wl, 7)
+    blk = slice(7 * wl.b2, 8 * wl.b2)
+    for h in range(wl.H):
+        kk = np.zeros((wl.b2, wl.d), dtype=np.float32)
+        kk[:, 0] = 100.0
+        x["k_bits"][0, h, blk] = I.round_to_bf16_bits(kk)
+        x["k"][0, h, blk] = kk
+    # the bound must be loose (gap > 60 bits) on most rows for the test to mean anything
+    c = math.log2(math.e) / math.sqrt(wl.d)
+    q0, k0 = x["q"][0, 0].astype(np.float64), x["k"][0, 0].astype(np.float64)
+    kbar = k0.reshape(wl.b1, wl.b2, wl.d).mean(axis=1)
+    bound = c * np.linalg.norm(q0, axis=1) * np.linalg.norm(kbar, axis=1).max()
+    top = c * (q0 @ kbar.T).max(axis=1)
+    assert np.mean(bound - top > 60.0) > 0.5
+    y = run_gpu(wl, x)
+    for h in range(wl.H):
+        ref = oracle.monarch_head(x["q"][0, h], x["k"][0, h], x["v"][0, h], wl.b1, wl.b2, wl.tiles, wl.iters)
+        mx, mean = errors(y[0, h], ref)
+        say(f"[ok] loose bound head {h}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS
