@@ -371,7 +371,7 @@ __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const
 //   dv[c1,c2] = sum_(g,a2) R dU,
 //   dk[c1,c2] = s sum_(g,a2) dz Qh + dKbar[c1] / b2   (dKbar already reduced).
 #ifndef MONARCH_BRB_BPS
-#define MONARCH_BRB_BPS 2
+#define MONARCH_BRB_BPS 4
 #endif
 
 template <typename T, int D>
