@@ -1,5 +1,5 @@
-"""CPU oracle for the gradient of the one-iteration tiled MonarchAttention
-forward (float64 numpy).
+"""CPU oracle for the gradient of the tiled MonarchAttention forward
+(float64 numpy), through one or several unrolled iterations.
 
 TEST INFRASTRUCTURE, like monarch_oracle: only the tests, the smoke check and
 the benchmark's CPU baseline may import or call it.
@@ -32,9 +32,10 @@ iteration, written out step by step in reverse:
     dq += s sum_c1 dl Kbar            dKbar = s sum_n dl q_n
     dk += dKbar / b2                  (the block mean)
 
-Pinned by central finite differences of the forward oracle and by the two
-block shapes where the method is exact softmax attention (tests).  Only one
-iteration: a gradient through several unrolled iterations is not covered.
+With several iterations the reverse also runs back through the earlier
+ones (see monarch_head_grad).  Pinned by central finite differences of the
+forward oracle, by the block shapes where the method is exact softmax
+attention, and by symmetries of the forward (tests).
 """
 from __future__ import annotations
 
@@ -47,75 +48,112 @@ from .monarch_oracle import _blocks, l_step, r_step, tile_bounds, uniform_R
 __all__ = ["monarch_head_grad", "monarch_attention_grad"]
 
 
-def monarch_head_grad(q, k, v, dy, b1: int, b2: int, tiles: int = 1):
-    """Gradient of sum(dy * y) for one (batch, head) at one iteration.
+def monarch_head_grad(q, k, v, dy, b1: int, b2: int, tiles: int = 1, iters: int = 1):
+    """Gradient of sum(dy * y) for one (batch, head) after ``iters`` iterations.
 
     q, k, v, dy: [N, d].  Returns (dq, dk, dv), each [N, d] float64.
+
+    For iters > 1 the reverse also runs through the earlier iterations: the
+    L-step of iteration i uses the keys Kt_(i-1) = R_(i-1) k and entropies
+    H_(i-1) = H(R_(i-1)) of the R-step before it, so its logit gradient dl_i
+    gives dKt_(i-1) = s sum_(a1 in g) dl_i q and dH_(i-1) = sum_(a1 in g) dl_i,
+    and from those dR_(i-1) = <dKt, k> - dH (log R_(i-1) + 1),
+    dk += sum_(g,a2) R_(i-1) dKt; the R-step of iteration i-1 then takes dR
+    back to dQhat, dk, G and dL_(i-1) as for the last one.  The first L-step
+    uses the block means (R_0 uniform and constant).
     """
     N, d = np.shape(q)
     if b1 * b2 != N:
         raise ValueError(f"b1*b2 = {b1 * b2} != N = {N}")
+    if iters < 1:
+        raise ValueError("iters must be >= 1")
     bounds = tile_bounds(b1, tiles)
     t = tiles
     s = 1.0 / math.sqrt(d)
     qb, kb, vb = _blocks(q, b1, b2), _blocks(k, b1, b2), _blocks(v, b1, b2)
     dyb = _blocks(dy, b1, b2)
 
-    # ---- forward, keeping what the reverse needs
-    kbar = kb.mean(axis=1)                                   # [c1, d]
-    L, _ = l_step(qb, kb, uniform_R(b1, b2, t), bounds, s)  # [a2, a1, c1]
-    R, q_hat, beta = r_step(qb, kb, L, bounds, s)            # [t,c1,a2,c2], [t,c1,a2,d], [t,c1,a2]
-    U = np.einsum("gcap,cpd->gcad", R, vb)                   # [t, c1, a2, d]
+    # ---- forward, keeping every iteration's factors
+    Rs = [uniform_R(b1, b2, t)]               # R_0 .. R_T
+    Ls, qhats, betas = [None], [None], [None]  # index i = 1..T
+    for _ in range(iters):
+        L, _ = l_step(qb, kb, Rs[-1], bounds, s)
+        R, q_hat, beta = r_step(qb, kb, L, bounds, s)
+        Ls.append(L)
+        qhats.append(q_hat)
+        betas.append(beta)
+        Rs.append(R)
+    T = iters
+    U = np.einsum("gcap,cpd->gcad", Rs[T], vb)                # [t, c1, a2, d]
 
     dqb = np.zeros_like(qb)
     dkb = np.zeros_like(kb)
     dvb = np.zeros_like(vb)
-    dL = np.zeros_like(L)                                    # [a2, a1, c1]
-    G = np.zeros_like(q_hat)                                 # [t, c1, a2, d]
+    q_perm = qb.transpose(1, 0, 2)                            # [a2, a1, d]
 
+    # gradient of the last L (through the apply) and of the last R (through U)
+    dL = np.zeros_like(Ls[T])                                 # [a2, a1, c1]
+    dR = np.zeros_like(Rs[T])                                 # [t, c1, a2, c2]
     for g in range(t):
         lo, hi = bounds[g], bounds[g + 1]
-        Lg = L[:, lo:hi, :]                                  # [a2, a1 in g, c1]
-        dy_cols = dyb[lo:hi].transpose(1, 0, 2)              # [a2, a1, d]
-        q_cols = qb[lo:hi].transpose(1, 0, 2)                # [a2, a1, d]
-        Ug = U[g].transpose(1, 0, 2)                         # [a2, c1, d]
-        # apply: y = L U
-        dL[:, lo:hi, :] = dy_cols @ Ug.transpose(0, 2, 1)    # <dy, U>
+        Lg = Ls[T][:, lo:hi, :]                               # [a2, a1 in g, c1]
+        dy_cols = dyb[lo:hi].transpose(1, 0, 2)               # [a2, a1, d]
+        Ug = U[g].transpose(1, 0, 2)                          # [a2, c1, d]
+        dL[:, lo:hi, :] = dy_cols @ Ug.transpose(0, 2, 1)     # <dy, U>
         dU = (Lg.transpose(0, 2, 1) @ dy_cols).transpose(1, 0, 2)  # [c1, a2, d]
-        # U = R v
-        dR = dU @ vb.transpose(0, 2, 1)                      # [c1, a2, c2]
-        dvb += R[g].transpose(0, 2, 1) @ dU                  # [c1, c2, d]
-        # R = softmax(z)
-        dz = R[g] * (dR - np.sum(R[g] * dR, axis=-1, keepdims=True))
-        dq_hat = s * (dz @ kb)                               # [c1, a2, d]
-        dkb += s * (dz.transpose(0, 2, 1) @ q_hat[g])        # [c1, c2, d]
-        # Qhat = sum L q / beta
-        mass = beta[g]                                       # [c1, a2]
-        Gg = np.where((mass > 0)[:, :, None], dq_hat / np.where(mass > 0, mass, 1.0)[:, :, None], 0.0)
-        G[g] = Gg
-        Gc = Gg.transpose(1, 0, 2)                           # [a2, c1, d]
-        qh_c = q_hat[g].transpose(1, 0, 2)                   # [a2, c1, d]
-        dL[:, lo:hi, :] += q_cols @ Gc.transpose(0, 2, 1) \
-            - np.sum(Gc * qh_c, axis=-1)[:, None, :]
-        dqb[lo:hi] += (Lg @ Gc).transpose(1, 0, 2)
+        dR[g] = dU @ vb.transpose(0, 2, 1)                    # [c1, a2, c2]
+        dvb += Rs[T][g].transpose(0, 2, 1) @ dU               # [c1, c2, d]
 
-    # L = softmax(l), l = s <q, Kbar>
-    dl = L * (dL - np.sum(L * dL, axis=-1, keepdims=True))  # [a2, a1, c1]
-    q_perm = qb.transpose(1, 0, 2)                           # [a2, a1, d]
-    dqb += (s * (dl @ kbar)).transpose(1, 0, 2)
-    dkbar = s * np.einsum("pac,pad->cd", dl, q_perm)         # [c1, d]
-    dkb += dkbar[:, None, :] / b2
+    for i in range(T, 0, -1):
+        R, L, q_hat, beta = Rs[i], Ls[i], qhats[i], betas[i]
+        # ---- R-step i: R = softmax(z), z = s <Qhat, k>; Qhat = sum L q / beta
+        for g in range(t):
+            lo, hi = bounds[g], bounds[g + 1]
+            Lg = L[:, lo:hi, :]
+            q_cols = q_perm[:, lo:hi, :]
+            dz = R[g] * (dR[g] - np.sum(R[g] * dR[g], axis=-1, keepdims=True))
+            dq_hat = s * (dz @ kb)                            # [c1, a2, d]
+            dkb += s * (dz.transpose(0, 2, 1) @ q_hat[g])     # [c1, c2, d]
+            mass = beta[g]                                    # [c1, a2]
+            Gg = np.where((mass > 0)[:, :, None], dq_hat / np.where(mass > 0, mass, 1.0)[:, :, None], 0.0)
+            Gc = Gg.transpose(1, 0, 2)                        # [a2, c1, d]
+            qh_c = q_hat[g].transpose(1, 0, 2)                # [a2, c1, d]
+            dL[:, lo:hi, :] += q_cols @ Gc.transpose(0, 2, 1) \
+                - np.sum(Gc * qh_c, axis=-1)[:, None, :]
+            dqb[lo:hi] += (Lg @ Gc).transpose(1, 0, 2)
+        # ---- L-step i: L = softmax(l), l = s <q, Kt_(i-1)> + H_(i-1)
+        dl = L * (dL - np.sum(L * dL, axis=-1, keepdims=True))  # [a2, a1, c1]
+        Rp = Rs[i - 1]
+        k_til = np.einsum("gcap,cpd->gcad", Rp, kb)           # [t, c1, a2, d]
+        dk_til = np.zeros_like(k_til)
+        dh = np.zeros(Rp.shape[:3])                           # [t, c1, a2]
+        for g in range(t):
+            lo, hi = bounds[g], bounds[g + 1]
+            dlg = dl[:, lo:hi, :]                             # [a2, a1 in g, c1]
+            k_cols = k_til[g].transpose(1, 0, 2)              # [a2, c1, d]
+            dqb[lo:hi] += (s * (dlg @ k_cols)).transpose(1, 0, 2)
+            dk_til[g] = (s * (dlg.transpose(0, 2, 1) @ q_perm[:, lo:hi, :])).transpose(1, 0, 2)
+            dh[g] = dlg.sum(axis=1).T                         # [c1, a2]
+        if i == 1:
+            # Kt_0 = Kbar for every tile and column; H_0 is a constant
+            dkb += dk_til.sum(axis=(0, 2))[:, None, :] / b2
+        else:
+            # Kt = R k and H = -sum R log R of the R-step before
+            logR = np.log(Rp)
+            dR = np.einsum("gcad,cpd->gcap", dk_til, kb) - dh[..., None] * (logR + 1.0)
+            dkb += np.einsum("gcap,gcad->cpd", Rp, dk_til)
+            dL = np.zeros_like(Ls[i - 1])
     return dqb.reshape(N, d), dkb.reshape(N, d), dvb.reshape(N, d)
 
 
-def monarch_attention_grad(q, k, v, dy, b1: int, b2: int, tiles: int = 1):
+def monarch_attention_grad(q, k, v, dy, b1: int, b2: int, tiles: int = 1, iters: int = 1):
     """[B, H, N, d] inputs -> (dq, dk, dv) float64, head by head."""
     q = np.asarray(q)
     B, H, N, d = q.shape
     out = [np.empty((B, H, N, d)) for _ in range(3)]
     for b in range(B):
         for h in range(H):
-            grads = monarch_head_grad(q[b, h], k[b, h], v[b, h], dy[b, h], b1, b2, tiles)
+            grads = monarch_head_grad(q[b, h], k[b, h], v[b, h], dy[b, h], b1, b2, tiles, iters)
             for o, gr in zip(out, grads):
                 o[b, h] = gr
     return tuple(out)

@@ -1,13 +1,15 @@
 """Checks that pin the CPU gradient oracle to facts outside itself.
 
 Each ``check_*`` takes a gradient module (``oracle.monarch_grad``, or a copy
-with a planted mistake) and raises AssertionError when the fact does not hold:
+with a planted mistake) and raises AssertionError when the fact does not hold
+(one and several iterations):
 
 * central finite differences of the forward oracle along random directions,
   for each input separately, and entry by entry on a tiny case;
-* the block shapes where one iteration is exact softmax attention
-  ((b1, b2) = (N, 1), any tiles; (1, N)), against torch autograd through
-  torch's own attention in float64;
+* the block shapes where the method is exact softmax attention
+  ((b1, b2) = (N, 1), any tiles; (1, N); one-row tiles with two or more
+  iterations), against torch autograd through torch's own attention in
+  float64;
 * one-row tiles (t = b1), where the forward has a closed form that does not
   go through the aggregation, against torch autograd of that closed form;
 * symmetries of the forward: a shift of every key leaves y unchanged (the
@@ -36,8 +38,8 @@ def _case(seed, b1, b2, d, scale=1.5):
     return q, k, v, dy
 
 
-def _loss(q, k, v, dy, b1, b2, t):
-    return float(np.sum(dy * oracle.monarch_head(q, k, v, b1, b2, t, 1)))
+def _loss(q, k, v, dy, b1, b2, t, T=1):
+    return float(np.sum(dy * oracle.monarch_head(q, k, v, b1, b2, t, T)))
 
 
 def _torch_grads(fn, q, k, v, dy):
@@ -59,10 +61,11 @@ def _close(a, b, rel, what):
 def check_grad_directional_fd(grd):
     """d/dh sum(dy * y(x + h u)) at h = 0 equals <grad, u>, per input."""
     h = 1e-5
-    for seed, (b1, b2, t, d) in enumerate([(6, 4, 1, 8), (6, 4, 2, 8), (5, 6, 3, 4), (7, 3, 7, 4),
-                                           (8, 5, 4, 16)]):
+    for seed, (b1, b2, t, d, T) in enumerate([(6, 4, 1, 8, 1), (6, 4, 2, 8, 1), (5, 6, 3, 4, 1), (7, 3, 7, 4, 1),
+                                              (8, 5, 4, 16, 1), (6, 4, 1, 8, 2), (6, 4, 2, 8, 3),
+                                              (5, 6, 3, 4, 2), (8, 5, 4, 16, 3)]):
         q, k, v, dy = _case(seed, b1, b2, d)
-        dq, dk, dv = grd.monarch_head_grad(q, k, v, dy, b1, b2, t)
+        dq, dk, dv = grd.monarch_head_grad(q, k, v, dy, b1, b2, t, T)
         rng = np.random.default_rng(100 + seed)
         for which, g in (("q", dq), ("k", dk), ("v", dv)):
             u = rng.standard_normal(q.shape)
@@ -70,30 +73,31 @@ def check_grad_directional_fd(grd):
             args_m = dict(args_p)
             args_p[which] = args_p[which] + h * u
             args_m[which] = args_m[which] - h * u
-            fd = (_loss(args_p["q"], args_p["k"], args_p["v"], dy, b1, b2, t)
-                  - _loss(args_m["q"], args_m["k"], args_m["v"], dy, b1, b2, t)) / (2 * h)
+            fd = (_loss(args_p["q"], args_p["k"], args_p["v"], dy, b1, b2, t, T)
+                  - _loss(args_m["q"], args_m["k"], args_m["v"], dy, b1, b2, t, T)) / (2 * h)
             an = float(np.sum(g * u))
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), \
-                f"{which} ({b1},{b2},t={t}): fd {fd:.10f} vs analytic {an:.10f}"
+                f"{which} ({b1},{b2},t={t},T={T}): fd {fd:.10f} vs analytic {an:.10f}"
 
 
 def check_grad_entrywise_fd(grd):
     """Every entry of dq, dk, dv by central differences on a tiny case."""
     b1, b2, t, d = 3, 2, 2, 3
     q, k, v, dy = _case(7, b1, b2, d)
-    grads = grd.monarch_head_grad(q, k, v, dy, b1, b2, t)
     h = 1e-5
-    for idx, (name, g) in enumerate(zip("qkv", grads)):
-        base = [q, k, v]
-        fd = np.empty_like(g)
-        for i in range(g.shape[0]):
-            for j in range(g.shape[1]):
-                xp = [x.copy() for x in base]
-                xm = [x.copy() for x in base]
-                xp[idx][i, j] += h
-                xm[idx][i, j] -= h
-                fd[i, j] = (_loss(*xp, dy, b1, b2, t) - _loss(*xm, dy, b1, b2, t)) / (2 * h)
-        _close(g, fd, 1e-6, f"d{name} entrywise")
+    for T in (1, 2):
+        grads = grd.monarch_head_grad(q, k, v, dy, b1, b2, t, T)
+        for idx, (name, g) in enumerate(zip("qkv", grads)):
+            base = [q, k, v]
+            fd = np.empty_like(g)
+            for i in range(g.shape[0]):
+                for j in range(g.shape[1]):
+                    xp = [x.copy() for x in base]
+                    xm = [x.copy() for x in base]
+                    xp[idx][i, j] += h
+                    xm[idx][i, j] -= h
+                    fd[i, j] = (_loss(*xp, dy, b1, b2, t, T) - _loss(*xm, dy, b1, b2, t, T)) / (2 * h)
+            _close(g, fd, 1e-6, f"d{name} entrywise T={T}")
 
 
 def check_grad_softmax_limits(grd):
@@ -103,12 +107,21 @@ def check_grad_softmax_limits(grd):
     def sdpa(tq, tk, tv):
         return F.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None])[0, 0]
 
-    for seed, (b1, b2, t) in enumerate([(12, 1, 1), (12, 1, 5), (1, 12, 1)]):
+    for seed, (b1, b2, t, T) in enumerate([(12, 1, 1, 1), (12, 1, 5, 1), (1, 12, 1, 1), (12, 1, 3, 3),
+                                            (1, 12, 1, 2)]):
         q, k, v, dy = _case(20 + seed, b1, b2, 8)
-        got = grd.monarch_head_grad(q, k, v, dy, b1, b2, t)
+        got = grd.monarch_head_grad(q, k, v, dy, b1, b2, t, T)
         ref = _torch_grads(sdpa, q, k, v, dy)
         for name, a, b in zip("qkv", got, ref):
-            _close(a, b, 1e-10, f"d{name} at (b1,b2,t)=({b1},{b2},{t})")
+            _close(a, b, 1e-10, f"d{name} at (b1,b2,t,T)=({b1},{b2},{t},{T})")
+    # one-row tiles with two or more iterations are exact attention too
+    b1, b2 = 5, 4
+    q, k, v, dy = _case(29, b1, b2, 6)
+    ref = _torch_grads(sdpa, q, k, v, dy)
+    for T in (2, 3):
+        got = grd.monarch_head_grad(q, k, v, dy, b1, b2, b1, T)
+        for name, a, b in zip("qkv", got, ref):
+            _close(a, b, 1e-9, f"d{name} one-row tiles T={T}")
 
 
 def check_grad_one_row_tiles(grd):
@@ -133,9 +146,10 @@ def check_grad_one_row_tiles(grd):
 
 
 def check_grad_symmetries(grd):
-    for seed, (b1, b2, t, d) in enumerate([(6, 5, 1, 8), (6, 5, 3, 8), (9, 4, 2, 4)]):
+    for seed, (b1, b2, t, d, T) in enumerate([(6, 5, 1, 8, 1), (6, 5, 3, 8, 1), (9, 4, 2, 4, 1), (6, 5, 3, 8, 2),
+                                              (9, 4, 2, 4, 3)]):
         q, k, v, dy = _case(40 + seed, b1, b2, d)
-        dq, dk, dv = grd.monarch_head_grad(q, k, v, dy, b1, b2, t)
+        dq, dk, dv = grd.monarch_head_grad(q, k, v, dy, b1, b2, t, T)
         scale = np.max(np.abs(dk)) * k.shape[0]
         assert np.max(np.abs(dk.sum(axis=0))) <= 1e-11 * scale, "key shift: sum dk != 0"
         assert np.max(np.abs(dv.sum(axis=0) - dy.sum(axis=0))) <= 1e-11 * np.max(np.abs(dy)) * k.shape[0], \

@@ -15,8 +15,8 @@ MUTANTS = {
     "dL_apply_missing": ("dL[:, lo:hi, :] = dy_cols @ Ug.transpose(0, 2, 1)",
                          "dL[:, lo:hi, :] = 0.0 * (dy_cols @ Ug.transpose(0, 2, 1))"),
     "dU_unweighted": ("dU = (Lg.transpose(0, 2, 1) @ dy_cols)", "dU = (np.ones_like(Lg).transpose(0, 2, 1) @ dy_cols)"),
-    "dv_R_not_transposed": ("dvb += R[g].transpose(0, 2, 1) @ dU", "dvb += R[g] @ dU"),
-    "dz_no_centering": ("dz = R[g] * (dR - np.sum(R[g] * dR, axis=-1, keepdims=True))", "dz = R[g] * dR"),
+    "dv_R_not_transposed": ("dvb += Rs[T][g].transpose(0, 2, 1) @ dU", "dvb += Rs[T][g] @ dU"),
+    "dz_no_centering": ("dz = R[g] * (dR[g] - np.sum(R[g] * dR[g], axis=-1, keepdims=True))", "dz = R[g] * dR[g]"),
     "dqhat_no_scale": ("dq_hat = s * (dz @ kb)", "dq_hat = (dz @ kb)"),
     "dk_r_missing": ("dkb += s * (dz.transpose(0, 2, 1) @ q_hat[g])", "pass"),
     "G_no_beta": ("dq_hat / np.where(mass > 0, mass, 1.0)[:, :, None]", "dq_hat"),
@@ -24,9 +24,18 @@ MUTANTS = {
     "dL_agg_sign": ("dL[:, lo:hi, :] += q_cols @ Gc.transpose(0, 2, 1)", "dL[:, lo:hi, :] -= q_cols @ Gc.transpose(0, 2, 1)"),
     "dq_agg_missing": ("dqb[lo:hi] += (Lg @ Gc).transpose(1, 0, 2)", "pass"),
     "dl_no_centering": ("dl = L * (dL - np.sum(L * dL, axis=-1, keepdims=True))", "dl = L * dL"),
-    "dq_l_missing": ("dqb += (s * (dl @ kbar)).transpose(1, 0, 2)", "pass"),
-    "dkbar_not_mean": ("dkb += dkbar[:, None, :] / b2", "dkb += dkbar[:, None, :]"),
-    "dkbar_wrong_axis": ('np.einsum("pac,pad->cd", dl, q_perm)', 'np.einsum("pca,pad->cd", dl, q_perm)'),
+    "dq_l_missing": ("dqb[lo:hi] += (s * (dlg @ k_cols)).transpose(1, 0, 2)", "pass"),
+    "dkbar_not_mean": ("dkb += dk_til.sum(axis=(0, 2))[:, None, :] / b2", "dkb += dk_til.sum(axis=(0, 2))[:, None, :]"),
+    "dktil_wrong_operand": ("dk_til[g] = (s * (dlg.transpose(0, 2, 1) @ q_perm[:, lo:hi, :]))",
+                            "dk_til[g] = (s * (dlg.transpose(0, 2, 1) @ q_perm[:, hi - (hi - lo):hi, :][:, ::-1, :]))"),
+    # several iterations
+    "entropy_grad_sign": ("- dh[..., None] * (logR + 1.0)", "+ dh[..., None] * (logR + 1.0)"),
+    "entropy_grad_missing": ("- dh[..., None] * (logR + 1.0)", "- 0.0 * dh[..., None]"),
+    "ktil_grad_to_k_missing": ('dkb += np.einsum("gcap,gcad->cpd", Rp, dk_til)', "pass"),
+    "ktil_grad_R_transposed": ('dkb += np.einsum("gcap,gcad->cpd", Rp, dk_til)', 'dkb += np.einsum("gcpa,gcad->cpd", Rp, dk_til)'),
+    "stale_dL_between_iterations": ("            dL = np.zeros_like(Ls[i - 1])", "            dL = dL * 1.0"),
+    "earlier_iterations_use_last_L": ("        R, L, q_hat, beta = Rs[i], Ls[i], qhats[i], betas[i]",
+                                      "        R, L, q_hat, beta = Rs[i], Ls[T], qhats[i], betas[i]"),
     "tile0_U": ("Ug = U[g].transpose(1, 0, 2)", "Ug = U[0].transpose(1, 0, 2)"),
 }
 
