@@ -2,9 +2,10 @@
 
 Default (--mode fwd): one step = one full forward call (block-mean keys,
 T x (L-step, R-step), L-apply) over one batch of seeded synthetic Q/K/V
-already resident in HBM.  --mode train: one step = the one-iteration training
-forward (which keeps its state) plus the backward pass for a seeded upstream
-gradient (dq, dk, dv).  Prints ONE JSON line with tokens/s (value),
+already resident in HBM.  --mode train: one step = the training forward
+(which keeps its state; the workload's iteration count, one for the 720p
+latent, or --iters) plus the backward pass for a seeded upstream gradient
+(dq, dk, dv).  Prints ONE JSON line with tokens/s (value),
 layer-calls/s, the roofline of the dominant kernel (timed with HIP events on
 the launch stream inside the timed region) and the CPU oracle timed on a
 bounded sample of the same workload.
@@ -88,6 +89,46 @@ def algorithmic_work(wl, it_last=True):
     }
 
 
+def step_work(wl, mode, launches):
+    """Per step: (flops, bytes) of each kernel, summed over its launches.
+
+    The forward kernels and the one-iteration backward do the same work at
+    every launch (algorithmic_work x launches).  The backward through T >= 2
+    iterations runs its kernels in two forms, per (batch, head):
+      last iteration (once):  kb_du, kb_rside_a, kb_dq, kb_rside_b as above,
+        except that the L-step's keys are the aggregated keys Kt and
+        entropies H (t*N*d*e + 4tN more read by kb_du and kb_dq);
+      each earlier iteration (T-1 times), with cotangents dKt, dH instead of dU:
+        kb_rside_a  dR = dKt k^T, dQh = dz k      4 t N b2 d; Qh, dKt, K, beta, dH in, G out
+        kb_dq       <q,G>, L G, dl Kt              6 N b1 d;  q, Kt, H (Kbar at i = 1), G, lse, e in
+        kb_rside_b  dk_R = dz^T Qh + R^T dKt       4 t N b2 d; Qh, dKt, K, dH in, dk out (once)
+        kb_dktil    dKt, dH of the R-step before   2 N b1 d;  q in, dKt, dH out   (T-1 launches)
+      kb_dkbar and its reduction once, at the first iteration; dq and dk are
+      written once.
+    """
+    per = algorithmic_work(wl)
+    tot = {kn: (per[kn][0] * n, per[kn][1] * n) for kn, n in launches.items() if kn in per}
+    T = wl.iters
+    if mode != "train" or T < 2:
+        return tot
+    e = 2 if wl.dtype == "bf16" else 4
+    BH, N, d, b1, b2, t = wl.B * wl.H, wl.N, wl.d, wl.b1, wl.b2, wl.tiles
+    nd = N * d * e
+    m = T - 1
+    extra_keys = t * nd + 4 * t * N
+    tot["kb_du"] = (per["kb_du"][0], per["kb_du"][1] + BH * extra_keys)
+    tot["kb_rside_a"] = (BH * 4.0 * t * N * b2 * d * T,
+                         per["kb_rside_a"][1] + m * BH * (3 * t * nd + nd + 20 * t * N))
+    # dq and dk are written once (counted with the last form's launch); the
+    # first L-step's keys are the block means (b1*d, not counted)
+    tot["kb_dq"] = (per["kb_dq"][0] + m * BH * 6.0 * N * b1 * d,
+                    per["kb_dq"][1] + BH * extra_keys + m * BH * (nd + t * nd + 4 * N + 4 * t * N)
+                    + (m - 1) * BH * extra_keys)
+    tot["kb_rside_b"] = (BH * 4.0 * t * N * b2 * d * T, per["kb_rside_b"][1] + m * BH * (2 * t * nd + nd + 12 * t * N))
+    tot["kb_dktil"] = (m * BH * 2.0 * N * b1 * d, m * BH * (nd + t * nd + 4 * t * N))
+    return tot
+
+
 def roofline_entry(name, flops, nbytes, avg_s, dtype, traffic):
     peak_f = (PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12
     peak_b = PEAK_HBM_GBS * 1e9
@@ -154,8 +195,8 @@ def cpu_baseline_train(wl, seed, budget_s=30.0):
         x = I.make_inputs(wl.with_(B=1), seed, heads=[h], want_bits=False)
         dy = I.make_cotangent(wl.with_(B=1), seed, heads=[h], want_bits=False)["dy"][0, 0]
         t0 = time.perf_counter()
-        oracle.monarch_head(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], wl.b1, wl.b2, wl.tiles, 1)
-        oracle.monarch_head_grad(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], dy, wl.b1, wl.b2, wl.tiles)
+        oracle.monarch_head(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], wl.b1, wl.b2, wl.tiles, wl.iters)
+        oracle.monarch_head_grad(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], dy, wl.b1, wl.b2, wl.tiles, wl.iters)
         spent += time.perf_counter() - t0
         done += 1
     per_call = spent / done * wl.B * wl.H
@@ -176,7 +217,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--mode", choices=["fwd", "train"], default="fwd",
-                    help="fwd: forward layer call; train: one-iteration training forward + backward")
+                    help="fwd: forward layer call; train: training forward + backward")
     ap.add_argument("--iters", type=int, default=0,
                     help="override the workload's iteration count (0: keep it)")
     ap.add_argument("--tol", type=float, default=None,
@@ -209,8 +250,6 @@ def main():
     wl = I.get_workload(args.workload)
     if args.iters:
         wl = wl.with_(iters=args.iters)
-    if args.mode == "train":
-        wl = wl.with_(iters=1)
     dev = torch.device("cuda:0")
     t0 = time.time()
     x = I.make_inputs(wl, args.seed, want_f32=(wl.dtype == "f32"))
@@ -265,10 +304,10 @@ def main():
             dy = torch.from_numpy(dyx["dy"]).to(dev)
         del dyx
         sb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles,
-                                              M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32)
+                                              wl.iters, M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32)
         state = torch.empty(sb, dtype=torch.uint8, device=dev)
         dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-        targs = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles)
+        targs = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
 
         def step():
             M.monarch_attn_fwd_train(q, k, v, out, *targs, state, stream)
@@ -291,19 +330,21 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
-    work = algorithmic_work(wl)
     kernels = {}
     for full, (ms, n) in per_kernel.items():
         short = full.split(" ")[0]
         if n:
             kernels[short] = {"avg_ms": round(ms / n, 5), "launches_per_step": n / args.steps,
                               "ms_per_step": round(ms / args.steps, 5)}
+    # work per launch: the kernel's work per step over its launches per step
+    tot = step_work(wl, args.mode, {kn: rec["launches_per_step"] for kn, rec in kernels.items()})
+    work = {kn: (tot[kn][0] / kernels[kn]["launches_per_step"], tot[kn][1] / kernels[kn]["launches_per_step"])
+            for kn in kernels}
     dom = max(kernels, key=lambda kname: kernels[kname]["ms_per_step"])
     launches = kernels[dom]["launches_per_step"]
     fl, by = work[dom]
-    # k_lse/k_aggregate/k_rstep run once per iteration: per-launch work is per iteration
     roof = roofline_entry(dom, fl, by, kernels[dom]["avg_ms"] / 1e3, wl.dtype,
-                          read_traffic(dom, wl.name))
+                          read_traffic(dom, wl.name) if wl.iters == 1 or args.mode == "fwd" else None)
     roof["launches_per_step"] = launches
     if iters_used is not None:
         roof["note"] = ("early stopping: launches after every head has stopped return at once and are "

@@ -141,41 +141,49 @@ int monarch_attn_fwd_kv_ws(const void* q, const void* k, const void* v, void* ou
                            int b1, int b2, int tiles, int iters, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* ---- training: the one-iteration form and its gradient ----
+/* ---- training: the forward that keeps its factors, and its gradient ----
  * The pages' deployed regime is one iteration after finetuning the video
  * model with this attention in place (yunpan.plus MonarchRT article,
  * "Innovation 3: finetuning and efficient kernels", Fig. 4 right), which
- * needs the gradient of the layer.  These calls fix iters = 1.
+ * needs the gradient of the layer; several iterations (iters >= 1, the
+ * same refinement as monarch_attn_fwd) are differentiated too.
  *
- * monarch_attn_fwd_train computes the same out as monarch_attn_fwd_ws with
- * iters = 1 and also leaves in `state` (a caller-owned device buffer of at
- * least monarch_attn_train_state_bytes(...) bytes, 256-byte aligned, not
+ * monarch_attn_fwd_train computes the same out as monarch_attn_fwd_ws and
+ * also leaves in `state` (a caller-owned device buffer of at least
+ * monarch_attn_train_state_bytes(...) bytes, 256-byte aligned, not
  * overlapping q, k, v or out) what the backward pass reads: the block-mean
- * keys, the L-row log-sum-exps, the column masses beta, the aggregated
- * queries Qh and U = R V of every tile.  Its size is
- *   B*H*(b1*d*e + 4*b1 + 4*N + 4*t*N + 2*t*N*d*e)  (+ alignment), e = element bytes.
+ * keys; per iteration the L-row log-sum-exps, the column masses beta and the
+ * aggregated queries Qh of every tile; U = R V of the last R-step; and for
+ * every R-step but the last the keys R k and entropies H(R) it hands to the
+ * next L-step.  Its size is, with e = element bytes and T = iters,
+ *   B*H*(b1*d*e + 4*b1 + T*(4*N + 4*t*N + t*N*d*e) + t*N*d*e
+ *        + (T-1)*(t*N*d*e + 4*t*N))  (+ alignment).
  *
  * monarch_attn_bwd takes the same q, k, v, the out and state of a
  * monarch_attn_fwd_train call with the same arguments, and dout = dLoss/dout,
  * and writes dq, dk, dv = dLoss/dq, dLoss/dk, dLoss/dv ([B,H,N,d], same
- * dtype).  Definition: with R starting uniform the L-step keys are the block
- * means Kbar[c1] = mean_c2 k_(c1,c2), and the gradient is the chain rule
- * through L = softmax(s q Kbar^T), Qh = sum L q / beta (0 where beta == 0),
- * R = softmax(s Qh k^T), U = R V and y = L U on the permuted index.
+ * dtype).  Definition: the chain rule through every step of the forward as
+ * monarch_attn_fwd computes it: with R starting uniform the first L-step's
+ * keys are the block means Kbar[c1] = mean_c2 k_(c1,c2); each L-step
+ * L = softmax(s q Kt^T + H) with the keys Kt = R k and entropies H of the
+ * R-step before; Qh = sum L q / beta (0 where beta == 0);
+ * R = softmax(s Qh k^T); U = R V of the last R-step and y = L U on the
+ * permuted index.
  * dq, dk, dv must not overlap each other or any input (state included).
  * It allocates a workspace stream-ordered (about 2*t*N*d*e + 16*t*N +
- * N*roundup(b1, 256)*e bytes per head).  The supported envelope is the
- * forward's.  State from another shape or dtype gives undefined results. */
+ * N*roundup(b1, 256)*e bytes per head, plus 4*t*N + 8*N*d for T > 1).  The
+ * supported envelope is the forward's.  State from another shape, iteration
+ * count or dtype gives undefined results. */
 size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d,
-                                      int b1, int b2, int tiles, int dtype);
+                                      int b1, int b2, int tiles, int iters, int dtype);
 int monarch_attn_fwd_train(const void* q, const void* k, const void* v, void* out,
                            int B, int H, int f, int h, int w, int d,
-                           int b1, int b2, int tiles, int dtype,
+                           int b1, int b2, int tiles, int iters, int dtype,
                            void* state, size_t state_bytes, void* stream);
 int monarch_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                      const void* dout, void* dq, void* dk, void* dv,
                      int B, int H, int f, int h, int w, int d,
-                     int b1, int b2, int tiles, int dtype,
+                     int b1, int b2, int tiles, int iters, int dtype,
                      void* state, size_t state_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
@@ -194,8 +202,9 @@ int monarch_attn_last_hip_error(void);
  * backward: 5 dU per tile column, 6 R-step per key block (G, statistics),
  * 7 row pass (dq), 8 block-mean key gradient (product over tokens),
  * 9 its reduction, 10 dv and dk per key block; 11 objective and early-stop
- * decision per head. */
-#define MONARCH_NUM_KERNELS 12
+ * decision per head; 12 (backward, several iterations) gradient of the
+ * aggregated keys and entropies per tile column. */
+#define MONARCH_NUM_KERNELS 13
 int monarch_attn_profile_enable(int on);
 int monarch_attn_profile_collect(double* ms, long* launches, int n);
 const char* monarch_attn_kernel_name(int id);

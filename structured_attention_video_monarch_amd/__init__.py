@@ -24,7 +24,7 @@ MONARCH_EHIP = -3
 MONARCH_ENOMEM = -4
 MONARCH_BF16 = 0
 MONARCH_F32 = 1
-MONARCH_NUM_KERNELS = 12
+MONARCH_NUM_KERNELS = 13
 
 _lib = None
 
@@ -58,7 +58,7 @@ def _declare(lib):
     lib.monarch_attn_fwd_kv.restype = c_int
     lib.monarch_attn_fwd_kv_ws.argtypes = [c_void_p] * 4 + kdims + [c_int, c_void_p, c_size_t, c_void_p]
     lib.monarch_attn_fwd_kv_ws.restype = c_int
-    tdims = [c_int] * 9  # B, H, f, h, w, d, b1, b2, tiles
+    tdims = [c_int] * 10  # B, H, f, h, w, d, b1, b2, tiles, iters
     lib.monarch_attn_train_state_bytes.argtypes = tdims + [c_int]
     lib.monarch_attn_train_state_bytes.restype = c_size_t
     lib.monarch_attn_fwd_train.argtypes = [c_void_p] * 4 + tdims + [c_int, c_void_p, c_size_t, c_void_p]
@@ -86,6 +86,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             from .build import build_library
             build_library()
+        # torch ships its own HIP runtime under the same soname: load torch
+        # first so that the library binds to that one runtime instead of
+        # bringing in a second copy that torch would then pick up
+        import torch  # noqa: F401
         _lib = _declare(ctypes.CDLL(LIB_PATH))
     return _lib
 
@@ -245,8 +249,8 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
-def monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, tiles, dtype=MONARCH_BF16) -> int:
-    return int(lib().monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, tiles, dtype))
+def monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, tiles, iters, dtype=MONARCH_BF16) -> int:
+    return int(lib().monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, tiles, iters, dtype))
 
 
 def _state(state):
@@ -256,21 +260,21 @@ def _state(state):
     return ctypes.c_void_p(state.data_ptr()), state.numel()
 
 
-def monarch_attn_fwd_train(q, k, v, out, f, h, w, b1, b2, tiles, state, stream=None):
-    """One-iteration forward that also fills ``state`` for the backward."""
+def monarch_attn_fwd_train(q, k, v, out, f, h, w, b1, b2, tiles, iters, state, stream=None):
+    """Forward (``iters`` iterations) that also fills ``state`` for the backward."""
     ptrs = _tensors(q, k, v, out, q.dtype)
     sp, sn = _state(state)
-    dims = _dims(q, f, h, w, b1, b2, tiles, 1)[:9]
+    dims = _dims(q, f, h, w, b1, b2, tiles, iters)
     _check(lib().monarch_attn_fwd_train(*ptrs, *dims, _dtype_code(q), sp, sn, _stream(stream)),
            "monarch_attn_fwd_train")
     return out
 
 
-def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, f, h, w, b1, b2, tiles, state, stream=None):
+def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, f, h, w, b1, b2, tiles, iters, state, stream=None):
     """dq, dk, dv <- gradients of sum(dout * out) (state from monarch_attn_fwd_train)."""
     ptrs = _tensors(q, k, v, out, q.dtype) + _tensors(dout, dq, dk, dv, q.dtype)
     sp, sn = _state(state)
-    dims = _dims(q, f, h, w, b1, b2, tiles, 1)[:9]
+    dims = _dims(q, f, h, w, b1, b2, tiles, iters)
     _check(lib().monarch_attn_bwd(*ptrs, *dims, _dtype_code(q), sp, sn, _stream(stream)),
            "monarch_attn_bwd")
     return dq, dk, dv

@@ -83,10 +83,12 @@ __device__ inline float dot_frags(const typename Elem<T>::frag (&a)[KS], const t
 // column a2; the rows a1 of the tile stream through LDS in steps of 64,
 // double-buffered by DMA:  dU[g,c1,a2] = sum_(a1 in g) L[a1,c1] dy_(a1,a2),
 // computed as dU^T = dy^T P (the forward's aggregation with dy as values).
-template <typename T, int D, int RW, int NW>
+// Keys of the L-step: the block means (BCAST) or, after two or more
+// iterations, the aggregated keys and entropies (bits) of the R-step before.
+template <typename T, int D, int RW, int NW, bool BCAST = true>
 __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, const T* __restrict__ dy,
-                                                    const T* __restrict__ kbar, const float* __restrict__ lse,
-                                                    T* __restrict__ du, LGeom p) {
+                                                    const T* __restrict__ kt, const float* __restrict__ h2,
+                                                    const float* __restrict__ lse, T* __restrict__ du, LGeom p) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -125,15 +127,17 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
   fetch(0, 0);
 
   typename E::frag bk[RW][KS];
+  float hb[RW];  // entropy bias of the lane's key block
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
     const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
+    const long long krow = BCAST ? static_cast<long long>(bh) * p.b1 + c1 : (gbase + c1) * p.b2 + a2;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int col = s * 32 + 8 * G;
-      bk[rt][s] = (c1 < p.b1 && col < D) ? E::load(kbar + (static_cast<long long>(bh) * p.b1 + c1) * D + col)
-                                         : E::zero();
+      bk[rt][s] = (c1 < p.b1 && col < D) ? E::load(kt + krow * D + col) : E::zero();
     }
+    hb[rt] = (BCAST || c1 >= p.b1) ? 0.0f : h2[krow];
   }
   f32x4 acc[NACC][2][RW];
 #pragma unroll
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
       for (int rt = 0; rt < RW; ++rt) {
         float w[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, -lr[j]));
+        for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, hb[rt] - lr[j]));
         if (tail) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) w[j] = r0 + 8 * G + j < nrows ? w[j] : 0.0f;
@@ -194,6 +198,10 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
 //   R = softmax_c2(s<Qh, k>), dR = <dU, v>, rho = <R, dR>, dz = R (dR - rho),
 //   G = s (K^T dz) / beta, e = <G, Qh>; stored: G, e and the row statistics
 //   (log-sum-exp of the logits in log2 units, and rho) for part 2.
+// MID (an R-step before the last, whose R feeds the next L-step as the keys
+// Kt = R k and entropies H = -sum R ln R): the cotangents are dKt and dH
+// (passed in du and dh), so dR = <dKt, k> - dH (ln R + 1); the constant
+// drops out of dz because R sums to 1, and keys past b2 (R = 0) get dR = 0.
 template <typename T, int D>
 inline size_t rside_bwd_lds_bytes(int b2p) {
   const int DK = D < 32 ? 32 : D;
@@ -225,9 +233,10 @@ __device__ inline void dma_block(T* tile, const T* src, int rows, int nvalid, in
 #define MONARCH_BRA_TB 2
 #endif
 
-template <typename T, int D, int NCP>
+template <typename T, int D, int NCP, bool MID = false>
 __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ qhat, const T* __restrict__ du,
+                                                  const float* __restrict__ dh,
                                                   const float* __restrict__ beta, T* __restrict__ gq,
                                                   float* __restrict__ ev, float* __restrict__ lser,
                                                   float* __restrict__ rho, BGeom p) {
@@ -241,7 +250,7 @@ __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int b2p = p.b2p;
   T* sK = reinterpret_cast<T*>(smem_raw);
-  T* sV = sK + b2p * DK;
+  T* sV = MID ? sK : sK + b2p * DK;  // MID: the cotangent pairs with k
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
   const int c1 = item % p.b1;
@@ -255,7 +264,7 @@ __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const
   auto qrow = [&](int g) { return ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2; };
 
   dma_block<T, D, DK>(sK, k + blk * D, b2p, p.b2, nw);
-  dma_block<T, D, DK>(sV, v + blk * D, b2p, p.b2, nw);
+  if (!MID) dma_block<T, D, DK>(sV, v + blk * D, b2p, p.b2, nw);
   typename E::frag bq[TB][KS], bd[TB][KS];
   auto load_rows_g = [&](int g0) {
 #pragma unroll
@@ -312,11 +321,17 @@ __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
       const float lse2 = mx + log2f(sum);
+      // MID: dH of this row in nats per log2 unit of the logit
+      const float dhl = MID ? (row_ok ? dh[row] * kLn2 : 0.0f) : 0.0f;
       float rh = 0.0f;
 #pragma unroll
       for (int cp = 0; cp < NCP; ++cp)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
+          if (MID) {
+            const bool valid = 32 * cp + 8 * G + j < p.b2;
+            DR[cp][j >> 2][j & 3] = valid ? DR[cp][j >> 2][j & 3] - dhl * (x[cp][j] - lse2) : 0.0f;
+          }
           x[cp][j] = fast_exp2(x[cp][j] - lse2);  // now R
           rh += x[cp][j] * DR[cp][j >> 2][j & 3];
         }
@@ -370,16 +385,27 @@ __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const
 // index, and
 //   dv[c1,c2] = sum_(g,a2) R dU,
 //   dk[c1,c2] = s sum_(g,a2) dz Qh + dKbar[c1] / b2   (dKbar already reduced).
+// With several iterations dk collects one term per R-step in the fp32
+// dk_acc, by MODE:
+//   kRbSingle  one iteration: dv and dk as above;
+//   kRbLast    last R-step: dv, and dk_acc = s sum dz Qh;
+//   kRbMid     an earlier R-step (du holds dKt, dh holds dH, dR as in
+//              kb_rside_a): dk_acc += s sum dz Qh + sum R dKt;
+//   kRbFirst   the first R-step (also MID): dk = dk_acc + s sum dz Qh +
+//              sum R dKt + dKbar / b2.
+constexpr int kRbSingle = 0, kRbLast = 1, kRbMid = 2, kRbFirst = 3;
 #ifndef MONARCH_BRB_BPS
 #define MONARCH_BRB_BPS 4
 #endif
 
-template <typename T, int D>
+template <typename T, int D, int MODE = kRbSingle>
 __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ qhat, const T* __restrict__ du,
                                                   const float* __restrict__ lser, const float* __restrict__ rho,
+                                                  const float* __restrict__ dh,
                                                   const float* __restrict__ dkbar, T* __restrict__ dk,
-                                                  T* __restrict__ dv, BGeom p) {
+                                                  float* __restrict__ dk_acc, T* __restrict__ dv, BGeom p) {
+  constexpr bool MID = MODE == kRbMid || MODE == kRbFirst;
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -391,6 +417,7 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
   __shared__ __align__(16) T sU[2][BPS][32 * DK];
   __shared__ __align__(16) float sLR[2][BPS][64];
   __shared__ __align__(16) float sRh[2][BPS][64];
+  __shared__ __align__(16) float sDh[MID ? 2 : 1][MID ? BPS : 1][64];
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
   const int c1 = item % p.b1;
@@ -417,6 +444,7 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
       dma_block<T, D, DK>(sU[buf][j], du + rb * D, 32, nvalid, nw);
       if (wave == 0) dma_floats64(sLR[buf][j], lser + rb, 1, nvalid);
       if (wave == nw - 1) dma_floats64(sRh[buf][j], rho + rb, 1, nvalid);
+      if (MID && wave == 1 % nw) dma_floats64(sDh[MID ? buf : 0][MID ? j : 0], dh + rb, 1, nvalid);
     }
   };
   fetch(0, 0);
@@ -426,7 +454,7 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
   for (int s = 0; s < KS; ++s) {
     const int col = 32 * s + 8 * G;
     bk2[0][s] = col < D ? E::load(k + (blk + c2c) * D + col) : E::zero();
-    bv2[0][s] = col < D ? E::load(v + (blk + c2c) * D + col) : E::zero();
+    bv2[0][s] = (!MID && col < D) ? E::load(v + (blk + c2c) * D + col) : E::zero();
   }
   f32x4 accv[NACC][2][1], acck[NACC][2][1];
 #pragma unroll
@@ -450,14 +478,20 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
       load_rows<T, DK, KS>(a, tq, 0, l16, G);
       logits<T, KS, 1>(Z, a, bk2);
       load_rows<T, DK, KS>(a, tu, 0, l16, G);
-      logits<T, KS, 1>(DR, a, bv2);
+      if (MID)
+        logits<T, KS, 1>(DR, a, bk2);  // <dKt, k>
+      else
+        logits<T, KS, 1>(DR, a, bv2);  // <dU, v>
       float r[8], z[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const bool ok = a0 + 8 * G + jj < p.b2;  // rows past b2 repeat the last row: weight 0
-        const float rr = fast_exp2(Z[jj >> 2][0][jj & 3] * p.c - sLR[cur][j][8 * G + jj]);
+        const float xl = Z[jj >> 2][0][jj & 3] * p.c - sLR[cur][j][8 * G + jj];  // log2 R
+        const float rr = fast_exp2(xl);
+        float dr = DR[jj >> 2][0][jj & 3];
+        if (MID) dr -= sDh[MID ? cur : 0][MID ? j : 0][8 * G + jj] * kLn2 * xl;
         r[jj] = ok ? rr : 0.0f;
-        z[jj] = ok ? rr * (DR[jj >> 2][0][jj & 3] - sRh[cur][j][8 * G + jj]) : 0.0f;
+        z[jj] = ok ? rr * (dr - sRh[cur][j][8 * G + jj]) : 0.0f;
       }
       const typename E::frag rf[1] = {E::pack(r)}, zf[1] = {E::pack(z)};
       typename E::frag vv[NACC][2];
@@ -470,22 +504,33 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
   }
 
   if (c2 < p.b2) {
-    store_rows<T, D, NACC, 1>(dv + (blk + c2) * D, accv, 0, 1.0f, G);
-    // dk = s * acck + dKbar[c1] / b2 (dkbar holds the sum already divided by b2)
+    const long long orow = (blk + c2) * D;
+    if (!MID) store_rows<T, D, NACC, 1>(dv + orow, accv, 0, 1.0f, G);
+    // this R-step's key gradient over the lane's d positions (32dp + 8G + j,
+    // or 4G + j when D == 16), combined as MODE says; dkbar holds the
+    // block-mean gradient already divided by b2
     const float* mk = dkbar + static_cast<long long>(item) * D;
-    if (D >= 32) {
+    constexpr int NJ = D >= 32 ? 8 : 4;
 #pragma unroll
-      for (int dp = 0; dp < NACC; ++dp) {
-        float o[8];
+    for (int dp = 0; dp < NACC; ++dp) {
+      const int d0 = D >= 32 ? 32 * dp + 8 * G : 4 * G;
+      float o[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = p.s * acck[dp][j >> 2][0][j & 3] + mk[32 * dp + 8 * G + j];
-        E::store8(dk + (blk + c2) * D + 32 * dp + 8 * G, o);
+      for (int j = 0; j < NJ; ++j) {
+        o[j] = p.s * acck[dp][j >> 2][0][j & 3];
+        if (MID) o[j] += accv[dp][j >> 2][0][j & 3];
+        if (MODE == kRbSingle || MODE == kRbFirst) o[j] += mk[d0 + j];
+        if (MODE == kRbMid || MODE == kRbFirst) o[j] += dk_acc[orow + d0 + j];
       }
-    } else {
-      float o[4];
+      if (MODE == kRbSingle || MODE == kRbFirst) {
+        if (D >= 32)
+          E::store8(dk + orow + d0, o);
+        else
+          E::store4(dk + orow + d0, o);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = p.s * acck[0][0][0][i] + mk[4 * G + i];
-      E::store4(dk + (blk + c2) * D + 4 * G, o);
+        for (int j = 0; j < NJ; ++j) dk_acc[orow + d0 + j] = o[j];
+      }
     }
   }
 }
@@ -495,14 +540,25 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
 // in column a2.  Pass 1 over c1: ghat = sum L G and eps = sum L e (a product
 // with e in every row of the A operand), then delta = <dy,y> + <q,ghat> - eps.
 // Pass 2 over c1: dl = L (<dy,U> + <q,G> - e - delta) and
-// dq = ghat + s sum_c1 dl Kbar; s*dl (as rounded for the product) is also
-// stored, [n][c1] with row stride ldl, for the key-mean gradient.
-template <typename T, int D, int RW, int NW>
+// dq = ghat + s sum_c1 dl Kt; s*dl (as rounded for the product) is also
+// stored, [n][c1] with row stride ldl, for the key gradient.
+// The L-step's keys Kt are the block means (BCAST, first iteration) or the
+// aggregated keys and entropies of the R-step before.  Without HAS_DY (an
+// earlier iteration, whose L feeds only the aggregation) the dy, y and U
+// terms are absent.  Over several iterations dq collects one term per L-step
+// in the fp32 dq_acc, by DQM:
+constexpr int kDqStore = 0;   // one iteration: dq = this term
+constexpr int kDqInit = 1;    // last L-step: dq_acc = this term
+constexpr int kDqAdd = 2;     // dq_acc += this term
+constexpr int kDqFinish = 3;  // first L-step: dq = dq_acc + this term
+template <typename T, int D, int RW, int NW, bool BCAST = true, bool HAS_DY = true, int DQM = kDqStore>
 __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, const T* __restrict__ dy,
-                                                    const T* __restrict__ y, const T* __restrict__ kbar,
+                                                    const T* __restrict__ y, const T* __restrict__ kt,
+                                                    const float* __restrict__ h2,
                                                     const float* __restrict__ lse, const T* __restrict__ u,
                                                     const T* __restrict__ gq, const float* __restrict__ ev,
                                                     float* __restrict__ delta, T* __restrict__ dq,
+                                                    float* __restrict__ dq_acc,
                                                     T* __restrict__ dlout, int ldl, LGeom p, float sc) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
@@ -514,9 +570,10 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   // double-buffered for bf16; f32 tiles are twice as large: one buffer
   constexpr int NB = sizeof(T) == 2 ? 2 : 1;
   __shared__ __align__(16) T sK[NB][kStep * DK];
-  __shared__ __align__(16) T sU[NB][kStep * DK];
+  __shared__ __align__(16) T sU[HAS_DY ? NB : 1][HAS_DY ? kStep * DK : 8];
   __shared__ __align__(16) T sG[NB][kStep * DK];
   __shared__ __align__(16) float sE[NB][kStep];
+  __shared__ __align__(16) float sH[BCAST ? 1 : NB][kStep];
 
   ColItem it(p, RB);
   if (it.nrows <= 0) return;
@@ -526,17 +583,18 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   const long long nstride = p.b2;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
-  const T* kb = kbar + static_cast<long long>(bh) * p.b1 * D;
+  const KeySrc<T, D, BCAST> ks(kt, h2, p, bh, g, a2);
   const long long cbase = (static_cast<long long>(bh) * p.t + g) * p.b1 * p.b2 + a2;  // (bh, g, c1 = 0, a2)
   const long long ustride = static_cast<long long>(p.b2) * D;
 
   const int nst = (p.b1 + kStep - 1) / kStep;
   auto fetch = [&](int st, int buf, bool with_u) {
     const int c1 = st * kStep;
-    Dma::issue(sK[buf], kb + static_cast<long long>(c1) * D, D, p.b1 - c1);
+    Dma::issue(sK[buf], ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
     Dma::issue(sG[buf], gq + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
-    if (with_u) Dma::issue(sU[buf], u + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
+    if (HAS_DY && with_u) Dma::issue(sU[buf], u + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
     if (wave == NW - 1) dma_floats64(sE[buf], ev + cbase + static_cast<long long>(c1) * p.b2, p.b2, p.b1 - c1);
+    if (!BCAST && wave == 0) dma_floats64(sH[buf], ks.h + static_cast<long long>(c1) * ks.hstride, ks.hstride, p.b1 - c1);
   };
   fetch(0, 0, false);
 
@@ -551,7 +609,7 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
     for (int s = 0; s < KS; ++s) {
       const int col = s * 32 + 8 * G;
       bq[rt][s] = (ok && col < D) ? E::load(q + row * D + col) : E::zero();
-      bdy[rt][s] = (ok && col < D) ? E::load(dy + row * D + col) : E::zero();
+      bdy[rt][s] = (HAS_DY && ok && col < D) ? E::load(dy + row * D + col) : E::zero();
     }
     nl[rt] = ok ? -lse[row] : 0.0f;
   }
@@ -579,16 +637,19 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
       load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
       f32x4 S[2][RW];
       logits<T, KS, RW>(S, a, bq);
-      float e8[8];
+      float e8[8], hb[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e8[j] = sE[cur][k0 + 8 * G + j];
+      for (int j = 0; j < 8; ++j) {
+        e8[j] = sE[cur][k0 + 8 * G + j];
+        hb[j] = BCAST ? 0.0f : sH[BCAST ? 0 : cur][k0 + 8 * G + j];
+      }
       const typename E::frag ef = E::pack(e8);
       typename E::frag pf[RW];
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         float w[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, nl[rt]));
+        for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, nl[rt] + hb[j]));
         if (tail) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) w[j] = c1_0 + 8 * G + j < p.b1 ? w[j] : 0.0f;
@@ -615,13 +676,16 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
     const int r = (wave * RW + rt) * 16 + l16;
     const bool ok = r < it.nrows;
     const long long row = hoff + n0 + (ok ? r : 0) * nstride;
-    typename E::frag by[KS];
+    float part = dot_acc_row<T, D, NACC, RW>(q + row * D, acc, rt, G);
+    if (HAS_DY) {
+      typename E::frag by[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int col = s * 32 + 8 * G;
-      by[s] = (ok && col < D) ? E::load(y + row * D + col) : E::zero();
+      for (int s = 0; s < KS; ++s) {
+        const int col = s * 32 + 8 * G;
+        by[s] = (ok && col < D) ? E::load(y + row * D + col) : E::zero();
+      }
+      part += dot_frags<T, KS>(bdy[rt], by);
     }
-    float part = dot_frags<T, KS>(bdy[rt], by) + dot_acc_row<T, D, NACC, RW>(q + row * D, acc, rt, G);
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     dlt[rt] = part - acce[rt][0];
@@ -643,27 +707,35 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
       f32x4 S[2][RW], X[2][RW];
       load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
       logits<T, KS, RW>(S, a, bq);
-      load_rows<T, DK, KS>(a, sU[cur], k0, l16, G);
-      logits<T, KS, RW>(X, a, bdy);  // <U, dy>
-      load_rows<T, DK, KS>(a, sG[cur], k0, l16, G);
-      products<T, KS, RW>(X, a, bq);  // + <G, q>
-      float e8[8];
+      if (HAS_DY) {
+        load_rows<T, DK, KS>(a, sU[HAS_DY ? cur : 0], k0, l16, G);
+        logits<T, KS, RW>(X, a, bdy);  // <U, dy>
+        load_rows<T, DK, KS>(a, sG[cur], k0, l16, G);
+        products<T, KS, RW>(X, a, bq);  // + <G, q>
+      } else {
+        load_rows<T, DK, KS>(a, sG[cur], k0, l16, G);
+        logits<T, KS, RW>(X, a, bq);  // <G, q>
+      }
+      float e8[8], hb[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e8[j] = sE[cur][k0 + 8 * G + j];
+      for (int j = 0; j < 8; ++j) {
+        e8[j] = sE[cur][k0 + 8 * G + j];
+        hb[j] = BCAST ? 0.0f : sH[BCAST ? 0 : cur][k0 + 8 * G + j];
+      }
       typename E::frag pf[RW];
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         float w[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          w[j] = sc * fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, nl[rt])) *
+          w[j] = sc * fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, nl[rt] + hb[j])) *
                  (X[j >> 2][rt][j & 3] - e8[j] - dlt[rt]);
         if (tail) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) w[j] = c1_0 + 8 * G + j < p.b1 ? w[j] : 0.0f;
         }
         pf[rt] = E::pack(w);
-        // s*dl of row n, keys c1_0 + 8G .. +7, for the key-mean product
+        // s*dl of row n, keys c1_0 + 8G .. +7, for the key gradient
         const int r = (wave * RW + rt) * 16 + l16;
         if (r < it.nrows) {
           T* dst = dlout + (hoff + n0 + r * nstride) * ldl + c1_0 + 8 * G;
@@ -689,7 +761,128 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   for (int rt = 0; rt < RW; ++rt) {
     const int r = (wave * RW + rt) * 16 + l16;
     if (r >= it.nrows) continue;
-    store_rows<T, D, NACC, RW>(dq + (hoff + n0 + r * nstride) * D, acc, rt, 1.0f, G);
+    const long long row = hoff + n0 + r * nstride;
+    if (DQM == kDqAdd || DQM == kDqFinish) {
+      // the lane's d positions, as store_rows lays them out
+      const float* src = dq_acc + row * D;
+#pragma unroll
+      for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+        for (int dt = 0; dt < (D >= 32 ? 2 : 1); ++dt)
+          acc[dp][dt][rt] += *reinterpret_cast<const f32x4*>(src + (D >= 32 ? 32 * dp + 8 * G + 4 * dt : 4 * G));
+    }
+    if (DQM == kDqInit || DQM == kDqAdd) {
+      float* dst = dq_acc + row * D;
+#pragma unroll
+      for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+        for (int dt = 0; dt < (D >= 32 ? 2 : 1); ++dt)
+          *reinterpret_cast<f32x4*>(dst + (D >= 32 ? 32 * dp + 8 * G + 4 * dt : 4 * G)) = acc[dp][dt][rt];
+    } else {
+      store_rows<T, D, NACC, RW>(dq + row * D, acc, rt, 1.0f, G);
+    }
+  }
+}
+
+// ------------------------------------------------------------- kb_dktil --
+// Key-side gradient of an L-step whose keys are the aggregated keys Kt and
+// entropies H of the R-step before (second and later iterations): the logit
+// s<q_n, Kt[g,c1,a2]> + H[g,c1,a2] of row n = (a1, a2), a1 in tile g, gives
+//   dKt[g,c1,a2] = sum_(a1 in g) (s dl)[n,c1] q_n,
+//   dH[g,c1,a2]  = sum_(a1 in g) dl[n,c1].
+// kb_du's column pass with the stored s*dl as the weights (transposed LDS
+// reads of its [rows][keys] block, as in kb_dkbar) instead of L; dH is a
+// product with an all-ones A operand, divided by s.
+template <typename T, int D, int RW, int NW>
+__global__ __launch_bounds__(NW * kWave) void kb_dktil(const T* __restrict__ q, const T* __restrict__ dl, int ldl,
+                                                       T* __restrict__ dkt, float* __restrict__ dh, LGeom p,
+                                                       float inv_s) {
+  using E = Elem<T>;
+  constexpr int DK = D < 32 ? 32 : D;
+  constexpr int CB = NW * RW * 16;
+  constexpr int NDP = D / 32;
+  constexpr int NACC = NDP > 0 ? NDP : 1;
+  using DmaQ = TileDma<T, D, DK, kStep, NW>;
+  using DmaL = TileDma<T, CB, CB, kStep, NW>;
+  __shared__ __align__(16) T sQ[2][kStep * DK];
+  __shared__ __align__(16) T sL[2][kStep * CB];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int cb = logical % p.nrb;
+  int rest = logical / p.nrb;
+  const int a2 = rest % p.b2;
+  rest /= p.b2;
+  const int g = rest % p.t;
+  const int bh = rest / p.t;
+  const int lo = tile_lo(g, p.b1r, p.t), hi = tile_lo(g + 1, p.b1r, p.t);
+  const int nrows = hi - lo;
+  const int nst = (nrows + kStep - 1) / kStep;
+
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int l16 = lane & 15, G = lane >> 4;
+  const long long hoff = static_cast<long long>(bh) * p.N;
+  const long long qstride = static_cast<long long>(p.b2) * D;
+  const long long lstride = static_cast<long long>(p.b2) * ldl;
+  const long long gbase = (static_cast<long long>(bh) * p.t + g) * p.b1;  // (bh, g, c1 = 0)
+
+  auto fetch = [&](int st, int buf) {
+    const long long n_first = hoff + static_cast<long long>(lo + st * kStep) * p.b2 + a2;
+    const int nvalid = nrows - st * kStep;
+    DmaQ::issue(sQ[buf], q + n_first * D, qstride, nvalid);
+    DmaL::issue(sL[buf], dl + n_first * ldl + cb * CB, lstride, nvalid);
+  };
+  fetch(0, 0);
+
+  float one8[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) one8[j] = 1.0f;
+  const typename E::frag ones = E::pack(one8);
+  f32x4 acc[NACC][2][RW];
+  f32x4 acch[RW];
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    acch[rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp) acc[dp][0][rt] = acc[dp][1][rt] = f32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nst) fetch(st + 1, cur ^ 1);
+#pragma unroll
+    for (int half = 0; half < kHalves; ++half) {
+      const int k0 = 32 * half;
+      const int r0 = st * kStep + k0;
+      if (r0 >= nrows) break;
+      const bool tail = r0 + 32 > nrows;
+      typename E::frag pf[RW];
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        pf[rt] = Tile<T, CB>::load_tr(sL[cur], k0, (wave * RW + rt) * 16, 4);
+        if (tail) {
+          // rows past the tile repeat its last row: zero their slots
+          float w[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = r0 + 8 * G + j < nrows ? E::slot(pf[rt], j) : 0.0f;
+          pf[rt] = E::pack(w);
+        }
+        acch[rt] = E::mma(ones, pf[rt], acch[rt]);
+      }
+      typename E::frag vv[NACC][2];
+      load_cols<T, D, DK, NACC>(vv, sQ[cur], k0);
+      weighted_sum<T, D, NACC, RW>(acc, vv, pf);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
+    if (c1 >= p.b1) continue;
+    const long long col = (gbase + c1) * p.b2 + a2;
+    store_rows<T, D, NACC, RW>(dkt + col * D, acc, rt, 1.0f, G);
+    if (G == 0) dh[col] = acch[rt][0] * inv_s;
   }
 }
 

@@ -28,6 +28,7 @@ typedef uint16_t bf16_t;  // bf16 storage
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kPosInf = __builtin_huge_valf();
 

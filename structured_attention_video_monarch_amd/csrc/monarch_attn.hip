@@ -196,11 +196,19 @@ const char* const kKernelNames[MONARCH_NUM_KERNELS] = {
     "kb_dq (backward: row pass, dq)", "kb_dkbar (backward: block-mean key gradient over tokens)",
     "kb_dkbar_reduce (backward: sum of the token-chunk partials)",
     "kb_rside_b (backward: dv and dk per key block)",
-    "k_objective (objective per head and the early-stop decision)"};
+    "k_objective (objective per head and the early-stop decision)",
+    "kb_dktil (backward: gradient of the aggregated keys and entropies per tile column)"};
+
+// The HIP runtime's last-error slot is per thread and shared with every other
+// user of the runtime in the process (a framework that loaded the same
+// runtime may leave an error there); clear it before a launch so that the
+// check after the launch sees only that launch's error.
+inline void clear_stale_error() { (void)hipGetLastError(); }
 
 // Launch wrapper: records events around the launch when profiling is on.
 template <typename F>
 hipError_t timed(int id, hipStream_t st, F&& launch) {
+  clear_stale_error();
   hipEvent_t a = nullptr, b = nullptr;
   if (g_prof.on) {
     a = g_prof.get();
@@ -220,7 +228,10 @@ hipError_t timed(int id, hipStream_t st, F&& launch) {
 // All kernels of one pass over `s.BH` heads starting at the given pointers.
 // Intermediates of one pass.  `u` receives R V (== qhat: written over the
 // aggregated queries); `beta` receives the column masses when not NULL (both
-// kept for the backward pass by the training forward).
+// kept for the backward pass by the training forward).  The *_it strides
+// (elements) place each iteration's log-sum-exps, masses, aggregated queries
+// and next keys/entropies in a copy of its own, as the backward pass through
+// several iterations needs; 0 writes every iteration over the same buffer.
 template <typename T>
 struct Bufs {
   T* kbar;
@@ -231,6 +242,14 @@ struct Bufs {
   float* hent;
   T* u;
   float* beta;
+  long long lse_it, qhat_it, beta_it, ktil_it, hent_it;
+  // views of iteration it (1-based); keys/entropies: those the R-step of
+  // iteration it writes (it < T), read by the L-step of it + 1
+  float* lse_of(int it) const { return lse + (it - 1) * lse_it; }
+  T* qhat_of(int it) const { return qhat + (it - 1) * qhat_it; }
+  float* beta_of(int it) const { return beta ? beta + (it - 1) * beta_it : nullptr; }
+  T* ktil_of(int it) const { return ktil ? ktil + (it - 1) * ktil_it : nullptr; }
+  float* hent_of(int it) const { return hent ? hent + (it - 1) * hent_it : nullptr; }
 };
 
 template <typename T>
@@ -260,12 +279,7 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
                     hipStream_t st, const Adaptive* ad = nullptr) {
   const float c = kLog2e / std::sqrt(static_cast<float>(D));
   T* kbar = bf.kbar;
-  float* lse = bf.lse;
-  T* qhat = bf.qhat;
-  T* ktil = bf.ktil;
-  float* hent = bf.hent;
   T* uout = bf.u == bf.qhat ? nullptr : bf.u;
-  float* beta = bf.beta;
   const int BH = static_cast<int>(s.BH), Nq = static_cast<int>(s.Nq);
   const int ngmax = (s.b1q + s.t - 1) / s.t;  // rows of the largest tile
   hipError_t err = hipSuccess;
@@ -317,6 +331,14 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds_last)));
   for (int it = 1; it <= s.T; ++it) {
     const bool first = it == 1, last = it == s.T;
+    float* lse = bf.lse_of(it);
+    T* qhat = bf.qhat_of(it);
+    float* beta = bf.beta_of(it);
+    // keys and entropies this L-step reads, and those this R-step writes
+    const T* ktil = first ? nullptr : bf.ktil_of(it - 1);
+    const float* hent = first ? nullptr : bf.hent_of(it - 1);
+    T* ktil_out = last ? nullptr : bf.ktil_of(it);
+    float* hent_out = last ? nullptr : bf.hent_of(it);
     if (first) {
       ok(timed(1, st, [&] {
         k_lse<T, D, kLseRW, kLseNW, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(q, kbar, nullptr, lse, lse_contig,
@@ -353,7 +375,8 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     }
     if (ad) {
       ok(timed(3, st, [&] {
-        k_rstep_adaptive<T, D><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, ktil, hent, ad->stop_at, it, rg);
+        k_rstep_adaptive<T, D><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, bf.ktil, bf.hent, ad->stop_at, it,
+                                                                       rg);
       }));
     } else if (last) {
       ok(timed(3, st, [&] {
@@ -361,17 +384,21 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
       }));
     } else {
       ok(timed(3, st, [&] {
-        k_rstep<T, D, false><<<r_grid, r_threads, r_lds_mid, st>>>(k, v, qhat, ktil, hent, nullptr, rg);
+        k_rstep<T, D, false><<<r_grid, r_threads, r_lds_mid, st>>>(k, v, qhat, ktil_out, hent_out, nullptr, rg);
       }));
     }
   }
+  const float* lse_last = bf.lse_of(s.T);
   if (s.T == 1) {
     ok(timed(4, st, [&] {
-      k_apply<T, D, kAppRW, kAppNW, true><<<app_grid, kAppNW * kWave, 0, st>>>(q, kbar, nullptr, lse, bf.u, out, app);
+      k_apply<T, D, kAppRW, kAppNW, true><<<app_grid, kAppNW * kWave, 0, st>>>(q, kbar, nullptr, lse_last, bf.u, out,
+                                                                              app);
     }));
   } else {
+    const T* kt = bf.ktil_of(s.T - 1);
+    const float* ht = bf.hent_of(s.T - 1);
     ok(timed(4, st, [&] {
-      k_apply<T, D, kAppRW, kAppNW, false><<<app_grid, kAppNW * kWave, 0, st>>>(q, ktil, hent, lse, bf.u, out, app);
+      k_apply<T, D, kAppRW, kAppNW, false><<<app_grid, kAppNW * kWave, 0, st>>>(q, kt, ht, lse_last, bf.u, out, app);
     }));
   }
   return err;
@@ -474,6 +501,7 @@ int fwd_adaptive(const void* q, const void* k, const void* v, void* out, const S
   const Workspace w = layout(s, elem, true);
   Adaptive ad{iters_used, reinterpret_cast<double*>(ws + fprev_off), tol};
   hipError_t e = hipSuccess;
+  clear_stale_error();
   k_fill_int<<<static_cast<unsigned>((s.BH + 255) / 256), 256, 0, st>>>(iters_used, static_cast<int>(s.BH), 0);
   e = hipGetLastError();
   auto go = [&](auto tag) {
@@ -501,44 +529,63 @@ int fwd_adaptive(const void* q, const void* k, const void* v, void* out, const S
 }
 
 // ------------------------------------------------------------ training --
-// Training state: what the backward pass reads from the one-iteration
-// forward, for all heads of the call.
+// Training state: what the backward pass reads from the forward, for all
+// heads of the call: the block means, and per iteration i = 1..T the L-row
+// log-sum-exps, the column masses and the aggregated queries; U = R V of the
+// last R-step; for i < T the keys and entropies the R-step of i hands to the
+// next L-step.  Each per-iteration array holds T (or T - 1) copies, one
+// aligned block apart.
 struct TrainState {
-  size_t kbar, knorm, lse, beta, qhat, u, total;
+  size_t kbar, knorm, lse, beta, qhat, u, ktil, hent, total;
+  size_t lse_blk, beta_blk, qhat_blk, hent_blk;  // bytes per iteration copy
 };
 
 TrainState train_layout(const Shape& s, size_t elem) {
   TrainState t{};
   const size_t BH = static_cast<size_t>(s.BH), N = static_cast<size_t>(s.N), d = static_cast<size_t>(s.d);
   const size_t tN = static_cast<size_t>(s.t) * N;
+  const size_t T = static_cast<size_t>(s.T);
+  t.lse_blk = align_up(BH * N * sizeof(float));
+  t.beta_blk = align_up(BH * tN * sizeof(float));
+  t.qhat_blk = align_up(BH * tN * d * elem);
+  t.hent_blk = t.beta_blk;
   size_t off = 0;
   t.kbar = off;
   off += align_up(BH * s.b1 * d * elem);
   t.knorm = off;
   off += align_up(BH * s.b1 * sizeof(float));
   t.lse = off;
-  off += align_up(BH * N * sizeof(float));
+  off += T * t.lse_blk;
   t.beta = off;
-  off += align_up(BH * tN * sizeof(float));
+  off += T * t.beta_blk;
   t.qhat = off;
-  off += align_up(BH * tN * d * elem);
+  off += T * t.qhat_blk;
   t.u = off;
-  off += align_up(BH * tN * d * elem);
+  off += t.qhat_blk;
+  t.ktil = off;
+  off += (T - 1) * t.qhat_blk;
+  t.hent = off;
+  off += (T - 1) * t.hent_blk;
   t.total = off;
   return t;
 }
 
 template <typename T>
-Bufs<T> train_bufs(unsigned char* st, const TrainState& t) {
+Bufs<T> train_bufs(unsigned char* st, const TrainState& t, int iters) {
   Bufs<T> b{};
   b.kbar = reinterpret_cast<T*>(st + t.kbar);
   b.knorm = reinterpret_cast<float*>(st + t.knorm);
   b.lse = reinterpret_cast<float*>(st + t.lse);
   b.qhat = reinterpret_cast<T*>(st + t.qhat);
-  b.ktil = nullptr;
-  b.hent = nullptr;
+  b.ktil = iters > 1 ? reinterpret_cast<T*>(st + t.ktil) : nullptr;
+  b.hent = iters > 1 ? reinterpret_cast<float*>(st + t.hent) : nullptr;
   b.u = reinterpret_cast<T*>(st + t.u);
   b.beta = reinterpret_cast<float*>(st + t.beta);
+  b.lse_it = static_cast<long long>(t.lse_blk / sizeof(float));
+  b.beta_it = static_cast<long long>(t.beta_blk / sizeof(float));
+  b.qhat_it = static_cast<long long>(t.qhat_blk / sizeof(T));
+  b.ktil_it = b.qhat_it;
+  b.hent_it = static_cast<long long>(t.hent_blk / sizeof(float));
   return b;
 }
 
@@ -572,17 +619,21 @@ template <> struct BwdCfg<float> {
   static constexpr int kDuRW = 1, kDuNW = 4, kDqRW = 1, kDqNW = 4, kGmRW = 2, kGmNW = 4;
 };
 
-// Backward workspace (allocated per call, stream-ordered).
+// Backward workspace (allocated per call, stream-ordered).  With several
+// iterations `du` also carries dKt of each earlier R-step, `dh` its dH, and
+// dq, dk add up in fp32 (dqacc, dkacc).
 struct BwdWorkspace {
   int ldl;          // row stride of the stored s*dl (keys padded to the product's key block)
   int nsplit, chunk;  // split of the tokens in the key-mean product
-  size_t du, gq, ev, lser, rho, delta, dl, part, dkbar, total;
+  size_t du, gq, ev, lser, rho, delta, dl, part, dkbar, dh, dqacc, dkacc, total;
 };
 
 template <typename T>
 BwdWorkspace bwd_layout_t(const Shape& s) {
   using C = BwdCfg<T>;
   constexpr int cb = C::kGmRW * C::kGmNW * 16;
+  // kb_dktil reads whole blocks of its own key width from the padded rows
+  static_assert(cb % (C::kDuRW * C::kDuNW * 16) == 0, "key blocks of kb_dktil must tile ldl");
   BwdWorkspace w{};
   const size_t elem = sizeof(T);
   const long long ncb = (s.b1 + cb - 1) / cb;
@@ -617,6 +668,14 @@ BwdWorkspace bwd_layout_t(const Shape& s) {
   off += align_up(BH * static_cast<size_t>(w.nsplit) * s.b1 * d * sizeof(float));
   w.dkbar = off;
   off += align_up(BH * static_cast<size_t>(s.b1) * d * sizeof(float));
+  if (s.T > 1) {
+    w.dh = off;
+    off += align_up(BH * tN * sizeof(float));
+    w.dqacc = off;
+    off += align_up(BH * N * d * sizeof(float));
+    w.dkacc = off;
+    off += align_up(BH * N * d * sizeof(float));
+  }
   w.total = off;
   return w;
 }
@@ -627,6 +686,12 @@ BwdWorkspace bwd_layout(const Shape& s, size_t elem) {
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
+// Reverse through the iterations, last to first.  Per iteration i:
+//   R-step part 1 (G, e, row statistics), row pass (dq term, s*dl),
+//   R-step part 2 (dv at i = T; the dk terms), then the key side of the
+//   L-step: dKt, dH of the R-step before (i > 1) or the block-mean gradient
+//   (i = 1).  The last iteration's cotangents come from dy through the apply
+//   (dU); an earlier one's from the next L-step (dKt, dH).
 template <typename T, int D>
 hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* dout, T* dq, T* dk,
                    T* dv, const Shape& s, const Bufs<T>& bf, unsigned char* ws, const BwdWorkspace& w,
@@ -643,73 +708,130 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   T* dl = reinterpret_cast<T*>(ws + w.dl);
   float* part = reinterpret_cast<float*>(ws + w.part);
   float* dkbar = reinterpret_cast<float*>(ws + w.dkbar);
+  float* dh = s.T > 1 ? reinterpret_cast<float*>(ws + w.dh) : nullptr;
+  float* dqacc = s.T > 1 ? reinterpret_cast<float*>(ws + w.dqacc) : nullptr;
+  float* dkacc = s.T > 1 ? reinterpret_cast<float*>(ws + w.dkacc) : nullptr;
   const int BH = static_cast<int>(s.BH), N = static_cast<int>(s.N);
   const int ngmax = (s.b1 + s.t - 1) / s.t;
+  const int T_ = s.T;
   hipError_t err = hipSuccess;
   auto ok = [&](hipError_t e) {
     if (e != hipSuccess && err == hipSuccess) err = e;
   };
+  // keys and entropies of the L-step of iteration i
+  auto keys_of = [&](int i) -> const T* { return i == 1 ? bf.kbar : bf.ktil_of(i - 1); };
+  auto ent_of = [&](int i) -> const float* { return i == 1 ? nullptr : bf.hent_of(i - 1); };
 
-  // dU = L^T dy per tile column
-  {
-    constexpr int cb = C::kDuRW * C::kDuNW * 16;
-    LGeom lg{BH, N, s.b1, s.b1, s.b2, s.t, (s.b1 + cb - 1) / cb, c};
-    const unsigned grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lg.nrb);
-    ok(timed(5, st, [&] {
-      kb_du<T, D, C::kDuRW, C::kDuNW><<<grid, C::kDuNW * kWave, 0, st>>>(q, dout, bf.kbar, bf.lse, du, lg);
-    }));
-  }
-  // R-step backward per key block, part 1: G, e and the R row statistics
+  constexpr int du_cb = C::kDuRW * C::kDuNW * 16;
+  const LGeom col_geom{BH, N, s.b1, s.b1, s.b2, s.t, (s.b1 + du_cb - 1) / du_cb, c};
+  const unsigned col_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * col_geom.nrb);
+  // dU = L^T dy per tile column (L of the last L-step)
+  ok(timed(5, st, [&] {
+    if (T_ == 1)
+      kb_du<T, D, C::kDuRW, C::kDuNW, true><<<col_grid, C::kDuNW * kWave, 0, st>>>(q, dout, bf.kbar, nullptr,
+                                                                                  bf.lse_of(1), du, col_geom);
+    else
+      kb_du<T, D, C::kDuRW, C::kDuNW, false><<<col_grid, C::kDuNW * kWave, 0, st>>>(
+          q, dout, keys_of(T_), ent_of(T_), bf.lse_of(T_), du, col_geom);
+  }));
+
   const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
   const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
-  {
-    const size_t lds = rside_bwd_lds_bytes<T, D>(bg.b2p);
-    auto launch = [&](auto kern) {
-      if (lds > 65536)
-        ok(hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(lds)));
-      ok(timed(6, st, [&] {
-        kern<<<r_grid, r_threads, lds, st>>>(k, v, bf.qhat, du, bf.beta, gq, ev, lser, rho, bg);
+  const size_t ra_lds = rside_bwd_lds_bytes<T, D>(bg.b2p);
+  constexpr int dq_rows = C::kDqRW * C::kDqNW * 16;
+  const LGeom row_geom{BH, N, s.b1, s.b1, s.b2, s.t, (ngmax + dq_rows - 1) / dq_rows, c};
+  const unsigned row_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * row_geom.nrb);
+
+  for (int i = T_; i >= 1; --i) {
+    const bool last = i == T_, first = i == 1;
+    const T* qh = bf.qhat_of(i);
+    const float* bt = bf.beta_of(i);
+    // R-step backward per key block, part 1: G, e and the R row statistics
+    {
+      auto launch = [&](auto kern) {
+        if (ra_lds > 65536)
+          ok(hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(ra_lds)));
+        ok(timed(6, st, [&] {
+          kern<<<r_grid, r_threads, ra_lds, st>>>(k, v, qh, du, dh, bt, gq, ev, lser, rho, bg);
+        }));
+      };
+      const int ncp = bg.b2p / 32;
+      if (last) {
+        switch (ncp) {
+          case 1: launch(&kb_rside_a<T, D, 1, false>); break;
+          case 2: launch(&kb_rside_a<T, D, 2, false>); break;
+          case 3: launch(&kb_rside_a<T, D, 3, false>); break;
+          default: launch(&kb_rside_a<T, D, 4, false>); break;
+        }
+      } else {
+        switch (ncp) {
+          case 1: launch(&kb_rside_a<T, D, 1, true>); break;
+          case 2: launch(&kb_rside_a<T, D, 2, true>); break;
+          case 3: launch(&kb_rside_a<T, D, 3, true>); break;
+          default: launch(&kb_rside_a<T, D, 4, true>); break;
+        }
+      }
+    }
+    // row pass: this L-step's dq term and the stored s*dl
+    {
+      auto launch = [&](auto kern) {
+        ok(timed(7, st, [&] {
+          kern<<<row_grid, C::kDqNW * kWave, 0, st>>>(q, dout, out, keys_of(i), ent_of(i), bf.lse_of(i), bf.u, gq,
+                                                        ev, delta, dq, dqacc, dl, w.ldl, row_geom, sc);
+        }));
+      };
+      constexpr int RW = C::kDqRW, NW = C::kDqNW;
+      if (T_ == 1)
+        launch(&kb_dq<T, D, RW, NW, true, true, kDqStore>);
+      else if (last)
+        launch(&kb_dq<T, D, RW, NW, false, true, kDqInit>);
+      else if (first)
+        launch(&kb_dq<T, D, RW, NW, true, false, kDqFinish>);
+      else
+        launch(&kb_dq<T, D, RW, NW, false, false, kDqAdd>);
+    }
+    if (first) {
+      // block-mean key gradient: partial sums over chunks of tokens, then
+      // their sum spread over the b2 keys of each block
+      constexpr int cb = C::kGmRW * C::kGmNW * 16;
+      const int ncb = w.ldl / cb;
+      const unsigned grid = static_cast<unsigned>(s.BH * ncb * w.nsplit);
+      ok(timed(8, st, [&] {
+        kb_dkbar<T, D, C::kGmRW, C::kGmNW><<<grid, C::kGmNW * kWave, 0, st>>>(q, dl, w.ldl, part, BH, N, s.b1, ncb,
+                                                                             w.nsplit, w.chunk);
       }));
-    };
-    switch (bg.b2p / 32) {
-      case 1: launch(&kb_rside_a<T, D, 1>); break;
-      case 2: launch(&kb_rside_a<T, D, 2>); break;
-      case 3: launch(&kb_rside_a<T, D, 3>); break;
-      default: launch(&kb_rside_a<T, D, 4>); break;
+      const long long threads = s.BH * s.b1 * (D / 4);
+      const unsigned rgrid = static_cast<unsigned>((threads + 255) / 256);
+      ok(timed(9, st, [&] { kb_dkbar_reduce<D><<<rgrid, 256, 0, st>>>(part, dkbar, BH, s.b1, s.b2, w.nsplit); }));
+    }
+    // R-step backward per key block, part 2: dv (last R-step) and the dk terms
+    {
+      auto launch = [&](auto kern) {
+        ok(timed(10, st, [&] {
+          kern<<<r_grid, r_threads, 0, st>>>(k, v, qh, du, lser, rho, dh, dkbar, dk, dkacc, dv, bg);
+        }));
+      };
+      if (T_ == 1)
+        launch(&kb_rside_b<T, D, kRbSingle>);
+      else if (last)
+        launch(&kb_rside_b<T, D, kRbLast>);
+      else if (first)
+        launch(&kb_rside_b<T, D, kRbFirst>);
+      else
+        launch(&kb_rside_b<T, D, kRbMid>);
+    }
+    // key side of an L-step on aggregated keys: dKt and dH of the R-step
+    // before, into du and dh (their last readers, this iteration's R-step
+    // kernels, have run)
+    if (!first) {
+      ok(timed(12, st, [&] {
+        kb_dktil<T, D, C::kDuRW, C::kDuNW><<<col_grid, C::kDuNW * kWave, 0, st>>>(q, dl, w.ldl, du, dh, col_geom,
+                                                                                 1.0f / sc);
+      }));
     }
   }
-  // row pass: delta, dq and the stored s*dl
-  {
-    constexpr int rows = C::kDqRW * C::kDqNW * 16;
-    LGeom lg{BH, N, s.b1, s.b1, s.b2, s.t, (ngmax + rows - 1) / rows, c};
-    const unsigned grid = static_cast<unsigned>(s.BH * s.t * s.b2 * lg.nrb);
-    ok(timed(7, st, [&] {
-      kb_dq<T, D, C::kDqRW, C::kDqNW><<<grid, C::kDqNW * kWave, 0, st>>>(
-          q, dout, out, bf.kbar, bf.lse, bf.u, gq, ev, delta, dq, dl, w.ldl, lg, sc);
-    }));
-  }
-  // block-mean key gradient: partial sums over chunks of tokens
-  {
-    constexpr int cb = C::kGmRW * C::kGmNW * 16;
-    const int ncb = w.ldl / cb;
-    const unsigned grid = static_cast<unsigned>(s.BH * ncb * w.nsplit);
-    ok(timed(8, st, [&] {
-      kb_dkbar<T, D, C::kGmRW, C::kGmNW><<<grid, C::kGmNW * kWave, 0, st>>>(q, dl, w.ldl, part, BH, N, s.b1, ncb,
-                                                                           w.nsplit, w.chunk);
-    }));
-  }
-  // sum of the partials, spread over the b2 keys of each block
-  {
-    const long long threads = s.BH * s.b1 * (D / 4);
-    const unsigned grid = static_cast<unsigned>((threads + 255) / 256);
-    ok(timed(9, st, [&] { kb_dkbar_reduce<D><<<grid, 256, 0, st>>>(part, dkbar, BH, s.b1, s.b2, w.nsplit); }));
-  }
-  // R-step backward per key block, part 2: dv and dk
-  ok(timed(10, st, [&] {
-    kb_rside_b<T, D><<<r_grid, r_threads, 0, st>>>(k, v, bf.qhat, du, lser, rho, dkbar, dk, dv, bg);
-  }));
   return err;
 }
 
@@ -720,7 +842,6 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int check_train(const Shape& s, size_t elem, const void* state, size_t state_bytes) {
   if (elem == 0) return MONARCH_EINVAL;
-  if (s.T != 1) return MONARCH_EINVAL;
   const TrainState t = train_layout(s, elem);
   if (!state || state_bytes < t.total) return MONARCH_ENOMEM;
   if (reinterpret_cast<uintptr_t>(state) % kAlign != 0) return MONARCH_EINVAL;
@@ -742,7 +863,7 @@ int fwd_train(const void* q, const void* k, const void* v, void* out, const Shap
   hipError_t e = hipSuccess;
   auto go = [&](auto tag) {
     using T = decltype(tag);
-    const Bufs<T> b = train_bufs<T>(sp, t);
+    const Bufs<T> b = train_bufs<T>(sp, t, s.T);
     const T* tq = static_cast<const T*>(q);
     const T* tk = static_cast<const T*>(k);
     const T* tv = static_cast<const T*>(v);
@@ -797,7 +918,7 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
   unsigned char* sp = static_cast<unsigned char*>(state);
   auto go = [&](auto tag) {
     using T = decltype(tag);
-    const Bufs<T> b = train_bufs<T>(sp, t);
+    const Bufs<T> b = train_bufs<T>(sp, t, s.T);
     const T* a[5] = {static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                      static_cast<const T*>(out), static_cast<const T*>(dout)};
     T* g3[3] = {static_cast<T*>(dq), static_cast<T*>(dk), static_cast<T*>(dv)};
@@ -901,26 +1022,26 @@ int monarch_attn_fwd_kv_ws(const void* q, const void* k, const void* v, void* ou
 }
 
 size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d, int b1, int b2,
-                                      int tiles, int dtype) {
+                                      int tiles, int iters, int dtype) {
   const size_t elem = elem_size(dtype);
   if (elem == 0) return 0;
-  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, 1);
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   static const char dummy[4] = {0};
   if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
   return train_layout(s, elem).total;
 }
 
 int monarch_attn_fwd_train(const void* q, const void* k, const void* v, void* out, int B, int H,
-                           int f, int h, int w, int d, int b1, int b2, int tiles, int dtype,
+                           int f, int h, int w, int d, int b1, int b2, int tiles, int iters, int dtype,
                            void* state, size_t state_bytes, void* stream) {
-  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, 1);
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   return fwd_train(q, k, v, out, s, dtype, state, state_bytes, static_cast<hipStream_t>(stream));
 }
 
 int monarch_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                      void* dq, void* dk, void* dv, int B, int H, int f, int h, int w, int d, int b1,
-                     int b2, int tiles, int dtype, void* state, size_t state_bytes, void* stream) {
-  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, 1);
+                     int b2, int tiles, int iters, int dtype, void* state, size_t state_bytes, void* stream) {
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   return bwd(q, k, v, out, dout, dq, dk, dv, s, dtype, state, state_bytes,
              static_cast<hipStream_t>(stream));
 }

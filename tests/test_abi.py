@@ -101,7 +101,7 @@ def _train_ptrs(n):
     return [ctypes.c_void_p((i + 1) * _GAP) for i in range(n)]
 
 
-def _bwd(state_bytes=None, B=1, H=2, f=3, h=30, w=52, d=128, b1=90, b2=52, t=1, dtype=0, null=None,
+def _bwd(state_bytes=None, B=1, H=2, f=3, h=30, w=52, d=128, b1=90, b2=52, t=1, T=1, dtype=0, null=None,
          alias=None):
     p = _train_ptrs(9)  # q k v out dout dq dk dv state
     if null is not None:
@@ -109,17 +109,20 @@ def _bwd(state_bytes=None, B=1, H=2, f=3, h=30, w=52, d=128, b1=90, b2=52, t=1, 
     if alias is not None:
         p[alias[0]] = p[alias[1]]
     if state_bytes is None:
-        state_bytes = M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, dtype)
-    return M.lib().monarch_attn_bwd(*p[:8], B, H, f, h, w, d, b1, b2, t, dtype, p[8], state_bytes, None)
+        state_bytes = M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, T, dtype)
+    return M.lib().monarch_attn_bwd(*p[:8], B, H, f, h, w, d, b1, b2, t, T, dtype, p[8], state_bytes, None)
 
 
-def test_train_state_bytes_formula():
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_train_state_bytes_formula(T):
     B, H, f, h, w, d, b1, b2, t = 1, 40, 21, 45, 80, 128, 945, 80, 4
     N, BH, e = f * h * w, B * H, 2
-    expect = (_align(BH * b1 * d * e) + _align(BH * b1 * 4) + _align(BH * N * 4) + _align(BH * t * N * 4)
-              + 2 * _align(BH * t * N * d * e))
-    assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, 0) == expect
-    assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1 + 1, b2, t, 0) == 0
+    per_iter = _align(BH * N * 4) + _align(BH * t * N * 4) + _align(BH * t * N * d * e)
+    expect = (_align(BH * b1 * d * e) + _align(BH * b1 * 4) + T * per_iter + _align(BH * t * N * d * e)
+              + (T - 1) * (_align(BH * t * N * d * e) + _align(BH * t * N * 4)))
+    assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, T, 0) == expect
+    assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1 + 1, b2, t, T, 0) == 0
+    assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, 0, 0) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -133,14 +136,18 @@ def test_train_state_bytes_formula():
     (dict(b1=91), M.MONARCH_EINVAL),
     (dict(d=48), M.MONARCH_EUNSUPPORTED),
     (dict(f=2, h=3, w=130, b1=6, b2=130), M.MONARCH_EUNSUPPORTED),
+    (dict(T=0, state_bytes=1 << 30), M.MONARCH_EINVAL),
+    (dict(T=2, state_bytes="T1"), M.MONARCH_ENOMEM),  # state of a one-iteration forward
 ])
 def test_bwd_bad_arguments_rejected_before_any_gpu_call(kw, status):
+    if kw.get("state_bytes") == "T1":
+        kw = dict(kw, state_bytes=M.monarch_attn_train_state_bytes(1, 2, 3, 30, 52, 128, 90, 52, 1, 1, 0))
     assert _bwd(**kw) == status
 
 
 def test_fwd_train_rejects_small_state():
     p = _train_ptrs(5)
-    rc = M.lib().monarch_attn_fwd_train(*p[:4], 1, 2, 3, 30, 52, 128, 90, 52, 1, 0, p[4], 256, None)
+    rc = M.lib().monarch_attn_fwd_train(*p[:4], 1, 2, 3, 30, 52, 128, 90, 52, 1, 1, 0, p[4], 256, None)
     assert rc == M.MONARCH_ENOMEM
 
 

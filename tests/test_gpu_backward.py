@@ -36,12 +36,14 @@ def run_train(wl, x, dyx):
     q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
     dy = to_device(dyx, "dy", wl.dtype)
     dt = M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32
-    nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles, dt)
+    nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles, wl.iters,
+                                          dt)
     state = torch.empty(nb, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
-    M.monarch_attn_fwd_train(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, state)
+    args = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
+    M.monarch_attn_fwd_train(q, k, v, out, *args, state)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, state)
+    M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, *args, state)
     torch.cuda.synchronize()
     return [to_host(t) for t in (out, dq, dk, dv)]
 
@@ -51,10 +53,10 @@ def rel_errors(got, ref):
     return float(d.max() / max(np.abs(ref).max(), 1e-30)), float(d.mean() / max(np.abs(ref).mean(), 1e-30))
 
 
-def compare_grad(wl, seed=0, heads=None, label=""):
-    wl = wl.with_(iters=1)
+def compare_grad(wl, seed=0, heads=None, label="", iters=1):
+    wl = wl.with_(iters=iters)
     say(f"[case] bwd {label or wl.name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} blocks=({wl.b1},{wl.b2}) "
-        f"t={wl.tiles} {wl.dtype} seed={seed}")
+        f"t={wl.tiles} T={wl.iters} {wl.dtype} seed={seed}")
     x = I.make_inputs(wl, seed)
     dyx = I.make_cotangent(wl, seed)
     y, dq, dk, dv = run_train(wl, x, dyx)
@@ -65,7 +67,7 @@ def compare_grad(wl, seed=0, heads=None, label=""):
     for b in range(wl.B):
         for h in heads:
             refs = oracle.monarch_head_grad(x["q"][b, h], x["k"][b, h], x["v"][b, h], dyx["dy"][b, h],
-                                            wl.b1, wl.b2, wl.tiles)
+                                            wl.b1, wl.b2, wl.tiles, wl.iters)
             for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
                 mx, mean = rel_errors(got[b, h], ref)
                 w = worst.get(name, (0.0, 0.0))
@@ -74,7 +76,7 @@ def compare_grad(wl, seed=0, heads=None, label=""):
                     assert mx <= BF16_REL_MAX and mean <= BF16_REL_MEAN, (name, b, h, mx, mean)
                 else:
                     assert mx <= F32_REL_MAX, (name, b, h, mx)
-    say(f"[ok] bwd {label or wl.name}: " + ", ".join(
+    say(f"[ok] bwd {label or wl.name} T={wl.iters}: " + ", ".join(
         f"{n} rel-max {w[0]:.2e} rel-mean {w[1]:.2e}" for n, w in worst.items()))
     return worst
 
@@ -125,17 +127,18 @@ def test_bwd_edge_shapes(case):
     compare_grad(I.Workload(name, B, H, d, f, h, w, b1, b2, t, 1, dt), seed=3, label=name)
 
 
-def test_train_forward_equals_forward_and_bwd_is_deterministic():
+@pytest.mark.parametrize("iters", [1, 2, 3])
+def test_train_forward_equals_forward_and_bwd_is_deterministic(iters):
     import structured_attention_video_monarch_amd as M
     wl = I.get_workload("clip480p_spikes_t4_T1").with_(H=2)
     x = I.make_inputs(wl, 1)
     dyx = I.make_cotangent(wl, 1)
     q, k, v = (to_device(x, n, "bf16") for n in "qkv")
     dy = to_device(dyx, "dy", "bf16")
-    args = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles)
+    args = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, iters)
     ref = torch.empty_like(q)
-    M.monarch_attn_fwd(q, k, v, ref, *args, 1)
-    nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles)
+    M.monarch_attn_fwd(q, k, v, ref, *args)
+    nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles, iters)
     state = torch.empty(nb, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
     M.monarch_attn_fwd_train(q, k, v, out, *args, state)
@@ -147,3 +150,41 @@ def test_train_forward_equals_forward_and_bwd_is_deterministic():
     assert torch.equal(out, ref)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+# ---- several iterations: the reverse runs back through every R-step and
+# L-step (keys and entropies of each R-step feed the next L-step)
+@pytest.mark.parametrize("t,T", [(1, 2), (2, 2), (4, 2), (2, 3), (4, 3)])
+def test_bwd_iters_tiny_f32(t, T):
+    compare_grad(I.get_workload("tiny").with_(tiles=t), label=f"tiny-t{t}", iters=T)
+
+
+@pytest.mark.parametrize("T", [2, 3])
+def test_bwd_iters_chunk480p_f32(T):
+    compare_grad(I.get_workload("chunk480p").with_(H=2, dtype="f32"), label="chunk480p-f32", iters=T)
+
+
+@pytest.mark.parametrize("T", [2, 3])
+def test_bwd_iters_chunk480p_bf16(T):
+    compare_grad(I.get_workload("chunk480p"), heads=[0, 11], iters=T)
+
+
+def test_bwd_iters_clip480p_spikes_bf16():
+    compare_grad(I.get_workload("clip480p_spikes_t4_T1"), heads=[0, 11], iters=2)
+
+
+def test_bwd_iters_latent720p_bf16():
+    compare_grad(I.get_workload("latent720p"), heads=[0, 39], iters=2)
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_bwd_iters_edge_shapes(case):
+    name, B, H, d, f, h, w, b1, b2, t, dt = case
+    compare_grad(I.Workload(name, B, H, d, f, h, w, b1, b2, t, 1, dt), seed=5, label=name, iters=2)
+
+
+@pytest.mark.parametrize("case", [c for c in EDGE if c[0] in ("odd_blocks", "b2_17_d16", "ragged_f32",
+                                                               "one_row_tiles")], ids=lambda c: c[0])
+def test_bwd_three_iters_edge_shapes(case):
+    name, B, H, d, f, h, w, b1, b2, t, dt = case
+    compare_grad(I.Workload(name, B, H, d, f, h, w, b1, b2, t, 1, dt), seed=6, label=name, iters=3)
