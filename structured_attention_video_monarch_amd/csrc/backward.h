@@ -377,12 +377,12 @@ __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const
 }
 
 // ------------------------------------------------------------- kb_rside_b --
-// Key-block pass, part 2: one workgroup per (bh, c1), each wave owning 16
-// keys c2 (K and V rows as B operands); Qh and dU stream through LDS in
-// blocks of 32 rows a2, tile after tile, BPS blocks per double-buffered DMA
-// stage.  R and dz
-// are recomputed from the stored row statistics with a2 as the contraction
-// index, and
+// Key-block pass, part 2: one workgroup per (bh, c1), each wave owning
+// RW*16 keys c2 (K and V rows as B operands).  The rows (g, a2) of all tiles
+// stream through LDS as one sequence of t*b2 rows in blocks of 32 (a block
+// may straddle two tiles: rows are gathered by address), BPS blocks per
+// double-buffered DMA stage.  R and dz are recomputed from the stored row
+// statistics with the rows as the contraction index, and
 //   dv[c1,c2] = sum_(g,a2) R dU,
 //   dk[c1,c2] = s sum_(g,a2) dz Qh + dKbar[c1] / b2   (dKbar already reduced).
 // With several iterations dk collects one term per R-step in the fp32
@@ -397,9 +397,47 @@ constexpr int kRbSingle = 0, kRbLast = 1, kRbMid = 2, kRbFirst = 3;
 #ifndef MONARCH_BRB_BPS
 #define MONARCH_BRB_BPS 4
 #endif
+#ifndef MONARCH_BRB_RW
+#define MONARCH_BRB_RW 1
+#endif
+
+// Global -> LDS DMA of 32 rows j0 .. j0+31 of the sequence of t*b2 rows
+// (g, a2) of one key block: row j lives at rbase + (j / b2) * tstride + j % b2
+// (rows past `total` repeat the last row).
+template <typename T, int D, int DK>
+__device__ inline void dma_rows32(T* tile, const T* src, long long rbase, int j0, int total, int b2,
+                                  long long tstride, int nw) {
+  constexpr int V = Elem<T>::kVec;
+  constexpr int ROWB = DK * static_cast<int>(sizeof(T));
+  constexpr int NINS = 32 * ROWB / 1024;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  for (int ci = wave; ci < NINS; ci += nw) {
+    const int byte = ci * 1024 + 16 * lane;
+    const int r = byte / ROWB;
+    const int c = ((byte % ROWB) / 16) ^ Tile<T, DK>::swz(r);
+    int col = c * V;
+    if (col >= D) col -= D;
+    int j = j0 + r;
+    if (j >= total) j = total - 1;
+    const long long row = rbase + static_cast<long long>(j / b2) * tstride + j % b2;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row * D + col),
+                                     (__attribute__((address_space(3))) void*)(tile + ci * (1024 / static_cast<int>(sizeof(T)))),
+                                     16, 0, 0);
+  }
+}
+
+// The same for one float per row (64 lanes, rows j0 .. j0+63).
+__device__ inline void dma_rowstat(float* dst, const float* src, long long rbase, int j0, int total, int b2,
+                                   long long tstride) {
+  int j = j0 + lane_id();
+  if (j >= total) j = total - 1;
+  const long long row = rbase + static_cast<long long>(j / b2) * tstride + j % b2;
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row),
+                                   (__attribute__((address_space(3))) void*)(dst), 4, 0, 0);
+}
 
 template <typename T, int D, int MODE = kRbSingle>
-__global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
+__global__ __launch_bounds__(MONARCH_BRB_RW == 1 ? 512 : 256) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ qhat, const T* __restrict__ du,
                                                   const float* __restrict__ lser, const float* __restrict__ rho,
                                                   const float* __restrict__ dh,
@@ -413,6 +451,7 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
   constexpr int NACC = NDP > 0 ? NDP : 1;
   // 32-row blocks per pipeline stage (f32 tiles are twice as large: one)
   constexpr int BPS = sizeof(T) == 2 ? MONARCH_BRB_BPS : 1;
+  constexpr int RW = MONARCH_BRB_RW;
   __shared__ __align__(16) T sQ[2][BPS][32 * DK];
   __shared__ __align__(16) T sU[2][BPS][32 * DK];
   __shared__ __align__(16) float sLR[2][BPS][64];
@@ -426,41 +465,46 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
   const int nw = blockDim.x / kWave;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
-  const int c2 = wave * 16 + l16;
-  const int c2c = c2 < p.b2 ? c2 : p.b2 - 1;
-  const int ncp = p.b2p / 32;
-  const int nblk = p.t * ncp;                 // (tile, 32-row block) pairs, in order
+  const int total = p.t * p.b2;               // rows (g, a2) of all tiles, in order
+  const int nblk = (total + 31) / 32;
   const int nst = (nblk + BPS - 1) / BPS;
+  const long long rbase = (static_cast<long long>(bh) * p.t * p.b1 + c1) * p.b2;  // row (g = 0, c1, a2 = 0)
+  const long long tstride = static_cast<long long>(p.b1) * p.b2;                  // rows between tiles
 
   auto fetch = [&](int st, int buf) {
 #pragma unroll
     for (int j = 0; j < BPS; ++j) {
       const int b = st * BPS + j;
       if (b >= nblk) break;
-      const int g = b / ncp, a0 = 32 * (b % ncp);
-      const long long rb = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a0;
-      const int nvalid = p.b2 - a0;
-      dma_block<T, D, DK>(sQ[buf][j], qhat + rb * D, 32, nvalid, nw);
-      dma_block<T, D, DK>(sU[buf][j], du + rb * D, 32, nvalid, nw);
-      if (wave == 0) dma_floats64(sLR[buf][j], lser + rb, 1, nvalid);
-      if (wave == nw - 1) dma_floats64(sRh[buf][j], rho + rb, 1, nvalid);
-      if (MID && wave == 1 % nw) dma_floats64(sDh[MID ? buf : 0][MID ? j : 0], dh + rb, 1, nvalid);
+      const int j0 = 32 * b;
+      dma_rows32<T, D, DK>(sQ[buf][j], qhat, rbase, j0, total, p.b2, tstride, nw);
+      dma_rows32<T, D, DK>(sU[buf][j], du, rbase, j0, total, p.b2, tstride, nw);
+      if (wave == 0) dma_rowstat(sLR[buf][j], lser, rbase, j0, total, p.b2, tstride);
+      if (wave == nw - 1) dma_rowstat(sRh[buf][j], rho, rbase, j0, total, p.b2, tstride);
+      if (MID && wave == 1 % nw) dma_rowstat(sDh[MID ? buf : 0][MID ? j : 0], dh, rbase, j0, total, p.b2, tstride);
     }
   };
   fetch(0, 0);
 
-  typename E::frag bk2[1][KS], bv2[1][KS];
+  typename E::frag bk2[RW][KS], bv2[RW][KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const int col = 32 * s + 8 * G;
-    bk2[0][s] = col < D ? E::load(k + (blk + c2c) * D + col) : E::zero();
-    bv2[0][s] = (!MID && col < D) ? E::load(v + (blk + c2c) * D + col) : E::zero();
+  for (int rt = 0; rt < RW; ++rt) {
+    const int c2 = (wave * RW + rt) * 16 + l16;
+    const int c2c = c2 < p.b2 ? c2 : p.b2 - 1;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int col = 32 * s + 8 * G;
+      bk2[rt][s] = col < D ? E::load(k + (blk + c2c) * D + col) : E::zero();
+      bv2[rt][s] = (!MID && col < D) ? E::load(v + (blk + c2c) * D + col) : E::zero();
+    }
   }
-  f32x4 accv[NACC][2][1], acck[NACC][2][1];
+  f32x4 accv[NACC][2][RW], acck[NACC][2][RW];
 #pragma unroll
   for (int dp = 0; dp < NACC; ++dp)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) accv[dp][dt][0] = acck[dp][dt][0] = f32x4{0, 0, 0, 0};
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) accv[dp][dt][rt] = acck[dp][dt][rt] = f32x4{0, 0, 0, 0};
   __syncthreads();
 
   for (int st = 0; st < nst; ++st) {
@@ -470,42 +514,50 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
     for (int j = 0; j < BPS; ++j) {
       const int b = st * BPS + j;
       if (b >= nblk) break;
-      const int a0 = 32 * (b % ncp);
+      const int j0 = 32 * b;
       const T* tq = sQ[cur][j];
       const T* tu = sU[cur][j];
       typename E::frag a[KS][2];
-      f32x4 Z[2][1], DR[2][1];
+      f32x4 Z[2][RW], DR[2][RW];
       load_rows<T, DK, KS>(a, tq, 0, l16, G);
-      logits<T, KS, 1>(Z, a, bk2);
+      logits<T, KS, RW>(Z, a, bk2);
       load_rows<T, DK, KS>(a, tu, 0, l16, G);
       if (MID)
-        logits<T, KS, 1>(DR, a, bk2);  // <dKt, k>
+        logits<T, KS, RW>(DR, a, bk2);  // <dKt, k>
       else
-        logits<T, KS, 1>(DR, a, bv2);  // <dU, v>
-      float r[8], z[8];
+        logits<T, KS, RW>(DR, a, bv2);  // <dU, v>
+      typename E::frag rf[RW], zf[RW];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const bool ok = a0 + 8 * G + jj < p.b2;  // rows past b2 repeat the last row: weight 0
-        const float xl = Z[jj >> 2][0][jj & 3] * p.c - sLR[cur][j][8 * G + jj];  // log2 R
-        const float rr = fast_exp2(xl);
-        float dr = DR[jj >> 2][0][jj & 3];
-        if (MID) dr -= sDh[MID ? cur : 0][MID ? j : 0][8 * G + jj] * kLn2 * xl;
-        r[jj] = ok ? rr : 0.0f;
-        z[jj] = ok ? rr * (dr - sRh[cur][j][8 * G + jj]) : 0.0f;
+      for (int rt = 0; rt < RW; ++rt) {
+        float r[8], z[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const bool ok = j0 + 8 * G + jj < total;  // rows past the sequence repeat the last row: weight 0
+          const float xl = Z[jj >> 2][rt][jj & 3] * p.c - sLR[cur][j][8 * G + jj];  // log2 R
+          const float rr = fast_exp2(xl);
+          float dr = DR[jj >> 2][rt][jj & 3];
+          if (MID) dr -= sDh[MID ? cur : 0][MID ? j : 0][8 * G + jj] * kLn2 * xl;
+          r[jj] = ok ? rr : 0.0f;
+          z[jj] = ok ? rr * (dr - sRh[cur][j][8 * G + jj]) : 0.0f;
+        }
+        rf[rt] = E::pack(r);
+        zf[rt] = E::pack(z);
       }
-      const typename E::frag rf[1] = {E::pack(r)}, zf[1] = {E::pack(z)};
       typename E::frag vv[NACC][2];
       load_cols<T, D, DK, NACC>(vv, tu, 0);
-      weighted_sum<T, D, NACC, 1>(accv, vv, rf);
+      weighted_sum<T, D, NACC, RW>(accv, vv, rf);
       load_cols<T, D, DK, NACC>(vv, tq, 0);
-      weighted_sum<T, D, NACC, 1>(acck, vv, zf);
+      weighted_sum<T, D, NACC, RW>(acck, vv, zf);
     }
     __syncthreads();
   }
 
-  if (c2 < p.b2) {
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    const int c2 = (wave * RW + rt) * 16 + l16;
+    if (c2 >= p.b2) continue;
     const long long orow = (blk + c2) * D;
-    if (!MID) store_rows<T, D, NACC, 1>(dv + orow, accv, 0, 1.0f, G);
+    if (!MID) store_rows<T, D, NACC, RW>(dv + orow, accv, rt, 1.0f, G);
     // this R-step's key gradient over the lane's d positions (32dp + 8G + j,
     // or 4G + j when D == 16), combined as MODE says; dkbar holds the
     // block-mean gradient already divided by b2
@@ -516,11 +568,11 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
       const int d0 = D >= 32 ? 32 * dp + 8 * G : 4 * G;
       float o[8];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        o[j] = p.s * acck[dp][j >> 2][0][j & 3];
-        if (MID) o[j] += accv[dp][j >> 2][0][j & 3];
-        if (MODE == kRbSingle || MODE == kRbFirst) o[j] += mk[d0 + j];
-        if (MODE == kRbMid || MODE == kRbFirst) o[j] += dk_acc[orow + d0 + j];
+      for (int jd = 0; jd < NJ; ++jd) {
+        o[jd] = p.s * acck[dp][jd >> 2][rt][jd & 3];
+        if (MID) o[jd] += accv[dp][jd >> 2][rt][jd & 3];
+        if (MODE == kRbSingle || MODE == kRbFirst) o[jd] += mk[d0 + jd];
+        if (MODE == kRbMid || MODE == kRbFirst) o[jd] += dk_acc[orow + d0 + jd];
       }
       if (MODE == kRbSingle || MODE == kRbFirst) {
         if (D >= 32)
@@ -529,7 +581,7 @@ __global__ __launch_bounds__(512) void kb_rside_b(const T* __restrict__ k, const
           E::store4(dk + orow + d0, o);
       } else {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) dk_acc[orow + d0 + j] = o[j];
+        for (int jd = 0; jd < NJ; ++jd) dk_acc[orow + d0 + jd] = o[jd];
       }
     }
   }
@@ -551,7 +603,8 @@ constexpr int kDqStore = 0;   // one iteration: dq = this term
 constexpr int kDqInit = 1;    // last L-step: dq_acc = this term
 constexpr int kDqAdd = 2;     // dq_acc += this term
 constexpr int kDqFinish = 3;  // first L-step: dq = dq_acc + this term
-template <typename T, int D, int RW, int NW, bool BCAST = true, bool HAS_DY = true, int DQM = kDqStore>
+template <typename T, int D, int RW, int NW, bool BCAST = true, bool HAS_DY = true, int DQM = kDqStore,
+          int STEP = kStep>
 __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, const T* __restrict__ dy,
                                                     const T* __restrict__ y, const T* __restrict__ kt,
                                                     const float* __restrict__ h2,
@@ -566,14 +619,15 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   constexpr int RB = NW * RW * 16;
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
-  using Dma = TileDma<T, D, DK, kStep, NW>;
+  using Dma = TileDma<T, D, DK, STEP, NW>;
+  constexpr int HALVES = STEP / 32;
   // double-buffered for bf16; f32 tiles are twice as large: one buffer
   constexpr int NB = sizeof(T) == 2 ? 2 : 1;
-  __shared__ __align__(16) T sK[NB][kStep * DK];
-  __shared__ __align__(16) T sU[HAS_DY ? NB : 1][HAS_DY ? kStep * DK : 8];
-  __shared__ __align__(16) T sG[NB][kStep * DK];
-  __shared__ __align__(16) float sE[NB][kStep];
-  __shared__ __align__(16) float sH[BCAST ? 1 : NB][kStep];
+  __shared__ __align__(16) T sK[NB][STEP * DK];
+  __shared__ __align__(16) T sU[HAS_DY ? NB : 1][HAS_DY ? STEP * DK : 8];
+  __shared__ __align__(16) T sG[NB][STEP * DK];
+  __shared__ __align__(16) float sE[NB][64];  // 64: one float per lane of the DMA
+  __shared__ __align__(16) float sH[BCAST ? 1 : NB][64];
 
   ColItem it(p, RB);
   if (it.nrows <= 0) return;
@@ -587,9 +641,9 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   const long long cbase = (static_cast<long long>(bh) * p.t + g) * p.b1 * p.b2 + a2;  // (bh, g, c1 = 0, a2)
   const long long ustride = static_cast<long long>(p.b2) * D;
 
-  const int nst = (p.b1 + kStep - 1) / kStep;
+  const int nst = (p.b1 + STEP - 1) / STEP;
   auto fetch = [&](int st, int buf, bool with_u) {
-    const int c1 = st * kStep;
+    const int c1 = st * STEP;
     Dma::issue(sK[buf], ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
     Dma::issue(sG[buf], gq + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
     if (HAS_DY && with_u) Dma::issue(sU[buf], u + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
@@ -628,9 +682,9 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
     const int cur = st % NB;
     if (NB == 2 && st + 1 < nst) fetch(st + 1, cur ^ 1, false);
 #pragma unroll
-    for (int half = 0; half < kHalves; ++half) {
+    for (int half = 0; half < HALVES; ++half) {
       const int k0 = 32 * half;
-      const int c1_0 = st * kStep + k0;
+      const int c1_0 = st * STEP + k0;
       if (c1_0 >= p.b1) break;
       const bool tail = c1_0 + 32 > p.b1;
       typename E::frag a[KS][2];
@@ -698,9 +752,9 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
     const int cur = st % NB;
     if (NB == 2 && st + 1 < nst) fetch(st + 1, cur ^ 1, true);
 #pragma unroll
-    for (int half = 0; half < kHalves; ++half) {
+    for (int half = 0; half < HALVES; ++half) {
       const int k0 = 32 * half;
-      const int c1_0 = st * kStep + k0;
+      const int c1_0 = st * STEP + k0;
       if (c1_0 >= p.b1) break;
       const bool tail = c1_0 + 32 > p.b1;
       typename E::frag a[KS][2];

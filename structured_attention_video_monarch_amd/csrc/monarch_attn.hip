@@ -598,6 +598,9 @@ template <typename T> struct BwdCfg;
 #ifndef MONARCH_BDQ_NW
 #define MONARCH_BDQ_NW 8
 #endif
+#ifndef MONARCH_BDQ_STEP
+#define MONARCH_BDQ_STEP 64
+#endif
 #ifndef MONARCH_BDU_RW
 #define MONARCH_BDU_RW 1
 #endif
@@ -612,11 +615,11 @@ template <typename T> struct BwdCfg;
 #endif
 template <> struct BwdCfg<bf16_t> {
   static constexpr int kDuRW = MONARCH_BDU_RW, kDuNW = MONARCH_BDU_NW;
-  static constexpr int kDqRW = MONARCH_BDQ_RW, kDqNW = MONARCH_BDQ_NW;
+  static constexpr int kDqRW = MONARCH_BDQ_RW, kDqNW = MONARCH_BDQ_NW, kDqStep = MONARCH_BDQ_STEP;
   static constexpr int kGmRW = MONARCH_BGM_RW, kGmNW = MONARCH_BGM_NW;
 };
 template <> struct BwdCfg<float> {
-  static constexpr int kDuRW = 1, kDuNW = 4, kDqRW = 1, kDqNW = 4, kGmRW = 2, kGmNW = 4;
+  static constexpr int kDuRW = 1, kDuNW = 4, kDqRW = 1, kDqNW = 4, kDqStep = 64, kGmRW = 2, kGmNW = 4;
 };
 
 // Backward workspace (allocated per call, stream-ordered).  With several
@@ -738,6 +741,8 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
   const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
+  constexpr int rb_keys = 16 * MONARCH_BRB_RW;  // keys c2 per wave of kb_rside_b
+  const unsigned rb_threads = static_cast<unsigned>(kWave * ((s.b2 + rb_keys - 1) / rb_keys));
   const size_t ra_lds = rside_bwd_lds_bytes<T, D>(bg.b2p);
   constexpr int dq_rows = C::kDqRW * C::kDqNW * 16;
   const LGeom row_geom{BH, N, s.b1, s.b1, s.b2, s.t, (ngmax + dq_rows - 1) / dq_rows, c};
@@ -782,15 +787,15 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
                                                         ev, delta, dq, dqacc, dl, w.ldl, row_geom, sc);
         }));
       };
-      constexpr int RW = C::kDqRW, NW = C::kDqNW;
+      constexpr int RW = C::kDqRW, NW = C::kDqNW, SP = C::kDqStep;
       if (T_ == 1)
-        launch(&kb_dq<T, D, RW, NW, true, true, kDqStore>);
+        launch(&kb_dq<T, D, RW, NW, true, true, kDqStore, SP>);
       else if (last)
-        launch(&kb_dq<T, D, RW, NW, false, true, kDqInit>);
+        launch(&kb_dq<T, D, RW, NW, false, true, kDqInit, SP>);
       else if (first)
-        launch(&kb_dq<T, D, RW, NW, true, false, kDqFinish>);
+        launch(&kb_dq<T, D, RW, NW, true, false, kDqFinish, SP>);
       else
-        launch(&kb_dq<T, D, RW, NW, false, false, kDqAdd>);
+        launch(&kb_dq<T, D, RW, NW, false, false, kDqAdd, SP>);
     }
     if (first) {
       // block-mean key gradient: partial sums over chunks of tokens, then
@@ -810,7 +815,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
     {
       auto launch = [&](auto kern) {
         ok(timed(10, st, [&] {
-          kern<<<r_grid, r_threads, 0, st>>>(k, v, qh, du, lser, rho, dh, dkbar, dk, dkacc, dv, bg);
+          kern<<<r_grid, rb_threads, 0, st>>>(k, v, qh, du, lser, rho, dh, dkbar, dk, dkacc, dv, bg);
         }));
       };
       if (T_ == 1)
