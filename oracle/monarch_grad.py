@@ -33,9 +33,12 @@ iteration, written out step by step in reverse:
     dk += dKbar / b2                  (the block mean)
 
 With several iterations the reverse also runs back through the earlier
-ones (see monarch_head_grad).  Pinned by central finite differences of the
-forward oracle, by the block shapes where the method is exact softmax
-attention, and by symmetries of the forward (tests).
+ones (see monarch_head_grad).  A chunk of query frames against cached keys
+(fewer query blocks b1q than key blocks b1, as in monarch_oracle) takes the
+same steps with a1 over the chunk's blocks and c1 over all key blocks.
+Pinned by central finite differences of the forward oracle, by the block
+shapes where the method is exact softmax attention, by symmetries of the
+forward, and for a chunk by the square layer's gradient (tests).
 """
 from __future__ import annotations
 
@@ -51,7 +54,10 @@ __all__ = ["monarch_head_grad", "monarch_attention_grad"]
 def monarch_head_grad(q, k, v, dy, b1: int, b2: int, tiles: int = 1, iters: int = 1):
     """Gradient of sum(dy * y) for one (batch, head) after ``iters`` iterations.
 
-    q, k, v, dy: [N, d].  Returns (dq, dk, dv), each [N, d] float64.
+    q, dy: [Nq, d]; k, v: [N, d] with N = b1*b2 and Nq a multiple of b2
+    (Nq = N for the square layer, fewer rows for a chunk against cached keys;
+    tiles split the b1q = Nq/b2 query blocks).  Returns (dq [Nq, d],
+    dk [N, d], dv [N, d]) float64.
 
     For iters > 1 the reverse also runs through the earlier iterations: the
     L-step of iteration i uses the keys Kt_(i-1) = R_(i-1) k and entropies
@@ -62,16 +68,20 @@ def monarch_head_grad(q, k, v, dy, b1: int, b2: int, tiles: int = 1, iters: int 
     back to dQhat, dk, G and dL_(i-1) as for the last one.  The first L-step
     uses the block means (R_0 uniform and constant).
     """
-    N, d = np.shape(q)
+    Nq, d = np.shape(q)
+    N = np.shape(k)[0]
     if b1 * b2 != N:
         raise ValueError(f"b1*b2 = {b1 * b2} != N = {N}")
+    if Nq % b2 != 0 or Nq == 0:
+        raise ValueError(f"query count {Nq} is not a positive multiple of b2 = {b2}")
     if iters < 1:
         raise ValueError("iters must be >= 1")
-    bounds = tile_bounds(b1, tiles)
+    b1q = Nq // b2
+    bounds = tile_bounds(b1q, tiles)
     t = tiles
     s = 1.0 / math.sqrt(d)
-    qb, kb, vb = _blocks(q, b1, b2), _blocks(k, b1, b2), _blocks(v, b1, b2)
-    dyb = _blocks(dy, b1, b2)
+    qb, kb, vb = _blocks(q, b1q, b2), _blocks(k, b1, b2), _blocks(v, b1, b2)
+    dyb = _blocks(dy, b1q, b2)
 
     # ---- forward, keeping every iteration's factors
     Rs = [uniform_R(b1, b2, t)]               # R_0 .. R_T
@@ -143,14 +153,15 @@ def monarch_head_grad(q, k, v, dy, b1: int, b2: int, tiles: int = 1, iters: int 
             dR = np.einsum("gcad,cpd->gcap", dk_til, kb) - dh[..., None] * (logR + 1.0)
             dkb += np.einsum("gcap,gcad->cpd", Rp, dk_til)
             dL = np.zeros_like(Ls[i - 1])
-    return dqb.reshape(N, d), dkb.reshape(N, d), dvb.reshape(N, d)
+    return dqb.reshape(Nq, d), dkb.reshape(N, d), dvb.reshape(N, d)
 
 
 def monarch_attention_grad(q, k, v, dy, b1: int, b2: int, tiles: int = 1, iters: int = 1):
-    """[B, H, N, d] inputs -> (dq, dk, dv) float64, head by head."""
-    q = np.asarray(q)
-    B, H, N, d = q.shape
-    out = [np.empty((B, H, N, d)) for _ in range(3)]
+    """q, dy [B, H, Nq, d], k, v [B, H, N, d] -> (dq, dk, dv) float64, head by head."""
+    q, k = np.asarray(q), np.asarray(k)
+    B, H, Nq, d = q.shape
+    N = k.shape[2]
+    out = [np.empty((B, H, Nq, d)), np.empty((B, H, N, d)), np.empty((B, H, N, d))]
     for b in range(B):
         for h in range(H):
             grads = monarch_head_grad(q[b, h], k[b, h], v[b, h], dy[b, h], b1, b2, tiles, iters)

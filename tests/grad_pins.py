@@ -15,7 +15,11 @@ with a planted mistake) and raises AssertionError when the fact does not hold
 * symmetries of the forward: a shift of every key leaves y unchanged (the
   key gradient sums to zero), a shift of every value shifts every output row
   (the value gradient sums to sum(dy)), and q -> a q, k -> k / a leaves y
-  unchanged (<dq, q> = <dk, k>).
+  unchanged (<dq, q> = <dk, k>);
+* a chunk of query frames against all keys: finite differences as above;
+  blocks of one key (b2 = 1), exact attention of the chunk's queries over all
+  keys; and the square layer over all frames whose tiles cover the chunk with
+  the same bounds, with dy zero outside the chunk, has the chunk's gradient.
 """
 from __future__ import annotations
 
@@ -158,5 +162,81 @@ def check_grad_symmetries(grd):
         assert abs(a - b) <= 1e-10 * max(1.0, abs(a)), f"q/k scaling: {a} vs {b}"
 
 
+def _chunk_case(seed, fk, fq, hw, d, scale=1.5):
+    rng = np.random.default_rng(seed)
+    N, Nq = fk * hw, fq * hw
+    q = scale * rng.standard_normal((Nq, d))
+    k = scale * rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    dy = rng.standard_normal((Nq, d))
+    return q, k, v, dy
+
+
+def check_grad_chunk_directional_fd(grd):
+    """Chunk of fq of fk frames (h*w tokens each), blocks (b1, b2) over all keys."""
+    h = 1e-5
+    for seed, (fk, fq, hw, b2, t, d, T) in enumerate([(4, 1, 12, 4, 1, 8, 1), (4, 2, 12, 4, 2, 8, 2),
+                                                       (3, 1, 12, 6, 2, 4, 3), (5, 2, 6, 3, 4, 8, 1),
+                                                       (4, 3, 8, 8, 3, 4, 2)]):
+        q, k, v, dy = _chunk_case(70 + seed, fk, fq, hw, d)
+        b1 = fk * hw // b2
+        dq, dk, dv = grd.monarch_head_grad(q, k, v, dy, b1, b2, t, T)
+        assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+        rng = np.random.default_rng(170 + seed)
+        for which, g in (("q", dq), ("k", dk), ("v", dv)):
+            args_p = {"q": q, "k": k, "v": v}
+            u = rng.standard_normal(args_p[which].shape)
+            args_m = dict(args_p)
+            args_p[which] = args_p[which] + h * u
+            args_m[which] = args_m[which] - h * u
+            fd = (_loss(args_p["q"], args_p["k"], args_p["v"], dy, b1, b2, t, T)
+                  - _loss(args_m["q"], args_m["k"], args_m["v"], dy, b1, b2, t, T)) / (2 * h)
+            an = float(np.sum(g * u))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), \
+                f"chunk d{which} (fk={fk},fq={fq},b2={b2},t={t},T={T}): fd {fd:.10f} vs analytic {an:.10f}"
+
+
+def check_grad_chunk_softmax_limit(grd):
+    """b2 = 1: every block holds one key, so the chunk's rows get exact
+    attention over all keys, for any tiles and iterations."""
+    import torch.nn.functional as F
+
+    def sdpa(tq, tk, tv):
+        return F.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None])[0, 0]
+
+    for seed, (N, Nq, t, T) in enumerate([(20, 5, 1, 1), (20, 8, 3, 2), (15, 15, 2, 3)]):
+        q, k, v, dy = _chunk_case(80 + seed, N, Nq, 1, 8)
+        got = grd.monarch_head_grad(q, k, v, dy, N, 1, t, T)
+        ref = _torch_grads(sdpa, q, k, v, dy)
+        for name, a, b in zip("qkv", got, ref):
+            _close(a, b, 1e-10, f"chunk d{name} at b2 = 1 (N={N}, Nq={Nq}, t={t}, T={T})")
+
+
+def check_grad_chunk_is_last_tiles_of_full_layer(grd):
+    """The last fq of fk frames with t tiles against all keys, and the square
+    layer over all frames with t*fk/fq tiles (whose last t tiles cover the
+    chunk with the same bounds) given dy = 0 outside the chunk: the same dk
+    and dv, the chunk's dq on the chunk's rows and 0 on the others (tiles are
+    independent query-row groups)."""
+    fk, fq, h, w, d = 6, 2, 3, 4, 8
+    b1, b2 = fk * h, w
+    N, Nq = b1 * b2, fq * h * w
+    rng = np.random.default_rng(90)
+    q = 1.5 * rng.standard_normal((N, d))
+    k = 1.5 * rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    dy = np.zeros((N, d))
+    dy[N - Nq:] = rng.standard_normal((Nq, d))
+    for t in (1, 2, 3):
+        for T in (1, 2):
+            fdq, fdk, fdv = grd.monarch_head_grad(q, k, v, dy, b1, b2, t * fk // fq, T)
+            cdq, cdk, cdv = grd.monarch_head_grad(q[N - Nq:], k, v, dy[N - Nq:], b1, b2, t, T)
+            scale = max(np.max(np.abs(fdk)), np.max(np.abs(fdq)), 1e-300)
+            assert np.max(np.abs(fdq[:N - Nq])) <= 1e-13 * scale, (t, T, "dq outside the chunk")
+            for name, a, b in (("dq", cdq, fdq[N - Nq:]), ("dk", cdk, fdk), ("dv", cdv, fdv)):
+                _close(a, b, 1e-11, f"chunk {name} vs square layer (t={t}, T={T})")
+
+
 ALL_CHECKS = [check_grad_directional_fd, check_grad_entrywise_fd, check_grad_softmax_limits,
-              check_grad_one_row_tiles, check_grad_symmetries]
+              check_grad_one_row_tiles, check_grad_symmetries, check_grad_chunk_directional_fd,
+              check_grad_chunk_softmax_limit, check_grad_chunk_is_last_tiles_of_full_layer]

@@ -37,6 +37,8 @@ MUTANTS = {
     "earlier_iterations_use_last_L": ("        R, L, q_hat, beta = Rs[i], Ls[i], qhats[i], betas[i]",
                                       "        R, L, q_hat, beta = Rs[i], Ls[T], qhats[i], betas[i]"),
     "tile0_U": ("Ug = U[g].transpose(1, 0, 2)", "Ug = U[0].transpose(1, 0, 2)"),
+    # a chunk of query frames against cached keys
+    "chunk_tiles_over_key_blocks": ("bounds = tile_bounds(b1q, tiles)", "bounds = tile_bounds(b1, tiles)"),
 }
 
 
