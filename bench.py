@@ -72,16 +72,17 @@ def algorithmic_work(wl, it_last=True):
         "k_rstep": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 2 * nd)),
         "k_apply": (BH * 2.0 * Nq * b1 * d, BH * (2 * nqd + 4 * Nq + t * nd)),
         # backward (one iteration), chain-rule products only (no logit
-        # recomputation, no stored s*dl), per (batch, head):
-        #   kb_du       dU = L^T dy                      2 N b1 d;  q, dy, lse in, dU out
+        # recomputation, no stored s*dl), per (batch, head); the row side
+        # has the Nq query tokens, the key side t*N rows (tile, key block, a2):
+        #   kb_du       dU = L^T dy                      2 Nq b1 d;  q, dy, lse in, dU out
         #   kb_rside_a  dR = dU v^T, dQh = dz k          4 t N b2 d; Qh, dU, K, V, beta in, G out
-        #   kb_dq       <dy,U>, <q,G>, L G, dl Kbar      8 N b1 d;  q, dy, y, U, G, lse, e in, dq out
-        #   kb_dkbar    dKbar = dl^T q                   2 N b1 d;  q in
+        #   kb_dq       <dy,U>, <q,G>, L G, dl Kbar      8 Nq b1 d;  q, dy, y, U, G, lse, e in, dq out
+        #   kb_dkbar    dKbar = dl^T q                   2 Nq b1 d;  q in
         #   kb_rside_b  dv = R^T dU, dk_R = dz^T Qh      4 t N b2 d; Qh, dU, K, V in, dk, dv out
-        "kb_du": (BH * 2.0 * N * b1 * d, BH * (2 * nd + 4 * N + t * nd)),
+        "kb_du": (BH * 2.0 * Nq * b1 * d, BH * (2 * nqd + 4 * Nq + t * nd)),
         "kb_rside_a": (BH * 4.0 * t * N * b2 * d, BH * (3 * t * nd + 2 * nd + 16 * t * N)),
-        "kb_dq": (BH * 8.0 * N * b1 * d, BH * (4 * nd + 2 * t * nd + 8 * N + 4 * t * N)),
-        "kb_dkbar": (BH * 2.0 * N * b1 * d, BH * nd),
+        "kb_dq": (BH * 8.0 * Nq * b1 * d, BH * (4 * nqd + 2 * t * nd + 8 * Nq + 4 * t * N)),
+        "kb_dkbar": (BH * 2.0 * Nq * b1 * d, BH * nqd),
         "kb_dkbar_reduce": (0.0, BH * b1 * d * 4.0),
         "kb_rside_b": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 4 * nd + 8 * t * N)),
         # early stopping: the objective per head reads the log-sum-exps once
@@ -100,9 +101,9 @@ def step_work(wl, mode, launches):
         entropies H (t*N*d*e + 4tN more read by kb_du and kb_dq);
       each earlier iteration (T-1 times), with cotangents dKt, dH instead of dU:
         kb_rside_a  dR = dKt k^T, dQh = dz k      4 t N b2 d; Qh, dKt, K, beta, dH in, G out
-        kb_dq       <q,G>, L G, dl Kt              6 N b1 d;  q, Kt, H (Kbar at i = 1), G, lse, e in
+        kb_dq       <q,G>, L G, dl Kt              6 Nq b1 d; q, Kt, H (Kbar at i = 1), G, lse, e in
         kb_rside_b  dk_R = dz^T Qh + R^T dKt       4 t N b2 d; Qh, dKt, K, dH in, dk out (once)
-        kb_dktil    dKt, dH of the R-step before   2 N b1 d;  q in, dKt, dH out   (T-1 launches)
+        kb_dktil    dKt, dH of the R-step before   2 Nq b1 d; q in, dKt, dH out   (T-1 launches)
       kb_dkbar and its reduction once, at the first iteration; dq and dk are
       written once.
     """
@@ -112,8 +113,8 @@ def step_work(wl, mode, launches):
     if mode != "train" or T < 2:
         return tot
     e = 2 if wl.dtype == "bf16" else 4
-    BH, N, d, b1, b2, t = wl.B * wl.H, wl.N, wl.d, wl.b1, wl.b2, wl.tiles
-    nd = N * d * e
+    BH, N, Nq, d, b1, b2, t = wl.B * wl.H, wl.N, wl.Nq, wl.d, wl.b1, wl.b2, wl.tiles
+    nd, nqd = N * d * e, Nq * d * e
     m = T - 1
     extra_keys = t * nd + 4 * t * N
     tot["kb_du"] = (per["kb_du"][0], per["kb_du"][1] + BH * extra_keys)
@@ -121,11 +122,11 @@ def step_work(wl, mode, launches):
                          per["kb_rside_a"][1] + m * BH * (3 * t * nd + nd + 20 * t * N))
     # dq and dk are written once (counted with the last form's launch); the
     # first L-step's keys are the block means (b1*d, not counted)
-    tot["kb_dq"] = (per["kb_dq"][0] + m * BH * 6.0 * N * b1 * d,
-                    per["kb_dq"][1] + BH * extra_keys + m * BH * (nd + t * nd + 4 * N + 4 * t * N)
+    tot["kb_dq"] = (per["kb_dq"][0] + m * BH * 6.0 * Nq * b1 * d,
+                    per["kb_dq"][1] + BH * extra_keys + m * BH * (nqd + t * nd + 4 * Nq + 4 * t * N)
                     + (m - 1) * BH * extra_keys)
     tot["kb_rside_b"] = (BH * 4.0 * t * N * b2 * d * T, per["kb_rside_b"][1] + m * BH * (2 * t * nd + nd + 12 * t * N))
-    tot["kb_dktil"] = (m * BH * 2.0 * N * b1 * d, m * BH * (nd + t * nd + 4 * t * N))
+    tot["kb_dktil"] = (m * BH * 2.0 * Nq * b1 * d, m * BH * (nqd + t * nd + 4 * t * N))
     return tot
 
 
@@ -200,7 +201,7 @@ def cpu_baseline_train(wl, seed, budget_s=30.0):
         spent += time.perf_counter() - t0
         done += 1
     per_call = spent / done * wl.B * wl.H
-    return {"value": round(wl.B * wl.N / per_call, 1), "unit": "tokens/s", "cores": int(cores),
+    return {"value": round(wl.B * wl.Nq / per_call, 1), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{done} of {wl.B * wl.H} heads of one {wl.name} training step (forward and "
                       f"gradient oracles, fp64 numpy), {spent:.1f} s; full step extrapolated as "
@@ -287,10 +288,6 @@ def main():
                                         args.tol, iters_used=iters_used, workspace=ws, stream=stream)
 
     if wl.kv:
-        if args.mode == "train":
-            print("bench.py: the training step is defined for the square layer only", file=sys.stderr)
-            sys.exit(2)
-
         def step():
             M.monarch_attn_fwd_kv(q, k, v, out, wl.fq, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles,
                                   wl.iters, workspace=ws, stream=stream)
@@ -303,15 +300,26 @@ def main():
         else:
             dy = torch.from_numpy(dyx["dy"]).to(dev)
         del dyx
-        sb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles,
-                                              wl.iters, M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32)
-        state = torch.empty(sb, dtype=torch.uint8, device=dev)
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-        targs = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        if wl.kv:
+            # a chunk of frames against cached keys: the chunk's training step
+            sb = M.monarch_attn_train_state_bytes_kv(wl.B, wl.H, wl.fq, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2,
+                                                     wl.tiles, wl.iters, dtc)
+            state = torch.empty(sb, dtype=torch.uint8, device=dev)
+            targs = (wl.fq, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
 
-        def step():
-            M.monarch_attn_fwd_train(q, k, v, out, *targs, state, stream)
-            M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, *targs, state, stream)
+            def step():
+                M.monarch_attn_fwd_train_kv(q, k, v, out, *targs, state, stream)
+                M.monarch_attn_bwd_kv(q, k, v, out, dy, dq, dk, dv, *targs, state, stream)
+        else:
+            sb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles,
+                                                  wl.iters, dtc)
+            state = torch.empty(sb, dtype=torch.uint8, device=dev)
+            targs = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
+
+            def step():
+                M.monarch_attn_fwd_train(q, k, v, out, *targs, state, stream)
+                M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, *targs, state, stream)
 
     for _ in range(args.warmup):
         step()

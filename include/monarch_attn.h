@@ -186,6 +186,29 @@ int monarch_attn_bwd(const void* q, const void* k, const void* v, const void* ou
                      int b1, int b2, int tiles, int iters, int dtype,
                      void* state, size_t state_bytes, void* stream);
 
+/* ---- training for a chunk of frames against cached keys ----
+ * The training forward and backward of monarch_attn_fwd_kv: fq query frames
+ * (q, out, dout, dq: [B,H,fq*h*w,d]) against all f key frames (k, v, dk, dv:
+ * [B,H,f*h*w,d]), same definitions as monarch_attn_fwd_train /
+ * monarch_attn_bwd with a1 over the chunk's fq*h*w/b2 query blocks (tiles
+ * split those) and c1 over the b1 key blocks.  The gradient of a chunk is
+ * the one of the square layer over all frames, with tiles that cover the
+ * chunk with the same bounds, restricted to dy = 0 outside the chunk.  State
+ * size as for the square layer with 4*Nq instead of 4*N per iteration for
+ * the log-sum-exps; the backward's workspace has Nq rows on its query side.
+ * fq == f is the square layer (same results as the calls above). */
+size_t monarch_attn_train_state_bytes_kv(int B, int H, int fq, int f, int h, int w, int d,
+                                         int b1, int b2, int tiles, int iters, int dtype);
+int monarch_attn_fwd_train_kv(const void* q, const void* k, const void* v, void* out,
+                              int B, int H, int fq, int f, int h, int w, int d,
+                              int b1, int b2, int tiles, int iters, int dtype,
+                              void* state, size_t state_bytes, void* stream);
+int monarch_attn_bwd_kv(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, void* dq, void* dk, void* dv,
+                        int B, int H, int fq, int f, int h, int w, int d,
+                        int b1, int b2, int tiles, int iters, int dtype,
+                        void* state, size_t state_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* monarch_attn_status_string(int status);
 

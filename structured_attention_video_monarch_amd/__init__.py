@@ -65,6 +65,12 @@ def _declare(lib):
     lib.monarch_attn_fwd_train.restype = c_int
     lib.monarch_attn_bwd.argtypes = [c_void_p] * 8 + tdims + [c_int, c_void_p, c_size_t, c_void_p]
     lib.monarch_attn_bwd.restype = c_int
+    lib.monarch_attn_train_state_bytes_kv.argtypes = kdims + [c_int]
+    lib.monarch_attn_train_state_bytes_kv.restype = c_size_t
+    lib.monarch_attn_fwd_train_kv.argtypes = [c_void_p] * 4 + kdims + [c_int, c_void_p, c_size_t, c_void_p]
+    lib.monarch_attn_fwd_train_kv.restype = c_int
+    lib.monarch_attn_bwd_kv.argtypes = [c_void_p] * 8 + kdims + [c_int, c_void_p, c_size_t, c_void_p]
+    lib.monarch_attn_bwd_kv.restype = c_int
     lib.monarch_attn_status_string.argtypes = [c_int]
     lib.monarch_attn_status_string.restype = ctypes.c_char_p
     lib.monarch_attn_last_hip_error.argtypes = []
@@ -214,19 +220,25 @@ def monarch_attn_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, iters, 
     return int(lib().monarch_attn_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, iters, dtype))
 
 
+def _kv_tensors(q, fq, f, h, w, query_side, key_side):
+    """Check [B,H,rows,d] GPU tensors of q's dtype: query_side ones have the
+    chunk's fq*h*w rows, key_side ones all f*h*w."""
+    named = [(n, t, fq * h * w) for n, t in query_side] + [(n, t, f * h * w) for n, t in key_side]
+    for name, t, rows in named:
+        if not t.is_cuda or t.dtype != q.dtype or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d GPU tensor of q's dtype")
+        if t.shape[0] != q.shape[0] or t.shape[1] != q.shape[1] or t.shape[3] != q.shape[3] \
+                or t.shape[2] != rows:
+            raise ValueError(f"{name} shape {tuple(t.shape)} does not match the chunk/frame sizes")
+
+
 def monarch_attn_fwd_kv(q, k, v, out, fq, f, h, w, b1, b2, tiles=1, iters=1, workspace=None,
                         stream=None):
     """Chunk of fq frames (q, out [B,H,fq*h*w,d]) against all f frames (k, v
     [B,H,f*h*w,d]); (b1, b2) block the keys.  Either dtype; with ``workspace``
     (a uint8 GPU tensor) nothing is allocated."""
     import torch
-    for name, t, rows in (("q", q, fq * h * w), ("out", out, fq * h * w), ("k", k, f * h * w),
-                          ("v", v, f * h * w)):
-        if not t.is_cuda or t.dtype != q.dtype or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous 4-d GPU tensor of q's dtype")
-        if t.shape[0] != q.shape[0] or t.shape[1] != q.shape[1] or t.shape[3] != q.shape[3] \
-                or t.shape[2] != rows:
-            raise ValueError(f"{name} shape {tuple(t.shape)} does not match the chunk/frame sizes")
+    _kv_tensors(q, fq, f, h, w, [("q", q), ("out", out)], [("k", k), ("v", v)])
     B, H, _, d = q.shape
     ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
     dims = [B, H, fq, f, h, w, d, b1, b2, tiles, iters]
@@ -277,6 +289,33 @@ def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, f, h, w, b1, b2, tiles, ite
     dims = _dims(q, f, h, w, b1, b2, tiles, iters)
     _check(lib().monarch_attn_bwd(*ptrs, *dims, _dtype_code(q), sp, sn, _stream(stream)),
            "monarch_attn_bwd")
+    return dq, dk, dv
+
+
+def monarch_attn_train_state_bytes_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters, dtype=MONARCH_BF16) -> int:
+    return int(lib().monarch_attn_train_state_bytes_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters, dtype))
+
+
+def monarch_attn_fwd_train_kv(q, k, v, out, fq, f, h, w, b1, b2, tiles, iters, state, stream=None):
+    """Training forward of a chunk of fq frames against all f frames (fills ``state``)."""
+    _kv_tensors(q, fq, f, h, w, [("q", q), ("out", out)], [("k", k), ("v", v)])
+    sp, sn = _state(state)
+    B, H, _, d = q.shape
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
+    _check(lib().monarch_attn_fwd_train_kv(*ptrs, B, H, fq, f, h, w, d, b1, b2, tiles, iters, _dtype_code(q),
+                                           sp, sn, _stream(stream)), "monarch_attn_fwd_train_kv")
+    return out
+
+
+def monarch_attn_bwd_kv(q, k, v, out, dout, dq, dk, dv, fq, f, h, w, b1, b2, tiles, iters, state, stream=None):
+    """dq [B,H,fq*h*w,d], dk, dv [B,H,f*h*w,d] <- gradients of sum(dout * out) of a chunk."""
+    _kv_tensors(q, fq, f, h, w, [("q", q), ("out", out), ("dout", dout), ("dq", dq)],
+                [("k", k), ("v", v), ("dk", dk), ("dv", dv)])
+    sp, sn = _state(state)
+    B, H, _, d = q.shape
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out, dout, dq, dk, dv)]
+    _check(lib().monarch_attn_bwd_kv(*ptrs, B, H, fq, f, h, w, d, b1, b2, tiles, iters, _dtype_code(q),
+                                     sp, sn, _stream(stream)), "monarch_attn_bwd_kv")
     return dq, dk, dv
 
 

@@ -543,9 +543,10 @@ struct TrainState {
 TrainState train_layout(const Shape& s, size_t elem) {
   TrainState t{};
   const size_t BH = static_cast<size_t>(s.BH), N = static_cast<size_t>(s.N), d = static_cast<size_t>(s.d);
+  const size_t Nq = static_cast<size_t>(s.Nq);
   const size_t tN = static_cast<size_t>(s.t) * N;
   const size_t T = static_cast<size_t>(s.T);
-  t.lse_blk = align_up(BH * N * sizeof(float));
+  t.lse_blk = align_up(BH * Nq * sizeof(float));
   t.beta_blk = align_up(BH * tN * sizeof(float));
   t.qhat_blk = align_up(BH * tN * d * elem);
   t.hent_blk = t.beta_blk;
@@ -641,16 +642,18 @@ BwdWorkspace bwd_layout_t(const Shape& s) {
   const size_t elem = sizeof(T);
   const long long ncb = (s.b1 + cb - 1) / cb;
   w.ldl = static_cast<int>(ncb * cb);
-  // enough workgroups to fill the chip, chunks of at least 512 tokens
+  // enough workgroups to fill the chip, chunks of at least 512 query tokens
   long long ns = (2048 + s.BH * ncb - 1) / (s.BH * ncb);
-  const long long ns_max = (s.N + 511) / 512;
+  const long long ns_max = (s.Nq + 511) / 512;
   if (ns > ns_max) ns = ns_max;
   if (ns < 1) ns = 1;
-  long long chunk = (s.N + ns - 1) / ns;
+  long long chunk = (s.Nq + ns - 1) / ns;
   chunk = (chunk + 31) / 32 * 32;
-  w.nsplit = static_cast<int>((s.N + chunk - 1) / chunk);
+  w.nsplit = static_cast<int>((s.Nq + chunk - 1) / chunk);
   w.chunk = static_cast<int>(chunk);
+  // query-side buffers have Nq rows, key-side ones t*N (per tile and key block)
   const size_t BH = static_cast<size_t>(s.BH), N = static_cast<size_t>(s.N), d = static_cast<size_t>(s.d);
+  const size_t Nq = static_cast<size_t>(s.Nq);
   const size_t tN = static_cast<size_t>(s.t) * N;
   size_t off = 0;
   w.du = off;
@@ -664,9 +667,9 @@ BwdWorkspace bwd_layout_t(const Shape& s) {
   w.rho = off;
   off += align_up(BH * tN * sizeof(float));
   w.delta = off;
-  off += align_up(BH * N * sizeof(float));
+  off += align_up(BH * Nq * sizeof(float));
   w.dl = off;
-  off += align_up(BH * N * static_cast<size_t>(w.ldl) * elem);
+  off += align_up(BH * Nq * static_cast<size_t>(w.ldl) * elem);
   w.part = off;
   off += align_up(BH * static_cast<size_t>(w.nsplit) * s.b1 * d * sizeof(float));
   w.dkbar = off;
@@ -675,7 +678,7 @@ BwdWorkspace bwd_layout_t(const Shape& s) {
     w.dh = off;
     off += align_up(BH * tN * sizeof(float));
     w.dqacc = off;
-    off += align_up(BH * N * d * sizeof(float));
+    off += align_up(BH * Nq * d * sizeof(float));
     w.dkacc = off;
     off += align_up(BH * N * d * sizeof(float));
   }
@@ -714,8 +717,10 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   float* dh = s.T > 1 ? reinterpret_cast<float*>(ws + w.dh) : nullptr;
   float* dqacc = s.T > 1 ? reinterpret_cast<float*>(ws + w.dqacc) : nullptr;
   float* dkacc = s.T > 1 ? reinterpret_cast<float*>(ws + w.dkacc) : nullptr;
-  const int BH = static_cast<int>(s.BH), N = static_cast<int>(s.N);
-  const int ngmax = (s.b1 + s.t - 1) / s.t;
+  // the row-side kernels see the Nq query tokens in b1q blocks (tiles split
+  // them); key blocks are b1
+  const int BH = static_cast<int>(s.BH), N = static_cast<int>(s.N), Nq = static_cast<int>(s.Nq);
+  const int ngmax = (s.b1q + s.t - 1) / s.t;
   const int T_ = s.T;
   hipError_t err = hipSuccess;
   auto ok = [&](hipError_t e) {
@@ -726,7 +731,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   auto ent_of = [&](int i) -> const float* { return i == 1 ? nullptr : bf.hent_of(i - 1); };
 
   constexpr int du_cb = C::kDuRW * C::kDuNW * 16;
-  const LGeom col_geom{BH, N, s.b1, s.b1, s.b2, s.t, (s.b1 + du_cb - 1) / du_cb, c};
+  const LGeom col_geom{BH, Nq, s.b1, s.b1q, s.b2, s.t, (s.b1 + du_cb - 1) / du_cb, c};
   const unsigned col_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * col_geom.nrb);
   // dU = L^T dy per tile column (L of the last L-step)
   ok(timed(5, st, [&] {
@@ -745,7 +750,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   const unsigned rb_threads = static_cast<unsigned>(kWave * ((s.b2 + rb_keys - 1) / rb_keys));
   const size_t ra_lds = rside_bwd_lds_bytes<T, D>(bg.b2p);
   constexpr int dq_rows = C::kDqRW * C::kDqNW * 16;
-  const LGeom row_geom{BH, N, s.b1, s.b1, s.b2, s.t, (ngmax + dq_rows - 1) / dq_rows, c};
+  const LGeom row_geom{BH, Nq, s.b1, s.b1q, s.b2, s.t, (ngmax + dq_rows - 1) / dq_rows, c};
   const unsigned row_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * row_geom.nrb);
 
   for (int i = T_; i >= 1; --i) {
@@ -804,7 +809,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
       const int ncb = w.ldl / cb;
       const unsigned grid = static_cast<unsigned>(s.BH * ncb * w.nsplit);
       ok(timed(8, st, [&] {
-        kb_dkbar<T, D, C::kGmRW, C::kGmNW><<<grid, C::kGmNW * kWave, 0, st>>>(q, dl, w.ldl, part, BH, N, s.b1, ncb,
+        kb_dkbar<T, D, C::kGmRW, C::kGmNW><<<grid, C::kGmNW * kWave, 0, st>>>(q, dl, w.ldl, part, BH, Nq, s.b1, ncb,
                                                                              w.nsplit, w.chunk);
       }));
       const long long threads = s.BH * s.b1 * (D / 4);
@@ -860,9 +865,12 @@ int fwd_train(const void* q, const void* k, const void* v, void* out, const Shap
   if (rc != MONARCH_OK) return rc;
   rc = check_train(s, elem, state, state_bytes);
   if (rc != MONARCH_OK) return rc;
-  const size_t io = static_cast<size_t>(s.BH * s.N * s.d) * elem;
-  for (const void* p : {q, k, v, static_cast<const void*>(out)})
-    if (overlaps(p, io, state, state_bytes)) return MONARCH_EINVAL;
+  const size_t qio = static_cast<size_t>(s.BH * s.Nq * s.d) * elem;
+  const size_t kio = static_cast<size_t>(s.BH * s.N * s.d) * elem;
+  const void* ios[] = {q, k, v, out};
+  const size_t iosz[] = {qio, kio, kio, qio};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(ios[i], iosz[i], state, state_bytes)) return MONARCH_EINVAL;
   const TrainState t = train_layout(s, elem);
   unsigned char* sp = static_cast<unsigned char*>(state);
   hipError_t e = hipSuccess;
@@ -896,15 +904,18 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
   if (!dout || !dq || !dk || !dv) return MONARCH_EINVAL;
   rc = check_train(s, elem, state, state_bytes);
   if (rc != MONARCH_OK) return rc;
-  const size_t io = static_cast<size_t>(s.BH * s.N * s.d) * elem;
+  // q, out, dout and dq have Nq rows per head; k, v, dk and dv N
+  const size_t qio = static_cast<size_t>(s.BH * s.Nq * s.d) * elem;
+  const size_t kio = static_cast<size_t>(s.BH * s.N * s.d) * elem;
   const void* ins[] = {q, k, v, out, dout, state};
-  const size_t insz[] = {io, io, io, io, io, state_bytes};
+  const size_t insz[] = {qio, kio, kio, qio, qio, state_bytes};
   void* outs[] = {dq, dk, dv};
+  const size_t outsz[] = {qio, kio, kio};
   for (int i = 0; i < 3; ++i) {
     for (int j = 0; j < 6; ++j)
-      if (overlaps(outs[i], io, ins[j], insz[j])) return MONARCH_EINVAL;
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return MONARCH_EINVAL;
     for (int j = 0; j < i; ++j)
-      if (overlaps(outs[i], io, outs[j], io)) return MONARCH_EINVAL;
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return MONARCH_EINVAL;
   }
   const int b2p = (s.b2 + 31) / 32 * 32;
   const int DK = s.d < 32 ? 32 : s.d;
@@ -1049,6 +1060,31 @@ int monarch_attn_bwd(const void* q, const void* k, const void* v, const void* ou
   const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   return bwd(q, k, v, out, dout, dq, dk, dv, s, dtype, state, state_bytes,
              static_cast<hipStream_t>(stream));
+}
+
+size_t monarch_attn_train_state_bytes_kv(int B, int H, int fq, int f, int h, int w, int d, int b1, int b2,
+                                         int tiles, int iters, int dtype) {
+  const size_t elem = elem_size(dtype);
+  if (elem == 0) return 0;
+  const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
+  static const char dummy[4] = {0};
+  if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
+  return train_layout(s, elem).total;
+}
+
+int monarch_attn_fwd_train_kv(const void* q, const void* k, const void* v, void* out, int B, int H, int fq,
+                              int f, int h, int w, int d, int b1, int b2, int tiles, int iters, int dtype,
+                              void* state, size_t state_bytes, void* stream) {
+  const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
+  return fwd_train(q, k, v, out, s, dtype, state, state_bytes, static_cast<hipStream_t>(stream));
+}
+
+int monarch_attn_bwd_kv(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        void* dq, void* dk, void* dv, int B, int H, int fq, int f, int h, int w, int d,
+                        int b1, int b2, int tiles, int iters, int dtype, void* state, size_t state_bytes,
+                        void* stream) {
+  const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
+  return bwd(q, k, v, out, dout, dq, dk, dv, s, dtype, state, state_bytes, static_cast<hipStream_t>(stream));
 }
 
 const char* monarch_attn_status_string(int status) {

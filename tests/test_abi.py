@@ -200,3 +200,39 @@ def test_adaptive_workspace_and_bad_arguments():
     assert rc == M.MONARCH_EINVAL
     rc = lib.monarch_attn_fwd_adaptive_ws(*p[:4], *base, 1e-3, 0, p[4], p[5], need - 256, None)
     assert rc == M.MONARCH_ENOMEM
+
+
+# ---- training for a chunk against cached keys
+def test_kv_train_state_bytes():
+    B, H, fq, f, h, w, d, b1, b2, t = 1, 40, 3, 21, 45, 80, 128, 945, 80, 1
+    N, Nq, BH, e = f * h * w, fq * h * w, B * H, 2
+    for T in (1, 2):
+        per_iter = _align(BH * Nq * 4) + _align(BH * t * N * 4) + _align(BH * t * N * d * e)
+        expect = (_align(BH * b1 * d * e) + _align(BH * b1 * 4) + T * per_iter + _align(BH * t * N * d * e)
+                  + (T - 1) * (_align(BH * t * N * d * e) + _align(BH * t * N * 4)))
+        assert M.monarch_attn_train_state_bytes_kv(B, H, fq, f, h, w, d, b1, b2, t, T, 0) == expect
+        # fq == f is the square layer
+        assert (M.monarch_attn_train_state_bytes_kv(B, H, f, f, h, w, d, b1, b2, 4, T, 0)
+                == M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, 4, T, 0))
+    assert M.monarch_attn_train_state_bytes_kv(B, H, fq, f, h, w, d, b1 + 1, b2, t, 1, 0) == 0
+
+
+def _bwd_kv(state_bytes=None, fq=1, f=4, h=3, w=5, d=64, b1=12, b2=5, t=1, T=1, alias=None):
+    p = _train_ptrs(9)  # q k v out dout dq dk dv state
+    if alias is not None:
+        p[alias[0]] = p[alias[1]]
+    if state_bytes is None:
+        state_bytes = M.monarch_attn_train_state_bytes_kv(1, 2, fq, f, h, w, d, b1, b2, t, T, 0)
+    return M.lib().monarch_attn_bwd_kv(*p[:8], 1, 2, fq, f, h, w, d, b1, b2, t, T, 0, p[8], state_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alias=(5, 0)), M.MONARCH_EINVAL),          # dq aliases q
+    (dict(alias=(6, 3)), M.MONARCH_EINVAL),          # dk aliases out
+    (dict(t=4), M.MONARCH_EINVAL),                   # tiles > query blocks (3)
+    (dict(b1=6, b2=10), M.MONARCH_EINVAL),           # Nq = 15 not a multiple of b2
+    (dict(state_bytes=4096), M.MONARCH_ENOMEM),
+    (dict(d=48, state_bytes=1 << 30), M.MONARCH_EUNSUPPORTED),
+])
+def test_kv_bwd_bad_arguments_rejected_before_any_gpu_call(kw, status):
+    assert _bwd_kv(**kw) == status

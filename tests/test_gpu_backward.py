@@ -36,14 +36,23 @@ def run_train(wl, x, dyx):
     q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
     dy = to_device(dyx, "dy", wl.dtype)
     dt = M.MONARCH_BF16 if wl.dtype == "bf16" else M.MONARCH_F32
-    nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles, wl.iters,
-                                          dt)
-    state = torch.empty(nb, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
-    args = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
-    M.monarch_attn_fwd_train(q, k, v, out, *args, state)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, *args, state)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if wl.kv:
+        # a chunk of fq frames against all f frames
+        nb = M.monarch_attn_train_state_bytes_kv(wl.B, wl.H, wl.fq, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2,
+                                                 wl.tiles, wl.iters, dt)
+        state = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        args = (wl.fq, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
+        M.monarch_attn_fwd_train_kv(q, k, v, out, *args, state)
+        M.monarch_attn_bwd_kv(q, k, v, out, dy, dq, dk, dv, *args, state)
+    else:
+        nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles,
+                                              wl.iters, dt)
+        state = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        args = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
+        M.monarch_attn_fwd_train(q, k, v, out, *args, state)
+        M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, *args, state)
     torch.cuda.synchronize()
     return [to_host(t) for t in (out, dq, dk, dv)]
 
@@ -55,7 +64,7 @@ def rel_errors(got, ref):
 
 def compare_grad(wl, seed=0, heads=None, label="", iters=1):
     wl = wl.with_(iters=iters)
-    say(f"[case] bwd {label or wl.name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} blocks=({wl.b1},{wl.b2}) "
+    say(f"[case] bwd {label or wl.name} B={wl.B} H={wl.H} Nq={wl.Nq} N={wl.N} d={wl.d} blocks=({wl.b1},{wl.b2}) "
         f"t={wl.tiles} T={wl.iters} {wl.dtype} seed={seed}")
     x = I.make_inputs(wl, seed)
     dyx = I.make_cotangent(wl, seed)
@@ -188,3 +197,60 @@ def test_bwd_iters_edge_shapes(case):
 def test_bwd_three_iters_edge_shapes(case):
     name, B, H, d, f, h, w, b1, b2, t, dt = case
     compare_grad(I.Workload(name, B, H, d, f, h, w, b1, b2, t, 1, dt), seed=6, label=name, iters=3)
+
+
+# ---- a chunk of frames against cached keys (queries: the chunk's rows;
+# keys and values: all frames)
+@pytest.mark.parametrize("T", [1, 2])
+def test_bwd_kv_chunk480p_f32(T):
+    compare_grad(I.get_workload("chunk480p_kv").with_(H=2, dtype="f32"), label="chunk480p_kv-f32", iters=T)
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_bwd_kv_chunk480p_bf16(T):
+    compare_grad(I.get_workload("chunk480p_kv"), heads=[0, 11], iters=T)
+
+
+def test_bwd_kv_chunk720p_bf16():
+    compare_grad(I.get_workload("chunk720p_kv"), heads=[0, 39])
+
+
+KV_EDGE = [
+    # name, B, H, d, fq, f, h, w, b1, b2, t, dtype
+    ("one_frame_of_four", 1, 2, 64, 1, 4, 3, 10, 12, 10, 1, "bf16"),
+    ("tiles_in_chunk", 2, 2, 32, 2, 5, 4, 6, 20, 6, 3, "bf16"),
+    ("blocks_off_grid", 1, 3, 16, 2, 6, 2, 9, 36, 3, 4, "f32"),
+    ("b2_1", 1, 2, 64, 1, 3, 5, 7, 105, 1, 2, "bf16"),
+    ("b2_128_f32", 1, 1, 128, 1, 2, 1, 128, 2, 128, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", KV_EDGE, ids=[c[0] for c in KV_EDGE])
+@pytest.mark.parametrize("T", [1, 2])
+def test_bwd_kv_edge_shapes(case, T):
+    name, B, H, d, fq, f, h, w, b1, b2, t, dt = case
+    compare_grad(I.Workload(name, B, H, d, f, h, w, b1, b2, t, 1, dt, fq=fq), seed=4, label=name, iters=T)
+
+
+def test_bwd_kv_chunk_matches_square_layer_rows():
+    """The chunk's gradient against the square layer's over all frames with
+    tiles that cover the chunk with the same bounds and dy = 0 outside the
+    chunk, both on the GPU (fp32): same dk, dv; dq on the chunk's rows, 0
+    elsewhere."""
+    import structured_attention_video_monarch_amd as M
+    fq, f, h, w, d, t, T = 2, 6, 3, 8, 64, 2, 2
+    b1, b2 = f * h, w
+    full = I.Workload("square", 1, 2, d, f, h, w, b1, b2, t * f // fq, T, "f32")
+    chunk = full.with_(fq=fq, tiles=t)
+    x = I.make_inputs(full, 9)
+    N, Nq = full.N, chunk.Nq
+    dyx = I.make_cotangent(chunk, 9)
+    dy_full = np.zeros((1, 2, N, d), dtype=np.float32)
+    dy_full[:, :, N - Nq:] = dyx["dy"]
+    _, fdq, fdk, fdv = run_train(full, x, {"dy": dy_full})
+    xc = {"q": x["q"][:, :, N - Nq:], "k": x["k"], "v": x["v"]}
+    _, cdq, cdk, cdv = run_train(chunk, xc, dyx)
+    assert np.max(np.abs(fdq[:, :, :N - Nq])) == 0.0
+    for name, a, b in (("dq", cdq, fdq[:, :, N - Nq:]), ("dk", cdk, fdk), ("dv", cdv, fdv)):
+        err = np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30)
+        assert err <= 2e-6, (name, err)

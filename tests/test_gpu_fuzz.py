@@ -5,7 +5,8 @@ fixed): batch and heads, head dimension d in {16, 32, 64, 128}, a small
 video (f, h, w), blocks (b1, b2) with b2 any divisor of N up to 128 (so the
 blocks need not follow the frame grid), tiles, iterations 1-3 and the dtype;
 chunk cases also draw the chunk's frame count.  The forward, the chunk
-against cached keys and the backward through every iteration are compared
+against cached keys and the backward through every iteration (square and
+chunk) are compared
 element by element with the same bars as the hand-picked cases
 (test_gpu_parity, test_gpu_kv, test_gpu_backward).
 """
@@ -29,13 +30,14 @@ def _need_gpu():
 
 
 def draw(kind, seed):
-    rng = np.random.default_rng([7001, {"fwd": 0, "kv": 1, "bwd": 2}[kind], seed])
+    rng = np.random.default_rng([7001, {"fwd": 0, "kv": 1, "bwd": 2, "bwdkv": 3}[kind], seed])
+    chunk = kind in ("kv", "bwdkv")
     d = int(rng.choice([16, 32, 64, 128]))
     f, h, w = (int(rng.integers(1, hi + 1)) for hi in (4, 8, 20))
-    if kind == "kv" and f == 1:
+    if chunk and f == 1:
         f = 2
     N = f * h * w
-    fq = int(rng.integers(1, f)) if kind == "kv" else 0
+    fq = int(rng.integers(1, f)) if chunk else 0
     Nq = fq * h * w if fq else N
     divisors = [x for x in range(1, min(N, 128) + 1) if N % x == 0 and Nq % x == 0]
     b2 = int(rng.choice(divisors))
@@ -64,3 +66,9 @@ def test_fuzz_chunk_against_cached_keys(seed):
 def test_fuzz_backward(seed):
     wl = draw("bwd", seed)
     compare_grad(wl, seed=seed, label=f"{wl.name} f,h,w=({wl.f},{wl.h},{wl.w})", iters=wl.iters)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fuzz_backward_chunk(seed):
+    wl = draw("bwdkv", seed)
+    compare_grad(wl, seed=seed, label=f"{wl.name} fq/f={wl.fq}/{wl.f} h,w=({wl.h},{wl.w})", iters=wl.iters)
