@@ -274,20 +274,30 @@ def main():
 
     iters_used = None
     if args.tol is not None:
-        if wl.kv or args.mode == "train":
-            print("bench.py: --tol applies to the square forward only", file=sys.stderr)
+        if args.mode == "train":
+            print("bench.py: --tol applies to the forward only", file=sys.stderr)
             sys.exit(2)
         del ws
-        nb = M.monarch_attn_adaptive_workspace_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2,
-                                                     wl.tiles, wl.iters, dtc)
-        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         iters_used = torch.empty((wl.B, wl.H), dtype=torch.int32, device=dev)
+        if wl.kv:
+            nb = M.monarch_attn_adaptive_kv_workspace_bytes(wl.B, wl.H, wl.fq, wl.f, wl.h, wl.w, wl.d, wl.b1,
+                                                            wl.b2, wl.tiles, wl.iters, dtc)
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
 
-        def step():
-            M.monarch_attn_fwd_adaptive(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters,
-                                        args.tol, iters_used=iters_used, workspace=ws, stream=stream)
+            def step():
+                M.monarch_attn_fwd_adaptive_kv(q, k, v, out, wl.fq, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles,
+                                               wl.iters, args.tol, iters_used=iters_used, workspace=ws,
+                                               stream=stream)
+        else:
+            nb = M.monarch_attn_adaptive_workspace_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2,
+                                                         wl.tiles, wl.iters, dtc)
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
 
-    if wl.kv:
+            def step():
+                M.monarch_attn_fwd_adaptive(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters,
+                                            args.tol, iters_used=iters_used, workspace=ws, stream=stream)
+
+    if wl.kv and args.tol is None:
         def step():
             M.monarch_attn_fwd_kv(q, k, v, out, wl.fq, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles,
                                   wl.iters, workspace=ws, stream=stream)

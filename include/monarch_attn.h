@@ -115,6 +115,16 @@ int monarch_attn_fwd_adaptive_ws(const void* q, const void* k, const void* v, vo
                                  int b1, int b2, int tiles, int max_iters, float tol, int dtype,
                                  int* iters_used, void* workspace, size_t workspace_bytes,
                                  void* stream);
+/* The same for a chunk of fq frames against all f frames (see
+ * monarch_attn_fwd_kv below): the objective sums the chunk's Nq = fq*h*w
+ * query rows and the gain is taken per query token. */
+size_t monarch_attn_adaptive_kv_workspace_bytes(int B, int H, int fq, int f, int h, int w, int d,
+                                                int b1, int b2, int tiles, int max_iters, int dtype);
+int monarch_attn_fwd_adaptive_kv_ws(const void* q, const void* k, const void* v, void* out,
+                                    int B, int H, int fq, int f, int h, int w, int d,
+                                    int b1, int b2, int tiles, int max_iters, float tol, int dtype,
+                                    int* iters_used, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /* ---- chunked queries against cached keys ----
  * Autoregressive video generation produces a chunk of frames at a time; the

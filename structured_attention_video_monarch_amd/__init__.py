@@ -65,6 +65,11 @@ def _declare(lib):
     lib.monarch_attn_fwd_train.restype = c_int
     lib.monarch_attn_bwd.argtypes = [c_void_p] * 8 + tdims + [c_int, c_void_p, c_size_t, c_void_p]
     lib.monarch_attn_bwd.restype = c_int
+    lib.monarch_attn_adaptive_kv_workspace_bytes.argtypes = kdims + [c_int]
+    lib.monarch_attn_adaptive_kv_workspace_bytes.restype = c_size_t
+    lib.monarch_attn_fwd_adaptive_kv_ws.argtypes = ([c_void_p] * 4 + kdims
+                                                    + [ctypes.c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p])
+    lib.monarch_attn_fwd_adaptive_kv_ws.restype = c_int
     lib.monarch_attn_train_state_bytes_kv.argtypes = kdims + [c_int]
     lib.monarch_attn_train_state_bytes_kv.restype = c_size_t
     lib.monarch_attn_fwd_train_kv.argtypes = [c_void_p] * 4 + kdims + [c_int, c_void_p, c_size_t, c_void_p]
@@ -290,6 +295,35 @@ def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, f, h, w, b1, b2, tiles, ite
     _check(lib().monarch_attn_bwd(*ptrs, *dims, _dtype_code(q), sp, sn, _stream(stream)),
            "monarch_attn_bwd")
     return dq, dk, dv
+
+
+def monarch_attn_adaptive_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, max_iters,
+                                              dtype=MONARCH_BF16) -> int:
+    return int(lib().monarch_attn_adaptive_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, max_iters,
+                                                              dtype))
+
+
+def monarch_attn_fwd_adaptive_kv(q, k, v, out, fq, f, h, w, b1, b2, tiles, max_iters, tol, iters_used=None,
+                                 workspace=None, stream=None):
+    """monarch_attn_fwd_adaptive for a chunk of fq frames against all f frames.
+    Returns (out, iters_used)."""
+    import torch
+    _kv_tensors(q, fq, f, h, w, [("q", q), ("out", out)], [("k", k), ("v", v)])
+    B, H, _, d = q.shape
+    dt = _dtype_code(q)
+    if iters_used is None:
+        iters_used = torch.empty((B, H), dtype=torch.int32, device=q.device)
+    if not iters_used.is_cuda or iters_used.dtype != torch.int32 or iters_used.numel() != B * H:
+        raise ValueError("iters_used must be an int32 GPU tensor of B*H elements")
+    if workspace is None:
+        nb = monarch_attn_adaptive_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, max_iters, dt)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
+    _check(lib().monarch_attn_fwd_adaptive_kv_ws(*ptrs, B, H, fq, f, h, w, d, b1, b2, tiles, max_iters, float(tol),
+                                                 dt, ctypes.c_void_p(iters_used.data_ptr()),
+                                                 ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                                 _stream(stream)), "monarch_attn_fwd_adaptive_kv_ws")
+    return out, iters_used
 
 
 def monarch_attn_train_state_bytes_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters, dtype=MONARCH_BF16) -> int:

@@ -1012,6 +1012,25 @@ int monarch_attn_fwd_adaptive_ws(const void* q, const void* k, const void* v, vo
                       static_cast<hipStream_t>(stream));
 }
 
+size_t monarch_attn_adaptive_kv_workspace_bytes(int B, int H, int fq, int f, int h, int w, int d, int b1, int b2,
+                                                int tiles, int max_iters, int dtype) {
+  const size_t elem = elem_size(dtype);
+  if (elem == 0) return 0;
+  const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, max_iters);
+  static const char dummy[4] = {0};
+  if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
+  return adaptive_bytes(s, elem, nullptr);
+}
+
+int monarch_attn_fwd_adaptive_kv_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int fq,
+                                    int f, int h, int w, int d, int b1, int b2, int tiles, int max_iters,
+                                    float tol, int dtype, int* iters_used, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, max_iters);
+  return fwd_adaptive(q, k, v, out, s, dtype, tol, iters_used, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream));
+}
+
 size_t monarch_attn_kv_workspace_bytes(int B, int H, int fq, int f, int h, int w, int d, int b1, int b2,
                                        int tiles, int iters, int dtype) {
   const size_t elem = elem_size(dtype);

@@ -236,3 +236,21 @@ def _bwd_kv(state_bytes=None, fq=1, f=4, h=3, w=5, d=64, b1=12, b2=5, t=1, T=1, 
 ])
 def test_kv_bwd_bad_arguments_rejected_before_any_gpu_call(kw, status):
     assert _bwd_kv(**kw) == status
+
+
+def test_adaptive_kv_workspace_and_bad_arguments():
+    shape = (1, 40, 3, 21, 45, 80, 128, 945, 80, 1, 10, 0)
+    nb = M.monarch_attn_adaptive_kv_workspace_bytes(*shape)
+    assert nb == M.monarch_attn_kv_workspace_bytes(*shape) + _align(40 * 8)
+    p = _train_ptrs(6)  # q k v out iters_used workspace
+    base = (1, 2, 1, 4, 3, 5, 64, 12, 5, 1, 10)
+    lib = M.lib()
+    need = M.monarch_attn_adaptive_kv_workspace_bytes(*base, 0)
+    assert lib.monarch_attn_fwd_adaptive_kv_ws(*p[:4], *base, float("nan"), 0, p[4], p[5], need,
+                                               None) == M.MONARCH_EINVAL
+    assert lib.monarch_attn_fwd_adaptive_kv_ws(*p[:4], *base, 1e-3, 0, None, p[5], need, None) == M.MONARCH_EINVAL
+    assert lib.monarch_attn_fwd_adaptive_kv_ws(*p[:4], *base, 1e-3, 0, p[4], p[5], need - 256,
+                                               None) == M.MONARCH_ENOMEM
+    bad = (1, 2, 1, 4, 3, 5, 64, 12, 5, 4, 10)      # tiles 4 > query blocks 3
+    assert lib.monarch_attn_fwd_adaptive_kv_ws(*p[:4], *bad, 1e-3, 0, p[4], p[5], 1 << 30,
+                                               None) == M.MONARCH_EINVAL

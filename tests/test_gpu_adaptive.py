@@ -32,7 +32,11 @@ def run_adaptive(wl, x, max_iters, tol):
     import structured_attention_video_monarch_amd as M
     q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
     out = torch.empty_like(q)
-    _, used = M.monarch_attn_fwd_adaptive(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, max_iters, tol)
+    if wl.kv:
+        _, used = M.monarch_attn_fwd_adaptive_kv(q, k, v, out, wl.fq, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles,
+                                                 max_iters, tol)
+    else:
+        _, used = M.monarch_attn_fwd_adaptive(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, max_iters, tol)
     torch.cuda.synchronize()
     return out, used.cpu().numpy()
 
@@ -43,7 +47,7 @@ def check_against_oracle(wl, x, y, used, max_iters, tol, heads):
         for h in heads:
             ref, used_o, F = oracle.monarch_head_adaptive(x["q"][b, h], x["k"][b, h], x["v"][b, h], wl.b1, wl.b2,
                                                           wl.tiles, max_iters, tol)
-            assert int(used[b, h]) == used_o, (b, h, int(used[b, h]), used_o, np.diff(F) / wl.N)
+            assert int(used[b, h]) == used_o, (b, h, int(used[b, h]), used_o, np.diff(F) / wl.Nq)
             mx, mean = errors(to_host(y)[b, h], ref)
             worst = (max(worst[0], mx), max(worst[1], mean))
             if wl.dtype == "bf16":
@@ -114,3 +118,29 @@ def test_adaptive_f32_small():
     y, used = run_adaptive(wl, x, 8, 1e-4)
     worst = check_against_oracle(wl, x, y, used, 8, 1e-4, heads=[0, 1])
     say(f"[ok] adaptive f32: {used.tolist()} max-abs {worst[0]:.3e}")
+
+
+# ---- a chunk of frames against cached keys: the objective sums the chunk's rows
+@pytest.mark.parametrize("tol", [1e-3, 1e-1])
+def test_adaptive_kv_chunk480p(tol):
+    wl = I.get_workload("chunk480p_kv")
+    say(f"[case] adaptive chunk480p_kv max_iters=10 tol={tol}")
+    x = I.make_inputs(wl, 0)
+    y, used = run_adaptive(wl, x, 10, tol)
+    worst = check_against_oracle(wl, x, y, used, 10, tol, heads=[0, 5, 11])
+    say(f"[ok] adaptive chunk480p_kv tol={tol}: iterations {used.tolist()}, max-abs {worst[0]:.3e} "
+        f"mean-abs {worst[1]:.3e}")
+
+
+def test_adaptive_kv_equals_fixed_iterations():
+    import structured_attention_video_monarch_amd as M
+    wl = I.get_workload("chunk720p_kv").with_(H=2)
+    say("[case] adaptive kv == fixed: chunk720p_kv max_iters=3 tol=-1")
+    x = I.make_inputs(wl, 1)
+    y, used = run_adaptive(wl, x, 3, -1.0)
+    assert np.all(used == 3), used
+    q, k, v = (to_device(x, n, "bf16") for n in "qkv")
+    ref = torch.empty_like(q)
+    M.monarch_attn_fwd_kv(q, k, v, ref, wl.fq, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
