@@ -610,7 +610,7 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
                                                     const float* __restrict__ h2,
                                                     const float* __restrict__ lse, const T* __restrict__ u,
                                                     const T* __restrict__ gq, const float* __restrict__ ev,
-                                                    float* __restrict__ delta, T* __restrict__ dq,
+                                                    T* __restrict__ dq,
                                                     float* __restrict__ dq_acc,
                                                     T* __restrict__ dlout, int ldl, LGeom p, float sc) {
   using E = Elem<T>;
@@ -743,7 +743,6 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     dlt[rt] = part - acce[rt][0];
-    if (ok && G == 0) delta[row] = dlt[rt];
   }
   __syncthreads();
 

@@ -629,7 +629,7 @@ template <> struct BwdCfg<float> {
 struct BwdWorkspace {
   int ldl;          // row stride of the stored s*dl (keys padded to the product's key block)
   int nsplit, chunk;  // split of the tokens in the key-mean product
-  size_t du, gq, ev, lser, rho, delta, dl, part, dkbar, dh, dqacc, dkacc, total;
+  size_t du, gq, ev, lser, rho, dl, part, dkbar, dh, dqacc, dkacc, total;
 };
 
 template <typename T>
@@ -666,8 +666,6 @@ BwdWorkspace bwd_layout_t(const Shape& s) {
   off += align_up(BH * tN * sizeof(float));
   w.rho = off;
   off += align_up(BH * tN * sizeof(float));
-  w.delta = off;
-  off += align_up(BH * Nq * sizeof(float));
   w.dl = off;
   off += align_up(BH * Nq * static_cast<size_t>(w.ldl) * elem);
   w.part = off;
@@ -710,7 +708,6 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   float* ev = reinterpret_cast<float*>(ws + w.ev);
   float* lser = reinterpret_cast<float*>(ws + w.lser);
   float* rho = reinterpret_cast<float*>(ws + w.rho);
-  float* delta = reinterpret_cast<float*>(ws + w.delta);
   T* dl = reinterpret_cast<T*>(ws + w.dl);
   float* part = reinterpret_cast<float*>(ws + w.part);
   float* dkbar = reinterpret_cast<float*>(ws + w.dkbar);
@@ -789,7 +786,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
       auto launch = [&](auto kern) {
         ok(timed(7, st, [&] {
           kern<<<row_grid, C::kDqNW * kWave, 0, st>>>(q, dout, out, keys_of(i), ent_of(i), bf.lse_of(i), bf.u, gq,
-                                                        ev, delta, dq, dqacc, dl, w.ldl, row_geom, sc);
+                                                        ev, dq, dqacc, dl, w.ldl, row_geom, sc);
         }));
       };
       constexpr int RW = C::kDqRW, NW = C::kDqNW, SP = C::kDqStep;
