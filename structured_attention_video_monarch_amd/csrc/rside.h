@@ -33,9 +33,13 @@ inline size_t rside_lds_bytes(int D, int b2p, bool last) {
   return sizeof(T) * static_cast<size_t>(b2p) * (D < 32 ? 32 : D) * (last ? 2 : 1);
 }
 
-// Tiles whose aggregated queries one wave loads together (bf16).
+// Tiles whose aggregated queries one wave loads together (bf16), for the
+// last R-step and for the ones before it (which also form the entropy).
 #ifndef MONARCH_RSTEP_TB
 #define MONARCH_RSTEP_TB 2
+#endif
+#ifndef MONARCH_RSTEP_TB_MID
+#define MONARCH_RSTEP_TB_MID 1
 #endif
 
 template <typename T, int D, bool LAST>
@@ -90,7 +94,7 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
     }
   }
   // aggregated queries of up to TB tiles in flight at once
-  constexpr int TB = sizeof(T) == 2 ? MONARCH_RSTEP_TB : 1;
+  constexpr int TB = sizeof(T) == 2 ? (LAST ? MONARCH_RSTEP_TB : MONARCH_RSTEP_TB_MID) : 1;
   typename E::frag bq[TB][KS];
   auto load_queries = [&](int g0) {
 #pragma unroll
@@ -128,40 +132,59 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
           }
       }
     }
-    // softmax over c2 for column a2: lane holds c2 = 32cp + 8G + j
+    // softmax over c2 for column a2: lane holds c2 = 32cp + 8G + j.  Keys
+    // past b2 get the finite logit kMaskLogit: 2^(x - m) is exactly 0 for
+    // them and x * 0 stays 0 in the entropy sum below.
+    constexpr float kMaskLogit = -1e30f;
     float x[MAXCP][8];
-    float mx = -1e30f;
+    float mx = kMaskLogit;
 #pragma unroll
     for (int cp = 0; cp < MAXCP; ++cp)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c2 = 32 * cp + 8 * G + j;
-        x[cp][j] = (cp < ncp && c2 < p.b2) ? S[cp][j >> 2][j & 3] * p.c : kNegInf;
+        x[cp][j] = (cp < ncp && c2 < p.b2) ? S[cp][j >> 2][j & 3] * p.c : kMaskLogit;
         mx = fmaxf(mx, x[cp][j]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float sum = 0.0f;
+    // sum of 2^(x - mx) and, for the entropy, of 2^(x - mx) * x; sum_c2 R x
+    // is their ratio.  Both are taken in one pass, as each exponential is
+    // made, so that none of them stays live.
+    float sum = 0.0f, sumx = 0.0f;
 #pragma unroll
     for (int cp = 0; cp < MAXCP; ++cp)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum += fast_exp2(x[cp][j] - mx);
+      for (int j = 0; j < 8; ++j) {
+        const float e = fast_exp2(x[cp][j] - mx);
+        sum += e;
+        if (!LAST) sumx = __builtin_fmaf(e, x[cp][j], sumx);
+      }
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
     const float lse2 = mx + log2f(sum);
+    // entropy in bits (the unit of the L-step's log2 logits):
+    // H2 = log2(sum 2^x) - sum R x = H / ln 2, sum R x = sumx / sum.  It is
+    // finished here, and the barrier keeps the compiler from sinking the sum
+    // to the store below (which would keep every exponential live across the
+    // products)
+    float h2 = 0.0f;
+    if (!LAST) {
+      sumx += __shfl_xor(sumx, 16);
+      sumx += __shfl_xor(sumx, 32);
+      h2 = lse2 - sumx / sum;
+      __builtin_amdgcn_sched_barrier(0);
+    }
     typename E::frag pf[MAXCP];
-    float rx = 0.0f;  // sum_c2 R * x (log2 units), for the entropy
 #pragma unroll
     for (int cp = 0; cp < MAXCP; ++cp) {
       float w[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        w[j] = fast_exp2(x[cp][j] - lse2);
-        if (!LAST && w[j] > 0.0f) rx += w[j] * x[cp][j];
-      }
+      for (int j = 0; j < 8; ++j) w[j] = fast_exp2(x[cp][j] - lse2);
       pf[cp] = E::pack(w);
     }
     // X^T P^T (X = V, or K for the next keys): rows d, columns a2
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[NACC][2][1];
 #pragma unroll
     for (int dp = 0; dp < NACC; ++dp) {
@@ -197,13 +220,7 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
         E::store4(dst + 4 * G, o);
       }
     }
-    if (!LAST) {
-      rx += __shfl_xor(rx, 16);
-      rx += __shfl_xor(rx, 32);
-      // entropy in bits (the unit of the L-step's log2 logits):
-      // H2 = log2(sum 2^x) - sum R x = H / ln 2
-      if (row_ok && G == 0) hent[row] = lse2 - rx;
-    }
+    if (!LAST && row_ok && G == 0) hent[row] = h2;
   }
   }
 }
