@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MonarchAttention fwd tokens/s & layer-calls/s at 1 MI355X; % MFMA/HBM roofline"
-METRIC_TRAIN = ("MonarchAttention one-iteration training step (fwd + bwd) tokens/s at 1 MI355X; "
+METRIC_TRAIN = ("MonarchAttention {iters}-iteration training step (fwd + bwd) tokens/s at 1 MI355X; "
                 "% MFMA/HBM roofline")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
@@ -71,7 +71,7 @@ def algorithmic_work(wl, it_last=True):
         "k_aggregate": (BH * 2.0 * Nq * b1 * d, BH * (nqd + 4 * Nq + t * nd)),
         "k_rstep": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 2 * nd)),
         "k_apply": (BH * 2.0 * Nq * b1 * d, BH * (2 * nqd + 4 * Nq + t * nd)),
-        # backward (one iteration), chain-rule products only (no logit
+        # backward (the one-iteration form), chain-rule products only (no logit
         # recomputation, no stored s*dl), per (batch, head); the row side
         # has the Nq query tokens, the key side t*N rows (tile, key block, a2):
         #   kb_du       dU = L^T dy                      2 Nq b1 d;  q, dy, lse in, dU out
@@ -374,7 +374,7 @@ def main():
 
     total_flops = sum(work[kn][0] * kernels[kn]["launches_per_step"] for kn in kernels)
     res = {
-        "metric": METRIC if args.mode == "fwd" else METRIC_TRAIN,
+        "metric": METRIC if args.mode == "fwd" else METRIC_TRAIN.format(iters=wl.iters),
         "value": round(wl.B * wl.Nq / (ms_step / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,

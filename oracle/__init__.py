@@ -1,5 +1,6 @@
-"""CPU oracle (float64 numpy) for the tiled MonarchAttention forward and the
-gradient of its one-iteration form.
+"""CPU oracle (float64 numpy) for the tiled MonarchAttention forward and its
+gradient through one or several unrolled iterations (square layer, or a
+chunk of query frames against cached keys).
 
 Test infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline use it; the GPU library does not.

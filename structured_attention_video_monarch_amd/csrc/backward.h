@@ -1,9 +1,11 @@
-// Backward kernels of the one-iteration MonarchAttention: the gradient of
-// sum(dy * y) with respect to q, k and v, as needed to finetune a video model
-// with the attention in place (yunpan.plus MonarchRT article, "Innovation 3:
-// finetuning and efficient kernels": the one-iteration form is trained).
+// Backward kernels of MonarchAttention: the gradient of sum(dy * y) with
+// respect to q, k and v, as needed to finetune a video model with the
+// attention in place (yunpan.plus MonarchRT article, "Innovation 3:
+// finetuning and efficient kernels": the one-iteration form is trained),
+// through one or several unrolled iterations, for the square layer and for a
+// chunk of query frames against cached keys (query blocks b1r, key blocks b1).
 //
-// Forward with R starting uniform (keys of the L-step are the block means
+// One iteration, R starting uniform (keys of the L-step are the block means
 // Kbar, whose entropy term is the same for every block and cancels):
 //   L = softmax_c1(s<q_n, Kbar[c1]>), beta = sum_(a1 in g) L,
 //   Qh = sum_(a1 in g) L q / beta, R = softmax_c2(s<Qh, k>), U = R V,
@@ -19,6 +21,10 @@
 //                   then kb_dkbar_reduce)
 //   kb_rside_b      per key block c1: dv = sum_(g,a2) R dU,
 //                   dk = s sum_(g,a2) dz Qh + dKbar / b2
+// Several iterations: the L-step of iteration i > 1 has the keys Kt = R k and
+// entropies H of the R-step before; its dl gives dKt and dH (kb_dktil), which
+// the R-step kernels of iteration i - 1 take back (their MID forms), and dq,
+// dk add up over the iterations in fp32.
 // MFMA operand conventions and the slot permutation are those of the forward
 // kernels (device_common.h); logits are in log2 units with c = log2(e)/sqrt(d)
 // and the log-sum-exps saved by the forward are in the same units.
