@@ -148,23 +148,27 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // sum of 2^(x - mx) and, for the entropy, of 2^(x - mx) * x; sum_c2 R x
-    // is their ratio.  Both are taken in one pass, as each exponential is
-    // made, so that none of them stays live.
+    // sum of 2^(x - mx) and, for the entropy, of 2^(x - mx) (x - mx);
+    // sum_c2 R (x - mx) is their ratio.  Both are taken in one pass, as each
+    // exponential is made, so that none of them stays live.
     float sum = 0.0f, sumx = 0.0f;
 #pragma unroll
     for (int cp = 0; cp < MAXCP; ++cp)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float e = fast_exp2(x[cp][j] - mx);
+        const float dx = x[cp][j] - mx;
+        const float e = fast_exp2(dx);
         sum += e;
-        if (!LAST) sumx = __builtin_fmaf(e, x[cp][j], sumx);
+        if (!LAST) sumx = __builtin_fmaf(e, dx, sumx);
       }
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
-    const float lse2 = mx + log2f(sum);
-    // entropy in bits (the unit of the L-step's log2 logits):
-    // H2 = log2(sum 2^x) - sum R x = H / ln 2, sum R x = sumx / sum.  It is
+    const float lsum = log2f(sum);
+    const float lse2 = mx + lsum;
+    // entropy in bits (the unit of the L-step's log2 logits), taken about
+    // the row maximum so that no large terms cancel when the logits are
+    // large: H2 = log2(sum 2^x) - sum R x = log2(sum 2^(x - mx)) -
+    // sum R (x - mx) = H / ln 2, with sum R (x - mx) = sumx / sum.  It is
     // finished here, and the barrier keeps the compiler from sinking the sum
     // to the store below (which would keep every exponential live across the
     // products)
@@ -172,7 +176,7 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
     if (!LAST) {
       sumx += __shfl_xor(sumx, 16);
       sumx += __shfl_xor(sumx, 32);
-      h2 = lse2 - sumx / sum;
+      h2 = lsum - sumx / sum;
       __builtin_amdgcn_sched_barrier(0);
     }
     typename E::frag pf[MAXCP];

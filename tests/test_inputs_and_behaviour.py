@@ -7,6 +7,7 @@ give more accuracy (same article, "Innovation 2: tiled Monarch
 parameterisation"; atlas.scime.ai summary, "Surprising findings").
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -117,3 +118,24 @@ def test_chunk_queries_are_the_tail_of_the_full_draw():
     assert x["q"].shape == (1, 2, 2 * 3 * 4, 16) and x["k"].shape == (1, 2, 6 * 3 * 4, 16)
     assert np.array_equal(x["q_bits"], full["q_bits"][:, :, -24:])
     assert np.array_equal(x["k_bits"], full["k_bits"]) and np.array_equal(x["v_bits"], full["v_bits"])
+
+
+def test_float32_steps_helper_is_the_oracle_in_float32():
+    """The float32 evaluation used as the scale for ill-conditioned fp32 cases
+    computes the oracle's method: float32 results, within float32 rounding of
+    the float64 oracle on ordinary inputs."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from f32_steps import float32_steps
+    import oracle
+    f32_fwd, f32_grad = float32_steps()
+    rng = np.random.default_rng(3)
+    b1, b2, t, d = 6, 4, 2, 8
+    q, k, v, dy = (rng.standard_normal((b1 * b2, d)) for _ in range(4))
+    for T in (1, 2):
+        y32 = f32_fwd.monarch_head(q, k, v, b1, b2, t, T)
+        y64 = oracle.monarch_head(q, k, v, b1, b2, t, T)
+        assert y32.dtype == np.float32 and np.abs(y32 - y64).max() <= 1e-5
+        for a, b in zip(f32_grad.monarch_head_grad(q, k, v, dy, b1, b2, t, T),
+                        oracle.monarch_head_grad(q, k, v, dy, b1, b2, t, T)):
+            assert a.dtype == np.float32 and np.abs(a - b).max() <= 1e-5 * max(1.0, np.abs(b).max())
