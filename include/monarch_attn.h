@@ -1,5 +1,7 @@
 /*
- * monarch_attn.h -- C ABI of the MonarchAttention forward for AMD MI355X (gfx950).
+ * monarch_attn.h -- C ABI of MonarchAttention for AMD MI355X (gfx950): the
+ * forward (square layer, or a chunk of frames against cached keys; fixed
+ * iteration count or early stop) and its gradient.
  *
  * The operation (MonarchRT pages):
  *   Video self-attention over N = f*h*w tokens is approximated by a Monarch
