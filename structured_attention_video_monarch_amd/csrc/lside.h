@@ -672,9 +672,16 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
   using Dma = TileDma<T, D, DK, kStep, NW>;
-  __shared__ __align__(16) T sK[2][kStep * DK];
-  __shared__ __align__(16) T sU[2][kStep * DK];
-  __shared__ __align__(16) float sH[2][kStep];
+  // the two stages' buffers are distinct LDS objects, used in a fixed
+  // alternation (see the stage loop): the compiler can then tell that the
+  // DMA into one never writes what the other stage reads, and the prefetch
+  // overlaps the products instead of being waited for at once
+  __shared__ __align__(16) T sK0[kStep * DK];
+  __shared__ __align__(16) T sK1[kStep * DK];
+  __shared__ __align__(16) T sU0[kStep * DK];
+  __shared__ __align__(16) T sU1[kStep * DK];
+  __shared__ __align__(16) float sH0[BCAST ? 1 : kStep];
+  __shared__ __align__(16) float sH1[BCAST ? 1 : kStep];
 
   ColItem it(p, RB);
   if (it.nrows <= 0) return;
@@ -691,13 +698,13 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
   const long long ustride = static_cast<long long>(p.b2) * D;
 
   const int nst = (p.b1 + kStep - 1) / kStep;
-  auto fetch = [&](int st, int buf) {
+  auto fetch = [&](int st, T* tK, T* tU, float* tH) {
     const int c1 = st * kStep;
-    Dma::issue(sK[buf], ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
-    Dma::issue(sU[buf], ucol + c1 * ustride, ustride, p.b1 - c1);
-    if (!BCAST && wave == NW - 1) dma_floats64(sH[buf], ks.h + static_cast<long long>(c1) * ks.hstride, ks.hstride, p.b1 - c1);
+    Dma::issue(tK, ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
+    Dma::issue(tU, ucol + c1 * ustride, ustride, p.b1 - c1);
+    if (!BCAST && wave == NW - 1) dma_floats64(tH, ks.h + static_cast<long long>(c1) * ks.hstride, ks.hstride, p.b1 - c1);
   };
-  fetch(0, 0);
+  fetch(0, sK0, sU0, sH0);
 
   typename E::frag bq[RW][KS];
   float nlrow[RW];  // -lse of the lane's rows
@@ -721,9 +728,9 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
       for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
   __syncthreads();
 
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nst) fetch(st + 1, cur ^ 1);
+  // one step: prefetch the next into (nK, nU, nH), products on (cK, cU, cH)
+  auto stage = [&](int st, const T* cK, const T* cU, const float* cH, T* nK, T* nU, float* nH) {
+    if (st + 1 < nst) fetch(st + 1, nK, nU, nH);
 #pragma unroll
     for (int half = 0; half < kHalves; ++half) {
       const int k0 = 32 * half;
@@ -733,12 +740,12 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
       const bool tail = c1_0 + 32 > p.b1;
       typename E::frag a[KS][2];
       typename E::frag v[NACC][2];
-      load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
-      load_cols<T, D, DK, NACC>(v, sU[cur], k0);
+      load_rows<T, DK, KS>(a, cK, k0, l16, G);
+      load_cols<T, D, DK, NACC>(v, cU, k0);
       float bias[8];
       if (!BCAST) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bias[j] = sH[cur][k0 + 8 * G + j];
+        for (int j = 0; j < 8; ++j) bias[j] = cH[k0 + 8 * G + j];
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x4 S[2][RW];
@@ -759,6 +766,10 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
       weighted_sum<T, D, NACC, RW>(acc, v, pf);
     }
     __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, sK0, sU0, sH0, sK1, sU1, sH1);
+    if (st + 1 < nst) stage(st + 1, sK1, sU1, sH1, sK0, sU0, sH0);
   }
 
   T* oh = out + static_cast<long long>(bh) * p.N * D;
