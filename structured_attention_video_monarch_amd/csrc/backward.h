@@ -102,9 +102,14 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
   using Dma = TileDma<T, D, DK, kStep, NW>;
-  __shared__ __align__(16) T sQ[2][kStep * DK];
-  __shared__ __align__(16) T sY[2][kStep * DK];
-  __shared__ __align__(16) float sLs[2][kStep];
+  // two stages' buffers as distinct LDS objects in a fixed alternation: the
+  // prefetch is not waited for before the current stage's reads
+  __shared__ __align__(16) T sQ0[kStep * DK];
+  __shared__ __align__(16) T sQ1[kStep * DK];
+  __shared__ __align__(16) T sY0[kStep * DK];
+  __shared__ __align__(16) T sY1[kStep * DK];
+  __shared__ __align__(16) float sL0[kStep];
+  __shared__ __align__(16) float sL1[kStep];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int cb = logical % p.nrb;
@@ -123,14 +128,14 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
   const long long qstride = static_cast<long long>(p.b2) * D;
   const long long gbase = (static_cast<long long>(bh) * p.t + g) * p.b1;  // (bh, g, c1 = 0)
 
-  auto fetch = [&](int st, int buf) {
+  auto fetch = [&](int st, T* tQ, T* tY, float* tL) {
     const long long n_first = hoff + static_cast<long long>(lo + st * kStep) * p.b2 + a2;
     const int nvalid = nrows - st * kStep;
-    Dma::issue(sQ[buf], q + n_first * D, qstride, nvalid);
-    Dma::issue(sY[buf], dy + n_first * D, qstride, nvalid);
-    if (wave == NW - 1) dma_floats64(sLs[buf], lse + n_first, p.b2, nvalid);
+    Dma::issue(tQ, q + n_first * D, qstride, nvalid);
+    Dma::issue(tY, dy + n_first * D, qstride, nvalid);
+    if (wave == NW - 1) dma_floats64(tL, lse + n_first, p.b2, nvalid);
   };
-  fetch(0, 0);
+  fetch(0, sQ0, sY0, sL0);
 
   typename E::frag bk[RW][KS];
   float hb[RW];  // entropy bias of the lane's key block
@@ -152,9 +157,8 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
     for (int rt = 0; rt < RW; ++rt) acc[dp][0][rt] = acc[dp][1][rt] = f32x4{0, 0, 0, 0};
   __syncthreads();
 
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nst) fetch(st + 1, cur ^ 1);
+  auto stage = [&](int st, const T* cQ, const T* cY, const float* cL, T* nQ, T* nY, float* nL) {
+    if (st + 1 < nst) fetch(st + 1, nQ, nY, nL);
 #pragma unroll
     for (int half = 0; half < kHalves; ++half) {
       const int k0 = 32 * half;
@@ -162,10 +166,10 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
       if (r0 >= nrows) break;
       const bool tail = r0 + 32 > nrows;
       typename E::frag a[KS][2];
-      load_rows<T, DK, KS>(a, sQ[cur], k0, l16, G);
+      load_rows<T, DK, KS>(a, cQ, k0, l16, G);
       float lr[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) lr[j] = sLs[cur][k0 + 8 * G + j];
+      for (int j = 0; j < 8; ++j) lr[j] = cL[k0 + 8 * G + j];
       f32x4 S[2][RW];
       logits<T, KS, RW>(S, a, bk);
       typename E::frag pf[RW];
@@ -181,10 +185,14 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
         pf[rt] = E::pack(w);
       }
       typename E::frag vv[NACC][2];
-      load_cols<T, D, DK, NACC>(vv, sY[cur], k0);
+      load_cols<T, D, DK, NACC>(vv, cY, k0);
       weighted_sum<T, D, NACC, RW>(acc, vv, pf);
     }
     __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, sQ0, sY0, sL0, sQ1, sY1, sL1);
+    if (st + 1 < nst) stage(st + 1, sQ1, sY1, sL1, sQ0, sY0, sL0);
   }
 
 #pragma unroll
@@ -629,11 +637,29 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   constexpr int HALVES = STEP / 32;
   // double-buffered for bf16; f32 tiles are twice as large: one buffer
   constexpr int NB = sizeof(T) == 2 ? 2 : 1;
-  __shared__ __align__(16) T sK[NB][STEP * DK];
-  __shared__ __align__(16) T sU[HAS_DY ? NB : 1][HAS_DY ? STEP * DK : 8];
-  __shared__ __align__(16) T sG[NB][STEP * DK];
-  __shared__ __align__(16) float sE[NB][64];  // 64: one float per lane of the DMA
-  __shared__ __align__(16) float sH[BCAST ? 1 : NB][64];
+  // the two stages' buffers are distinct LDS objects in a fixed alternation
+  // (the prefetch is not waited for before the current stage's reads); with
+  // one buffer the second set is the first
+  constexpr int TB = STEP * DK;
+  __shared__ __align__(16) T sK0[TB];
+  __shared__ __align__(16) T sK1[NB == 2 ? TB : 8];
+  __shared__ __align__(16) T sU0[HAS_DY ? TB : 8];
+  __shared__ __align__(16) T sU1[HAS_DY && NB == 2 ? TB : 8];
+  __shared__ __align__(16) T sG0[TB];
+  __shared__ __align__(16) T sG1[NB == 2 ? TB : 8];
+  __shared__ __align__(16) float sE0[64];  // 64: one float per lane of the DMA
+  __shared__ __align__(16) float sE1[64];
+  __shared__ __align__(16) float sH0[64];
+  __shared__ __align__(16) float sH1[64];
+  struct Stage {
+    T* K;
+    T* U;
+    T* G;
+    float* E;
+    float* H;
+  };
+  const Stage B0{sK0, sU0, sG0, sE0, sH0};
+  const Stage B1 = NB == 2 ? Stage{sK1, sU1, sG1, sE1, BCAST ? sH0 : sH1} : B0;
 
   ColItem it(p, RB);
   if (it.nrows <= 0) return;
@@ -648,15 +674,15 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   const long long ustride = static_cast<long long>(p.b2) * D;
 
   const int nst = (p.b1 + STEP - 1) / STEP;
-  auto fetch = [&](int st, int buf, bool with_u) {
+  auto fetch = [&](int st, const Stage& t, bool with_u) {
     const int c1 = st * STEP;
-    Dma::issue(sK[buf], ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
-    Dma::issue(sG[buf], gq + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
-    if (HAS_DY && with_u) Dma::issue(sU[buf], u + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
-    if (wave == NW - 1) dma_floats64(sE[buf], ev + cbase + static_cast<long long>(c1) * p.b2, p.b2, p.b1 - c1);
-    if (!BCAST && wave == 0) dma_floats64(sH[buf], ks.h + static_cast<long long>(c1) * ks.hstride, ks.hstride, p.b1 - c1);
+    Dma::issue(t.K, ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
+    Dma::issue(t.G, gq + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
+    if (HAS_DY && with_u) Dma::issue(t.U, u + (cbase + static_cast<long long>(c1) * p.b2) * D, ustride, p.b1 - c1);
+    if (wave == NW - 1) dma_floats64(t.E, ev + cbase + static_cast<long long>(c1) * p.b2, p.b2, p.b1 - c1);
+    if (!BCAST && wave == 0) dma_floats64(t.H, ks.h + static_cast<long long>(c1) * ks.hstride, ks.hstride, p.b1 - c1);
   };
-  fetch(0, 0, false);
+  fetch(0, B0, false);
 
   typename E::frag bq[RW][KS], bdy[RW][KS];
   float nl[RW];
@@ -684,9 +710,8 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   __syncthreads();
 
   // ---------------- pass 1: ghat and eps
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st % NB;
-    if (NB == 2 && st + 1 < nst) fetch(st + 1, cur ^ 1, false);
+  auto stage1 = [&](int st, const Stage& c, const Stage& n) {
+    if (NB == 2 && st + 1 < nst) fetch(st + 1, n, false);
 #pragma unroll
     for (int half = 0; half < HALVES; ++half) {
       const int k0 = 32 * half;
@@ -694,14 +719,14 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
       if (c1_0 >= p.b1) break;
       const bool tail = c1_0 + 32 > p.b1;
       typename E::frag a[KS][2];
-      load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
+      load_rows<T, DK, KS>(a, c.K, k0, l16, G);
       f32x4 S[2][RW];
       logits<T, KS, RW>(S, a, bq);
       float e8[8], hb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        e8[j] = sE[cur][k0 + 8 * G + j];
-        hb[j] = BCAST ? 0.0f : sH[BCAST ? 0 : cur][k0 + 8 * G + j];
+        e8[j] = c.E[k0 + 8 * G + j];
+        hb[j] = BCAST ? 0.0f : c.H[k0 + 8 * G + j];
       }
       const typename E::frag ef = E::pack(e8);
       typename E::frag pf[RW];
@@ -718,16 +743,20 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
         acce[rt] = E::mma(ef, pf[rt], acce[rt]);
       }
       typename E::frag vv[NACC][2];
-      load_cols<T, D, DK, NACC>(vv, sG[cur], k0);
+      load_cols<T, D, DK, NACC>(vv, c.G, k0);
       weighted_sum<T, D, NACC, RW>(acc, vv, pf);
     }
     __syncthreads();
     if (NB == 1 && st + 1 < nst) {
-      fetch(st + 1, 0, false);
+      fetch(st + 1, n, false);
       __syncthreads();
     }
+  };
+  for (int st = 0; st < nst; st += 2) {
+    stage1(st, B0, B1);
+    if (st + 1 < nst) stage1(st + 1, B1, B0);
   }
-  fetch(0, 0, true);
+  fetch(0, B0, true);
 
   // delta = <dy, y> + <q, ghat> - eps (every lane group holds a quarter of d)
   float dlt[RW];
@@ -753,9 +782,8 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   __syncthreads();
 
   // ---------------- pass 2: dl and dq
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st % NB;
-    if (NB == 2 && st + 1 < nst) fetch(st + 1, cur ^ 1, true);
+  auto stage2 = [&](int st, const Stage& c, const Stage& n) {
+    if (NB == 2 && st + 1 < nst) fetch(st + 1, n, true);
 #pragma unroll
     for (int half = 0; half < HALVES; ++half) {
       const int k0 = 32 * half;
@@ -764,22 +792,22 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
       const bool tail = c1_0 + 32 > p.b1;
       typename E::frag a[KS][2];
       f32x4 S[2][RW], X[2][RW];
-      load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
+      load_rows<T, DK, KS>(a, c.K, k0, l16, G);
       logits<T, KS, RW>(S, a, bq);
       if (HAS_DY) {
-        load_rows<T, DK, KS>(a, sU[HAS_DY ? cur : 0], k0, l16, G);
+        load_rows<T, DK, KS>(a, c.U, k0, l16, G);
         logits<T, KS, RW>(X, a, bdy);  // <U, dy>
-        load_rows<T, DK, KS>(a, sG[cur], k0, l16, G);
+        load_rows<T, DK, KS>(a, c.G, k0, l16, G);
         products<T, KS, RW>(X, a, bq);  // + <G, q>
       } else {
-        load_rows<T, DK, KS>(a, sG[cur], k0, l16, G);
+        load_rows<T, DK, KS>(a, c.G, k0, l16, G);
         logits<T, KS, RW>(X, a, bq);  // <G, q>
       }
       float e8[8], hb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        e8[j] = sE[cur][k0 + 8 * G + j];
-        hb[j] = BCAST ? 0.0f : sH[BCAST ? 0 : cur][k0 + 8 * G + j];
+        e8[j] = c.E[k0 + 8 * G + j];
+        hb[j] = BCAST ? 0.0f : c.H[k0 + 8 * G + j];
       }
       typename E::frag pf[RW];
 #pragma unroll
@@ -806,14 +834,18 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
         }
       }
       typename E::frag vv[NACC][2];
-      load_cols<T, D, DK, NACC>(vv, sK[cur], k0);
+      load_cols<T, D, DK, NACC>(vv, c.K, k0);
       weighted_sum<T, D, NACC, RW>(acc, vv, pf);
     }
     __syncthreads();
     if (NB == 1 && st + 1 < nst) {
-      fetch(st + 1, 0, true);
+      fetch(st + 1, n, true);
       __syncthreads();
     }
+  };
+  for (int st = 0; st < nst; st += 2) {
+    stage2(st, B0, B1);
+    if (st + 1 < nst) stage2(st + 1, B1, B0);
   }
 
 #pragma unroll
@@ -863,8 +895,11 @@ __global__ __launch_bounds__(NW * kWave) void kb_dktil(const T* __restrict__ q, 
   constexpr int NACC = NDP > 0 ? NDP : 1;
   using DmaQ = TileDma<T, D, DK, kStep, NW>;
   using DmaL = TileDma<T, CB, CB, kStep, NW>;
-  __shared__ __align__(16) T sQ[2][kStep * DK];
-  __shared__ __align__(16) T sL[2][kStep * CB];
+  // two stages' buffers as distinct LDS objects in a fixed alternation
+  __shared__ __align__(16) T sQ0[kStep * DK];
+  __shared__ __align__(16) T sQ1[kStep * DK];
+  __shared__ __align__(16) T sL0[kStep * CB];
+  __shared__ __align__(16) T sL1[kStep * CB];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int cb = logical % p.nrb;
@@ -884,13 +919,13 @@ __global__ __launch_bounds__(NW * kWave) void kb_dktil(const T* __restrict__ q, 
   const long long lstride = static_cast<long long>(p.b2) * ldl;
   const long long gbase = (static_cast<long long>(bh) * p.t + g) * p.b1;  // (bh, g, c1 = 0)
 
-  auto fetch = [&](int st, int buf) {
+  auto fetch = [&](int st, T* tQ, T* tL) {
     const long long n_first = hoff + static_cast<long long>(lo + st * kStep) * p.b2 + a2;
     const int nvalid = nrows - st * kStep;
-    DmaQ::issue(sQ[buf], q + n_first * D, qstride, nvalid);
-    DmaL::issue(sL[buf], dl + n_first * ldl + cb * CB, lstride, nvalid);
+    DmaQ::issue(tQ, q + n_first * D, qstride, nvalid);
+    DmaL::issue(tL, dl + n_first * ldl + cb * CB, lstride, nvalid);
   };
-  fetch(0, 0);
+  fetch(0, sQ0, sL0);
 
   float one8[8];
 #pragma unroll
@@ -906,9 +941,8 @@ __global__ __launch_bounds__(NW * kWave) void kb_dktil(const T* __restrict__ q, 
   }
   __syncthreads();
 
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nst) fetch(st + 1, cur ^ 1);
+  auto stage = [&](int st, const T* cQ, const T* cL, T* nQ, T* nL) {
+    if (st + 1 < nst) fetch(st + 1, nQ, nL);
 #pragma unroll
     for (int half = 0; half < kHalves; ++half) {
       const int k0 = 32 * half;
@@ -918,7 +952,7 @@ __global__ __launch_bounds__(NW * kWave) void kb_dktil(const T* __restrict__ q, 
       typename E::frag pf[RW];
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
-        pf[rt] = Tile<T, CB>::load_tr(sL[cur], k0, (wave * RW + rt) * 16, 4);
+        pf[rt] = Tile<T, CB>::load_tr(cL, k0, (wave * RW + rt) * 16, 4);
         if (tail) {
           // rows past the tile repeat its last row: zero their slots
           float w[8];
@@ -929,10 +963,14 @@ __global__ __launch_bounds__(NW * kWave) void kb_dktil(const T* __restrict__ q, 
         acch[rt] = E::mma(ones, pf[rt], acch[rt]);
       }
       typename E::frag vv[NACC][2];
-      load_cols<T, D, DK, NACC>(vv, sQ[cur], k0);
+      load_cols<T, D, DK, NACC>(vv, cQ, k0);
       weighted_sum<T, D, NACC, RW>(acc, vv, pf);
     }
     __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, sQ0, sL0, sQ1, sL1);
+    if (st + 1 < nst) stage(st + 1, sQ1, sL1, sQ0, sL0);
   }
 
 #pragma unroll
@@ -965,8 +1003,11 @@ __global__ __launch_bounds__(NW * kWave) void kb_dkbar(const T* __restrict__ q, 
   constexpr int NACC = NDP > 0 ? NDP : 1;
   using DmaQ = TileDma<T, D, DK, kGemmStep, NW>;
   using DmaL = TileDma<T, CB, CB, kGemmStep, NW>;
-  __shared__ __align__(16) T sQ[2][kGemmStep * DK];
-  __shared__ __align__(16) T sL[2][kGemmStep * CB];
+  // two stages' buffers as distinct LDS objects in a fixed alternation
+  __shared__ __align__(16) T sQ0[kGemmStep * DK];
+  __shared__ __align__(16) T sQ1[kGemmStep * DK];
+  __shared__ __align__(16) T sL0[kGemmStep * CB];
+  __shared__ __align__(16) T sL1[kGemmStep * CB];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int split = logical % nsplit;
@@ -986,24 +1027,23 @@ __global__ __launch_bounds__(NW * kWave) void kb_dkbar(const T* __restrict__ q, 
     const T* qh = q + (static_cast<long long>(bh) * N) * D;
     const T* lh = dl + (static_cast<long long>(bh) * N) * ldl + cb * CB;
     const int nst = static_cast<int>((n_hi - n_lo + kGemmStep - 1) / kGemmStep);
-    auto fetch = [&](int st, int buf) {
+    auto fetch = [&](int st, T* tQ, T* tL) {
       const long long n0 = n_lo + static_cast<long long>(st) * kGemmStep;
       const int nvalid = static_cast<int>(n_hi - n0);
-      DmaQ::issue(sQ[buf], qh + n0 * D, D, nvalid);
-      DmaL::issue(sL[buf], lh + n0 * ldl, ldl, nvalid);
+      DmaQ::issue(tQ, qh + n0 * D, D, nvalid);
+      DmaL::issue(tL, lh + n0 * ldl, ldl, nvalid);
     };
-    fetch(0, 0);
+    fetch(0, sQ0, sL0);
     __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-      const int cur = st & 1;
-      if (st + 1 < nst) fetch(st + 1, cur ^ 1);
+    auto stage = [&](int st, const T* cQ, const T* cL, T* nQ, T* nL) {
+      if (st + 1 < nst) fetch(st + 1, nQ, nL);
       const int nvalid = static_cast<int>(n_hi - (n_lo + static_cast<long long>(st) * kGemmStep));
       typename E::frag vv[NACC][2];
-      load_cols<T, D, DK, NACC>(vv, sQ[cur], 0);
+      load_cols<T, D, DK, NACC>(vv, cQ, 0);
       typename E::frag pf[RW];
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
-        pf[rt] = Tile<T, CB>::load_tr(sL[cur], 0, (wave * RW + rt) * 16, 4);
+        pf[rt] = Tile<T, CB>::load_tr(cL, 0, (wave * RW + rt) * 16, 4);
         if (nvalid < kGemmStep) {
           // rows past the chunk repeat its last row: zero their slots
           float w[8];
@@ -1014,6 +1054,10 @@ __global__ __launch_bounds__(NW * kWave) void kb_dkbar(const T* __restrict__ q, 
       }
       weighted_sum<T, D, NACC, RW>(acc, vv, pf);
       __syncthreads();
+    };
+    for (int st = 0; st < nst; st += 2) {
+      stage(st, sQ0, sL0, sQ1, sL1);
+      if (st + 1 < nst) stage(st + 1, sQ1, sL1, sQ0, sL0);
     }
   }
 #pragma unroll
