@@ -73,6 +73,20 @@ __device__ inline float dot_acc_row(const T* xrow, const f32x4 (&acc)[NACC][2][R
   return r;
 }
 
+// The same dot product with x already in registers as the row fragments of a
+// contraction over d (lane slots d = 32s + 8G + j: the accumulator's layout
+// when D >= 32, so s = dp and j = 4dt + i).
+template <typename T, int NACC, int RW>
+__device__ inline float dot_acc_frags(const typename Elem<T>::frag (&x)[NACC], const f32x4 (&acc)[NACC][2][RW],
+                                      int rt) {
+  float r = 0.0f;
+#pragma unroll
+  for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r += Elem<T>::slot(x[dp], j) * acc[dp][j >> 2][rt][j & 3];
+  return r;
+}
+
 // Sum over the lane's contraction slots of two row fragments (same layout).
 template <typename T, int KS>
 __device__ inline float dot_frags(const typename Elem<T>::frag (&a)[KS], const typename Elem<T>::frag (&b)[KS]) {
@@ -765,7 +779,11 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
     const int r = (wave * RW + rt) * 16 + l16;
     const bool ok = r < it.nrows;
     const long long row = hoff + n0 + (ok ? r : 0) * nstride;
-    float part = dot_acc_row<T, D, NACC, RW>(q + row * D, acc, rt, G);
+    float part;
+    if constexpr (D >= 32)
+      part = dot_acc_frags<T, NACC, RW>(bq[rt], acc, rt);  // q of the row, held in bq
+    else
+      part = dot_acc_row<T, D, NACC, RW>(q + row * D, acc, rt, G);
     if (HAS_DY) {
       typename E::frag by[KS];
 #pragma unroll
