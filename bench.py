@@ -362,7 +362,9 @@ def main():
     launches = kernels[dom]["launches_per_step"]
     fl, by = work[dom]
     roof = roofline_entry(dom, fl, by, kernels[dom]["avg_ms"] / 1e3, wl.dtype,
-                          read_traffic(dom, wl.name) if wl.iters == 1 or args.mode == "fwd" else None)
+                          # the counters are taken on one-iteration runs: later iterations'
+                          # launches read the aggregated keys as well, so they have no figure
+                          read_traffic(dom, wl.name) if wl.iters == 1 else None)
     roof["launches_per_step"] = launches
     if iters_used is not None:
         roof["note"] = ("early stopping: launches after every head has stopped return at once and are "
