@@ -41,8 +41,13 @@
  *   failure; monarch_attn_last_hip_error() gives its code.  The library never
  *   prints or aborts.  NaN/Inf in the inputs propagate to the output.
  *
- * Supported envelope: d in {16, 32, 64, 128}; 1 <= b2 <= 128; any b1 >= 1;
+ * Supported envelope: d in {16, 32, 64, 128}; 1 <= b2 <= 16384; any b1 >= 1;
  *   b1*b2 == f*h*w; 1 <= tiles <= b1; iters >= 1; tiles*N*d < 2^31.
+ *   Key blocks longer than 128 tokens, e.g. whole frames, (b1, b2) =
+ *   (f, h*w) (the spatio-temporal factorisation of the VMonarch abstract,
+ *   listed on the same pages), run the forward entry points with an
+ *   R-step that takes the block softmax online; the training entry points
+ *   take b2 <= 128 only (MONARCH_EUNSUPPORTED above, and a state size of 0).
  */
 #ifndef MONARCH_ATTN_H
 #define MONARCH_ATTN_H
@@ -184,7 +189,8 @@ int monarch_attn_fwd_kv_ws(const void* q, const void* k, const void* v, void* ou
  * dq, dk, dv must not overlap each other or any input (state included).
  * It allocates a workspace stream-ordered (about 2*t*N*d*e + 16*t*N +
  * N*roundup(b1, 256)*e bytes per head, plus 4*t*N + 8*N*d for T > 1).  The
- * supported envelope is the forward's.  State from another shape, iteration
+ * supported envelope is the forward's with b2 <= 128 (the training
+ * forward's too).  State from another shape, iteration
  * count or dtype gives undefined results. */
 size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d,
                                       int b1, int b2, int tiles, int iters, int dtype);

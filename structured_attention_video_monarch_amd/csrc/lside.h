@@ -831,6 +831,63 @@ __global__ __launch_bounds__(256) void k_kbar(const T* __restrict__ k, T* __rest
   }
 }
 
+// The same block means for long key blocks (thousands of keys, e.g. a whole
+// frame): one workgroup of four waves per block c1, each wave summing every
+// fourth group of rows, the four partial sums added in LDS in a fixed order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_kbar_long(const T* __restrict__ k, T* __restrict__ kbar,
+                                                   float* __restrict__ knorm, int b2) {
+  using E = Elem<T>;
+  constexpr int V = E::kVec;
+  constexpr int LPR = D / V;        // lanes per row
+  constexpr int RPI = kWave / LPR;  // rows per wave and pass
+  constexpr int NWV = 4;
+  __shared__ float part[NWV][D];
+  const long long item = blockIdx.x;  // bh*b1 + c1
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = (lane % LPR) * V, ro = lane / LPR;
+  const T* src = k + item * b2 * D;
+  float acc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) acc[j] = 0.0f;
+  for (int c2 = wave * RPI + ro; c2 < b2; c2 += NWV * RPI) {
+    uint4 raw = *reinterpret_cast<const uint4*>(src + static_cast<long long>(c2) * D + col);
+    const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[j] += E::to_f32(e[j]);
+  }
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[j] += __shfl_xor(acc[j], off);
+  if (ro == 0) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) part[wave][col + j] = acc[j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int j = 0; j < V; ++j) acc[j] = ((part[0][col + j] + part[1][col + j]) + part[2][col + j]) + part[3][col + j];
+  // round the means as they are stored and take |Kbar| of the rounded row
+  const float inv = 1.0f / static_cast<float>(b2);
+  T mean[V];
+  float sq = 0.0f;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    mean[j] = E::from_f32(acc[j] * inv);
+    const float x = E::to_f32(mean[j]);
+    sq = __builtin_fmaf(x, x, sq);
+  }
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) sq += __shfl_xor(sq, off);
+  if (ro == 0) {
+    T* dst = kbar + item * D + col;
+#pragma unroll
+    for (int j = 0; j < V; ++j) dst[j] = mean[j];
+    if (knorm && lane == 0) knorm[item] = sqrtf(sq);
+  }
+}
+
 // ------------------------------------------------------------- k_objective --
 // After the L-step of iteration `it`: F = sum_n lse_n (nats) is the objective
 // of the current factors (the L-step is the exact maximiser).  Per head, one

@@ -22,6 +22,7 @@
 #include "backward.h"
 #include "lside.h"
 #include "rside.h"
+#include "rside_long.h"
 #include "../../include/monarch_attn.h"
 
 using namespace monarch;
@@ -54,6 +55,17 @@ thread_local int g_last_hip_error = 0;
 constexpr int kLseRW = MONARCH_LSE_RW, kLseNW = MONARCH_LSE_NW;
 constexpr int kAggRW = MONARCH_AGG_RW, kAggNW = MONARCH_AGG_NW;
 constexpr int kAppRW = MONARCH_APP_RW, kAppNW = MONARCH_APP_NW;
+// the R-step of long key blocks (b2 > kShortB2): rows a2 per workgroup
+#ifndef MONARCH_RL_RW
+#define MONARCH_RL_RW 2
+#endif
+#ifndef MONARCH_RL_NW
+#define MONARCH_RL_NW 4
+#endif
+constexpr int kRlRW = MONARCH_RL_RW, kRlNW = MONARCH_RL_NW;
+// longest key block the forward takes (the long R-step has no limit of its
+// own; this bounds the grid and index arithmetic)
+constexpr int kMaxB2 = 16384;
 
 // ------------------------------------------------------------------ checks --
 // Shapes of one call.  Keys and values: f frames, N = f*h*w tokens in b1
@@ -81,7 +93,7 @@ int check_args(const void* q, const void* k, const void* v, const void* out, con
   if (s.t < 1 || s.t > b1q) return MONARCH_EINVAL;
   if (s.T < 1) return MONARCH_EINVAL;
   if (s.d != 16 && s.d != 32 && s.d != 64 && s.d != 128) return MONARCH_EUNSUPPORTED;
-  if (s.b2 > 128) return MONARCH_EUNSUPPORTED;
+  if (s.b2 > kMaxB2) return MONARCH_EUNSUPPORTED;
   if (static_cast<long long>(s.t) * N * s.d >= (1LL << 31)) return MONARCH_EUNSUPPORTED;
   if (Nq * s.d >= (1LL << 31)) return MONARCH_EUNSUPPORTED;
   const long long BH = static_cast<long long>(s.B) * s.H;
@@ -291,7 +303,12 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
   {
     const long long items = s.BH * s.b1;
     const unsigned grid = static_cast<unsigned>((items + 3) / 4);
-    ok(timed(0, st, [&] { k_kbar<T, D><<<grid, 256, 0, st>>>(k, kbar, bf.knorm, BH, s.b1, s.b2); }));
+    if (s.b2 > kShortB2)
+      ok(timed(0, st, [&] {
+        k_kbar_long<T, D><<<static_cast<unsigned>(items), 256, 0, st>>>(k, kbar, bf.knorm, s.b2);
+      }));
+    else
+      ok(timed(0, st, [&] { k_kbar<T, D><<<grid, 256, 0, st>>>(k, kbar, bf.knorm, BH, s.b1, s.b2); }));
   }
 
   constexpr int lse_rows = kLseRW * kLseNW * 16, agg_rows = kAggRW * kAggNW * 16,
@@ -313,11 +330,17 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
 #endif
   const bool col_fits = MONARCH_AGG_COL && sizeof(T) == 2 && ngmax <= kColRows;
 
+  // R-step: a whole block row per wave (b2 <= kShortB2), else the online
+  // softmax over blocks of 64 keys with RB rows a2 per workgroup
+  const bool long_blocks = s.b2 > kShortB2;
   RGeom rg{BH, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
   const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
-  const size_t r_lds_last = rside_lds_bytes<T>(D, rg.b2p, true);
-  const size_t r_lds_mid = rside_lds_bytes<T>(D, rg.b2p, false);
+  const size_t r_lds_last = long_blocks ? 0 : rside_lds_bytes<T>(D, rg.b2p, true);
+  const size_t r_lds_mid = long_blocks ? 0 : rside_lds_bytes<T>(D, rg.b2p, false);
+  constexpr int rl_rows = kRlRW * kRlNW * 16;
+  RLGeom rl{BH, s.b1, s.b2, s.t, (s.b2 + rl_rows - 1) / rl_rows, c};
+  const unsigned rl_grid = static_cast<unsigned>(s.BH * s.b1 * s.t * rl.nrb);
   if (r_lds_last > 65536)
     ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rstep<T, D, true>),
                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds_last)));
@@ -373,7 +396,19 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
                                                                                       sa, it);
       }));
     }
-    if (ad) {
+    if (long_blocks) {
+      ok(timed(3, st, [&] {
+        if (ad)
+          k_rstep_long_adaptive<T, D, kRlRW, kRlNW><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, bf.ktil, bf.hent,
+                                                                                      ad->stop_at, it, rl);
+        else if (last)
+          k_rstep_long<T, D, kRlRW, kRlNW, true><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, nullptr, nullptr,
+                                                                                   uout, rl);
+        else
+          k_rstep_long<T, D, kRlRW, kRlNW, false><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, ktil_out, hent_out,
+                                                                                    nullptr, rl);
+      }));
+    } else if (ad) {
       ok(timed(3, st, [&] {
         k_rstep_adaptive<T, D><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, bf.ktil, bf.hent, ad->stop_at, it,
                                                                        rg);
@@ -849,6 +884,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int check_train(const Shape& s, size_t elem, const void* state, size_t state_bytes) {
   if (elem == 0) return MONARCH_EINVAL;
+  // the backward's key-block kernels hold a whole block row per wave
+  if (s.b2 > kShortB2) return MONARCH_EUNSUPPORTED;
   const TrainState t = train_layout(s, elem);
   if (!state || state_bytes < t.total) return MONARCH_ENOMEM;
   if (reinterpret_cast<uintptr_t>(state) % kAlign != 0) return MONARCH_EINVAL;
@@ -1060,6 +1097,7 @@ size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d, 
   const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   static const char dummy[4] = {0};
   if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
+  if (s.b2 > kShortB2) return 0;  // training keeps key blocks within one wave's registers
   return train_layout(s, elem).total;
 }
 
@@ -1085,6 +1123,7 @@ size_t monarch_attn_train_state_bytes_kv(int B, int H, int fq, int f, int h, int
   const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
   static const char dummy[4] = {0};
   if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
+  if (s.b2 > kShortB2) return 0;  // training keeps key blocks within one wave's registers
   return train_layout(s, elem).total;
 }
 

@@ -1,0 +1,221 @@
+// R-side kernel for long key blocks (b2 > 128): the same R-step as rside.h,
+//   R[g,c1,a2,:] = softmax_c2( s<Qh[g,c1,a2], k_(c1,c2)> ),
+//   last iteration:  U[g,c1,a2,:]  = sum_c2 R v_(c1,c2)
+//   otherwise:       Kt[g,c1,a2,:] = sum_c2 R k_(c1,c2),  H[g,c1,a2] = -sum_c2 R log2 R
+// (yunpan.plus MonarchRT article, "Monarch matrices" and "Innovation 2").
+// Blocks this long arise when a block spans a whole frame, b1 = f frames and
+// b2 = h*w positions: the spatio-temporal factorisation the VMonarch abstract
+// names (inter-frame mixing in L, intra-frame mixing in R).
+//
+// A block row no longer fits one wave's registers, so the softmax over c2 is
+// taken online, as in FlashAttention: one workgroup owns (bh, c1, g) and RB
+// rows a2, and the b2 keys (and values) of block c1 stream through LDS 64 at a
+// time by double-buffered DMA.  Per row the running maximum m (log2 units),
+// the running sum l = sum 2^(x - m) and, for the entropy, the running
+// sx = sum 2^(x - m) (x - m) are kept; when m rises to m' they become
+//   l' = a l,   sx' = a (sx - (m' - m) l),   acc' = a acc,   a = 2^(m - m'),
+// which is the entropy taken online alongside the block softmax (the fused
+// "online entropy" of the VMonarch abstract).  At the end U (or Kt) = acc / l
+// and H in bits = log2 l - sx / l.
+#pragma once
+
+#include "lside.h"
+
+namespace monarch {
+
+// Key blocks up to this length use the register-resident R-step (rside.h).
+constexpr int kShortB2 = 128;
+
+struct RLGeom {
+  int BH, b1, b2, t;
+  int nrb;  // blocks of RB rows a2 per (key block, tile)
+  float c;  // log2(e) / sqrt(d)
+};
+
+template <typename T, int D, int RW, int NW, bool LAST>
+__device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T* __restrict__ v,
+                                                T* qhat,  // [BH][t][b1][b2][D]; U written over it when LAST
+                                                T* __restrict__ ktil, float* __restrict__ hent,
+                                                T* uout,  // U goes here instead when not NULL
+                                                const RLGeom& p, int item, T* sK0, T* sK1, T* sV0, T* sV1) {
+  using E = Elem<T>;
+  constexpr int DK = D < 32 ? 32 : D;
+  constexpr int KS = DK / 32;
+  constexpr int RB = NW * RW * 16;
+  constexpr int NDP = D / 32;
+  constexpr int NACC = NDP > 0 ? NDP : 1;
+  using Dma = TileDma<T, D, DK, kStep, NW>;
+  constexpr float kMaskLogit = -1e30f;
+
+  // item = ((bh * b1 + c1) * t + g) * nrb + rb: the row blocks and tiles of
+  // one key block are neighbours, so its K and V blocks are shared in L2
+  const int rb = item % p.nrb;
+  int rest = item / p.nrb;
+  const int g = rest % p.t;
+  rest /= p.t;
+  const int c1 = rest % p.b1;
+  const int bh = rest / p.b1;
+  const int a2_0 = rb * RB;
+  const int nrows = p.b2 - a2_0 < RB ? p.b2 - a2_0 : RB;
+  const long long qbase = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2_0;
+  const long long kblk = (static_cast<long long>(bh) * p.b1 + c1) * p.b2 * D;
+
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int l16 = lane & 15, G = lane >> 4;
+  const int nst = (p.b2 + kStep - 1) / kStep;
+  auto fetch = [&](int st, T* tK, T* tV) {
+    const int c2 = st * kStep;
+    Dma::issue(tK, k + kblk + static_cast<long long>(c2) * D, D, p.b2 - c2);
+    if (LAST) Dma::issue(tV, v + kblk + static_cast<long long>(c2) * D, D, p.b2 - c2);
+  };
+  fetch(0, sK0, sV0);
+
+  typename E::frag bq[RW][KS];
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    const int r = (wave * RW + rt) * 16 + l16;
+    const bool ok = r < nrows;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int col = s * 32 + 8 * G;
+      bq[rt][s] = (ok && col < D) ? E::load(qhat + (qbase + r) * D + col) : E::zero();
+    }
+  }
+  f32x4 acc[NACC][2][RW];
+  float m[RW], l[RW], sx[RW];
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    m[rt] = kMaskLogit;
+    l[rt] = 0.0f;
+    sx[rt] = 0.0f;
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp) acc[dp][0][rt] = acc[dp][1][rt] = f32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+
+  // one step of 64 keys: prefetch the next into (nK, nV), products on (cK, cV)
+  auto stage = [&](int st, const T* cK, const T* cV, T* nK, T* nV) {
+    if (st + 1 < nst) fetch(st + 1, nK, nV);
+    const int c2s = st * kStep;
+    // logits of both 32-key halves (lane: keys 8G + j of each half, row l16
+    // of each row tile), in log2 units, keys past b2 masked
+    f32x4 S[kHalves][2][RW];
+#pragma unroll
+    for (int h = 0; h < kHalves; ++h) {
+      typename E::frag a[KS][2];
+      load_rows<T, DK, KS>(a, cK, 32 * h, l16, G);
+      logits<T, KS, RW>(S[h], a, bq);
+    }
+    const bool tail = c2s + kStep > p.b2;
+#pragma unroll
+    for (int rt = 0; rt < RW; ++rt) {
+      float mx = kMaskLogit;
+#pragma unroll
+      for (int h = 0; h < kHalves; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float x = S[h][j >> 2][rt][j & 3] * p.c;
+          if (tail && c2s + 32 * h + 8 * G + j >= p.b2) x = kMaskLogit;
+          S[h][j >> 2][rt][j & 3] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[rt], mx);
+      const float a = fast_exp2(m[rt] - mnew);
+      if (!LAST) sx[rt] = a * (sx[rt] - (mnew - m[rt]) * l[rt]);
+      l[rt] *= a;
+      m[rt] = mnew;
+#pragma unroll
+      for (int dp = 0; dp < NACC; ++dp) {
+        acc[dp][0][rt] *= a;
+        acc[dp][1][rt] *= a;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kHalves; ++h) {
+      typename E::frag pf[RW];
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float dx = S[h][j >> 2][rt][j & 3] - m[rt];
+          w[j] = fast_exp2(dx);
+          l[rt] += w[j];
+          if (!LAST) sx[rt] = __builtin_fmaf(w[j], dx, sx[rt]);
+        }
+        pf[rt] = E::pack(w);
+      }
+      // X^T P^T (X = V, or K for the next keys): rows d, columns a2
+      typename E::frag vv[NACC][2];
+      load_cols<T, D, DK, NACC>(vv, LAST ? cV : cK, 32 * h);
+      weighted_sum<T, D, NACC, RW>(acc, vv, pf);
+    }
+    __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, sK0, sV0, sK1, sV1);
+    if (st + 1 < nst) stage(st + 1, sK1, sV1, sK0, sV0);
+  }
+
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) {
+    // the row's sums over its four lane groups (all lanes take part)
+    float lt = l[rt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    float st = sx[rt];
+    if (!LAST) {
+      st += __shfl_xor(st, 16);
+      st += __shfl_xor(st, 32);
+    }
+    const int r = (wave * RW + rt) * 16 + l16;
+    if (r >= nrows) continue;
+    const long long row = qbase + r;
+    T* dst = (LAST ? (uout ? uout : qhat) : ktil) + row * D;
+    store_rows<T, D, NACC, RW>(dst, acc, rt, 1.0f / lt, G);
+    if (!LAST && G == 0) hent[row] = log2f(lt) - st / lt;
+  }
+}
+
+// LDS of the long R-step: two stages of K (and V for the last R-step) as
+// distinct objects, so that each stage's prefetch overlaps the other's products.
+#define MONARCH_RSTEP_LONG_LDS(T, DK, WITH_V)                  \
+  __shared__ __align__(16) T sK0[kStep * (DK)];                \
+  __shared__ __align__(16) T sK1[kStep * (DK)];                \
+  __shared__ __align__(16) T sV0[(WITH_V) ? kStep * (DK) : 8]; \
+  __shared__ __align__(16) T sV1[(WITH_V) ? kStep * (DK) : 8];
+
+template <typename T, int D, int RW, int NW, bool LAST>
+__global__ __launch_bounds__(NW * kWave) void k_rstep_long(const T* __restrict__ k, const T* __restrict__ v, T* qhat,
+                                                           T* __restrict__ ktil, float* __restrict__ hent, T* uout,
+                                                           RLGeom p) {
+  MONARCH_RSTEP_LONG_LDS(T, (D < 32 ? 32 : D), LAST)
+  rstep_long_body<T, D, RW, NW, LAST>(k, v, qhat, ktil, hent, uout, p, xcd_remap(blockIdx.x, gridDim.x), sK0, sK1,
+                                      sV0, sV1);
+}
+
+// Iteration `it` of a run that stops each head on its own (stop_at as for
+// k_rstep_adaptive): heads that stopped earlier are skipped, a head that stops
+// now gets R V, the others the next L-step's keys and entropies.
+template <typename T, int D, int RW, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_rstep_long_adaptive(const T* __restrict__ k, const T* __restrict__ v,
+                                                                    T* qhat, T* __restrict__ ktil,
+                                                                    float* __restrict__ hent,
+                                                                    const int* __restrict__ stop_at, int it,
+                                                                    RLGeom p) {
+  MONARCH_RSTEP_LONG_LDS(T, (D < 32 ? 32 : D), true)
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = item / (p.nrb * p.t * p.b1);
+  const int sa = stop_at[bh];
+  if (sa != 0 && sa < it) return;
+  if (sa == it)
+    rstep_long_body<T, D, RW, NW, true>(k, v, qhat, nullptr, nullptr, nullptr, p, item, sK0, sK1, sV0, sV1);
+  else
+    rstep_long_body<T, D, RW, NW, false>(k, v, qhat, ktil, hent, nullptr, p, item, sK0, sK1, sV0, sV1);
+}
+
+#undef MONARCH_RSTEP_LONG_LDS
+
+}  // namespace monarch

@@ -97,6 +97,12 @@ WORKLOADS = {
     # cached frames plus itself, at the 480p and 720p latent sizes
     "chunk480p_kv": Workload("chunk480p_kv", 1, 12, 128, 21, 30, 52, 630, 52, 1, 1, "bf16", fq=3),
     "chunk720p_kv": Workload("chunk720p_kv", 1, 40, 128, 21, 45, 80, 945, 80, 1, 1, "bf16", fq=3),
+    # blocks of whole frames, (b1, b2) = (f, h*w): L mixes frames at one
+    # position, R mixes the positions of one frame (the spatio-temporal
+    # factorisation of the VMonarch abstract), at the 480p and 720p sizes
+    "clip480p_frames": Workload("clip480p_frames", 1, 12, 128, 21, 30, 52, 21, 1560, 1, 1, "bf16"),
+    "latent720p_frames": Workload("latent720p_frames", 1, 40, 128, 21, 45, 80, 21, 3600, 1, 1, "bf16"),
+    "chunk480p_kv_frames": Workload("chunk480p_kv_frames", 1, 12, 128, 21, 30, 52, 21, 1560, 1, 1, "bf16", fq=3),
 }
 for _t in (1, 2, 4, 8):
     for _T in (1, 2):

@@ -49,7 +49,7 @@ def _fwd(q=1, k=2, v=3, out=4, B=1, H=2, f=3, h=30, w=52, d=128, b1=90, b2=52, t
     (dict(T=0), M.MONARCH_EINVAL),
     (dict(d=48), M.MONARCH_EUNSUPPORTED),
     (dict(d=256), M.MONARCH_EUNSUPPORTED),
-    (dict(f=3, h=20, w=260, b1=60, b2=260), M.MONARCH_EUNSUPPORTED),
+    (dict(f=1, h=1, w=16400, b1=1, b2=16400), M.MONARCH_EUNSUPPORTED),  # key blocks beyond 16384
     (dict(out=1 + 1000), M.MONARCH_EINVAL),  # overlaps q (bytes 1 .. 1 + 2*N*d*2)
 ])
 def test_bad_arguments_rejected_before_any_gpu_call(kw, status):
@@ -143,6 +143,18 @@ def test_bwd_bad_arguments_rejected_before_any_gpu_call(kw, status):
     if kw.get("state_bytes") == "T1":
         kw = dict(kw, state_bytes=M.monarch_attn_train_state_bytes(1, 2, 3, 30, 52, 128, 90, 52, 1, 1, 0))
     assert _bwd(**kw) == status
+
+
+def test_long_key_blocks_forward_only():
+    # blocks of whole frames (b2 = h*w > 128) run the forward, not training
+    assert M.monarch_attn_workspace_bytes(1, 2, 3, 20, 26, 64, 3, 520, 1, 2, 0) > 0
+    assert M.monarch_attn_kv_workspace_bytes(1, 2, 1, 3, 20, 26, 64, 3, 520, 1, 2, 0) > 0
+    assert M.monarch_attn_train_state_bytes(1, 2, 3, 20, 26, 64, 3, 520, 1, 2, 0) == 0
+    assert M.monarch_attn_train_state_bytes_kv(1, 2, 1, 3, 20, 26, 64, 3, 520, 1, 2, 0) == 0
+    assert M.monarch_attn_train_state_bytes(1, 2, 3, 20, 26, 64, 60, 26, 1, 2, 0) > 0
+    p = _train_ptrs(5)
+    rc = M.lib().monarch_attn_fwd_train(*p[:4], 1, 2, 3, 20, 26, 64, 3, 520, 1, 2, 0, p[4], 1 << 30, None)
+    assert rc == M.MONARCH_EUNSUPPORTED
 
 
 def test_fwd_train_rejects_small_state():

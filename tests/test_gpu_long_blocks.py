@@ -1,0 +1,156 @@
+"""Key blocks longer than 128 tokens on the GPU (needs an MI355X).
+
+Blocks of whole frames, (b1, b2) = (f, h*w), and any other factorisation
+with b2 > 128 run the R-step with the online softmax over blocks of 64 keys
+(the kernel for shorter blocks keeps a whole block row per wave).  Compared
+with the CPU oracle element by element: bf16 max-abs <= 2e-2 and mean-abs
+<= 2e-3 as for every workload, and in addition mean-abs <= 2e-2 of the
+reference's mean magnitude (softmaxes over thousands of keys give small
+outputs, where the absolute bars alone would say little); fp32 max-abs <=
+1e-5.  One key block, (1, N), is exact softmax attention: checked against
+scaled dot-product attention in float64 on the CPU, not against the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, errors, say, to_device, to_host
+from structured_attention_video_monarch_amd import inputs as I
+from test_gpu_adaptive import check_against_oracle, run_adaptive
+from test_gpu_kv import run_kv
+from test_gpu_parity import run_gpu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+REL_MEAN = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def check(wl, x, y, heads, label):
+    assert np.all(np.isfinite(y))
+    worst = (0.0, 0.0, 0.0)
+    for b in range(wl.B):
+        for h in heads:
+            ref = oracle.monarch_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], wl.b1, wl.b2, wl.tiles, wl.iters)
+            mx, mean = errors(y[b, h], ref)
+            rel = mean / np.abs(ref).mean()
+            worst = (max(worst[0], mx), max(worst[1], mean), max(worst[2], rel))
+            if wl.dtype == "bf16":
+                assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS and rel <= REL_MEAN, (b, h, mx, mean, rel)
+            else:
+                assert mx <= F32_MAX_ABS, (b, h, mx)
+    say(f"[ok] {label}: max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e} relative mean {worst[2]:.3e}")
+
+
+def compare_long(wl, seed=0, heads=None, label=""):
+    label = label or wl.name
+    say(f"[case] long blocks {label} B={wl.B} H={wl.H} N={wl.N} d={wl.d} blocks=({wl.b1},{wl.b2}) "
+        f"t={wl.tiles} T={wl.iters} {wl.dtype} seed={seed}")
+    x = I.make_inputs(wl, seed)
+    y = run_gpu(wl, x)
+    check(wl, x, y, range(wl.H) if heads is None else heads, label)
+
+
+# (name, B, H, d, f, h, w, b1, b2, tiles, iters, dtype)
+LONG_EDGE = [
+    ("frames_f32_d32", 1, 2, 32, 3, 5, 40, 3, 200, 1, 1, "f32"),
+    ("frames_f32_d32_t3_T3", 1, 2, 32, 3, 5, 40, 3, 200, 3, 3, "f32"),
+    ("b2_129_f32_d16", 1, 2, 16, 3, 1, 129, 3, 129, 3, 2, "f32"),
+    ("b2_130_bf16_d64", 1, 3, 64, 2, 5, 26, 2, 130, 1, 2, "bf16"),
+    ("frames_bf16_d128_t2", 1, 2, 128, 4, 9, 33, 4, 297, 2, 2, "bf16"),
+    ("half_frames_bf16_d64", 2, 2, 64, 3, 20, 20, 6, 200, 3, 1, "bf16"),
+    ("f32_d128_T2", 1, 1, 128, 2, 8, 40, 2, 320, 1, 2, "f32"),
+    ("f32_d64_b2_1000", 1, 1, 64, 2, 20, 50, 2, 1000, 2, 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", LONG_EDGE, ids=[c[0] for c in LONG_EDGE])
+def test_long_block_edge_shapes(case):
+    name, B, H, d, f, h, w, b1, b2, t, T, dt = case
+    compare_long(I.Workload(name, B, H, d, f, h, w, b1, b2, t, T, dt))
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_clip480p_frames(T):
+    wl = I.get_workload("clip480p_frames").with_(iters=T)
+    if T > 1:
+        wl = wl.with_(H=2)
+    compare_long(wl, heads=[0, wl.H - 1])
+
+
+def test_latent720p_frames_head():
+    # the whole workload in the benchmark's launch configuration, one head checked
+    wl = I.get_workload("latent720p_frames")
+    compare_long(wl, heads=[wl.H - 1])
+
+
+def test_chunk_against_cached_keys_long_blocks():
+    for wl, heads in ((I.get_workload("chunk480p_kv_frames"), [0, 11]),
+                      (I.Workload("kv_frames_f32", 1, 2, 32, 3, 5, 40, 3, 200, 1, 2, "f32", fq=1), [0, 1])):
+        say(f"[case] long blocks kv {wl.name} Nq={wl.Nq} N={wl.N} blocks=({wl.b1q}|{wl.b1},{wl.b2}) "
+            f"T={wl.iters} {wl.dtype}")
+        x = I.make_inputs(wl, 0)
+        y = run_kv(wl, x)
+        check(wl, x, y, heads, f"kv {wl.name}")
+
+
+@pytest.mark.parametrize("dtype,T", [("f32", 1), ("f32", 2), ("bf16", 1)])
+def test_one_key_block_is_exact_attention(dtype, T):
+    """(b1, b2) = (1, N): every L is 1, Qh = q, and R is the softmax of s q k^T
+    over all keys, so the layer is softmax attention at any iteration count."""
+    wl = I.Workload("one_block", 1, 2, 64, 2, 6, 50, 1, 600, 1, T, dtype)
+    say(f"[case] one key block of {wl.N} keys, {dtype}, T={T}")
+    x = I.make_inputs(wl, 3)
+    y = run_gpu(wl, x)
+    for h in range(wl.H):
+        q, k, v = (torch.from_numpy(x[n][0, h]).to(torch.float64)[None, None] for n in "qkv")
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)[0, 0].numpy()
+        mx, mean = errors(y[0, h], ref)
+        if dtype == "bf16":
+            assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
+        else:
+            assert mx <= F32_MAX_ABS, (h, mx)
+    say(f"[ok] one key block {dtype} T={T}: max-abs {mx:.3e}")
+
+
+@pytest.mark.parametrize("tol", [1e-3, -1.0])
+def test_adaptive_long_blocks(tol):
+    wl = I.Workload("adaptive_frames", 1, 3, 64, 4, 9, 33, 4, 297, 2, 1, "bf16")
+    say(f"[case] adaptive long blocks max_iters=5 tol={tol}")
+    x = I.make_inputs(wl, 1)
+    y, used = run_adaptive(wl, x, 5, tol)
+    if tol < 0:
+        assert np.all(used == 5), used
+    worst = check_against_oracle(wl, x, y, used, 5, tol, heads=range(wl.H))
+    say(f"[ok] adaptive long blocks tol={tol}: iterations {used.tolist()}, max-abs {worst[0]:.3e}")
+
+
+def draw_long(seed):
+    """A seeded shape with a key block longer than 128 tokens."""
+    rng = np.random.default_rng([7101, seed])
+    while True:
+        d = int(rng.choice([16, 32, 64, 128]))
+        f, h, w = int(rng.integers(1, 5)), int(rng.integers(1, 13)), int(rng.integers(20, 90))
+        N = f * h * w
+        divisors = [x for x in range(129, min(N, 2048) + 1) if N % x == 0]
+        if divisors:
+            break
+    b2 = int(rng.choice(divisors))
+    b1 = N // b2
+    t = int(rng.integers(1, b1 + 1))
+    T = int(rng.integers(1, 4))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    return I.Workload(f"fuzz-long{seed}", 1, int(rng.integers(1, 3)), d, f, h, w, b1, b2, t, T, dtype)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fuzz_long_blocks(seed):
+    wl = draw_long(seed)
+    compare_long(wl, seed=seed, label=f"{wl.name} f,h,w=({wl.f},{wl.h},{wl.w})")
