@@ -15,6 +15,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
@@ -33,11 +34,10 @@ METRIC_TRAIN = ("MonarchAttention {iters}-iteration training step (fwd + bwd) to
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SOURCES = ["structured_attention_video_monarch_amd/csrc/device_common.h",
-                  "structured_attention_video_monarch_amd/csrc/lside.h",
-                  "structured_attention_video_monarch_amd/csrc/rside.h",
-                  "structured_attention_video_monarch_amd/csrc/backward.h",
-                  "structured_attention_video_monarch_amd/csrc/monarch_attn.hip"]
+# every kernel source (headers and the library's translation unit), in a fixed order
+KERNEL_SOURCES = sorted(os.path.relpath(p, ROOT) for p in
+                        glob.glob(os.path.join(ROOT, "structured_attention_video_monarch_amd", "csrc", "*"))
+                        if p.endswith((".h", ".hip")))
 
 
 def kernel_source_hash() -> str:

@@ -21,6 +21,7 @@
 
 #include "backward.h"
 #include "lside.h"
+#include "lside_cols.h"
 #include "rside.h"
 #include "rside_long.h"
 #include "../../include/monarch_attn.h"
@@ -329,6 +330,11 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
 #define MONARCH_AGG_COL 1
 #endif
   const bool col_fits = MONARCH_AGG_COL && sizeof(T) == 2 && ngmax <= kColRows;
+  // short tile columns (few key blocks, few rows per tile, e.g. blocks of
+  // whole frames): one column per wave
+  constexpr int cols_nw = 4;
+  const bool cols = s.b1 <= kColsRows && ngmax <= kColsRows;
+  const unsigned cols_grid = static_cast<unsigned>(s.BH * s.t * ((s.b2 + cols_nw - 1) / cols_nw));
 
   // R-step: a whole block row per wave (b2 <= kShortB2), else the online
   // softmax over blocks of 64 keys with RB rows a2 per workgroup
@@ -379,7 +385,16 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
                                                                   ad->tol);
       }));
     }
-    if (first) {
+    if (cols) {
+      ok(timed(2, st, [&] {
+        if (first)
+          k_aggregate_cols<T, D, cols_nw, true><<<cols_grid, cols_nw * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat,
+                                                                                     beta, base);
+        else
+          k_aggregate_cols<T, D, cols_nw, false><<<cols_grid, cols_nw * kWave, 0, st>>>(q, ktil, hent, lse, qhat,
+                                                                                      beta, base, sa, it);
+      }));
+    } else if (first) {
       ok(timed(2, st, [&] {
         if (col_fits)
           k_aggregate_col<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
@@ -424,7 +439,16 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     }
   }
   const float* lse_last = bf.lse_of(s.T);
-  if (s.T == 1) {
+  if (cols) {
+    ok(timed(4, st, [&] {
+      if (s.T == 1)
+        k_apply_cols<T, D, cols_nw, true><<<cols_grid, cols_nw * kWave, 0, st>>>(q, kbar, nullptr, lse_last, bf.u,
+                                                                               out, base);
+      else
+        k_apply_cols<T, D, cols_nw, false><<<cols_grid, cols_nw * kWave, 0, st>>>(
+            q, bf.ktil_of(s.T - 1), bf.hent_of(s.T - 1), lse_last, bf.u, out, base);
+    }));
+  } else if (s.T == 1) {
     ok(timed(4, st, [&] {
       k_apply<T, D, kAppRW, kAppNW, true><<<app_grid, kAppNW * kWave, 0, st>>>(q, kbar, nullptr, lse_last, bf.u, out,
                                                                               app);
