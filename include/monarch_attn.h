@@ -45,9 +45,8 @@
  *   b1*b2 == f*h*w; 1 <= tiles <= b1; iters >= 1; tiles*N*d < 2^31.
  *   Key blocks longer than 128 tokens, e.g. whole frames, (b1, b2) =
  *   (f, h*w) (the spatio-temporal factorisation of the VMonarch abstract,
- *   listed on the same pages), run the forward entry points with an
- *   R-step that takes the block softmax online; the training entry points
- *   take b2 <= 128 only (MONARCH_EUNSUPPORTED above, and a state size of 0).
+ *   listed on the same pages), run an R-step that takes the block softmax
+ *   online, forward and backward.
  */
 #ifndef MONARCH_ATTN_H
 #define MONARCH_ATTN_H
@@ -172,9 +171,10 @@ int monarch_attn_fwd_kv_ws(const void* q, const void* k, const void* v, void* ou
  * keys; per iteration the L-row log-sum-exps, the column masses beta and the
  * aggregated queries Qh of every tile; U = R V of the last R-step; and for
  * every R-step but the last the keys R k and entropies H(R) it hands to the
- * next L-step.  Its size is, with e = element bytes and T = iters,
+ * next L-step; with b2 > 128 also every R-step's row log-sum-exps.  Its
+ * size is, with e = element bytes and T = iters,
  *   B*H*(b1*d*e + 4*b1 + T*(4*N + 4*t*N + t*N*d*e) + t*N*d*e
- *        + (T-1)*(t*N*d*e + 4*t*N))  (+ alignment).
+ *        + (T-1)*(t*N*d*e + 4*t*N) + [b2 > 128] T*4*t*N)  (+ alignment).
  *
  * monarch_attn_bwd takes the same q, k, v, the out and state of a
  * monarch_attn_fwd_train call with the same arguments, and dout = dLoss/dout,
@@ -189,8 +189,7 @@ int monarch_attn_fwd_kv_ws(const void* q, const void* k, const void* v, void* ou
  * dq, dk, dv must not overlap each other or any input (state included).
  * It allocates a workspace stream-ordered (about 2*t*N*d*e + 16*t*N +
  * N*roundup(b1, 256)*e bytes per head, plus 4*t*N + 8*N*d for T > 1).  The
- * supported envelope is the forward's with b2 <= 128 (the training
- * forward's too).  State from another shape, iteration
+ * supported envelope is the forward's.  State from another shape, iteration
  * count or dtype gives undefined results. */
 size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d,
                                       int b1, int b2, int tiles, int iters, int dtype);

@@ -39,6 +39,8 @@ struct BGeom {
   int b2p;     // b2 rounded up to 32
   float c;     // log2(e) / sqrt(d)
   float s;     // 1 / sqrt(d)
+  int nks;     // kb_rside_b: slices of a key block's b2 keys (1 unless b2 > 128)
+  int ksw;     // kb_rside_b: keys per slice
 };
 
 // S[ct][rt] += a[s][ct] * b[rt][s] over the contraction (no reset).
@@ -486,10 +488,13 @@ __global__ __launch_bounds__(MONARCH_BRB_RW == 1 ? 512 : 256) void kb_rside_b(co
   __shared__ __align__(16) float sRh[2][BPS][64];
   __shared__ __align__(16) float sDh[MID ? 2 : 1][MID ? BPS : 1][64];
 
-  const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);  // (bh*b1 + c1)*nks + slice
+  const int slice = logical % p.nks;
+  const int item = logical / p.nks;  // bh*b1 + c1
   const int c1 = item % p.b1;
   const int bh = item / p.b1;
   const long long blk = static_cast<long long>(item) * p.b2;
+  const int kofs = slice * p.ksw;  // the slice's first key c2
   const int nw = blockDim.x / kWave;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(MONARCH_BRB_RW == 1 ? 512 : 256) void kb_rside_b(co
   typename E::frag bk2[RW][KS], bv2[RW][KS];
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
-    const int c2 = (wave * RW + rt) * 16 + l16;
+    const int c2 = kofs + (wave * RW + rt) * 16 + l16;
     const int c2c = c2 < p.b2 ? c2 : p.b2 - 1;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -582,7 +587,7 @@ __global__ __launch_bounds__(MONARCH_BRB_RW == 1 ? 512 : 256) void kb_rside_b(co
 
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
-    const int c2 = (wave * RW + rt) * 16 + l16;
+    const int c2 = kofs + (wave * RW + rt) * 16 + l16;
     if (c2 >= p.b2) continue;
     const long long orow = (blk + c2) * D;
     if (!MID) store_rows<T, D, NACC, RW>(dv + orow, accv, rt, 1.0f, G);

@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "backward.h"
+#include "backward_long.h"
 #include "lside.h"
 #include "lside_cols.h"
 #include "rside.h"
@@ -255,6 +256,7 @@ struct Bufs {
   float* hent;
   T* u;
   float* beta;
+  float* rlse;  // training with key blocks over 128: the R rows' log-sum-exps
   long long lse_it, qhat_it, beta_it, ktil_it, hent_it;
   // views of iteration it (1-based); keys/entropies: those the R-step of
   // iteration it writes (it < T), read by the L-step of it + 1
@@ -263,6 +265,7 @@ struct Bufs {
   float* beta_of(int it) const { return beta ? beta + (it - 1) * beta_it : nullptr; }
   T* ktil_of(int it) const { return ktil ? ktil + (it - 1) * ktil_it : nullptr; }
   float* hent_of(int it) const { return hent ? hent + (it - 1) * hent_it : nullptr; }
+  float* rlse_of(int it) const { return rlse ? rlse + (it - 1) * beta_it : nullptr; }
 };
 
 template <typename T>
@@ -276,6 +279,7 @@ Bufs<T> bufs_of(const Shape& s, unsigned char* ws, const Workspace& w) {
   b.hent = s.T > 1 ? reinterpret_cast<float*>(ws + w.hent) : nullptr;
   b.u = b.qhat;
   b.beta = nullptr;
+  b.rlse = nullptr;
   return b;
 }
 
@@ -418,10 +422,10 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
                                                                                       ad->stop_at, it, rl);
         else if (last)
           k_rstep_long<T, D, kRlRW, kRlNW, true><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, nullptr, nullptr,
-                                                                                   uout, rl);
+                                                                                   uout, bf.rlse_of(it), rl);
         else
           k_rstep_long<T, D, kRlRW, kRlNW, false><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, ktil_out, hent_out,
-                                                                                    nullptr, rl);
+                                                                                    nullptr, bf.rlse_of(it), rl);
       }));
     } else if (ad) {
       ok(timed(3, st, [&] {
@@ -595,7 +599,7 @@ int fwd_adaptive(const void* q, const void* k, const void* v, void* out, const S
 // next L-step.  Each per-iteration array holds T (or T - 1) copies, one
 // aligned block apart.
 struct TrainState {
-  size_t kbar, knorm, lse, beta, qhat, u, ktil, hent, total;
+  size_t kbar, knorm, lse, beta, qhat, u, ktil, hent, rlse, total;
   size_t lse_blk, beta_blk, qhat_blk, hent_blk;  // bytes per iteration copy
 };
 
@@ -626,6 +630,10 @@ TrainState train_layout(const Shape& s, size_t elem) {
   off += (T - 1) * t.qhat_blk;
   t.hent = off;
   off += (T - 1) * t.hent_blk;
+  // key blocks over 128: every R-step's row log-sum-exps (the backward's
+  // key-block pass takes them instead of a pass over the block of its own)
+  t.rlse = off;
+  if (s.b2 > kShortB2) off += T * t.beta_blk;
   t.total = off;
   return t;
 }
@@ -641,6 +649,7 @@ Bufs<T> train_bufs(unsigned char* st, const TrainState& t, int iters) {
   b.hent = iters > 1 ? reinterpret_cast<float*>(st + t.hent) : nullptr;
   b.u = reinterpret_cast<T*>(st + t.u);
   b.beta = reinterpret_cast<float*>(st + t.beta);
+  b.rlse = t.rlse < t.total ? reinterpret_cast<float*>(st + t.rlse) : nullptr;
   b.lse_it = static_cast<long long>(t.lse_blk / sizeof(float));
   b.beta_it = static_cast<long long>(t.beta_blk / sizeof(float));
   b.qhat_it = static_cast<long long>(t.qhat_blk / sizeof(T));
@@ -799,12 +808,22 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
           q, dout, keys_of(T_), ent_of(T_), bf.lse_of(T_), du, col_geom);
   }));
 
-  const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc};
+  // key-block kernels: a whole block row per wave (b2 <= kShortB2), else
+  // the row statistics taken online over 64-key steps (kb_rside_a_long) and
+  // the block's keys in slices of 8 waves (kb_rside_b)
+  const bool long_blocks = s.b2 > kShortB2;
+  constexpr int rb_keys = 16 * MONARCH_BRB_RW;  // keys c2 per wave of kb_rside_b
+  const int nks = long_blocks ? (s.b2 + 8 * rb_keys - 1) / (8 * rb_keys) : 1;
+  const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc, nks, 8 * rb_keys};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
   const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
-  constexpr int rb_keys = 16 * MONARCH_BRB_RW;  // keys c2 per wave of kb_rside_b
-  const unsigned rb_threads = static_cast<unsigned>(kWave * ((s.b2 + rb_keys - 1) / rb_keys));
-  const size_t ra_lds = rside_bwd_lds_bytes<T, D>(bg.b2p);
+  const unsigned rb_threads =
+      static_cast<unsigned>(kWave * (long_blocks ? 8 : (s.b2 + rb_keys - 1) / rb_keys));
+  const unsigned rb_grid = static_cast<unsigned>(s.BH * s.b1 * nks);
+  const size_t ra_lds = long_blocks ? 0 : rside_bwd_lds_bytes<T, D>(bg.b2p);
+  constexpr int ral_nw = 4;
+  const RBLGeom ral{BH, s.b1, s.b2, s.t, (s.b2 + 32 * ral_nw - 1) / (32 * ral_nw), c, sc};
+  const unsigned ral_grid = static_cast<unsigned>(s.BH * s.b1 * s.t * ral.nrb);
   constexpr int dq_rows = C::kDqRW * C::kDqNW * 16;
   const LGeom row_geom{BH, Nq, s.b1, s.b1q, s.b2, s.t, (ngmax + dq_rows - 1) / dq_rows, c};
   const unsigned row_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * row_geom.nrb);
@@ -814,7 +833,18 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
     const T* qh = bf.qhat_of(i);
     const float* bt = bf.beta_of(i);
     // R-step backward per key block, part 1: G, e and the R row statistics
-    {
+    if (long_blocks) {
+      ok(timed(6, st, [&] {
+        // the R rows' lse from the forward; rho from U (last R-step) or from
+        // the keys Kt and entropies H this R-step handed to the next L-step
+        if (last)
+          kb_rside_a_long<T, D, ral_nw, false><<<ral_grid, ral_nw * kWave, 0, st>>>(
+              k, v, qh, du, dh, bt, bf.rlse_of(i), bf.u, nullptr, gq, ev, lser, rho, ral);
+        else
+          kb_rside_a_long<T, D, ral_nw, true><<<ral_grid, ral_nw * kWave, 0, st>>>(
+              k, v, qh, du, dh, bt, bf.rlse_of(i), bf.ktil_of(i), bf.hent_of(i), gq, ev, lser, rho, ral);
+      }));
+    } else {
       auto launch = [&](auto kern) {
         if (ra_lds > 65536)
           ok(hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -876,7 +906,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
     {
       auto launch = [&](auto kern) {
         ok(timed(10, st, [&] {
-          kern<<<r_grid, rb_threads, 0, st>>>(k, v, qh, du, lser, rho, dh, dkbar, dk, dkacc, dv, bg);
+          kern<<<rb_grid, rb_threads, 0, st>>>(k, v, qh, du, lser, rho, dh, dkbar, dk, dkacc, dv, bg);
         }));
       };
       if (T_ == 1)
@@ -908,8 +938,6 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int check_train(const Shape& s, size_t elem, const void* state, size_t state_bytes) {
   if (elem == 0) return MONARCH_EINVAL;
-  // the backward's key-block kernels hold a whole block row per wave
-  if (s.b2 > kShortB2) return MONARCH_EUNSUPPORTED;
   const TrainState t = train_layout(s, elem);
   if (!state || state_bytes < t.total) return MONARCH_ENOMEM;
   if (reinterpret_cast<uintptr_t>(state) % kAlign != 0) return MONARCH_EINVAL;
@@ -977,7 +1005,7 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
   }
   const int b2p = (s.b2 + 31) / 32 * 32;
   const int DK = s.d < 32 ? 32 : s.d;
-  if (static_cast<size_t>(b2p) * DK * elem * 2 > kLdsBytes) return MONARCH_EUNSUPPORTED;
+  if (s.b2 <= kShortB2 && static_cast<size_t>(b2p) * DK * elem * 2 > kLdsBytes) return MONARCH_EUNSUPPORTED;
 
   const TrainState t = train_layout(s, elem);
   const BwdWorkspace w = bwd_layout(s, elem);
@@ -1121,7 +1149,6 @@ size_t monarch_attn_train_state_bytes(int B, int H, int f, int h, int w, int d, 
   const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   static const char dummy[4] = {0};
   if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
-  if (s.b2 > kShortB2) return 0;  // training keeps key blocks within one wave's registers
   return train_layout(s, elem).total;
 }
 
@@ -1147,7 +1174,6 @@ size_t monarch_attn_train_state_bytes_kv(int B, int H, int fq, int f, int h, int
   const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
   static const char dummy[4] = {0};
   if (check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0) != MONARCH_OK) return 0;
-  if (s.b2 > kShortB2) return 0;  // training keeps key blocks within one wave's registers
   return train_layout(s, elem).total;
 }
 

@@ -16,7 +16,8 @@
 //   l' = a l,   sx' = a (sx - (m' - m) l),   acc' = a acc,   a = 2^(m - m'),
 // which is the entropy taken online alongside the block softmax (the fused
 // "online entropy" of the VMonarch abstract).  At the end U (or Kt) = acc / l
-// and H in bits = log2 l - sx / l.
+// and H in bits = log2 l - sx / l; a training forward also keeps each row's
+// log-sum-exp m + log2 l for the backward.
 #pragma once
 
 #include "lside.h"
@@ -37,6 +38,7 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
                                                 T* qhat,  // [BH][t][b1][b2][D]; U written over it when LAST
                                                 T* __restrict__ ktil, float* __restrict__ hent,
                                                 T* uout,  // U goes here instead when not NULL
+                                                float* rlse,  // the rows' log-sum-exps (log2), when not NULL
                                                 const RLGeom& p, int item, T* sK0, T* sK1, T* sV0, T* sV1) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
@@ -176,6 +178,7 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
     T* dst = (LAST ? (uout ? uout : qhat) : ktil) + row * D;
     store_rows<T, D, NACC, RW>(dst, acc, rt, 1.0f / lt, G);
     if (!LAST && G == 0) hent[row] = log2f(lt) - st / lt;
+    if (rlse && G == 0) rlse[row] = m[rt] + log2f(lt);
   }
 }
 
@@ -190,10 +193,10 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
 template <typename T, int D, int RW, int NW, bool LAST>
 __global__ __launch_bounds__(NW * kWave) void k_rstep_long(const T* __restrict__ k, const T* __restrict__ v, T* qhat,
                                                            T* __restrict__ ktil, float* __restrict__ hent, T* uout,
-                                                           RLGeom p) {
+                                                           float* __restrict__ rlse, RLGeom p) {
   MONARCH_RSTEP_LONG_LDS(T, (D < 32 ? 32 : D), LAST)
-  rstep_long_body<T, D, RW, NW, LAST>(k, v, qhat, ktil, hent, uout, p, xcd_remap(blockIdx.x, gridDim.x), sK0, sK1,
-                                      sV0, sV1);
+  rstep_long_body<T, D, RW, NW, LAST>(k, v, qhat, ktil, hent, uout, rlse, p, xcd_remap(blockIdx.x, gridDim.x), sK0,
+                                      sK1, sV0, sV1);
 }
 
 // Iteration `it` of a run that stops each head on its own (stop_at as for
@@ -211,9 +214,10 @@ __global__ __launch_bounds__(NW * kWave) void k_rstep_long_adaptive(const T* __r
   const int sa = stop_at[bh];
   if (sa != 0 && sa < it) return;
   if (sa == it)
-    rstep_long_body<T, D, RW, NW, true>(k, v, qhat, nullptr, nullptr, nullptr, p, item, sK0, sK1, sV0, sV1);
+    rstep_long_body<T, D, RW, NW, true>(k, v, qhat, nullptr, nullptr, nullptr, nullptr, p, item, sK0, sK1, sV0,
+                                        sV1);
   else
-    rstep_long_body<T, D, RW, NW, false>(k, v, qhat, ktil, hent, nullptr, p, item, sK0, sK1, sV0, sV1);
+    rstep_long_body<T, D, RW, NW, false>(k, v, qhat, ktil, hent, nullptr, nullptr, p, item, sK0, sK1, sV0, sV1);
 }
 
 #undef MONARCH_RSTEP_LONG_LDS

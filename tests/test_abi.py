@@ -135,7 +135,7 @@ def test_train_state_bytes_formula(T):
     (dict(alias=(6, 8)), M.MONARCH_EINVAL),               # dk aliases the state
     (dict(b1=91), M.MONARCH_EINVAL),
     (dict(d=48), M.MONARCH_EUNSUPPORTED),
-    (dict(f=2, h=3, w=130, b1=6, b2=130), M.MONARCH_EUNSUPPORTED),
+    (dict(f=1, h=1, w=16400, b1=1, b2=16400), M.MONARCH_EUNSUPPORTED),  # key blocks beyond 16384
     (dict(T=0, state_bytes=1 << 30), M.MONARCH_EINVAL),
     (dict(T=2, state_bytes="T1"), M.MONARCH_ENOMEM),  # state of a one-iteration forward
 ])
@@ -145,16 +145,18 @@ def test_bwd_bad_arguments_rejected_before_any_gpu_call(kw, status):
     assert _bwd(**kw) == status
 
 
-def test_long_key_blocks_forward_only():
-    # blocks of whole frames (b2 = h*w > 128) run the forward, not training
-    assert M.monarch_attn_workspace_bytes(1, 2, 3, 20, 26, 64, 3, 520, 1, 2, 0) > 0
-    assert M.monarch_attn_kv_workspace_bytes(1, 2, 1, 3, 20, 26, 64, 3, 520, 1, 2, 0) > 0
-    assert M.monarch_attn_train_state_bytes(1, 2, 3, 20, 26, 64, 3, 520, 1, 2, 0) == 0
-    assert M.monarch_attn_train_state_bytes_kv(1, 2, 1, 3, 20, 26, 64, 3, 520, 1, 2, 0) == 0
-    assert M.monarch_attn_train_state_bytes(1, 2, 3, 20, 26, 64, 60, 26, 1, 2, 0) > 0
-    p = _train_ptrs(5)
-    rc = M.lib().monarch_attn_fwd_train(*p[:4], 1, 2, 3, 20, 26, 64, 3, 520, 1, 2, 0, p[4], 1 << 30, None)
-    assert rc == M.MONARCH_EUNSUPPORTED
+def test_long_key_blocks_sizes():
+    # blocks of whole frames (b2 = h*w > 128): the state of short blocks plus
+    # every R-step's row log-sum-exps
+    B, H, f, h, w, d, b1, b2, t, T = 1, 2, 3, 20, 26, 64, 3, 520, 1, 2
+    assert M.monarch_attn_workspace_bytes(B, H, f, h, w, d, b1, b2, t, T, 0) > 0
+    assert M.monarch_attn_kv_workspace_bytes(B, H, 1, f, h, w, d, b1, b2, t, T, 0) > 0
+    N, e = f * h * w, 2
+    expect = (_align(B * H * b1 * d * e) + _align(B * H * b1 * 4)
+              + T * (_align(B * H * N * 4) + _align(B * H * t * N * 4) + _align(B * H * t * N * d * e))
+              + _align(B * H * t * N * d * e) + (T - 1) * (_align(B * H * t * N * d * e) + _align(B * H * t * N * 4)))
+    assert M.monarch_attn_train_state_bytes(B, H, f, h, w, d, b1, b2, t, T, 0) == expect + T * _align(B * H * t * N * 4)
+    assert M.monarch_attn_train_state_bytes_kv(B, H, 1, f, h, w, d, b1, b2, t, T, 0) > 0
 
 
 def test_fwd_train_rejects_small_state():

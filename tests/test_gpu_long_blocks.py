@@ -1,4 +1,5 @@
-"""Key blocks longer than 128 tokens on the GPU (needs an MI355X).
+"""Key blocks longer than 128 tokens on the GPU (needs an MI355X), forward
+and backward.
 
 Blocks of whole frames, (b1, b2) = (f, h*w), and any other factorisation
 with b2 > 128 run the R-step with the online softmax over blocks of 64 keys
@@ -9,6 +10,8 @@ reference's mean magnitude (softmaxes over thousands of keys give small
 outputs, where the absolute bars alone would say little); fp32 max-abs <=
 1e-5.  One key block, (1, N), is exact softmax attention: checked against
 scaled dot-product attention in float64 on the CPU, not against the oracle.
+The gradients (dq, dk, dv through every iteration, square layer and chunk)
+are compared with the gradient oracle with the bars of test_gpu_backward.
 """
 import numpy as np
 import pytest
@@ -17,6 +20,7 @@ import oracle
 from gpu_util import BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, errors, say, to_device, to_host
 from structured_attention_video_monarch_amd import inputs as I
 from test_gpu_adaptive import check_against_oracle, run_adaptive
+from test_gpu_backward import compare_grad
 from test_gpu_kv import run_kv
 from test_gpu_parity import run_gpu
 
@@ -154,3 +158,28 @@ def draw_long(seed):
 def test_fuzz_long_blocks(seed):
     wl = draw_long(seed)
     compare_long(wl, seed=seed, label=f"{wl.name} f,h,w=({wl.f},{wl.h},{wl.w})")
+
+
+# (name, B, H, d, f, h, w, b1, b2, tiles, iters, dtype, query frames (0: all))
+LONG_BWD = [
+    ("bwd_frames_f32_d32", 1, 2, 32, 3, 5, 40, 3, 200, 1, 1, "f32", 0),
+    ("bwd_frames_f32_d32_t3_T2", 1, 2, 32, 3, 5, 40, 3, 200, 3, 2, "f32", 0),
+    ("bwd_b2_129_f32_d16_T3", 1, 2, 16, 3, 1, 129, 3, 129, 3, 3, "f32", 0),
+    ("bwd_b2_130_bf16_d64_T2", 1, 3, 64, 2, 5, 26, 2, 130, 1, 2, "bf16", 0),
+    ("bwd_frames_bf16_d128_t2", 1, 2, 128, 4, 9, 33, 4, 297, 2, 1, "bf16", 0),
+    ("bwd_frames_bf16_d128_t2_T2", 1, 2, 128, 4, 9, 33, 4, 297, 2, 2, "bf16", 0),
+    ("bwd_f32_d128_b2_320_T2", 1, 1, 128, 2, 8, 40, 2, 320, 1, 2, "f32", 0),
+    ("bwd_kv_frames_f32_T2", 1, 2, 32, 3, 5, 40, 3, 200, 1, 2, "f32", 1),
+    ("bwd_kv_frames_bf16", 1, 2, 64, 4, 9, 33, 4, 297, 1, 1, "bf16", 2),
+]
+
+
+@pytest.mark.parametrize("case", LONG_BWD, ids=[c[0] for c in LONG_BWD])
+def test_bwd_long_blocks(case):
+    name, B, H, d, f, h, w, b1, b2, t, T, dt, fq = case
+    compare_grad(I.Workload(name, B, H, d, f, h, w, b1, b2, t, T, dt, fq=fq), iters=T)
+
+
+def test_bwd_clip480p_frames():
+    wl = I.get_workload("clip480p_frames").with_(H=2)
+    compare_grad(wl, heads=[1])
