@@ -466,8 +466,8 @@ __device__ inline void dma_rowstat(float* dst, const float* src, long long rbase
                                    (__attribute__((address_space(3))) void*)(dst), 4, 0, 0);
 }
 
-template <typename T, int D, int MODE = kRbSingle>
-__global__ __launch_bounds__(MONARCH_BRB_RW == 1 ? 512 : 256) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
+template <typename T, int D, int MODE = kRbSingle, int RWK = MONARCH_BRB_RW>
+__global__ __launch_bounds__(RWK == 1 || RWK != MONARCH_BRB_RW ? 512 : 256) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ qhat, const T* __restrict__ du,
                                                   const float* __restrict__ lser, const float* __restrict__ rho,
                                                   const float* __restrict__ dh,
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(MONARCH_BRB_RW == 1 ? 512 : 256) void kb_rside_b(co
   constexpr int NACC = NDP > 0 ? NDP : 1;
   // 32-row blocks per pipeline stage (f32 tiles are twice as large: one)
   constexpr int BPS = sizeof(T) == 2 ? MONARCH_BRB_BPS : 1;
-  constexpr int RW = MONARCH_BRB_RW;
+  constexpr int RW = RWK;
   __shared__ __align__(16) T sQ[2][BPS][32 * DK];
   __shared__ __align__(16) T sU[2][BPS][32 * DK];
   __shared__ __align__(16) float sLR[2][BPS][64];

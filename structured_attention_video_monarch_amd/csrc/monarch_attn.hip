@@ -670,6 +670,9 @@ template <typename T> struct BwdCfg;
 #ifndef MONARCH_BDQ_STEP
 #define MONARCH_BDQ_STEP 64
 #endif
+#ifndef MONARCH_BRBL_RW
+#define MONARCH_BRBL_RW 2  // keys per wave / 16 of kb_rside_b for key blocks over 128
+#endif
 #ifndef MONARCH_BDU_RW
 #define MONARCH_BDU_RW 1
 #endif
@@ -813,8 +816,9 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   // the block's keys in slices of 8 waves (kb_rside_b)
   const bool long_blocks = s.b2 > kShortB2;
   constexpr int rb_keys = 16 * MONARCH_BRB_RW;  // keys c2 per wave of kb_rside_b
-  const int nks = long_blocks ? (s.b2 + 8 * rb_keys - 1) / (8 * rb_keys) : 1;
-  const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc, nks, 8 * rb_keys};
+  constexpr int rbl_keys = 16 * MONARCH_BRBL_RW;  // keys per wave of kb_rside_b for long blocks
+  const int nks = long_blocks ? (s.b2 + 8 * rbl_keys - 1) / (8 * rbl_keys) : 1;
+  const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc, nks, 8 * rbl_keys};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
   const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
   const unsigned rb_threads =
@@ -909,14 +913,25 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
           kern<<<rb_grid, rb_threads, 0, st>>>(k, v, qh, du, lser, rho, dh, dkbar, dk, dkacc, dv, bg);
         }));
       };
-      if (T_ == 1)
+      constexpr int RL = MONARCH_BRBL_RW;
+      if (long_blocks) {
+        if (T_ == 1)
+          launch(&kb_rside_b<T, D, kRbSingle, RL>);
+        else if (last)
+          launch(&kb_rside_b<T, D, kRbLast, RL>);
+        else if (first)
+          launch(&kb_rside_b<T, D, kRbFirst, RL>);
+        else
+          launch(&kb_rside_b<T, D, kRbMid, RL>);
+      } else if (T_ == 1) {
         launch(&kb_rside_b<T, D, kRbSingle>);
-      else if (last)
+      } else if (last) {
         launch(&kb_rside_b<T, D, kRbLast>);
-      else if (first)
+      } else if (first) {
         launch(&kb_rside_b<T, D, kRbFirst>);
-      else
+      } else {
         launch(&kb_rside_b<T, D, kRbMid>);
+      }
     }
     // key side of an L-step on aggregated keys: dKt and dH of the R-step
     // before, into du and dh (their last readers, this iteration's R-step
