@@ -21,6 +21,7 @@
 
 #include "backward.h"
 #include "backward_long.h"
+#include "backward_cols.h"
 #include "lside.h"
 #include "lside_cols.h"
 #include "rside.h"
@@ -801,9 +802,20 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   constexpr int du_cb = C::kDuRW * C::kDuNW * 16;
   const LGeom col_geom{BH, Nq, s.b1, s.b1q, s.b2, s.t, (s.b1 + du_cb - 1) / du_cb, c};
   const unsigned col_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * col_geom.nrb);
+  // short tile columns (few key blocks, few rows per tile): one column per
+  // wave in kb_du and kb_dq
+  constexpr int cols_nw = 4;
+  const bool cols = s.b1 <= kColsRows && ngmax <= kColsRows;
+  const unsigned cols_grid = static_cast<unsigned>(s.BH * s.t * ((s.b2 + cols_nw - 1) / cols_nw));
   // dU = L^T dy per tile column (L of the last L-step)
   ok(timed(5, st, [&] {
-    if (T_ == 1)
+    if (cols && T_ == 1)
+      kb_du_cols<T, D, cols_nw, true><<<cols_grid, cols_nw * kWave, 0, st>>>(q, dout, bf.kbar, nullptr, bf.lse_of(1),
+                                                                             du, col_geom);
+    else if (cols)
+      kb_du_cols<T, D, cols_nw, false><<<cols_grid, cols_nw * kWave, 0, st>>>(q, dout, keys_of(T_), ent_of(T_),
+                                                                              bf.lse_of(T_), du, col_geom);
+    else if (T_ == 1)
       kb_du<T, D, C::kDuRW, C::kDuNW, true><<<col_grid, C::kDuNW * kWave, 0, st>>>(q, dout, bf.kbar, nullptr,
                                                                                   bf.lse_of(1), du, col_geom);
     else
@@ -875,7 +887,25 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
       }
     }
     // row pass: this L-step's dq term and the stored s*dl
-    {
+    if (cols) {
+      // f32 tiles are twice as large: two columns per workgroup
+      constexpr int dq_nw = sizeof(T) == 2 ? cols_nw : 2;
+      const unsigned dq_grid = static_cast<unsigned>(s.BH * s.t * ((s.b2 + dq_nw - 1) / dq_nw));
+      auto launch = [&](auto kern) {
+        ok(timed(7, st, [&] {
+          kern<<<dq_grid, dq_nw * kWave, 0, st>>>(q, dout, out, keys_of(i), ent_of(i), bf.lse_of(i), bf.u, gq, ev,
+                                                  dq, dqacc, dl, w.ldl, row_geom, sc);
+        }));
+      };
+      if (T_ == 1)
+        launch(&kb_dq_cols<T, D, dq_nw, true, true, kDqStore>);
+      else if (last)
+        launch(&kb_dq_cols<T, D, dq_nw, false, true, kDqInit>);
+      else if (first)
+        launch(&kb_dq_cols<T, D, dq_nw, true, false, kDqFinish>);
+      else
+        launch(&kb_dq_cols<T, D, dq_nw, false, false, kDqAdd>);
+    } else {
       auto launch = [&](auto kern) {
         ok(timed(7, st, [&] {
           kern<<<row_grid, C::kDqNW * kWave, 0, st>>>(q, dout, out, keys_of(i), ent_of(i), bf.lse_of(i), bf.u, gq,
