@@ -4,8 +4,8 @@ For strongly peaked softmaxes the layer is ill-conditioned: a relative
 rounding error of the order of float32's moves the next L-step's logits by
 about s|q||k| times as much, so any float32 evaluation of the method lands
 visibly away from the float64 oracle.  How far the oracle's own steps land
-when run in float32 is then the scale against which the fp32 GPU path is
-judged on such inputs.  The modules below are the oracle sources with every
+when run in float32 is then the scale the fp32 GPU path is held to on such
+inputs.  The modules below are the oracle sources with every
 float64 array made float32 (nothing else changes); they are built from the
 source text, as the planted-mistake tests build theirs.
 """
