@@ -226,6 +226,21 @@ int monarch_attn_bwd_kv(const void* q, const void* k, const void* v, const void*
                         int b1, int b2, int tiles, int iters, int dtype,
                         void* state, size_t state_bytes, void* stream);
 
+/* ---- the factors themselves (test-only export) ----
+ * monarch_attn_debug_factors_f32 runs the fp32 forward of monarch_attn_fwd_f32
+ * (square layer) and writes the factors of its last iteration, the L and R
+ * that the output y = P^T L P R v applies (MonarchRT article, "Monarch
+ * matrices"), as fp32 device arrays the caller owns:
+ *   L_out [B,H,b2,b1,b1]:   L[a2][a1][c1], each row a1 sums to 1 over c1;
+ *   R_out [B,H,t,b1,b2,b2]: R[g][c1][a2][c2], each row sums to 1 over c2.
+ * For parity tests of the factors on small shapes: the counts B*H*b2*b1*b1
+ * and B*H*t*N*b2 must each be at most 2^28 (else MONARCH_EUNSUPPORTED); the
+ * outputs must not overlap the inputs or each other (MONARCH_EINVAL).  It
+ * allocates a temporary training state stream-ordered and is not tuned. */
+int monarch_attn_debug_factors_f32(const float* q, const float* k, const float* v, float* L_out, float* R_out,
+                                   int B, int H, int f, int h, int w, int d,
+                                   int b1, int b2, int tiles, int iters, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* monarch_attn_status_string(int status);
 

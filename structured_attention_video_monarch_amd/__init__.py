@@ -42,6 +42,8 @@ def _declare(lib):
     lib.monarch_attn_fwd.restype = c_int
     lib.monarch_attn_fwd_f32.argtypes = [c_void_p] * 4 + dims + [c_void_p]
     lib.monarch_attn_fwd_f32.restype = c_int
+    lib.monarch_attn_debug_factors_f32.argtypes = [c_void_p] * 5 + dims + [c_void_p]
+    lib.monarch_attn_debug_factors_f32.restype = c_int
     lib.monarch_attn_workspace_bytes.argtypes = dims + [c_int]
     lib.monarch_attn_workspace_bytes.restype = c_size_t
     lib.monarch_attn_fwd_ws.argtypes = [c_void_p] * 4 + dims + [c_int, c_void_p, c_size_t, c_void_p]
@@ -163,6 +165,20 @@ def monarch_attn_fwd_f32(q, k, v, out, f, h, w, b1, b2, tiles=1, iters=1, stream
     _check(lib().monarch_attn_fwd_f32(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, iters), _stream(stream)),
            "monarch_attn_fwd_f32")
     return out
+
+
+def monarch_attn_debug_factors_f32(q, k, v, f, h, w, b1, b2, tiles=1, iters=1, stream=None):
+    """Test-only: the factors of the last iteration of the float32 forward,
+    L [B,H,b2,b1,b1] (L[a2][a1][c1]) and R [B,H,t,b1,b2,b2] (R[g][c1][a2][c2]),
+    as new GPU tensors."""
+    import torch
+    dims = _dims(q, f, h, w, b1, b2, tiles, iters)
+    B, H = dims[0], dims[1]
+    L = torch.empty((B, H, b2, b1, b1), dtype=torch.float32, device=q.device)
+    R = torch.empty((B, H, tiles, b1, b2, b2), dtype=torch.float32, device=q.device)
+    ptrs = _tensors(q, k, v, q, torch.float32)[:3] + [ctypes.c_void_p(L.data_ptr()), ctypes.c_void_p(R.data_ptr())]
+    _check(lib().monarch_attn_debug_factors_f32(*ptrs, *dims, _stream(stream)), "monarch_attn_debug_factors_f32")
+    return L, R
 
 
 def monarch_attn_workspace_bytes(B, H, f, h, w, d, b1, b2, tiles, iters, dtype=MONARCH_BF16) -> int:

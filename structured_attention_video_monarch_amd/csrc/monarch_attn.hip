@@ -22,6 +22,7 @@
 #include "backward.h"
 #include "backward_long.h"
 #include "backward_cols.h"
+#include "debug_factors.h"
 #include "lside.h"
 #include "lside_cols.h"
 #include "rside.h"
@@ -1089,6 +1090,71 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
 }  // namespace
 
 // ------------------------------------------------------------------- C ABI --
+// The factors of the last iteration (test-only export): a fp32 training
+// forward into a stream-ordered temporary state, then L and R written from
+// its lse, keys, entropies and aggregated queries.
+int debug_factors(const float* q, const float* k, const float* v, float* L_out, float* R_out, const Shape& s,
+                  hipStream_t st) {
+  if (!q || !k || !v || !L_out || !R_out) return MONARCH_EINVAL;
+  static const char dummy[4] = {0};
+  int rc = check_args(dummy, dummy + 1, dummy + 2, dummy + 3, s, 0);  // shape checks
+  if (rc != MONARCH_OK) return rc;
+  const long long lcount = s.BH * s.b2 * static_cast<long long>(s.b1) * s.b1;
+  const long long rcount = s.BH * s.t * s.N * static_cast<long long>(s.b2);
+  if (lcount > (1LL << 28) || rcount > (1LL << 28)) return MONARCH_EUNSUPPORTED;
+  const size_t io = static_cast<size_t>(s.BH * s.N * s.d) * sizeof(float);
+  const void* ins[] = {q, k, v};
+  void* outs[] = {L_out, R_out};
+  const size_t outsz[] = {static_cast<size_t>(lcount) * sizeof(float), static_cast<size_t>(rcount) * sizeof(float)};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], io)) return MONARCH_EINVAL;
+  if (overlaps(L_out, outsz[0], R_out, outsz[1])) return MONARCH_EINVAL;
+
+  const TrainState t = train_layout(s, sizeof(float));
+  void* tmp = nullptr;
+  hipError_t e = hipMallocAsync(&tmp, t.total + io, st);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    (void)hipGetLastError();
+    return e == hipErrorOutOfMemory ? MONARCH_ENOMEM : MONARCH_EHIP;
+  }
+  unsigned char* state = static_cast<unsigned char*>(tmp);
+  float* y = reinterpret_cast<float*>(state + t.total);
+  rc = fwd_train(q, k, v, y, s, MONARCH_F32, state, t.total, st);
+  if (rc == MONARCH_OK) {
+    const Bufs<float> b = train_bufs<float>(state, t, s.T);
+    const FGeom fg{static_cast<int>(s.BH), static_cast<int>(s.N), s.b1, s.b2, s.t,
+                   kLog2e / std::sqrt(static_cast<float>(s.d))};
+    const float* kt = s.T == 1 ? b.kbar : b.ktil_of(s.T - 1);
+    const float* h2 = s.T == 1 ? nullptr : b.hent_of(s.T - 1);
+    const unsigned lgrid = static_cast<unsigned>((lcount + 255) / 256);
+    const unsigned rgrid = static_cast<unsigned>((s.BH * s.t * s.N + 255) / 256);
+    auto go = [&](auto dtag) {
+      constexpr int D = decltype(dtag)::value;
+      k_factor_L<D><<<lgrid, 256, 0, st>>>(q, kt, h2, b.lse_of(s.T), L_out, fg);
+      k_factor_R<D><<<rgrid, 256, 0, st>>>(b.qhat_of(s.T), k, R_out, fg);
+    };
+    switch (s.d) {
+      case 16: go(std::integral_constant<int, 16>{}); break;
+      case 32: go(std::integral_constant<int, 32>{}); break;
+      case 64: go(std::integral_constant<int, 64>{}); break;
+      default: go(std::integral_constant<int, 128>{}); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      g_last_hip_error = static_cast<int>(e);
+      rc = MONARCH_EHIP;
+    }
+  }
+  const hipError_t ef = hipFreeAsync(tmp, st);
+  if (rc == MONARCH_OK && ef != hipSuccess) {
+    g_last_hip_error = static_cast<int>(ef);
+    rc = MONARCH_EHIP;
+  }
+  return rc;
+}
+
 extern "C" {
 
 int monarch_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int f,
@@ -1235,6 +1301,13 @@ int monarch_attn_bwd_kv(const void* q, const void* k, const void* v, const void*
                         void* stream) {
   const Shape s = make_shape_kv(B, H, fq, f, h, w, d, b1, b2, tiles, iters);
   return bwd(q, k, v, out, dout, dq, dk, dv, s, dtype, state, state_bytes, static_cast<hipStream_t>(stream));
+}
+
+int monarch_attn_debug_factors_f32(const float* q, const float* k, const float* v, float* L_out, float* R_out,
+                                   int B, int H, int f, int h, int w, int d, int b1, int b2, int tiles, int iters,
+                                   void* stream) {
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
+  return debug_factors(q, k, v, L_out, R_out, s, static_cast<hipStream_t>(stream));
 }
 
 const char* monarch_attn_status_string(int status) {

@@ -268,3 +268,24 @@ def test_adaptive_kv_workspace_and_bad_arguments():
     bad = (1, 2, 1, 4, 3, 5, 64, 12, 5, 4, 10)      # tiles 4 > query blocks 3
     assert lib.monarch_attn_fwd_adaptive_kv_ws(*p[:4], *bad, 1e-3, 0, p[4], p[5], 1 << 30,
                                                None) == M.MONARCH_EINVAL
+
+
+# ---- the factors (test-only export)
+def _factors(q=1, k=2, v=3, L=4, R=5, B=1, H=2, f=2, h=4, w=4, d=16, b1=8, b2=4, t=1, T=1):
+    P = ctypes.c_void_p
+    return M.lib().monarch_attn_debug_factors_f32(P(q), P(k), P(v), P(L), P(R), B, H, f, h, w, d, b1, b2, t, T, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), M.MONARCH_EINVAL),
+    (dict(R=0), M.MONARCH_EINVAL),
+    (dict(b1=7), M.MONARCH_EINVAL),
+    (dict(T=0), M.MONARCH_EINVAL),
+    (dict(d=48), M.MONARCH_EUNSUPPORTED),
+    (dict(H=1 << 20, f=4, h=16, w=16, b1=64, b2=16), M.MONARCH_EUNSUPPORTED),  # more than 2^28 factor entries
+    (dict(L=_GAP, R=_GAP + 64), M.MONARCH_EINVAL),  # L and R overlap
+])
+def test_factors_bad_arguments_rejected_before_any_gpu_call(kw, status):
+    if "L" in kw and kw["L"] == _GAP:
+        kw = dict(kw, q=2 * _GAP, k=3 * _GAP, v=4 * _GAP)
+    assert _factors(**kw) == status
