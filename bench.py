@@ -224,6 +224,9 @@ def main():
     ap.add_argument("--tol", type=float, default=None,
                     help="iterate until the objective gain per token is <= tol (at most --iters or the "
                          "workload's count; each head stops on its own)")
+    ap.add_argument("--graph", action="store_true",
+                    help="forward: also capture one call in a HIP graph and report the time per replay "
+                         "(the value then comes from the replays; per-kernel figures from the eager run)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (float32 read + write), "
                          "to scale HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
@@ -348,6 +351,37 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
+    graph_rec = None
+    if args.graph:
+        if args.mode != "fwd" or args.tol is not None:
+            print("bench.py: --graph times the forward with a fixed iteration count", file=sys.stderr)
+            sys.exit(2)
+        # capture on a side stream (the step functions launch on `stream`)
+        eager_stream = stream
+        stream = torch.cuda.Stream(dev)
+        stream.wait_stream(eager_stream)
+        with torch.cuda.stream(stream):
+            step()  # one call off the capture
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize(dev)
+        for _ in range(args.warmup):
+            graph.replay()
+        cur = torch.cuda.current_stream(dev)
+        torch.cuda.synchronize(dev)
+        ev0.record(cur)
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record(cur)
+        torch.cuda.synchronize(dev)
+        ms_graph = ev0.elapsed_time(ev1) / args.steps
+        print(f"[bench] {args.steps} graph replays, {ms_graph:.4f} ms/step", file=sys.stderr, flush=True)
+        graph_rec = {"eager_ms_per_step_with_kernel_events": round(ms_step, 5),
+                     "replay_ms_per_step": round(ms_graph, 5)}
+        ms_step = ms_graph
+
     kernels = {}
     for full, (ms, n) in per_kernel.items():
         short = full.split(" ")[0]
@@ -404,6 +438,8 @@ def main():
         "kernels": kernels,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if graph_rec is not None:
+        res["graph"] = graph_rec
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = (cpu_baseline(wl, args.seed, args.cpu_budget) if args.mode == "fwd"

@@ -1,0 +1,86 @@
+"""The forward captured in a HIP graph and replayed (needs an MI355X).
+
+Callers that launch many small layers (a chunk of three frames is launch
+bound: five kernels of 10-20 us each) can capture the workspace entry points,
+which allocate nothing and record no memset, in a graph and replay it.  Each
+case captures one call, then replays it three times with eager work of the
+program and a synchronisation between the replays, and checks every replay
+bit for bit against the eager result of the same call; the eager result is
+checked against the oracle on one head with the usual bars.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import BF16_MAX_ABS, BF16_MEAN_ABS, errors, say, to_device, to_host
+from structured_attention_video_monarch_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _layer(wl):
+    """(workspace bytes, call(q, k, v, out, ws)) of the workload's entry point."""
+    import structured_attention_video_monarch_amd as M
+    if wl.kv:
+        nb = M.monarch_attn_kv_workspace_bytes(wl.B, wl.H, wl.fq, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles,
+                                               wl.iters)
+        return nb, lambda q, k, v, out, ws: M.monarch_attn_fwd_kv(q, k, v, out, wl.fq, wl.f, wl.h, wl.w, wl.b1,
+                                                                 wl.b2, wl.tiles, wl.iters, workspace=ws)
+    nb = M.monarch_attn_workspace_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles, wl.iters)
+    return nb, lambda q, k, v, out, ws: M.monarch_attn_fwd_ws(q, k, v, out, wl.f, wl.h, wl.w, wl.b1, wl.b2,
+                                                             wl.tiles, wl.iters, ws)
+
+
+CASES = [
+    ("chunk480p", {}),
+    ("clip480p", {"H": 2, "iters": 2}),
+    ("chunk480p_kv", {"H": 2}),
+    ("clip480p_frames", {"H": 1}),
+]
+
+
+@pytest.mark.parametrize("name,over", CASES, ids=[c[0] for c in CASES])
+def test_graph_replays_match_eager(name, over):
+    wl = I.get_workload(name).with_(**over)
+    say(f"[case] graph {name} H={wl.H} T={wl.iters} blocks=({wl.b1},{wl.b2})")
+    x = I.make_inputs(wl, 4)
+    q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
+    nb, call = _layer(wl)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    eager = torch.empty_like(q)
+    call(q, k, v, eager, ws)
+    torch.cuda.synchronize()
+
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one call off the capture, as torch asks before capturing
+        call(q, k, v, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(q, k, v, out, ws)
+    torch.cuda.synchronize()
+
+    other = torch.empty_like(q)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        call(k[:, :, :q.shape[2]].contiguous(), q if not wl.kv else k, v, other, ws)  # eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
+    y = to_host(eager)
+    ref = oracle.monarch_head(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], wl.b1, wl.b2, wl.tiles, wl.iters)
+    mx, mean = errors(y[0, 0], ref)
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    say(f"[ok] graph {name}: 3 replays equal to the eager call; eager vs oracle max-abs {mx:.3e}")
