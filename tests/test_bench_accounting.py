@@ -1,0 +1,39 @@
+"""bench.py's algorithmic work model against the closed form of the path.
+
+Per layer call the method's products are, per (batch, head): the L logits,
+L^T q and L U over b1 key blocks for every query token, once per iteration
+except L U (once), and the R logits and R V (or R K) over b2 keys for every
+(tile, key) row once per iteration:
+  flops = 2 d [(2T + 1) Nq b1 + 2 T t N b2]
+(a chunk against cached keys has Nq query tokens; the R side runs over all N).
+The per-kernel figures bench.py reports the roofline with must add up to
+this, whatever the launch counts of an iteration count.
+"""
+import pytest
+
+import bench
+from structured_attention_video_monarch_amd import inputs as I
+
+
+def closed_form_flops(wl):
+    T = wl.iters
+    return wl.B * wl.H * 2.0 * wl.d * ((2 * T + 1) * wl.Nq * wl.b1 + 2 * T * wl.tiles * wl.N * wl.b2)
+
+
+@pytest.mark.parametrize("name", ["latent720p", "clip480p_spikes_t4_T1", "chunk480p_kv", "clip480p_frames"])
+@pytest.mark.parametrize("T", [1, 2, 10])
+def test_forward_work_sums_to_closed_form(name, T):
+    wl = I.get_workload(name).with_(iters=T)
+    launches = {"k_kbar": 1, "k_lse": T, "k_aggregate": T, "k_rstep": T, "k_apply": 1}
+    tot = bench.step_work(wl, "fwd", launches)
+    flops = sum(tot[k][0] for k in launches)
+    assert abs(flops - closed_form_flops(wl)) <= 1e-9 * closed_form_flops(wl)
+
+
+def test_latent720p_one_iteration_is_2690_gflop():
+    # 40 heads of 75600 tokens, d = 128, blocks (945, 80), 4 tiles:
+    # 2*128*(3*75600*945 + 2*4*75600*80) per head = 6.726e10; x 40 = 2.690e12
+    wl = I.get_workload("latent720p")
+    tot = bench.step_work(wl, "fwd", {"k_kbar": 1, "k_lse": 1, "k_aggregate": 1, "k_rstep": 1, "k_apply": 1})
+    flops = sum(v[0] for v in tot.values())
+    assert abs(flops - 2.690e12) <= 0.001 * 2.690e12
