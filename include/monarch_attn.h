@@ -258,7 +258,9 @@ int monarch_attn_last_hip_error(void);
  * 7 row pass (dq), 8 block-mean key gradient (product over tokens),
  * 9 its reduction, 10 dv and dk per key block; 11 objective and early-stop
  * decision per head; 12 (backward, several iterations) gradient of the
- * aggregated keys and entropies per tile column. */
+ * aggregated keys and entropies per tile column.  Each id covers every form
+ * of its step that the library picks by shape (key blocks over 128 tokens,
+ * tile columns of at most 32 rows and keys). */
 #define MONARCH_NUM_KERNELS 13
 int monarch_attn_profile_enable(int on);
 int monarch_attn_profile_collect(double* ms, long* launches, int n);
