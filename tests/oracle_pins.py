@@ -17,7 +17,8 @@ never from the oracle's own output:
   decreases, and the objective equals sum lse - sum KL to dense attention;
 * block rank at most the tile count, and the KKT (log-softmax) conditions;
 * an exactly separable positional input is reproduced exactly by aligned
-  blocks in one iteration;
+  blocks in one iteration, and an input separable into frame and position
+  parts by blocks of whole frames;
 * chunked queries against cached keys: row-stochastic non-square M equal to
   the factored apply, exact attention where the blocks degenerate, and a chunk
   equal to the matching rows of the square layer over all frames.
@@ -294,6 +295,28 @@ def check_separable_positional_exact(orc):
     assert orc.row_kl(Ms, _dense_A(qs, ks)).mean() >= 1e-4
 
 
+def check_frame_separable_exact(orc):
+    """Blocks of whole frames, (b1, b2) = (f, h*w) (reading D15): logits that
+    split into a part depending on the two frames plus a part depending on
+    the two positions within a frame make attention the product of a frame
+    softmax and a position softmax, which these blocks reproduce exactly in
+    one iteration for any tile count; blocks of half frames do not."""
+    f, hw, d1, d2 = 4, 6, 5, 7
+    rng = np.random.default_rng(11)
+    qf, kf = rng.standard_normal((f, d1)), rng.standard_normal((f, d1))
+    qp, kp = rng.standard_normal((hw, d2)), rng.standard_normal((hw, d2))
+    # token n = frame * hw + position; features [frame part, position part]
+    q = 1.3 * np.concatenate([np.repeat(qf, hw, axis=0), np.tile(qp, (f, 1))], axis=1)
+    k = 1.3 * np.concatenate([np.repeat(kf, hw, axis=0), np.tile(kp, (f, 1))], axis=1)
+    v = rng.standard_normal((f * hw, d1 + d2))
+    dense = _sdpa(q, k, v)
+    for t in (1, 2, 4):
+        y = orc.monarch_head(q, k, v, f, hw, t, 1)
+        assert np.max(np.abs(y - dense)) <= TOL, t
+    y = orc.monarch_head(q, k, v, 2 * f, hw // 2, 1, 1)
+    assert np.max(np.abs(y - dense)) >= 1e-4
+
+
 # --------------------------------------- chunked queries, cached keys (KV) --
 
 def check_kv_row_stochastic_and_dense_apply(orc):
@@ -398,4 +421,5 @@ ALL_CHECKS = [
     check_kv_chunk_is_last_tiles_of_full_layer,
     check_adaptive_iterations,
     check_separable_positional_exact,
+    check_frame_separable_exact,
 ]
