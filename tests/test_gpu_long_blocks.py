@@ -183,3 +183,35 @@ def test_bwd_long_blocks(case):
 def test_bwd_clip480p_frames():
     wl = I.get_workload("clip480p_frames").with_(H=2)
     compare_grad(wl, heads=[1])
+
+
+@pytest.mark.parametrize("dtype,t", [("f32", 1), ("f32", 3), ("bf16", 1)])
+def test_frame_separable_input_is_exact_attention(dtype, t):
+    """Logits that split into a frame part plus a position part: attention is
+    a frame softmax times a position softmax, which blocks of whole frames
+    reproduce exactly in one iteration at any tile count (checked against
+    scaled dot-product attention in float64, not against the oracle)."""
+    import structured_attention_video_monarch_amd as M
+    f, h, w, d1, d2 = 6, 10, 20, 32, 32
+    hw = h * w
+    rng = np.random.default_rng(12)
+    qf, kf = rng.standard_normal((f, d1)), rng.standard_normal((f, d1))
+    qp, kp = rng.standard_normal((hw, d2)), rng.standard_normal((hw, d2))
+    q = 1.3 * np.concatenate([np.repeat(qf, hw, axis=0), np.tile(qp, (f, 1))], axis=1)
+    k = 1.3 * np.concatenate([np.repeat(kf, hw, axis=0), np.tile(kp, (f, 1))], axis=1)
+    v = rng.standard_normal((f * hw, d1 + d2))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tq, tk, tv = (torch.from_numpy(a).to(tdt).cuda()[None, None].contiguous() for a in (q, k, v))
+    say(f"[case] frame-separable input, blocks ({f},{hw}), t={t}, {dtype}")
+    out = torch.empty_like(tq)
+    (M.monarch_attn_fwd if dtype == "bf16" else M.monarch_attn_fwd_f32)(tq, tk, tv, out, f, h, w, f, hw, t, 1)
+    torch.cuda.synchronize()
+    # the reference reads the values the GPU read (bf16-rounded for bf16)
+    rq, rk, rv = (x[0, 0].to(torch.float64).cpu()[None, None] for x in (tq, tk, tv))
+    ref = torch.nn.functional.scaled_dot_product_attention(rq, rk, rv)[0, 0].numpy()
+    mx, mean = errors(out[0, 0].float().cpu().numpy().astype(np.float64), ref)
+    if dtype == "bf16":
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    else:
+        assert mx <= F32_MAX_ABS, mx
+    say(f"[ok] frame-separable input t={t} {dtype}: max-abs {mx:.3e}")
