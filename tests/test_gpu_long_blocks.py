@@ -8,8 +8,10 @@ with the CPU oracle element by element: bf16 max-abs <= 2e-2 and mean-abs
 <= 2e-3 as for every workload, and in addition mean-abs <= 2e-2 of the
 reference's mean magnitude (softmaxes over thousands of keys give small
 outputs, where the absolute bars alone would say little); fp32 max-abs <=
-1e-5.  One key block, (1, N), is exact softmax attention: checked against
-scaled dot-product attention in float64 on the CPU, not against the oracle.
+1e-5.  One key block, (1, N), is exact softmax attention: its output and its
+gradients are checked against scaled dot-product attention (and autograd
+through it) in float64 on the CPU, not against the oracle; so is the output
+on an input whose logits split into a frame term plus a position term.
 The gradients (dq, dk, dv through every iteration, square layer and chunk)
 are compared with the gradient oracle with the bars of test_gpu_backward.
 """
@@ -215,3 +217,36 @@ def test_frame_separable_input_is_exact_attention(dtype, t):
     else:
         assert mx <= F32_MAX_ABS, mx
     say(f"[ok] frame-separable input t={t} {dtype}: max-abs {mx:.3e}")
+
+
+@pytest.mark.parametrize("dtype,b2,T", [("f32", 600, 1), ("f32", 600, 2), ("bf16", 600, 2), ("f32", 100, 2),
+                                        ("bf16", 100, 1)])
+def test_one_key_block_gradients_are_attention_gradients(dtype, b2, T):
+    """(b1, b2) = (1, N) is softmax attention as a function of q, k and v, not
+    only in value (every L is identically 1 and Qh = q), so its gradients are
+    those of dense attention: checked against autograd through scaled
+    dot-product attention in float64 on the CPU, not against the gradient
+    oracle, for the online R-step (600 keys) and the register-resident one
+    (100 keys), with the bars of test_gpu_backward."""
+    from test_gpu_backward import BF16_REL_MAX, BF16_REL_MEAN, F32_REL_MAX, rel_errors, run_train
+    f, h, w = (2, 6, 50) if b2 == 600 else (1, 10, 10)
+    wl = I.Workload("one_block_grad", 1, 2, 64, f, h, w, 1, b2, 1, T, dtype)
+    say(f"[case] gradients of one key block of {wl.N} keys, {dtype}, T={T}")
+    x = I.make_inputs(wl, 5)
+    dyx = I.make_cotangent(wl, 5)
+    _, dq, dk, dv = run_train(wl, x, dyx)
+    worst = {}
+    for hh in range(wl.H):
+        q, k, v = (torch.from_numpy(x[n][0, hh]).to(torch.float64).requires_grad_() for n in "qkv")
+        y = torch.nn.functional.scaled_dot_product_attention(q[None, None], k[None, None], v[None, None])[0, 0]
+        y.backward(torch.from_numpy(dyx["dy"][0, hh]).to(torch.float64))
+        for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), (q.grad, k.grad, v.grad)):
+            mx, mean = rel_errors(got[0, hh], ref.numpy())
+            wv = worst.get(name, (0.0, 0.0))
+            worst[name] = (max(wv[0], mx), max(wv[1], mean))
+            if dtype == "bf16":
+                assert mx <= BF16_REL_MAX and mean <= BF16_REL_MEAN, (name, hh, mx, mean)
+            else:
+                assert mx <= F32_REL_MAX, (name, hh, mx)
+    say(f"[ok] one key block gradients {dtype} N={wl.N} T={T}: " + ", ".join(
+        f"{n} rel-max {wv[0]:.2e}" for n, wv in worst.items()))
