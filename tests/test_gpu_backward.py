@@ -32,7 +32,9 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def run_train(wl, x, dyx):
+def run_train(wl, x, dyx, host=True):
+    """(y, dq, dk, dv) of the training forward and the backward: float64 host
+    arrays, or the device tensors themselves when host is False."""
     import structured_attention_video_monarch_amd as M
     q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
     dy = to_device(dyx, "dy", wl.dtype)
@@ -55,6 +57,8 @@ def run_train(wl, x, dyx):
         M.monarch_attn_fwd_train(q, k, v, out, *args, state)
         M.monarch_attn_bwd(q, k, v, out, dy, dq, dk, dv, *args, state)
     torch.cuda.synchronize()
+    if not host:
+        return out, dq, dk, dv
     return [to_host(t) for t in (out, dq, dk, dv)]
 
 
