@@ -219,26 +219,39 @@ def test_frame_separable_input_is_exact_attention(dtype, t):
     say(f"[ok] frame-separable input t={t} {dtype}: max-abs {mx:.3e}")
 
 
+# key block length -> (frames, height, width, heads); 16384 is the largest
+# key block the library takes
+ONE_BLOCK = {100: (1, 10, 10, 2), 600: (2, 6, 50, 2), 16384: (1, 128, 128, 1)}
+
+
 @pytest.mark.parametrize("dtype,b2,T", [("f32", 600, 1), ("f32", 600, 2), ("bf16", 600, 2), ("f32", 100, 2),
-                                        ("bf16", 100, 1)])
+                                        ("bf16", 100, 1), ("f32", 16384, 1), ("bf16", 16384, 2)])
 def test_one_key_block_gradients_are_attention_gradients(dtype, b2, T):
     """(b1, b2) = (1, N) is softmax attention as a function of q, k and v, not
     only in value (every L is identically 1 and Qh = q), so its gradients are
     those of dense attention: checked against autograd through scaled
     dot-product attention in float64 on the CPU, not against the gradient
-    oracle, for the online R-step (600 keys) and the register-resident one
-    (100 keys), with the bars of test_gpu_backward."""
+    oracle, for the online R-step (600 keys, and 16384, the largest key block)
+    and the register-resident one (100 keys), with the bars of
+    test_gpu_backward; the training forward's output against the same
+    attention with the forward bars."""
     from test_gpu_backward import BF16_REL_MAX, BF16_REL_MEAN, F32_REL_MAX, rel_errors, run_train
-    f, h, w = (2, 6, 50) if b2 == 600 else (1, 10, 10)
-    wl = I.Workload("one_block_grad", 1, 2, 64, f, h, w, 1, b2, 1, T, dtype)
+    f, h, w, H = ONE_BLOCK[b2]
+    wl = I.Workload("one_block_grad", 1, H, 64, f, h, w, 1, b2, 1, T, dtype)
     say(f"[case] gradients of one key block of {wl.N} keys, {dtype}, T={T}")
     x = I.make_inputs(wl, 5)
     dyx = I.make_cotangent(wl, 5)
-    _, dq, dk, dv = run_train(wl, x, dyx)
+    yg, dq, dk, dv = run_train(wl, x, dyx)
     worst = {}
     for hh in range(wl.H):
         q, k, v = (torch.from_numpy(x[n][0, hh]).to(torch.float64).requires_grad_() for n in "qkv")
         y = torch.nn.functional.scaled_dot_product_attention(q[None, None], k[None, None], v[None, None])[0, 0]
+        mx, mean = errors(yg[0, hh], y.detach().numpy())
+        if dtype == "bf16":
+            assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, ("y", hh, mx, mean)
+        else:
+            assert mx <= F32_MAX_ABS, ("y", hh, mx)
+        worst["y"] = (max(worst.get("y", (0.0, 0.0))[0], mx), 0.0)
         y.backward(torch.from_numpy(dyx["dy"][0, hh]).to(torch.float64))
         for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), (q.grad, k.grad, v.grad)):
             mx, mean = rel_errors(got[0, hh], ref.numpy())
@@ -249,4 +262,4 @@ def test_one_key_block_gradients_are_attention_gradients(dtype, b2, T):
             else:
                 assert mx <= F32_REL_MAX, (name, hh, mx)
     say(f"[ok] one key block gradients {dtype} N={wl.N} T={T}: " + ", ".join(
-        f"{n} rel-max {wv[0]:.2e}" for n, wv in worst.items()))
+        f"{n} {'max-abs' if n == 'y' else 'rel-max'} {wv[0]:.2e}" for n, wv in worst.items()))
