@@ -128,6 +128,17 @@ def _dims(q, f, h, w, b1, b2, tiles, iters):
     return [B, H, f, h, w, d, b1, b2, tiles, iters]
 
 
+def _ptr(t):
+    """Device address of a tensor on the current GPU: the kernels run on the
+    current device, so a tensor elsewhere is refused before any launch."""
+    import torch
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def _tensors(q, k, v, out, dtype):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
@@ -139,7 +150,7 @@ def _tensors(q, k, v, out, dtype):
             raise ValueError(f"{name} must be contiguous")
         if t.shape != q.shape:
             raise ValueError(f"{name} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
-    return [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
+    return [_ptr(t) for t in (q, k, v, out)]
 
 
 def _stream(stream):
@@ -176,7 +187,7 @@ def monarch_attn_debug_factors_f32(q, k, v, f, h, w, b1, b2, tiles=1, iters=1, s
     B, H = dims[0], dims[1]
     L = torch.empty((B, H, b2, b1, b1), dtype=torch.float32, device=q.device)
     R = torch.empty((B, H, tiles, b1, b2, b2), dtype=torch.float32, device=q.device)
-    ptrs = _tensors(q, k, v, q, torch.float32)[:3] + [ctypes.c_void_p(L.data_ptr()), ctypes.c_void_p(R.data_ptr())]
+    ptrs = _tensors(q, k, v, q, torch.float32)[:3] + [_ptr(L), _ptr(R)]
     _check(lib().monarch_attn_debug_factors_f32(*ptrs, *dims, _stream(stream)), "monarch_attn_debug_factors_f32")
     return L, R
 
@@ -194,7 +205,7 @@ def monarch_attn_fwd_ws(q, k, v, out, f, h, w, b1, b2, tiles, iters, workspace, 
         raise ValueError("workspace must be a uint8 GPU tensor")
     nbytes = workspace.numel()
     _check(lib().monarch_attn_fwd_ws(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, iters), dtype,
-                                     ctypes.c_void_p(workspace.data_ptr()), nbytes, _stream(stream)),
+                                     _ptr(workspace), nbytes, _stream(stream)),
            "monarch_attn_fwd_ws")
     return out
 
@@ -231,8 +242,8 @@ def monarch_attn_fwd_adaptive(q, k, v, out, f, h, w, b1, b2, tiles, max_iters, t
         nb = monarch_attn_adaptive_workspace_bytes(B, H, f, h, w, d, b1, b2, tiles, max_iters, dt)
         workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
     _check(lib().monarch_attn_fwd_adaptive_ws(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, max_iters), float(tol), dt,
-                                              ctypes.c_void_p(iters_used.data_ptr()),
-                                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                              _ptr(iters_used),
+                                              _ptr(workspace), workspace.numel(),
                                               _stream(stream)), "monarch_attn_fwd_adaptive_ws")
     return out, iters_used
 
@@ -261,14 +272,14 @@ def monarch_attn_fwd_kv(q, k, v, out, fq, f, h, w, b1, b2, tiles=1, iters=1, wor
     import torch
     _kv_tensors(q, fq, f, h, w, [("q", q), ("out", out)], [("k", k), ("v", v)])
     B, H, _, d = q.shape
-    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
+    ptrs = [_ptr(t) for t in (q, k, v, out)]
     dims = [B, H, fq, f, h, w, d, b1, b2, tiles, iters]
     if workspace is None:
         _check(lib().monarch_attn_fwd_kv(*ptrs, *dims, _dtype_code(q), _stream(stream)), "monarch_attn_fwd_kv")
     else:
         if not workspace.is_cuda or workspace.dtype != torch.uint8:
             raise ValueError("workspace must be a uint8 GPU tensor")
-        _check(lib().monarch_attn_fwd_kv_ws(*ptrs, *dims, _dtype_code(q), ctypes.c_void_p(workspace.data_ptr()),
+        _check(lib().monarch_attn_fwd_kv_ws(*ptrs, *dims, _dtype_code(q), _ptr(workspace),
                                             workspace.numel(), _stream(stream)), "monarch_attn_fwd_kv_ws")
     return out
 
@@ -290,7 +301,7 @@ def _state(state):
     import torch
     if not state.is_cuda or state.dtype != torch.uint8:
         raise ValueError("state must be a uint8 GPU tensor")
-    return ctypes.c_void_p(state.data_ptr()), state.numel()
+    return _ptr(state), state.numel()
 
 
 def monarch_attn_fwd_train(q, k, v, out, f, h, w, b1, b2, tiles, iters, state, stream=None):
@@ -334,10 +345,10 @@ def monarch_attn_fwd_adaptive_kv(q, k, v, out, fq, f, h, w, b1, b2, tiles, max_i
     if workspace is None:
         nb = monarch_attn_adaptive_kv_workspace_bytes(B, H, fq, f, h, w, d, b1, b2, tiles, max_iters, dt)
         workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
-    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
+    ptrs = [_ptr(t) for t in (q, k, v, out)]
     _check(lib().monarch_attn_fwd_adaptive_kv_ws(*ptrs, B, H, fq, f, h, w, d, b1, b2, tiles, max_iters, float(tol),
-                                                 dt, ctypes.c_void_p(iters_used.data_ptr()),
-                                                 ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                                 dt, _ptr(iters_used),
+                                                 _ptr(workspace), workspace.numel(),
                                                  _stream(stream)), "monarch_attn_fwd_adaptive_kv_ws")
     return out, iters_used
 
@@ -351,7 +362,7 @@ def monarch_attn_fwd_train_kv(q, k, v, out, fq, f, h, w, b1, b2, tiles, iters, s
     _kv_tensors(q, fq, f, h, w, [("q", q), ("out", out)], [("k", k), ("v", v)])
     sp, sn = _state(state)
     B, H, _, d = q.shape
-    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out)]
+    ptrs = [_ptr(t) for t in (q, k, v, out)]
     _check(lib().monarch_attn_fwd_train_kv(*ptrs, B, H, fq, f, h, w, d, b1, b2, tiles, iters, _dtype_code(q),
                                            sp, sn, _stream(stream)), "monarch_attn_fwd_train_kv")
     return out
@@ -363,7 +374,7 @@ def monarch_attn_bwd_kv(q, k, v, out, dout, dq, dk, dv, fq, f, h, w, b1, b2, til
                 [("k", k), ("v", v), ("dk", dk), ("dv", dv)])
     sp, sn = _state(state)
     B, H, _, d = q.shape
-    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, out, dout, dq, dk, dv)]
+    ptrs = [_ptr(t) for t in (q, k, v, out, dout, dq, dk, dv)]
     _check(lib().monarch_attn_bwd_kv(*ptrs, B, H, fq, f, h, w, d, b1, b2, tiles, iters, _dtype_code(q),
                                      sp, sn, _stream(stream)), "monarch_attn_bwd_kv")
     return dq, dk, dv

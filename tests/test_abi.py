@@ -289,3 +289,23 @@ def test_factors_bad_arguments_rejected_before_any_gpu_call(kw, status):
     if "L" in kw and kw["L"] == _GAP:
         kw = dict(kw, q=2 * _GAP, k=3 * _GAP, v=4 * _GAP)
     assert _factors(**kw) == status
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """The Python binding passes device addresses only: host tensors are
+    refused with ValueError before the library is called."""
+    import torch
+    q = torch.zeros(1, 1, 12, 16, dtype=torch.bfloat16)
+    ws = torch.zeros(64, dtype=torch.uint8)
+    calls = [
+        lambda: M.monarch_attn_fwd(q, q, q, q.clone(), 1, 3, 4, 3, 4),
+        lambda: M.monarch_attn_fwd_f32(q.float(), q.float(), q.float(), q.float().clone(), 1, 3, 4, 3, 4),
+        lambda: M.monarch_attn_fwd_ws(q, q, q, q.clone(), 1, 3, 4, 3, 4, 1, 1, ws),
+        lambda: M.monarch_attn_fwd_kv(q, q, q, q.clone(), 1, 1, 3, 4, 3, 4),
+        lambda: M.monarch_attn_fwd_adaptive(q, q, q, q.clone(), 1, 3, 4, 3, 4, 1, 3, 1e-3),
+        lambda: M.monarch_attn_fwd_train(q, q, q, q.clone(), 1, 3, 4, 3, 4, 1, 1, ws),
+        lambda: M.monarch_attn_bwd(q, q, q, q, q, q.clone(), q.clone(), q.clone(), 1, 3, 4, 3, 4, 1, 1, ws),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError):
+            call()
