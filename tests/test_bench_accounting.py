@@ -37,3 +37,16 @@ def test_latent720p_one_iteration_is_2690_gflop():
     tot = bench.step_work(wl, "fwd", {"k_kbar": 1, "k_lse": 1, "k_aggregate": 1, "k_rstep": 1, "k_apply": 1})
     flops = sum(v[0] for v in tot.values())
     assert abs(flops - 2.690e12) <= 0.001 * 2.690e12
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """bench.py measures one GPU; --gpus above 1 exits with status 2 and says
+    so, before any GPU work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2", "--steps", "1"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
