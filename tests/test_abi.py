@@ -309,3 +309,16 @@ def test_binding_refuses_host_tensors_before_any_call():
     for call in calls:
         with pytest.raises(ValueError):
             call()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: when the library is absent and the build produces none,
+    the first call into the binding raises instead of computing anything."""
+    import structured_attention_video_monarch_amd.build as B
+    monkeypatch.setattr(M, "LIB_PATH", str(tmp_path / "libmonarch_attn.so"))
+    monkeypatch.setattr(M, "_lib", None)
+    monkeypatch.setattr(B, "build_library", lambda *a, **k: None)
+    with pytest.raises(OSError):
+        M.lib()
+    with pytest.raises(OSError):
+        M.monarch_attn_workspace_bytes(1, 1, 2, 4, 4, 16, 8, 4, 1, 1)
