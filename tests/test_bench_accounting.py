@@ -50,3 +50,29 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_counters_are_used_only_on_the_sources_they_were_taken_on(monkeypatch, tmp_path):
+    """A committed HBM-traffic figure is reported only while the kernel
+    sources hash to the value recorded with it; any change to a kernel
+    source changes the hash, and the figure is then dropped (null)."""
+    import json
+    import os
+    rec = {"kernel": "k_demo", "workload": "demo", "hbm_bytes_per_launch": 12345, "kernel_source_hash": "abc"}
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "traffic_k_demo_demo.json").write_text(json.dumps(rec))
+    src = tmp_path / "k.h"
+    src.write_text("// kernel v1\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", ["k.h"])
+    h1 = bench.kernel_source_hash()
+    assert bench.read_traffic("k_demo", "demo") is None          # recorded on other sources
+    rec["kernel_source_hash"] = h1
+    (prof / "traffic_k_demo_demo.json").write_text(json.dumps(rec))
+    assert bench.read_traffic("k_demo", "demo") == 12345
+    src.write_text("// kernel v2\n")
+    assert bench.kernel_source_hash() != h1
+    assert bench.read_traffic("k_demo", "demo") is None
+    assert bench.read_traffic("k_other", "demo") is None          # never measured
+    assert os.path.exists(prof / "traffic_k_demo_demo.json")
