@@ -2,7 +2,8 @@
 
 Callers that launch many small layers (a chunk of three frames is launch
 bound: five kernels of 10-20 us each) can capture the workspace entry points,
-which allocate nothing and record no memset, in a graph and replay it.  Each
+which allocate nothing and record no memset, in a graph and replay it (the
+early-stopping entry point included).  Each
 case captures one call, then replays it three times with eager work of the
 program and a synchronisation between the replays, and checks every replay
 bit for bit against the eager result of the same call; the eager result is
@@ -84,3 +85,56 @@ def test_graph_replays_match_eager(name, over):
     mx, mean = errors(y[0, 0], ref)
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
     say(f"[ok] graph {name}: 3 replays equal to the eager call; eager vs oracle max-abs {mx:.3e}")
+
+
+def test_graph_replays_match_eager_early_stopping():
+    """The early-stopping entry point: the iteration counts are set by a fill
+    kernel and stopped heads are skipped on the device, with no memset and no
+    synchronisation, so it captures too. Every replay's output and counts
+    equal the eager call's; the eager call matches the oracle's early stop."""
+    import structured_attention_video_monarch_amd as M
+    wl = I.get_workload("clip480p").with_(H=2, iters=5)
+    tol = 1e-3
+    say(f"[case] graph early stopping clip480p H={wl.H} max_iters={wl.iters} tol={tol}")
+    x = I.make_inputs(wl, 5)
+    q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
+    nb = M.monarch_attn_adaptive_workspace_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles,
+                                                 wl.iters)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def call(q_, k_, v_, out_, used_):
+        M.monarch_attn_fwd_adaptive(q_, k_, v_, out_, wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters, tol,
+                                    iters_used=used_, workspace=ws)
+
+    eager, used_e = torch.empty_like(q), torch.empty((wl.B, wl.H), dtype=torch.int32, device="cuda")
+    call(q, k, v, eager, used_e)
+    torch.cuda.synchronize()
+    out, used = torch.empty_like(q), torch.empty_like(used_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(q, k, v, out, used)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(q, k, v, out, used)
+    torch.cuda.synchronize()
+    other, used_o = torch.empty_like(q), torch.empty_like(used_e)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        used.fill_(-1)
+        call(k, q, v, other, used_o)  # eager work in between, other inputs
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}: output differs from the eager call"
+        assert torch.equal(used, used_e), f"replay {rep}: iteration counts differ"
+    counts = used_e.cpu().numpy()
+    for h in range(wl.H):
+        ref, used_ref, _ = oracle.monarch_head_adaptive(x["q"][0, h], x["k"][0, h], x["v"][0, h], wl.b1, wl.b2,
+                                                        wl.tiles, wl.iters, tol)
+        assert int(counts[0, h]) == used_ref, (h, int(counts[0, h]), used_ref)
+        mx, mean = errors(to_host(eager)[0, h], ref)
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
+    say(f"[ok] graph early stopping: 3 replays equal to the eager call; iterations {counts.tolist()}")
