@@ -138,3 +138,59 @@ def test_graph_replays_match_eager_early_stopping():
         mx, mean = errors(to_host(eager)[0, h], ref)
         assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
     say(f"[ok] graph early stopping: 3 replays equal to the eager call; iterations {counts.tolist()}")
+
+
+@pytest.mark.parametrize("name,over", [("clip480p", {"H": 2, "iters": 2}), ("clip480p_frames", {"H": 1})],
+                         ids=["clip480p_T2", "clip480p_frames"])
+def test_graph_replays_training_forward(name, over):
+    """The training forward writes only the caller's output and state, so it
+    captures too. Every replay's output and state equal the eager call's bit
+    for bit, and the backward run from a replayed state gives the eager
+    gradients bit for bit (the backward is deterministic)."""
+    import structured_attention_video_monarch_amd as M
+    wl = I.get_workload(name).with_(**over)
+    say(f"[case] graph training forward {name} H={wl.H} T={wl.iters} blocks=({wl.b1},{wl.b2})")
+    x = I.make_inputs(wl, 6)
+    q, k, v = (to_device(x, n, wl.dtype) for n in "qkv")
+    dy = to_device(I.make_cotangent(wl, 6), "dy", wl.dtype)
+    args = (wl.f, wl.h, wl.w, wl.b1, wl.b2, wl.tiles, wl.iters)
+    nb = M.monarch_attn_train_state_bytes(wl.B, wl.H, wl.f, wl.h, wl.w, wl.d, wl.b1, wl.b2, wl.tiles, wl.iters,
+                                          M.MONARCH_BF16)
+
+    def grads(out_, state_):
+        g = [torch.empty_like(q) for _ in range(3)]
+        M.monarch_attn_bwd(q, k, v, out_, dy, *g, *args, state_)
+        torch.cuda.synchronize()
+        return g
+
+    # states start filled with one byte value, so that alignment padding the
+    # forward never writes compares equal and every written byte is compared
+    eager, st_e = torch.empty_like(q), torch.full((nb,), 255, dtype=torch.uint8, device="cuda")
+    M.monarch_attn_fwd_train(q, k, v, eager, *args, st_e)
+    torch.cuda.synchronize()
+    g_eager = grads(eager, st_e)
+    out, st = torch.empty_like(q), torch.full_like(st_e, 255)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        M.monarch_attn_fwd_train(q, k, v, out, *args, st)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        M.monarch_attn_fwd_train(q, k, v, out, *args, st)
+    torch.cuda.synchronize()
+    other, st_o = torch.empty_like(q), torch.empty_like(st_e)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        st.fill_(255)
+        M.monarch_attn_fwd_train(k, q, v, other, *args, st_o)  # eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}: output differs"
+        assert torch.equal(st, st_e), f"replay {rep}: training state differs"
+    for name_g, a, b in zip(("dq", "dk", "dv"), grads(out, st), g_eager):
+        assert torch.equal(a, b), f"{name_g} from the replayed state differs"
+    say(f"[ok] graph training forward {name}: 3 replays equal to the eager call (output and "
+        f"{nb} state bytes); gradients from the replayed state equal")
