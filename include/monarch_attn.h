@@ -35,6 +35,15 @@
  *   NULL = the null stream) and the call returns without synchronising: the
  *   caller keeps the buffers alive until the stream has run the work.
  *
+ * Graph capture: the entry points that take a caller's workspace or state
+ *   (monarch_attn_fwd_ws, monarch_attn_fwd_kv_ws, monarch_attn_fwd_adaptive_ws
+ *   and its _kv form, monarch_attn_fwd_train and its _kv form) allocate
+ *   nothing, record no memset and never synchronise, so a caller may capture
+ *   them in a HIP graph and replay it (with per-kernel timing off: timing
+ *   records HIP events around each launch).  The entry points without a workspace
+ *   argument, and the backward, allocate their scratch memory stream-ordered
+ *   (hipMallocAsync / hipFreeAsync on `stream`).
+ *
  * Errors: every entry point returns a monarch_status.  Arguments are checked
  *   before any GPU call; on MONARCH_EINVAL / MONARCH_EUNSUPPORTED nothing is
  *   launched and `out` is untouched.  MONARCH_EHIP reports a HIP runtime
