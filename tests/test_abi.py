@@ -322,3 +322,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         M.lib()
     with pytest.raises(OSError):
         M.monarch_attn_workspace_bytes(1, 1, 2, 4, 4, 16, 8, 4, 1, 1)
+
+
+def test_binding_refuses_a_tensor_on_another_device(monkeypatch):
+    """The kernels run on the current device: a GPU tensor elsewhere is
+    refused before any call (a stand-in tensor and a patched current device,
+    so no GPU is needed)."""
+    import torch
+
+    class OnDevice1:
+        is_cuda = True
+        device = torch.device("cuda", 1)
+
+        def data_ptr(self):
+            return 4096
+
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    with pytest.raises(ValueError, match="current device"):
+        M._ptr(OnDevice1())
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 1)
+    assert M._ptr(OnDevice1()).value == 4096
