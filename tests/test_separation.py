@@ -65,3 +65,9 @@ def test_bench_uses_the_oracle_only_for_the_cpu_baseline():
     uses = [(m, f) for m, f in _imports(os.path.join(ROOT, "bench.py")) if m.split(".")[0] == "oracle"]
     assert uses
     assert all(f is not None and f.startswith("cpu_baseline") for _, f in uses), uses
+
+
+def test_entry_point_uses_the_oracle_only_in_smoke():
+    uses = [(m, f) for m, f in _imports(os.path.join(ROOT, "__graft_entry__.py")) if m.split(".")[0] == "oracle"]
+    assert uses
+    assert all(f == "smoke" for _, f in uses), uses
