@@ -48,91 +48,119 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_work(wl, it_last=True):
+def algorithmic_work(wl):
     """Per launch: (flops, bytes) each kernel must do by the method's definition.
 
-    Per (batch, head), e = element bytes, N = b1*b2 (for a chunk against
-    cached keys the query terms below use Nq, the chunk's tokens):
-      k_kbar       0 flops;   bytes  N*d*e (read K) + b1*d*e (write means)
-      k_lse        2*N*b1*d   (L logits);          bytes N*d*e + 4N
-      k_aggregate  2*N*b1*d   (L^T q per tile);    bytes N*d*e + 4N + t*N*d*e
-      k_rstep      4*t*N*b2*d (R logits + R V);    bytes t*N*d*e (Qh) + 2*N*d*e (K,V) + t*N*d*e (U)
-      k_apply      2*N*b1*d   (L U);               bytes N*d*e + 4N + t*N*d*e + N*d*e
-    Logit recomputation in k_aggregate/k_apply is not counted (an
-    implementation choice, not part of the method).
+    flops: the method's own products, per (batch, head), e = element bytes,
+    N = b1*b2 key tokens, Nq query tokens (N for the square layer):
+      k_kbar       0
+      k_lse        2*Nq*b1*d    (L logits)
+      k_aggregate  2*Nq*b1*d    (L^T q per tile)
+      k_rstep      4*t*N*b2*d   (R logits + R V)
+      k_apply      2*Nq*b1*d    (L U)
+    Logit recomputation in k_aggregate/k_apply and padding are not counted.
+    bytes: only the layer's own tensors (q, k, v, out; in training also dy,
+    dq, dk, dv) that the kernel must read or write, each once:
+      k_kbar K; k_lse Q; k_aggregate Q; k_rstep K, V; k_apply Q, O.
+    The implementation's intermediates (block-mean keys, log-sum-exps,
+    aggregated queries Qh, U = R V, next keys and entropies, and the
+    backward's) are not algorithmic bytes; ``intermediate_bytes`` models the
+    forward's, and the rocprofv3 counters measure all of them.
     """
     e = 2 if wl.dtype == "bf16" else 4
     BH, N, d, b1, b2, t = wl.B * wl.H, wl.N, wl.d, wl.b1, wl.b2, wl.tiles
     Nq = wl.Nq   # query tokens (== N for the square layer; a chunk against cached keys has fewer)
     nd, nqd = N * d * e, Nq * d * e
     return {
-        "k_kbar": (0.0, BH * (nd + b1 * d * e)),
-        "k_lse": (BH * 2.0 * Nq * b1 * d, BH * (nqd + 4 * Nq)),
-        "k_aggregate": (BH * 2.0 * Nq * b1 * d, BH * (nqd + 4 * Nq + t * nd)),
-        "k_rstep": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 2 * nd)),
-        "k_apply": (BH * 2.0 * Nq * b1 * d, BH * (2 * nqd + 4 * Nq + t * nd)),
+        "k_kbar": (0.0, BH * nd),
+        "k_lse": (BH * 2.0 * Nq * b1 * d, BH * nqd),
+        "k_aggregate": (BH * 2.0 * Nq * b1 * d, BH * nqd),
+        "k_rstep": (BH * 4.0 * t * N * b2 * d, BH * 2 * nd),
+        "k_apply": (BH * 2.0 * Nq * b1 * d, BH * 2 * nqd),
         # backward (the one-iteration form), chain-rule products only (no logit
         # recomputation, no stored s*dl), per (batch, head); the row side
         # has the Nq query tokens, the key side t*N rows (tile, key block, a2):
-        #   kb_du       dU = L^T dy                      2 Nq b1 d;  q, dy, lse in, dU out
-        #   kb_rside_a  dR = dU v^T, dQh = dz k          4 t N b2 d; Qh, dU, K, V, beta in, G out
-        #   kb_dq       <dy,U>, <q,G>, L G, dl Kbar      8 Nq b1 d;  q, dy, y, U, G, lse, e in, dq out
-        #   kb_dkbar    dKbar = dl^T q                   2 Nq b1 d;  q in
-        #   kb_rside_b  dv = R^T dU, dk_R = dz^T Qh      4 t N b2 d; Qh, dU, K, V in, dk, dv out
-        "kb_du": (BH * 2.0 * Nq * b1 * d, BH * (2 * nqd + 4 * Nq + t * nd)),
-        "kb_rside_a": (BH * 4.0 * t * N * b2 * d, BH * (3 * t * nd + 2 * nd + 16 * t * N)),
-        "kb_dq": (BH * 8.0 * Nq * b1 * d, BH * (4 * nqd + 2 * t * nd + 8 * Nq + 4 * t * N)),
+        #   kb_du       dU = L^T dy                      2 Nq b1 d;  q, dy
+        #   kb_rside_a  dR = dU v^T, dQh = dz k          4 t N b2 d; k, v
+        #   kb_dq       <dy,U>, <q,G>, L G, dl Kbar      8 Nq b1 d;  q, dy, y in, dq out
+        #   kb_dkbar    dKbar = dl^T q                   2 Nq b1 d;  q
+        #   kb_rside_b  dv = R^T dU, dk_R = dz^T Qh      4 t N b2 d; k, v in, dk, dv out
+        "kb_du": (BH * 2.0 * Nq * b1 * d, BH * 2 * nqd),
+        "kb_rside_a": (BH * 4.0 * t * N * b2 * d, BH * 2 * nd),
+        "kb_dq": (BH * 8.0 * Nq * b1 * d, BH * 4 * nqd),
         "kb_dkbar": (BH * 2.0 * Nq * b1 * d, BH * nqd),
-        "kb_dkbar_reduce": (0.0, BH * b1 * d * 4.0),
-        "kb_rside_b": (BH * 4.0 * t * N * b2 * d, BH * (2 * t * nd + 4 * nd + 8 * t * N)),
-        # early stopping: the objective per head reads the log-sum-exps once
-        "k_objective": (0.0, BH * 4.0 * Nq),
+        "kb_dkbar_reduce": (0.0, 0.0),
+        "kb_rside_b": (BH * 4.0 * t * N * b2 * d, BH * 4 * nd),
+        # early stopping: the objective per head reads only log-sum-exps
+        "k_objective": (0.0, 0.0),
     }
+
+
+def intermediate_bytes(wl):
+    """Per launch of each forward kernel (one-iteration form): the bytes of
+    the implementation's intermediates it reads or writes, per (batch, head),
+    e = element bytes:
+      k_kbar       b1*d*e (block means out)
+      k_lse        b1*d*e (block means) + 4*Nq (log-sum-exps out)
+      k_aggregate  b1*d*e + 4*Nq + t*N*d*e (Qh out)
+      k_rstep      t*N*d*e (Qh in) + t*N*d*e (U out)
+      k_apply      b1*d*e + 4*Nq + t*N*d*e (U in)
+    """
+    e = 2 if wl.dtype == "bf16" else 4
+    BH, N, Nq, d, b1, t = wl.B * wl.H, wl.N, wl.Nq, wl.d, wl.b1, wl.tiles
+    kb, ls, tnd = b1 * d * e, 4 * Nq, t * N * d * e
+    return {"k_kbar": BH * kb, "k_lse": BH * (kb + ls), "k_aggregate": BH * (kb + ls + tnd),
+            "k_rstep": BH * 2 * tnd, "k_apply": BH * (kb + ls + tnd)}
 
 
 def step_work(wl, mode, launches):
     """Per step: (flops, bytes) of each kernel, summed over its launches.
 
     The forward kernels and the one-iteration backward do the same work at
-    every launch (algorithmic_work x launches).  The backward through T >= 2
-    iterations runs its kernels in two forms, per (batch, head):
-      last iteration (once):  kb_du, kb_rside_a, kb_dq, kb_rside_b as above,
-        except that the L-step's keys are the aggregated keys Kt and
-        entropies H (t*N*d*e + 4tN more read by kb_du and kb_dq);
+    every launch (algorithmic_work x launches), except that with T >= 2 only
+    the last R-step reads V (the earlier ones form R K).  The backward through
+    T >= 2 iterations runs its kernels in two forms, per (batch, head):
+      last iteration (once):  kb_du, kb_rside_a, kb_dq, kb_rside_b as above;
       each earlier iteration (T-1 times), with cotangents dKt, dH instead of dU:
-        kb_rside_a  dR = dKt k^T, dQh = dz k      4 t N b2 d; Qh, dKt, K, beta, dH in, G out
-        kb_dq       <q,G>, L G, dl Kt              6 Nq b1 d; q, Kt, H (Kbar at i = 1), G, lse, e in
-        kb_rside_b  dk_R = dz^T Qh + R^T dKt       4 t N b2 d; Qh, dKt, K, dH in, dk out (once)
-        kb_dktil    dKt, dH of the R-step before   2 Nq b1 d; q in, dKt, dH out   (T-1 launches)
-      kb_dkbar and its reduction once, at the first iteration; dq and dk are
-      written once.
+        kb_rside_a  dR = dKt k^T, dQh = dz k      4 t N b2 d; k
+        kb_dq       <q,G>, L G, dl Kt              6 Nq b1 d; q
+        kb_rside_b  dk_R = dz^T Qh + R^T dKt       4 t N b2 d; k
+        kb_dktil    dKt, dH of the R-step before   2 Nq b1 d; q   (T-1 launches)
+      kb_dkbar and its reduction once, at the first iteration; dq, dk and dv
+      are written once.
     """
     per = algorithmic_work(wl)
     tot = {kn: (per[kn][0] * n, per[kn][1] * n) for kn, n in launches.items() if kn in per}
     T = wl.iters
-    if mode != "train" or T < 2:
+    if T < 2:
         return tot
     e = 2 if wl.dtype == "bf16" else 4
     BH, N, Nq, d, b1, b2, t = wl.B * wl.H, wl.N, wl.Nq, wl.d, wl.b1, wl.b2, wl.tiles
     nd, nqd = N * d * e, Nq * d * e
     m = T - 1
-    extra_keys = t * nd + 4 * t * N
-    tot["kb_du"] = (per["kb_du"][0], per["kb_du"][1] + BH * extra_keys)
-    tot["kb_rside_a"] = (BH * 4.0 * t * N * b2 * d * T,
-                         per["kb_rside_a"][1] + m * BH * (3 * t * nd + nd + 20 * t * N))
-    # dq and dk are written once (counted with the last form's launch); the
-    # first L-step's keys are the block means (b1*d, not counted)
-    tot["kb_dq"] = (per["kb_dq"][0] + m * BH * 6.0 * Nq * b1 * d,
-                    per["kb_dq"][1] + BH * extra_keys + m * BH * (nqd + t * nd + 4 * Nq + 4 * t * N)
-                    + (m - 1) * BH * extra_keys)
-    tot["kb_rside_b"] = (BH * 4.0 * t * N * b2 * d * T, per["kb_rside_b"][1] + m * BH * (2 * t * nd + nd + 12 * t * N))
-    tot["kb_dktil"] = (m * BH * 2.0 * Nq * b1 * d, m * BH * (nqd + t * nd + 4 * t * N))
+    if "k_rstep" in tot:
+        n = launches["k_rstep"]
+        tot["k_rstep"] = (tot["k_rstep"][0], BH * (n * nd + nd))
+    if mode != "train":
+        return tot
+    tot["kb_rside_a"] = (BH * 4.0 * t * N * b2 * d * T, BH * (2 * nd + m * nd))
+    tot["kb_dq"] = (per["kb_dq"][0] + m * BH * 6.0 * Nq * b1 * d, BH * (4 * nqd + m * nqd))
+    tot["kb_rside_b"] = (BH * 4.0 * t * N * b2 * d * T, BH * (4 * nd + m * nd))
+    tot["kb_dktil"] = (m * BH * 2.0 * Nq * b1 * d, m * BH * nqd)
     return tot
 
 
 def roofline_entry(name, flops, nbytes, avg_s, dtype, traffic):
+    """Roofline of one kernel from its algorithmic flops and bytes (per
+    launch) and its average launch duration: MFMA-bound when its flops take
+    longer at peak than its bytes do, else HBM-bound.  ``traffic`` is the
+    measured HBM bytes per launch (or None); it is reported with its ratio
+    to the algorithmic bytes."""
     peak_f = (PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12
     peak_b = PEAK_HBM_GBS * 1e9
+    if flops <= 0 and nbytes <= 0:
+        return {"kernel": name, "bound": "none", "achieved": None, "peak": None, "unit": None,
+                "frac": None, "traffic": traffic}
     if flops / peak_f >= nbytes / peak_b:
         ach = flops / avg_s / 1e12
         return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2),
@@ -337,8 +365,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+    # the headline: K steps with no per-kernel events
+    M.monarch_attn_profile_enable(False)
     M.monarch_attn_profile_collect()
-    M.monarch_attn_profile_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     ev0.record(stream)
@@ -346,10 +375,22 @@ def main():
         step()
     ev1.record(stream)
     torch.cuda.synchronize(dev)
-    M.monarch_attn_profile_enable(False)
-    per_kernel = M.monarch_attn_profile_collect()
     ms_step = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    # the per-kernel breakdown: K more steps, HIP events around every launch
+    # on the launch stream
+    M.monarch_attn_profile_enable(True)
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev3.record(stream)
+    torch.cuda.synchronize(dev)
+    M.monarch_attn_profile_enable(False)
+    per_kernel = M.monarch_attn_profile_collect()
+    ms_step_events = ev2.elapsed_time(ev3) / args.steps
+    print(f"[bench] {args.steps} steps with per-kernel events, {ms_step_events:.4f} ms/step",
+          file=sys.stderr, flush=True)
 
     graph_rec = None
     if args.graph:
@@ -378,7 +419,7 @@ def main():
         torch.cuda.synchronize(dev)
         ms_graph = ev0.elapsed_time(ev1) / args.steps
         print(f"[bench] {args.steps} graph replays, {ms_graph:.4f} ms/step", file=sys.stderr, flush=True)
-        graph_rec = {"eager_ms_per_step_with_kernel_events": round(ms_step, 5),
+        graph_rec = {"eager_ms_per_step": round(ms_step, 5),
                      "replay_ms_per_step": round(ms_graph, 5)}
         ms_step = ms_graph
 
@@ -400,6 +441,12 @@ def main():
                           # launches read the aggregated keys as well, so they have no figure
                           read_traffic(dom, wl.name) if wl.iters == 1 else None)
     roof["launches_per_step"] = launches
+    roof["alg_bytes"] = by
+    roof["alg_flops"] = fl
+    inter = intermediate_bytes(wl).get(dom) if args.mode == "fwd" and wl.iters == 1 else None
+    roof["intermediate_bytes"] = inter
+    roof["traffic_over_alg_bytes"] = (round(roof["traffic"] / by, 3)
+                                      if roof["traffic"] is not None and by > 0 else None)
     if iters_used is not None:
         roof["note"] = ("early stopping: launches after every head has stopped return at once and are "
                         "counted in the per-launch average")
@@ -431,6 +478,7 @@ def main():
                         "iters_used_mean": round(float(iters_used.float().mean().item()), 3),
                         "iters_used_max": int(iters_used.max().item())}),
         "layer_calls_per_s": round(1e3 / ms_step, 2),
+        "ms_per_step_with_kernel_events": round(ms_step_events, 5),
         "path_alg_tflops": round(total_flops / (ms_step / 1e3) / 1e12, 2),
         "path_frac_of_mfma_peak": round(total_flops / (ms_step / 1e3) / 1e12 /
                                         (PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS), 4),

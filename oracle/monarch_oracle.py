@@ -41,7 +41,12 @@ Readings fixed here (the pages leave them open):
             Ktil[g,c1,a2] = sum_c2 R[g,c1,a2,c2] k_(c1,c2);
     R-step: logits s*<Qhat[g,c1,a2], k_(c1,c2)>,
             Qhat[g,c1,a2] = sum_(a1 in g) L[a2][a1,c1] q_(a1,a2) / beta,
-            beta = sum_(a1 in g) L[a2][a1,c1]   (Qhat := 0 when beta == 0).
+            beta = sum_(a1 in g) L[a2][a1,c1].
+  Where a whole tile column of L is exactly zero (beta == 0, every weight
+  underflowed), Qhat := 0, so that R row is uniform.  In the last R-step that
+  row only meets zero weights of L and the output does not depend on it; with
+  more iterations it hands the next L-step the block mean of the keys and the
+  entropy log(b2), which do enter that tile's logits.
 * Start from uniform R (1/b2); one iteration = L-step then R-step; the apply
   uses the last L and R.  ``iters`` counts iterations.
 * Tiles split the a1 (frame*row) index into t contiguous ranges with bounds
@@ -68,9 +73,9 @@ import numpy as np
 
 __all__ = [
     "tile_bounds", "tile_of_rows", "softmax", "entropy", "uniform_R",
-    "l_step", "r_step", "apply_factors", "monarch_head", "monarch_head_adaptive", "monarch_attention",
+    "l_step", "r_step", "apply_factors", "monarch_head", "monarch_head_adaptive",
     "dense_monarch_matrix", "explicit_monarch_matrix", "permutation_matrix",
-    "softmax_attention_head", "objective", "row_kl",
+    "objective", "row_kl",
 ]
 
 
@@ -252,17 +257,6 @@ def monarch_head_adaptive(q, k, v, b1: int, b2: int, tiles: int, max_iters: int,
     return out, it, F
 
 
-def monarch_attention(q, k, v, b1: int, b2: int, tiles: int = 1, iters: int = 1):
-    """q [B, H, Nq, d], k, v [B, H, N, d] -> y [B, H, Nq, d] float64, head by head."""
-    q = np.asarray(q)
-    B, H, N, d = q.shape
-    y = np.empty((B, H, N, d))
-    for b in range(B):
-        for h in range(H):
-            y[b, h] = monarch_head(q[b, h], k[b, h], v[b, h], b1, b2, tiles, iters)
-    return y
-
-
 # ----------------------------------------------- dense forms and objective --
 
 def dense_monarch_matrix(L: np.ndarray, R: np.ndarray, bounds) -> np.ndarray:
@@ -306,15 +300,6 @@ def explicit_monarch_matrix(L: np.ndarray, R0: np.ndarray) -> np.ndarray:
     for c1 in range(b1):
         Rbd[c1 * b2:(c1 + 1) * b2, c1 * b2:(c1 + 1) * b2] = R0[c1]
     return P.T @ Lbd @ P @ Rbd
-
-
-def softmax_attention_head(q, k, v) -> np.ndarray:
-    """Textbook dense attention softmax(Q K^T / sqrt(d)) V in float64."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    s = 1.0 / math.sqrt(q.shape[-1])
-    return softmax(s * (q @ k.T), axis=-1) @ v
 
 
 def objective(M: np.ndarray, q, k) -> float:

@@ -199,7 +199,7 @@ def monarch_attn_workspace_bytes(B, H, f, h, w, d, b1, b2, tiles, iters, dtype=M
 def monarch_attn_fwd_ws(q, k, v, out, f, h, w, b1, b2, tiles, iters, workspace, stream=None):
     """Either dtype, with a caller-provided workspace (a uint8 GPU tensor)."""
     import torch
-    dtype = MONARCH_BF16 if q.dtype == torch.bfloat16 else MONARCH_F32
+    dtype = _dtype_code(q)
     ptrs = _tensors(q, k, v, out, q.dtype)
     if not workspace.is_cuda or workspace.dtype != torch.uint8:
         raise ValueError("workspace must be a uint8 GPU tensor")
@@ -316,6 +316,8 @@ def monarch_attn_fwd_train(q, k, v, out, f, h, w, b1, b2, tiles, iters, state, s
 
 def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, f, h, w, b1, b2, tiles, iters, state, stream=None):
     """dq, dk, dv <- gradients of sum(dout * out) (state from monarch_attn_fwd_train)."""
+    if dout.shape != q.shape:
+        raise ValueError(f"dout shape {tuple(dout.shape)} != q shape {tuple(q.shape)}")
     ptrs = _tensors(q, k, v, out, q.dtype) + _tensors(dout, dq, dk, dv, q.dtype)
     sp, sn = _state(state)
     dims = _dims(q, f, h, w, b1, b2, tiles, iters)

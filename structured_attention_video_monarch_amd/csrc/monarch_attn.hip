@@ -222,19 +222,31 @@ const char* const kKernelNames[MONARCH_NUM_KERNELS] = {
 inline void clear_stale_error() { (void)hipGetLastError(); }
 
 // Launch wrapper: records events around the launch when profiling is on.
+// The profiler's state (switch, event pool, pending records) is shared by
+// every thread that launches through the library, so it is only touched with
+// its lock held; the launch itself runs outside the lock.
 template <typename F>
 hipError_t timed(int id, hipStream_t st, F&& launch) {
-  clear_stale_error();
   hipEvent_t a = nullptr, b = nullptr;
-  if (g_prof.on) {
-    a = g_prof.get();
-    b = g_prof.get();
-    if (a && b) (void)hipEventRecord(a, st);
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.on) {
+      a = g_prof.get();
+      b = g_prof.get();
+      if (!a || !b) {  // no event pair: this launch goes untimed
+        if (a) g_prof.pool.push_back(a);
+        if (b) g_prof.pool.push_back(b);
+        a = b = nullptr;
+      }
+    }
   }
+  if (a) (void)hipEventRecord(a, st);
+  clear_stale_error();
   launch();
   hipError_t err = hipGetLastError();
-  if (g_prof.on && a && b) {
+  if (a) {
     (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof.mu);
     g_prof.pending.push_back({id, a, b});
   }
   return err;

@@ -146,6 +146,48 @@ def check_one_row_tiles(orc):
     assert np.max(np.abs(y1 - expect)) <= TOL
 
 
+def _sdpa_masked(q, k, v, keep):
+    """torch's dense attention in float64 over the keys where ``keep``."""
+    import torch
+    import torch.nn.functional as F
+    mask = torch.where(torch.from_numpy(np.asarray(keep)), 0.0, -math.inf).to(torch.float64)
+    tq, tk, tv = (torch.from_numpy(np.asarray(x, dtype=np.float64))[None, None] for x in (q, k, v))
+    return F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask[None, :])[0, 0].numpy()
+
+
+def check_beta_zero_branch(orc):
+    """A key block whose weight underflows to exactly 0 in every tile column
+    (beta = 0, reading D6: that R row is uniform, i.e. Qhat := 0).
+
+    The block mean of block c* lies about 890 nats below every other block
+    for every query, so the first L-step gives it weight 0 exactly; its key 0
+    is every query's best single match.  Under the reading the uniform R row
+    hands the next L-step the block mean again (plus log b2), so the block
+    keeps weight 0 and can be deleted:
+      * one-row tiles, T = 2, 3: exact softmax attention over the keys outside
+        block c* (torch SDPA with a mask; t = b1 with T >= 2 is exact attention
+        over blocks that keep their weight);
+      * two tiles, T = 2: the same layer with block c* removed from the keys
+        (queries over 8 blocks, keys over 7).
+    Any other choice for Qhat (a tile mean of q, say) gives the block its
+    best key in the second L-step and a weight near 1."""
+    from structured_attention_video_monarch_amd.inputs import make_underflow_head
+    b1, b2, d, cstar = 8, 4, 16, 3
+    q, k, v = (x.astype(np.float64) for x in make_underflow_head(0, b1, b2, d, cstar))
+    keep = np.ones(b1 * b2, dtype=bool)
+    keep[cstar * b2:(cstar + 1) * b2] = False
+    # the branch is reached: the first L-step's weights on block c* are 0
+    _, (_, _, hist) = orc.monarch_head(q, k, v, b1, b2, b1, 2, return_factors=True)
+    assert np.all(hist[0][1][:, :, cstar] == 0.0)
+    ref = _sdpa_masked(q, k, v, keep)
+    for T in (2, 3):
+        y = orc.monarch_head(q, k, v, b1, b2, b1, T)
+        assert np.max(np.abs(y - ref)) <= TOL, T
+    y2 = orc.monarch_head(q, k, v, b1, b2, 2, 2)
+    y2_del = orc.monarch_head(q, k[keep], v[keep], b1 - 1, b2, 2, 2)
+    assert np.max(np.abs(y2 - y2_del)) <= 1e-12
+
+
 def check_zero_queries_uniform(orc):
     """O5: Q = 0 makes every logit equal, so M = 1/N and y_n = mean(V)."""
     b1, b2, d = 6, 4, 8
@@ -412,6 +454,7 @@ ALL_CHECKS = [
     check_degenerate_blocks_are_dense_attention,
     check_one_row_tiles,
     check_zero_queries_uniform,
+    check_beta_zero_branch,
     check_objective_ascent_and_identity,
     check_steps_are_exact_maximisers,
     check_block_rank_at_most_tiles,

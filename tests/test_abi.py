@@ -342,3 +342,67 @@ def test_binding_refuses_a_tensor_on_another_device(monkeypatch):
         M._ptr(OnDevice1())
     monkeypatch.setattr(torch.cuda, "current_device", lambda: 1)
     assert M._ptr(OnDevice1()).value == 4096
+
+
+class _StandIn:
+    """A stand-in for a contiguous GPU tensor (no GPU needed): the attributes
+    the binding reads before it calls the library."""
+
+    def __init__(self, shape, dtype):
+        import torch
+        self.shape = torch.Size(shape)
+        self.dtype = dtype
+        self.is_cuda = True
+        self.device = torch.device("cuda", 0)
+
+    def is_contiguous(self):
+        return True
+
+    def dim(self):
+        return len(self.shape)
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def data_ptr(self):
+        return 1 << 20
+
+
+class _NoCalls:
+    """A library stub: any entry point that is reached fails the test."""
+
+    def __getattr__(self, name):
+        def called(*args):
+            raise AssertionError(f"library entry point {name} was called")
+        return called
+
+
+def test_binding_refuses_other_dtypes_and_bad_gradient_shapes(monkeypatch):
+    """fp16 and fp64 tensors are refused with ValueError before the library
+    is called (the library has bf16 and fp32 kernels only), and so is a
+    gradient whose shape differs from q's: the dimensions passed down are
+    q's, so a smaller dout/dq/dk/dv would be read and written out of bounds."""
+    import torch
+    monkeypatch.setattr(M, "_lib", _NoCalls())
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    shp = (1, 1, 12, 16)
+    ws = _StandIn((4096,), torch.uint8)
+    for dt in (torch.float16, torch.float64):
+        q = _StandIn(shp, dt)
+        with pytest.raises(ValueError):
+            M.monarch_attn_fwd_ws(q, q, q, _StandIn(shp, dt), 1, 3, 4, 3, 4, 1, 1, ws)
+        with pytest.raises(ValueError):
+            M.monarch_attn_fwd_train(q, q, q, _StandIn(shp, dt), 1, 3, 4, 3, 4, 1, 1, ws)
+        with pytest.raises(ValueError):
+            M.monarch_attn_fwd_adaptive(q, q, q, _StandIn(shp, dt), 1, 3, 4, 3, 4, 1, 3, 1e-3,
+                                        iters_used=_StandIn((1, 1), torch.int32), workspace=ws)
+        with pytest.raises(ValueError):
+            M.monarch_attn_fwd_kv(q, q, q, _StandIn(shp, dt), 1, 1, 3, 4, 3, 4, workspace=ws)
+    q = _StandIn((1, 12, 4680, 128), torch.bfloat16)
+    small = _StandIn((1, 1, 32, 16), torch.bfloat16)
+    with pytest.raises(ValueError):
+        M.monarch_attn_bwd(q, q, q, _StandIn(q.shape, torch.bfloat16), small, small, small, small,
+                           3, 30, 52, 90, 52, 1, 1, ws)

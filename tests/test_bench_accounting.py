@@ -39,6 +39,45 @@ def test_latent720p_one_iteration_is_2690_gflop():
     assert abs(flops - 2.690e12) <= 0.001 * 2.690e12
 
 
+def test_per_kernel_bytes_are_the_layer_tensors_only():
+    """Algorithmic bytes are the layer's own tensors each kernel touches
+    (Q, K, V, O), never the implementation's intermediates: the first
+    L-step's kernels read Q, the R-step reads K and V, the apply reads Q and
+    writes O; over the call Q, K, V are read and O is written once each
+    (4*B*H*N*d*e, 3097 MB at the 720p latent in bf16)."""
+    wl = I.get_workload("latent720p")
+    e = 2
+    x = wl.B * wl.H * wl.N * wl.d * e
+    w = bench.algorithmic_work(wl)
+    assert w["k_kbar"][1] == x and w["k_lse"][1] == x and w["k_aggregate"][1] == x
+    assert w["k_rstep"][1] == 2 * x and w["k_apply"][1] == 2 * x
+    assert abs(4 * x - 3.097e9) <= 0.001 * 3.097e9
+    # the aggregated queries and U (t*N*d*e each, written and read) are
+    # intermediates, reported apart: 12.4 GB over the call
+    inter = bench.intermediate_bytes(wl)
+    tnd = wl.B * wl.H * wl.tiles * wl.N * wl.d * e
+    assert inter["k_aggregate"] >= tnd and inter["k_rstep"] == 2 * tnd and inter["k_apply"] >= tnd
+    assert abs(4 * tnd - 12.39e9) <= 0.01 * 12.39e9
+
+
+def test_roofline_bounds_follow_the_method_work():
+    """The logit kernels and the R-step are MFMA-bound by their algorithmic
+    work at the 720p latent (arithmetic intensity above the 312 flop/B
+    ridge), the block means HBM-bound; k_aggregate at 2240.7 us per launch is
+    0.7316 TFLOP / 2.2407 ms = 326.5 TFLOP/s, 0.131 of 2.5 PFLOP/s."""
+    wl = I.get_workload("latent720p")
+    w = bench.algorithmic_work(wl)
+    fl, by = w["k_aggregate"]
+    assert abs(fl - 2 * wl.B * wl.H * wl.Nq * wl.b1 * wl.d) == 0
+    r = bench.roofline_entry("k_aggregate", fl, by, 2240.7e-6, "bf16", None)
+    assert r["bound"] == "mfma" and abs(r["frac"] - 0.1306) <= 5e-4, r
+    r = bench.roofline_entry("k_rstep", *w["k_rstep"], 1614.3e-6, "bf16", None)
+    assert r["bound"] == "mfma" and abs(r["frac"] - 0.1228) <= 5e-4, r
+    r = bench.roofline_entry("k_kbar", *w["k_kbar"], 145.1e-6, "bf16", None)
+    assert r["bound"] == "hbm" and abs(r["frac"] - 0.6669) <= 5e-4, r
+    assert bench.roofline_entry("k_objective", *w["k_objective"], 1e-5, "bf16", None)["bound"] == "none"
+
+
 def test_more_than_one_gpu_is_refused_with_a_message():
     """bench.py measures one GPU; --gpus above 1 exits with status 2 and says
     so, before any GPU work."""

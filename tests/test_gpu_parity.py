@@ -183,3 +183,33 @@ def test_loose_logit_bound_falls_back_to_running_max():
         mx, mean = errors(y[0, h], ref)
         say(f"[ok] loose bound head {h}: max-abs {mx:.3e} mean-abs {mean:.3e}")
         assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("t,T", [(8, 2), (2, 2), (8, 3), (1, 2)])
+def test_beta_zero_tile_columns(dtype, t, T):
+    """Key block 3 gets weight exactly 0 from every query in the first L-step
+    (its mean key lies ~1290 bits below the others: exp2 underflows in fp32
+    as exp does in fp64), so every tile column of that block has beta = 0 on
+    both sides and the R row is uniform (Qhat := 0).  With T >= 2 that row
+    feeds the next L-step, so the output depends on the choice; one-row
+    tiles (t = 8) and four-row tiles (t = 2) against the oracle."""
+    b1, b2, d, cstar = 8, 4, 16, 3
+    say(f"[case] beta=0 tile columns {dtype} t={t} T={T}")
+    heads = [I.make_underflow_head(s, b1, b2, d, cstar, dtype) for s in (0, 1)]
+    wl = I.Workload("underflow", 1, len(heads), d, 2, 4, 4, b1, b2, t, T, dtype, pos_amp=0.0)
+    x = {n: np.stack([hd[i] for hd in heads])[None] for i, n in enumerate("qkv")}
+    if dtype == "bf16":
+        for i, n in enumerate("qkv"):
+            x[n + "_bits"] = np.stack([hd[3][i] for hd in heads])[None]
+    y = run_gpu(wl, x)
+    for h in range(len(heads)):
+        q, k, v = (x[n][0, h].astype(np.float64) for n in "qkv")
+        ref, (_, _, hist) = oracle.monarch_head(q, k, v, b1, b2, t, T, return_factors=True)
+        assert np.all(hist[0][1][:, :, cstar] == 0.0)  # the oracle takes the beta = 0 branch
+        mx, mean = errors(y[0, h], ref)
+        say(f"[ok] beta=0 head {h}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+        if dtype == "bf16":
+            assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
+        else:
+            assert mx <= F32_MAX_ABS, (h, mx)

@@ -49,6 +49,12 @@ MUTANTS = {
     "adaptive_gain_not_per_token": ("(F[-1] - F[-2]) / Nq <= tol", "(F[-1] - F[-2]) <= tol"),
     "adaptive_stops_after_one": ("(it >= 2 and (F[-1] - F[-2]) / Nq <= tol)", "(it >= 1 and (F[-1] - F[-2 if it > 1 else -1]) / Nq <= tol)"),
     "adaptive_objective_without_max": ("F.append(float(np.sum(m[..., 0] + np.log(", "F.append(float(np.sum(0 * m[..., 0] + np.log("),
+    "beta_zero_tile_mean": ("qh = np.where((mass > 0)[:, :, None], q_til / safe[:, :, None], 0.0)",
+                            "qh = np.where((mass > 0)[:, :, None], q_til / safe[:, :, None], "
+                            "q_cols.mean(axis=1)[:, None, :])"),
+    "beta_zero_first_query": ("qh = np.where((mass > 0)[:, :, None], q_til / safe[:, :, None], 0.0)",
+                              "qh = np.where((mass > 0)[:, :, None], q_til / safe[:, :, None], "
+                              "q_cols[:, :1, :])"),
     "stale_L_in_apply": ("        R, _, _ = r_step(qb, kb, L, bounds, s)\n        history",
                          "        R, _, _ = r_step(qb, kb, L, bounds, s)\n        L = L[:, ::-1, :]\n        history"),
 }
