@@ -1,0 +1,11 @@
+// The forward kernels for bf16 I/O, one instantiation per head dimension
+// (a translation unit of its own, so the library builds in parallel).
+#include "run_fwd.h"
+
+using monarch::bf16_t;
+using namespace monarch_host;
+
+MONARCH_INSTANTIATE_RUN_PASS(bf16_t, 16)
+MONARCH_INSTANTIATE_RUN_PASS(bf16_t, 32)
+MONARCH_INSTANTIATE_RUN_PASS(bf16_t, 64)
+MONARCH_INSTANTIATE_RUN_PASS(bf16_t, 128)

@@ -897,6 +897,9 @@ __global__ __launch_bounds__(256) void k_kbar_long(const T* __restrict__ k, T* _
 // The first L-step leaves out the entropy of the uniform R, log(b2), which is
 // the same for every key block (it cancels in the softmax); it is added back
 // here so that F_1 is the objective proper.
+// (A template only so that every translation unit that launches it shares
+// one definition.)
+template <int kUnused = 0>
 __global__ __launch_bounds__(256) void k_objective(const float* __restrict__ lse, int N, int b2,
                                                    double* __restrict__ fprev, int* __restrict__ stop_at, int it,
                                                    int max_it, float tol) {
@@ -921,6 +924,7 @@ __global__ __launch_bounds__(256) void k_objective(const float* __restrict__ lse
   }
 }
 
+template <int kUnused = 0>
 __global__ __launch_bounds__(256) void k_fill_int(int* __restrict__ p, int n, int value) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = value;

@@ -260,15 +260,17 @@ def make_underflow_head(seed: int, b1: int, b2: int, d: int, cstar: int, dtype: 
     """A head whose block ``cstar`` of keys is pushed far away from every query.
 
     Standard normal q, k, v (``default_rng([seed, 7])``, drawn in that order),
-    then, in channel 0 only: every query is set to 8; key 0 of block
-    ``cstar`` to +16 and its other keys to -600 (``b2 >= 2``).  At scale
+    then, in channel 0 only: every query is set to 2; key 0 of block
+    ``cstar`` to +64 and its other keys to -2400 (``b2 >= 2``).  At scale
     ``1/sqrt(d)`` the mean key of that block then sits about
-    ``8*(16 - 600*(b2-1))/(b2*sqrt(d))`` nats (-892 at b2 = 4, d = 16) below
+    ``2*(64 - 2400*(b2-1))/(b2*sqrt(d))`` nats (-892 at b2 = 4, d = 16) below
     every other block for every query, beyond where exp underflows in fp64
-    and fp32 alike, while its key 0 is the best single match of every
-    query.  All set values are exact in bf16.  ``dtype == "bf16"`` rounds the
-    noise to bf16 as :func:`make_inputs` does.  Returns float32 ``(q, k, v)``
-    of shape ``[b1*b2, d]`` and, for bf16, their bit patterns as a 4th item.
+    and fp32 alike, while its key 0 is the best single match of every query
+    (+32 nats at d = 16).  All set values are exact in bf16, and the queries
+    keep a norm close to that of the standard normal draws.  ``dtype ==
+    "bf16"`` rounds the draws to bf16 as :func:`make_inputs` does.  Returns
+    float32 ``(q, k, v)`` of shape ``[b1*b2, d]`` and, for bf16, their bit
+    patterns as a 4th item.
     """
     if b2 < 2 or not 0 <= cstar < b1:
         raise ValueError("need b2 >= 2 and 0 <= cstar < b1")
@@ -277,9 +279,9 @@ def make_underflow_head(seed: int, b1: int, b2: int, d: int, cstar: int, dtype: 
     q = rng.standard_normal((N, d), dtype=np.float32)
     k = rng.standard_normal((N, d), dtype=np.float32)
     v = rng.standard_normal((N, d), dtype=np.float32)
-    q[:, 0] = 8.0
-    k[cstar * b2:(cstar + 1) * b2, 0] = -600.0
-    k[cstar * b2, 0] = 16.0
+    q[:, 0] = 2.0
+    k[cstar * b2:(cstar + 1) * b2, 0] = -2400.0
+    k[cstar * b2, 0] = 64.0
     if dtype == "bf16":
         bits = [round_to_bf16_bits(x) for x in (q, k, v)]
         q, k, v = (bf16_bits_to_f32(x) for x in bits)

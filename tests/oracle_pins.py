@@ -159,7 +159,7 @@ def check_beta_zero_branch(orc):
     """A key block whose weight underflows to exactly 0 in every tile column
     (beta = 0, reading D6: that R row is uniform, i.e. Qhat := 0).
 
-    The block mean of block c* lies about 890 nats below every other block
+    The block mean of block c* lies about 892 nats below every other block
     for every query, so the first L-step gives it weight 0 exactly; its key 0
     is every query's best single match.  Under the reading the uniform R row
     hands the next L-step the block mean again (plus log b2), so the block

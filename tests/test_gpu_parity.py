@@ -189,7 +189,7 @@ def test_loose_logit_bound_falls_back_to_running_max():
 @pytest.mark.parametrize("t,T", [(8, 2), (2, 2), (8, 3), (1, 2)])
 def test_beta_zero_tile_columns(dtype, t, T):
     """Key block 3 gets weight exactly 0 from every query in the first L-step
-    (its mean key lies ~1290 bits below the others: exp2 underflows in fp32
+    (its mean key lies ~890 nats, ~1290 bits, below the others: exp2 underflows in fp32
     as exp does in fp64), so every tile column of that block has beta = 0 on
     both sides and the R row is uniform (Qhat := 0).  With T >= 2 that row
     feeds the next L-step, so the output depends on the choice; one-row
