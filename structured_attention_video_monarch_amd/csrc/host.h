@@ -48,6 +48,12 @@ using namespace monarch;
 constexpr int kLseRW = MONARCH_LSE_RW, kLseNW = MONARCH_LSE_NW;
 constexpr int kAggRW = MONARCH_AGG_RW, kAggNW = MONARCH_AGG_NW;
 constexpr int kAppRW = MONARCH_APP_RW, kAppNW = MONARCH_APP_NW;
+// the first L-step's aggregation with the whole tile column in LDS (bf16,
+// at most kColRows rows per tile)
+#ifndef MONARCH_AGG_COL
+#define MONARCH_AGG_COL 1
+#endif
+
 // the R-step of long key blocks (b2 > kShortB2): rows a2 per workgroup
 #ifndef MONARCH_RL_RW
 #define MONARCH_RL_RW 2
@@ -251,6 +257,9 @@ struct Bufs {
   T* u;
   float* beta;
   float* rlse;  // training with key blocks over 128: the R rows' log-sum-exps
+  // the inference forward may store the block means pre-scaled to log2 units
+  // (c Kbar); the training forward keeps Kbar itself, as its backward reads it
+  bool prescale;
   long long lse_it, qhat_it, beta_it, ktil_it, hent_it;
   // views of iteration it (1-based); keys/entropies: those the R-step of
   // iteration it writes (it < T), read by the L-step of it + 1
@@ -274,6 +283,7 @@ Bufs<T> bufs_of(const Shape& s, unsigned char* ws, const Workspace& w) {
   b.u = b.qhat;
   b.beta = nullptr;
   b.rlse = nullptr;
+  b.prescale = true;
   return b;
 }
 
@@ -343,6 +353,7 @@ Bufs<T> train_bufs(unsigned char* st, const TrainState& t, int iters) {
   b.u = reinterpret_cast<T*>(st + t.u);
   b.beta = reinterpret_cast<float*>(st + t.beta);
   b.rlse = t.rlse < t.total ? reinterpret_cast<float*>(st + t.rlse) : nullptr;
+  b.prescale = false;
   b.lse_it = static_cast<long long>(t.lse_blk / sizeof(float));
   b.beta_it = static_cast<long long>(t.beta_blk / sizeof(float));
   b.qhat_it = static_cast<long long>(t.qhat_blk / sizeof(T));

@@ -166,6 +166,20 @@ __device__ inline void logits(f32x4 (&S)[2][RW], const typename Elem<T>::frag (&
       for (int rt = 0; rt < RW; ++rt) S[ct][rt] = Elem<T>::mma(a[s][ct], b[rt][s], S[ct][rt]);
 }
 
+// The same products accumulated onto S as given (S holds a bias per logit:
+// with keys pre-scaled to log2 units the first MFMA then starts from the
+// bias, and no multiply-add is left for the exponent).
+template <typename T, int KS, int RW>
+__device__ inline void logits_onto(f32x4 (&S)[2][RW], const typename Elem<T>::frag (&a)[KS][2],
+                                   const typename Elem<T>::frag (&b)[RW][KS]) {
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) S[ct][rt] = Elem<T>::mma(a[s][ct], b[rt][s], S[ct][rt]);
+}
+
 // acc[dp][dt][rt] += v[dp][dt] * pf[rt]
 template <typename T, int D, int NACC, int RW>
 __device__ inline void weighted_sum(f32x4 (&acc)[NACC][2][RW], const typename Elem<T>::frag (&v)[NACC][2],
@@ -190,7 +204,12 @@ __device__ inline void weighted_sum(f32x4 (&acc)[NACC][2][RW], const typename El
 // bound is so loose that a row's sum falls below 2^-60 (very large norms
 // with nearly orthogonal q and keys), the workgroup recomputes with the
 // running maximum.
-template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG>
+//
+// PRE (first L-step of the inference forward): the block means are stored
+// already multiplied by c = log2(e)/sqrt(d) (k_kbar with cscale = c), so the
+// products are logits in log2 units as they stand, knorm holds |c Kbar_c1|,
+// and each product starts from -m_n in place of a multiply-add per logit.
+template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG, bool PRE = false>
 __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
                                                                       const T* __restrict__ kt,
                                                                       const float* __restrict__ h2,
@@ -276,7 +295,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
         sq += __shfl_xor(sq, 16);
         sq += __shfl_xor(sq, 32);
         // a little above the bound: the MFMA sums in fp32
-        mrow[rt] = p.c * sqrtf(sq) * km * 1.00390625f + 0.00390625f;
+        mrow[rt] = (PRE ? 1.0f : p.c) * sqrtf(sq) * km * 1.00390625f + 0.00390625f;
         ls[rt] = 0.0f;
       }
       // one 32-key block: masked only where keys run past b1
@@ -284,12 +303,20 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
         typename E::frag a[KS][2];
         load_rows<T, DK, KS>(a, tile, k0, l16, G);
         f32x4 S[2][RW];
-        logits<T, KS, RW>(S, a, bq);
+        if constexpr (PRE) {
+#pragma unroll
+          for (int rt = 0; rt < RW; ++rt)
+            S[0][rt] = S[1][rt] = f32x4{-mrow[rt], -mrow[rt], -mrow[rt], -mrow[rt]};
+          logits_onto<T, KS, RW>(S, a, bq);
+        } else {
+          logits<T, KS, RW>(S, a, bq);
+        }
 #pragma unroll
         for (int rt = 0; rt < RW; ++rt)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float w = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, -mrow[rt]));
+            const float w = PRE ? fast_exp2(S[j >> 2][rt][j & 3])
+                                : fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, -mrow[rt]));
             if constexpr (decltype(masked)::value)
               ls[rt] += c1_0 + 8 * G + j < p.b1 ? w : 0.0f;
             else
@@ -360,7 +387,9 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
       for (int rt = 0; rt < RW; ++rt) {
         float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = BCAST ? S[j >> 2][rt][j & 3] * p.c : __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
+        for (int j = 0; j < 8; ++j)
+          x[j] = PRE ? S[j >> 2][rt][j & 3]
+                     : BCAST ? S[j >> 2][rt][j & 3] * p.c : __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
         if (tail) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[j] = c1_0 + 8 * G + j < p.b1 ? x[j] : kNegInf;
@@ -540,7 +569,9 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
 // all its 32-row blocks run with no further barrier or wait.
 constexpr int kColRows = 256;
 
-template <typename T, int D, int RW, int NW, bool BCAST>
+// PRE: block-mean keys pre-scaled by c (see k_lse); each logit product starts
+// from -lse of its row.
+template <typename T, int D, int RW, int NW, bool BCAST, bool PRE = false>
 __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(const T* __restrict__ q,
                                                                                 const T* __restrict__ kt,
                                                                                 const float* __restrict__ h2,
@@ -624,14 +655,24 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
     for (int j = 0; j < 8; ++j) lr[j] = sL[st][k0 + 8 * G + j];
     __builtin_amdgcn_sched_barrier(0);
     f32x4 S[2][RW];
-    logits<T, KS, RW>(S, a, bk);
+    if constexpr (PRE) {
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        S[0][rt] = f32x4{-lr[0], -lr[1], -lr[2], -lr[3]};
+        S[1][rt] = f32x4{-lr[4], -lr[5], -lr[6], -lr[7]};
+      }
+      logits_onto<T, KS, RW>(S, a, bk);
+    } else {
+      logits<T, KS, RW>(S, a, bk);
+    }
     typename E::frag pf[RW];
 #pragma unroll
     for (int rt = 0; rt < RW; ++rt) {
       float w[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? -lr[j] : bias[rt] - lr[j]));
+        w[j] = PRE ? fast_exp2(S[j >> 2][rt][j & 3])
+                   : fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? -lr[j] : bias[rt] - lr[j]));
       if (tail) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) w[j] = r0 + 8 * G + j < nrows ? w[j] : 0.0f;
@@ -658,7 +699,9 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
 // One workgroup: (bh, g, a2) and a block of RB = NW*RW*16 rows a1 of tile g.
 // y[a1,:] = sum_c1 L[a1,c1] U[g,c1,a2,:], with L normalised by the stored
 // log-sum-exp (no running rescale), computed as y^T = U^T P^T.
-template <typename T, int D, int RW, int NW, bool BCAST>
+// PRE: block-mean keys pre-scaled by c (see k_lse); each logit product starts
+// from -lse of its row.
+template <typename T, int D, int RW, int NW, bool BCAST, bool PRE = false>
 __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T* __restrict__ q,
                                                                         const T* __restrict__ kt,
                                                                         const float* __restrict__ h2,
@@ -749,14 +792,22 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x4 S[2][RW];
-      logits<T, KS, RW>(S, a, bq);
+      if constexpr (PRE) {
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt)
+          S[0][rt] = S[1][rt] = f32x4{nlrow[rt], nlrow[rt], nlrow[rt], nlrow[rt]};
+        logits_onto<T, KS, RW>(S, a, bq);
+      } else {
+        logits<T, KS, RW>(S, a, bq);
+      }
       typename E::frag pf[RW];
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         float w[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? nlrow[rt] : bias[j] + nlrow[rt]));
+          w[j] = PRE ? fast_exp2(S[j >> 2][rt][j & 3])
+                     : fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? nlrow[rt] : bias[j] + nlrow[rt]));
         if (tail) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) w[j] = c1_0 + 8 * G + j < p.b1 ? w[j] : 0.0f;
@@ -785,9 +836,12 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
 // First L-step: with R uniform, every aggregated key is the block mean
 // Kbar[c1] = (1/b2) sum_c2 k_(c1,c2), shared by all tiles and columns (and the
 // entropy term log(b2) is the same for every c1, so it cancels in the softmax).
+// cscale multiplies the means before they are rounded and stored: 1, or
+// c = log2(e)/sqrt(d) for the kernels that take pre-scaled keys (PRE).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_kbar(const T* __restrict__ k, T* __restrict__ kbar,
-                                              float* __restrict__ knorm, int BH, int b1, int b2) {
+                                              float* __restrict__ knorm, int BH, int b1, int b2,
+                                              float cscale = 1.0f) {
   using E = Elem<T>;
   constexpr int V = E::kVec;
   constexpr int LPR = D / V;        // lanes per row
@@ -812,7 +866,7 @@ __global__ __launch_bounds__(256) void k_kbar(const T* __restrict__ k, T* __rest
     for (int j = 0; j < V; ++j) acc[j] += __shfl_xor(acc[j], off);
   // every lane now holds the sums of its columns; round the means as they
   // are stored and take |Kbar| of the rounded row (the bound k_lse uses)
-  const float inv = 1.0f / static_cast<float>(b2);
+  const float inv = cscale / static_cast<float>(b2);
   T mean[V];
   float sq = 0.0f;
 #pragma unroll
@@ -836,7 +890,7 @@ __global__ __launch_bounds__(256) void k_kbar(const T* __restrict__ k, T* __rest
 // fourth group of rows, the four partial sums added in LDS in a fixed order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_kbar_long(const T* __restrict__ k, T* __restrict__ kbar,
-                                                   float* __restrict__ knorm, int b2) {
+                                                   float* __restrict__ knorm, int b2, float cscale = 1.0f) {
   using E = Elem<T>;
   constexpr int V = E::kVec;
   constexpr int LPR = D / V;        // lanes per row
@@ -869,7 +923,7 @@ __global__ __launch_bounds__(256) void k_kbar_long(const T* __restrict__ k, T* _
 #pragma unroll
   for (int j = 0; j < V; ++j) acc[j] = ((part[0][col + j] + part[1][col + j]) + part[2][col + j]) + part[3][col + j];
   // round the means as they are stored and take |Kbar| of the rounded row
-  const float inv = 1.0f / static_cast<float>(b2);
+  const float inv = cscale / static_cast<float>(b2);
   T mean[V];
   float sq = 0.0f;
 #pragma unroll

@@ -20,16 +20,25 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     if (e != hipSuccess && err == hipSuccess) err = e;
   };
 
+  // The first L-step's kernels take the block means pre-scaled by c (one
+  // multiply-add less per logit) in the inference forward, where k_lse,
+  // k_aggregate_col and k_apply run them; the training forward keeps Kbar
+  // for its backward.
+  const int ngmax0 = (s.b1q + s.t - 1) / s.t;
+  const bool pre = sizeof(T) == 2 && bf.prescale && !(s.b1 <= kColsRows && ngmax0 <= kColsRows) &&
+                   ngmax0 <= kColRows && MONARCH_AGG_COL;
+  const float cscale = pre ? c : 1.0f;
+
   // block means of K
   {
     const long long items = s.BH * s.b1;
     const unsigned grid = static_cast<unsigned>((items + 3) / 4);
     if (s.b2 > kShortB2)
       ok(timed(0, st, [&] {
-        k_kbar_long<T, D><<<static_cast<unsigned>(items), 256, 0, st>>>(k, kbar, bf.knorm, s.b2);
+        k_kbar_long<T, D><<<static_cast<unsigned>(items), 256, 0, st>>>(k, kbar, bf.knorm, s.b2, cscale);
       }));
     else
-      ok(timed(0, st, [&] { k_kbar<T, D><<<grid, 256, 0, st>>>(k, kbar, bf.knorm, BH, s.b1, s.b2); }));
+      ok(timed(0, st, [&] { k_kbar<T, D><<<grid, 256, 0, st>>>(k, kbar, bf.knorm, BH, s.b1, s.b2, cscale); }));
   }
 
   constexpr int lse_rows = kLseRW * kLseNW * 16, agg_rows = kAggRW * kAggNW * 16,
@@ -46,9 +55,6 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
   const unsigned agg_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * agg.nrb);
   // whole tile column resident in LDS when it is short enough (bf16 only:
   // the f32 column would not fit)
-#ifndef MONARCH_AGG_COL
-#define MONARCH_AGG_COL 1
-#endif
   const bool col_fits = MONARCH_AGG_COL && sizeof(T) == 2 && ngmax <= kColRows;
   // short tile columns (few key blocks, few rows per tile, e.g. blocks of
   // whole frames): one column per wave
@@ -90,6 +96,13 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     float* hent_out = last ? nullptr : bf.hent_of(it);
     if (first) {
       ok(timed(1, st, [&] {
+        if constexpr (sizeof(T) == 2) {
+          if (pre) {
+            k_lse<T, D, kLseRW, kLseNW, true, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(
+                q, kbar, nullptr, lse, lse_contig, nullptr, 0, bf.knorm);
+            return;
+          }
+        }
         k_lse<T, D, kLseRW, kLseNW, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(q, kbar, nullptr, lse, lse_contig,
                                                                                           nullptr, 0, bf.knorm);
       }));
@@ -116,6 +129,13 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
       }));
     } else if (first) {
       ok(timed(2, st, [&] {
+        if constexpr (sizeof(T) == 2) {
+          if (pre) {
+            k_aggregate_col<T, D, kAggRW, kAggNW, true, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse,
+                                                                                                qhat, beta, agg);
+            return;
+          }
+        }
         if (col_fits)
           k_aggregate_col<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
         else
@@ -170,6 +190,13 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     }));
   } else if (s.T == 1) {
     ok(timed(4, st, [&] {
+      if constexpr (sizeof(T) == 2) {
+        if (pre) {
+          k_apply<T, D, kAppRW, kAppNW, true, true><<<app_grid, kAppNW * kWave, 0, st>>>(q, kbar, nullptr, lse_last, bf.u,
+                                                                                      out, app);
+          return;
+        }
+      }
       k_apply<T, D, kAppRW, kAppNW, true><<<app_grid, kAppNW * kWave, 0, st>>>(q, kbar, nullptr, lse_last, bf.u, out,
                                                                               app);
     }));
