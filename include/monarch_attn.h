@@ -108,6 +108,28 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
                         int b1, int b2, int tiles, int iters, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- a forward that allocates nothing ----
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * operation and arguments as monarch_attn_fwd_ws without the workspace:
+ * the intermediates live in one static device array of the library,
+ * MONARCH_SCRATCH_BYTES (128 MiB) per GPU, allocated with the library's code
+ * on that GPU and held until the process ends.  A call whose workspace
+ * (monarch_attn_workspace_bytes) exceeds it returns MONARCH_ENOMEM and
+ * launches nothing: it covers, e.g., the 3-frame 480p chunk (12 heads,
+ * 15 MB) and the 21-frame 480p clip (12 heads, 101 MB), not the 40-head
+ * 720p latent.  The first call on a device looks up the array's device
+ * address (hipGetSymbolAddress) with that device current.  Every call on one
+ * GPU uses the same array: calls that overlap on one GPU (two host threads,
+ * or two streams whose work runs concurrently) race and give undefined
+ * results; calls on one stream are ordered and safe.  Nothing in the array
+ * needs clearing between calls (every intermediate is written before it is
+ * read). */
+#define MONARCH_SCRATCH_BYTES ((size_t)128 << 20)
+int monarch_attn_fwd_scratch(const void* q, const void* k, const void* v, void* out,
+                             int B, int H, int f, int h, int w, int d,
+                             int b1, int b2, int tiles, int iters, int dtype, void* stream);
+
 /* ---- iterating until the factors converge ----
  * Without finetuning the pages run about ten iterations (yunpan.plus
  * MonarchRT article, "Innovation 3: finetuning and efficient kernels",

@@ -48,6 +48,8 @@ def _declare(lib):
     lib.monarch_attn_workspace_bytes.restype = c_size_t
     lib.monarch_attn_fwd_ws.argtypes = [c_void_p] * 4 + dims + [c_int, c_void_p, c_size_t, c_void_p]
     lib.monarch_attn_fwd_ws.restype = c_int
+    lib.monarch_attn_fwd_scratch.argtypes = [c_void_p] * 4 + dims + [c_int, c_void_p]
+    lib.monarch_attn_fwd_scratch.restype = c_int
     lib.monarch_attn_adaptive_workspace_bytes.argtypes = dims + [c_int]
     lib.monarch_attn_adaptive_workspace_bytes.restype = c_size_t
     lib.monarch_attn_fwd_adaptive_ws.argtypes = ([c_void_p] * 4 + dims + [ctypes.c_float, c_int, c_void_p,
@@ -207,6 +209,20 @@ def monarch_attn_fwd_ws(q, k, v, out, f, h, w, b1, b2, tiles, iters, workspace, 
     _check(lib().monarch_attn_fwd_ws(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, iters), dtype,
                                      _ptr(workspace), nbytes, _stream(stream)),
            "monarch_attn_fwd_ws")
+    return out
+
+
+MONARCH_SCRATCH_BYTES = 128 << 20
+
+
+def monarch_attn_fwd_scratch(q, k, v, out, f, h, w, b1, b2, tiles=1, iters=1, stream=None):
+    """Either dtype, with the library's static device scratch array instead of
+    a workspace: allocates nothing (MonarchError ENOMEM when the workspace
+    would exceed MONARCH_SCRATCH_BYTES).  Calls that overlap on one GPU race."""
+    dtype = _dtype_code(q)
+    ptrs = _tensors(q, k, v, out, q.dtype)
+    _check(lib().monarch_attn_fwd_scratch(*ptrs, *_dims(q, f, h, w, b1, b2, tiles, iters), dtype,
+                                          _stream(stream)), "monarch_attn_fwd_scratch")
     return out
 
 

@@ -118,6 +118,60 @@ int fwd_alloc(const void* q, const void* k, const void* v, void* out, const Shap
   return rc;
 }
 
+// ------------------------------------------------- no-allocation forward --
+// The intermediates of monarch_attn_fwd_scratch live in this array, one copy
+// per GPU the library's code is loaded on.  In host code its name is only a
+// stand-in: the device address of each GPU's copy comes from
+// hipGetSymbolAddress on that GPU (scratch_ptr) and is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[MONARCH_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This GPU's copy of the scratch array (looked up once per device, with the
+// device current), or nullptr with *err set.
+void* scratch_ptr(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+int fwd_scratch(const void* q, const void* k, const void* v, void* out, const Shape& s, int dtype,
+                hipStream_t st) {
+  const size_t elem = elem_size(dtype);
+  if (elem == 0) return MONARCH_EINVAL;
+  const int rc = check_args(q, k, v, out, s, elem);
+  if (rc != MONARCH_OK) return rc;
+  if (layout(s, elem).total > MONARCH_SCRATCH_BYTES) return MONARCH_ENOMEM;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_ptr(&e);
+  if (!ws) {
+    g_last_hip_error = static_cast<int>(e);
+    (void)hipGetLastError();
+    return MONARCH_EHIP;
+  }
+  return fwd_ws(q, k, v, out, s, dtype, ws, MONARCH_SCRATCH_BYTES, st);
+}
+
 // --------------------------------------------------- iterate to converge --
 // Workspace of the early-stopping call: the forward's for max_iters
 // iterations over all heads at once, then the previous objective per head.
@@ -380,6 +434,12 @@ int monarch_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, 
   const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
   return fwd_ws(q, k, v, out, s, dtype, workspace, workspace_bytes,
                 static_cast<hipStream_t>(stream));
+}
+
+int monarch_attn_fwd_scratch(const void* q, const void* k, const void* v, void* out, int B, int H, int f, int h,
+                             int w, int d, int b1, int b2, int tiles, int iters, int dtype, void* stream) {
+  const Shape s = make_shape(B, H, f, h, w, d, b1, b2, tiles, iters);
+  return fwd_scratch(q, k, v, out, s, dtype, static_cast<hipStream_t>(stream));
 }
 
 size_t monarch_attn_adaptive_workspace_bytes(int B, int H, int f, int h, int w, int d, int b1, int b2,
