@@ -291,6 +291,7 @@ Bufs<T> bufs_of(const Shape& s, unsigned char* ws, const Workspace& w) {
 // stop iterations (zeroed before the call) and the previous objectives.
 struct Adaptive {
   int* stop_at;
+  int* nstop_upto;  // [max_iters + 1]: heads stopped after iteration <= i (zeroed before the call)
   double* fprev;
   float tol;
 };
@@ -464,6 +465,28 @@ inline BwdWorkspace bwd_layout(const Shape& s, size_t elem) {
 }
 
 constexpr size_t kLdsBytes = 160 * 1024;
+
+// Workgroups of a launch that loops over `items` work items: a few times as
+// many as the chip holds at once (the kernel's occupancy per CU times the
+// CUs, times kPersistOver, a multiple of 8 so that every item keeps its XCD),
+// and never more than the items.  Each workgroup then takes several items,
+// so a launch whose items are all skipped dispatches few workgroups, while
+// workgroups still come and go as in a full grid (a CU refills as soon as
+// one of its workgroups ends, and the occupancy estimate need not be exact).
+constexpr int kPersistOver = 8;
+inline unsigned persistent_grid(const void* kernel, int threads, size_t lds, long long items) {
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu < 1) {
+    (void)hipGetLastError();
+    ncu = 256;
+    per_cu = 1;
+  }
+  long long g = static_cast<long long>(ncu) * per_cu * kPersistOver / 8 * 8;
+  if (g < 8) g = 8;
+  return static_cast<unsigned>(g < items ? g : items);
+}
 
 // Launch schedules (forward: run_fwd.h; backward: run_bwd.h).
 template <typename T, int D>

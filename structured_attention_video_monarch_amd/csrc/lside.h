@@ -65,8 +65,9 @@ struct KeySrc {
 // Work item of a per-column kernel: rows a1 in [a1_0, a1_0 + nrows) of tile g.
 struct ColItem {
   int bh, g, a2, a1_0, nrows, lo, hi;
-  __device__ ColItem(const LGeom& p, int rb_rows) {
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  // work item wi of wn (default: this workgroup of the grid)
+  __device__ ColItem(const LGeom& p, int rb_rows, int wi = -1, int wn = 0) {
+    const int logical = wi < 0 ? xcd_remap(blockIdx.x, gridDim.x) : xcd_remap(wi, wn);
     const int rb = logical % p.nrb;
     int rest = logical / p.nrb;
     a2 = rest % p.b2;
@@ -210,13 +211,13 @@ __device__ inline void weighted_sum(f32x4 (&acc)[NACC][2][RW], const typename El
 // products are logits in log2 units as they stand, knorm holds |c Kbar_c1|,
 // and each product starts from -m_n in place of a multiply-add per logit.
 template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG, bool PRE = false>
-__global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
+__device__ __forceinline__ void k_lse_item(const T* __restrict__ q,
                                                                       const T* __restrict__ kt,
                                                                       const float* __restrict__ h2,
                                                                       float* __restrict__ lse, LGeom p,
-                                                                      const int* __restrict__ stop_at = nullptr,
-                                                                      int it = 0,
-                                                                      const float* __restrict__ knorm = nullptr) {
+                                                                      const int* __restrict__ stop_at,
+                                                                      int it,
+                                                                      const float* __restrict__ knorm, int wi, int wn) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -229,13 +230,13 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
   int bh, g = 0, a2 = 0, nrows;
   long long n0, nstride;
   if (CONTIG) {
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(wi, wn);
     bh = logical / p.nrb;
     n0 = static_cast<long long>(logical % p.nrb) * RB;
     nstride = 1;
     nrows = p.N - n0 < RB ? static_cast<int>(p.N - n0) : RB;
   } else {
-    ColItem it(p, RB);
+    ColItem it(p, RB, wi, wn);
     bh = it.bh; g = it.g; a2 = it.a2;
     n0 = static_cast<long long>(it.a1_0) * p.b2 + a2;
     nstride = p.b2;
@@ -424,6 +425,25 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
   }
 }
 
+// Work items k_lse_item, one per workgroup, or looped over by fewer workgroups
+// (nitems > 0); nothing runs once every head has stopped iterating (nstop).
+template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG, bool PRE = false>
+__global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
+                                                                      const T* __restrict__ kt,
+                                                                      const float* __restrict__ h2,
+                                                                      float* __restrict__ lse, LGeom p,
+                                                                      const int* __restrict__ stop_at = nullptr,
+                                                                      int it = 0,
+                                                                      const float* __restrict__ knorm = nullptr,
+    const int* __restrict__ nstop = nullptr, int nitems = 0) {
+  if (nstop && *nstop >= p.BH) return;
+  const int wn = nitems > 0 ? nitems : static_cast<int>(gridDim.x);
+  for (int wi = blockIdx.x; wi < wn; wi += gridDim.x) {
+    if (wi != static_cast<int>(blockIdx.x)) __syncthreads();
+    k_lse_item<T, D, RW, NW, BCAST, CONTIG, PRE>(q, kt, h2, lse, p, stop_at, it, knorm, wi, wn);
+  }
+}
+
 // ------------------------------------------------------------ k_aggregate --
 // One workgroup: (bh, g, a2) and a block of CB = NW*RW*16 key blocks c1.
 // Qh[c1,:] = sum_(a1 in g) L[a1,c1] q_a1 / sum_(a1 in g) L[a1,c1], computed as
@@ -432,13 +452,13 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* _
 // beta comes from one more product with a ones fragment, so it sums exactly
 // the rounded weights the weighted sum uses.
 template <typename T, int D, int RW, int NW, bool BCAST>
-__global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(const T* __restrict__ q,
+__device__ __forceinline__ void k_aggregate_item(const T* __restrict__ q,
                                                           const T* __restrict__ kt,
                                                           const float* __restrict__ h2,
                                                           const float* __restrict__ lse,
                                                           T* __restrict__ qhat, float* __restrict__ beta_out,
-                                                          LGeom p, const int* __restrict__ stop_at = nullptr,
-                                                          int it = 0) {
+                                                          LGeom p, const int* __restrict__ stop_at,
+                                                          int it, int wi, int wn) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -450,7 +470,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
   __shared__ float sL[2][kStep];
 
   // decode (bh, g, a2, cb)
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = xcd_remap(wi, wn);
   const int cb = logical % p.nrb;
   int rest = logical / p.nrb;
   const int a2 = rest % p.b2;
@@ -563,6 +583,25 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
   }
 }
 
+// Work items k_aggregate_item, one per workgroup, or looped over by fewer workgroups
+// (nitems > 0); nothing runs once every head has stopped iterating (nstop).
+template <typename T, int D, int RW, int NW, bool BCAST>
+__global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(const T* __restrict__ q,
+                                                          const T* __restrict__ kt,
+                                                          const float* __restrict__ h2,
+                                                          const float* __restrict__ lse,
+                                                          T* __restrict__ qhat, float* __restrict__ beta_out,
+                                                          LGeom p, const int* __restrict__ stop_at = nullptr,
+                                                          int it = 0,
+    const int* __restrict__ nstop = nullptr, int nitems = 0) {
+  if (nstop && *nstop >= p.BH) return;
+  const int wn = nitems > 0 ? nitems : static_cast<int>(gridDim.x);
+  for (int wi = blockIdx.x; wi < wn; wi += gridDim.x) {
+    if (wi != static_cast<int>(blockIdx.x)) __syncthreads();
+    k_aggregate_item<T, D, RW, NW, BCAST>(q, kt, h2, lse, qhat, beta_out, p, stop_at, it, wi, wn);
+  }
+}
+
 // ------------------------------------------------------- k_aggregate_col --
 // Same result as k_aggregate for tiles of at most kColRows rows: the whole q
 // column of the tile and its log-sum-exps are copied to LDS once (DMA), then
@@ -572,14 +611,14 @@ constexpr int kColRows = 256;
 // PRE: block-mean keys pre-scaled by c (see k_lse); each logit product starts
 // from -lse of its row.
 template <typename T, int D, int RW, int NW, bool BCAST, bool PRE = false>
-__global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(const T* __restrict__ q,
+__device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
                                                                                 const T* __restrict__ kt,
                                                                                 const float* __restrict__ h2,
                                                                                 const float* __restrict__ lse,
                                                                                 T* __restrict__ qhat,
                                                                                 float* __restrict__ beta_out, LGeom p,
-                                                                                const int* __restrict__ stop_at = nullptr,
-                                                                                int it = 0) {
+                                                                                const int* __restrict__ stop_at,
+                                                                                int it, int wi, int wn) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -591,7 +630,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
   __shared__ __align__(16) T sQ[NSTEP][kStep * DK];
   __shared__ __align__(16) float sL[NSTEP][kStep];
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = xcd_remap(wi, wn);
   const int cb = logical % p.nrb;
   int rest = logical / p.nrb;
   const int a2 = rest % p.b2;
@@ -692,6 +731,26 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
     const long long row = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
     store_rows<T, D, NACC, RW>(qhat + row * D, acc, rt, inv, G);
     if (beta_out && G == 0) beta_out[row] = b;
+  }
+}
+
+// Work items k_aggregate_col_item, one per workgroup, or looped over by fewer workgroups
+// (nitems > 0); nothing runs once every head has stopped iterating (nstop).
+template <typename T, int D, int RW, int NW, bool BCAST, bool PRE = false>
+__global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(const T* __restrict__ q,
+                                                                                const T* __restrict__ kt,
+                                                                                const float* __restrict__ h2,
+                                                                                const float* __restrict__ lse,
+                                                                                T* __restrict__ qhat,
+                                                                                float* __restrict__ beta_out, LGeom p,
+                                                                                const int* __restrict__ stop_at = nullptr,
+                                                                                int it = 0,
+    const int* __restrict__ nstop = nullptr, int nitems = 0) {
+  if (nstop && *nstop >= p.BH) return;
+  const int wn = nitems > 0 ? nitems : static_cast<int>(gridDim.x);
+  for (int wi = blockIdx.x; wi < wn; wi += gridDim.x) {
+    if (wi != static_cast<int>(blockIdx.x)) __syncthreads();
+    k_aggregate_col_item<T, D, RW, NW, BCAST, PRE>(q, kt, h2, lse, qhat, beta_out, p, stop_at, it, wi, wn);
   }
 }
 
@@ -953,19 +1012,32 @@ __global__ __launch_bounds__(256) void k_kbar_long(const T* __restrict__ k, T* _
 // here so that F_1 is the objective proper.
 // (A template only so that every translation unit that launches it shares
 // one definition.)
+// 1024 threads per head; each thread keeps eight loads in flight (strided
+// by the block, so every load instruction of the block is coalesced).
+constexpr int kObjThreads = 1024;
 template <int kUnused = 0>
-__global__ __launch_bounds__(256) void k_objective(const float* __restrict__ lse, int N, int b2,
-                                                   double* __restrict__ fprev, int* __restrict__ stop_at, int it,
-                                                   int max_it, float tol) {
+__global__ __launch_bounds__(kObjThreads) void k_objective(const float* __restrict__ lse, int N, int b2,
+                                                           double* __restrict__ fprev, int* __restrict__ stop_at,
+                                                           int it, int max_it, float tol,
+                                                           int* __restrict__ nstop_upto) {
+  constexpr int U = 8;
   const int bh = blockIdx.x;
   if (stop_at[bh] != 0) return;
-  __shared__ double red[256];
+  __shared__ double red[kObjThreads];
   double acc = 0.0;
   const float* l = lse + static_cast<long long>(bh) * N;
-  for (int n = threadIdx.x; n < N; n += 256) acc += static_cast<double>(l[n]);
+  int n = threadIdx.x;
+  for (; n + (U - 1) * kObjThreads < N; n += U * kObjThreads) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = l[n + u * kObjThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += static_cast<double>(x[u]);
+  }
+  for (; n < N; n += kObjThreads) acc += static_cast<double>(l[n]);
   red[threadIdx.x] = acc;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
+  for (int off = kObjThreads / 2; off > 0; off >>= 1) {
     if (static_cast<int>(threadIdx.x) < off) red[threadIdx.x] += red[threadIdx.x + off];
     __syncthreads();
   }
@@ -974,7 +1046,12 @@ __global__ __launch_bounds__(256) void k_objective(const float* __restrict__ lse
     if (it == 1) F += static_cast<double>(N) * log(static_cast<double>(b2));
     const bool stop = it >= max_it || (it >= 2 && F - fprev[bh] <= static_cast<double>(tol) * N);
     fprev[bh] = F;
-    if (stop) stop_at[bh] = it;
+    if (stop) {
+      stop_at[bh] = it;
+      // nstop_upto[i] counts the heads stopped after iteration <= i; once
+      // nstop_upto[it - 1] reaches BH every launch of iteration it returns at once
+      for (int i = it; i <= max_it; ++i) atomicAdd(nstop_upto + i, 1);
+    }
   }
 }
 

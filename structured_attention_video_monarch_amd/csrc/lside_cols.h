@@ -42,8 +42,9 @@ __device__ inline void wave_tile_dma(T* tile, const T* g, long long rstride, int
 struct ColsItem {
   int bh, g, a2, lo, nrows;
   bool valid;
-  __device__ ColsItem(const LGeom& p, int nw, int wave) {
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  // work item wi of wn (default: this workgroup of the grid)
+  __device__ ColsItem(const LGeom& p, int nw, int wave, int wi = -1, int wn = 0) {
+    const int logical = wi < 0 ? xcd_remap(blockIdx.x, gridDim.x) : xcd_remap(wi, wn);
     const int ncg = (p.b2 + nw - 1) / nw;
     const int cg = logical % ncg;
     const int rest = logical / ncg;
@@ -62,12 +63,12 @@ struct ColsItem {
 // the RW = 2 key tiles of the wave cover all b1 <= 32 keys, the column's rows
 // form one 32-row block.
 template <typename T, int D, int NW, bool BCAST>
-__global__ __launch_bounds__(NW * kWave) void k_aggregate_cols(const T* __restrict__ q, const T* __restrict__ kt,
+__device__ __forceinline__ void k_aggregate_cols_item(const T* __restrict__ q, const T* __restrict__ kt,
                                                                const float* __restrict__ h2,
                                                                const float* __restrict__ lse,
                                                                T* __restrict__ qhat, float* __restrict__ beta_out,
-                                                               LGeom p, const int* __restrict__ stop_at = nullptr,
-                                                               int it = 0) {
+                                                               LGeom p, const int* __restrict__ stop_at,
+                                                               int it, int wi, int wn) {
   using E = Elem<T>;
   constexpr int RW = 2;
   constexpr int DK = D < 32 ? 32 : D;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate_cols(const T* __restri
 
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
-  const ColsItem ci(p, NW, wave);
+  const ColsItem ci(p, NW, wave, wi, wn);
   if (stop_at && stop_at[ci.bh] != 0 && stop_at[ci.bh] < it) return;  // head done iterating
   const int bh = ci.bh, g = ci.g, a2 = ci.a2, nrows = ci.nrows;
   const KeySrc<T, D, BCAST> ks(kt, h2, p, bh, g, a2);
@@ -146,6 +147,24 @@ __global__ __launch_bounds__(NW * kWave) void k_aggregate_cols(const T* __restri
     const long long row = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
     store_rows<T, D, NACC, RW>(qhat + row * D, acc, rt, inv, G);
     if (beta_out && G == 0) beta_out[row] = b;
+  }
+}
+
+// Work items k_aggregate_cols_item, one per workgroup, or looped over by fewer workgroups
+// (nitems > 0); nothing runs once every head has stopped iterating (nstop).
+template <typename T, int D, int NW, bool BCAST>
+__global__ __launch_bounds__(NW * kWave) void k_aggregate_cols(const T* __restrict__ q, const T* __restrict__ kt,
+                                                               const float* __restrict__ h2,
+                                                               const float* __restrict__ lse,
+                                                               T* __restrict__ qhat, float* __restrict__ beta_out,
+                                                               LGeom p, const int* __restrict__ stop_at = nullptr,
+                                                               int it = 0,
+    const int* __restrict__ nstop = nullptr, int nitems = 0) {
+  if (nstop && *nstop >= p.BH) return;
+  const int wn = nitems > 0 ? nitems : static_cast<int>(gridDim.x);
+  for (int wi = blockIdx.x; wi < wn; wi += gridDim.x) {
+    if (wi != static_cast<int>(blockIdx.x)) __syncthreads();
+    k_aggregate_cols_item<T, D, NW, BCAST>(q, kt, h2, lse, qhat, beta_out, p, stop_at, it, wi, wn);
   }
 }
 

@@ -174,11 +174,14 @@ int fwd_scratch(const void* q, const void* k, const void* v, void* out, const Sh
 
 // --------------------------------------------------- iterate to converge --
 // Workspace of the early-stopping call: the forward's for max_iters
-// iterations over all heads at once, then the previous objective per head.
-size_t adaptive_bytes(const Shape& s, size_t elem, size_t* fprev_off) {
+// iterations over all heads at once, then the previous objective per head,
+// then the counts of heads stopped after each iteration (max_iters + 1 ints).
+size_t adaptive_bytes(const Shape& s, size_t elem, size_t* fprev_off, size_t* nstop_off = nullptr) {
   const Workspace w = layout(s, elem, true);
+  const size_t f = align_up(static_cast<size_t>(s.BH) * sizeof(double));
   if (fprev_off) *fprev_off = w.total;
-  return w.total + align_up(static_cast<size_t>(s.BH) * sizeof(double));
+  if (nstop_off) *nstop_off = w.total + f;
+  return w.total + f + align_up(static_cast<size_t>(s.T + 1) * sizeof(int));
 }
 
 int fwd_adaptive(const void* q, const void* k, const void* v, void* out, const Shape& s, int dtype,
@@ -188,16 +191,19 @@ int fwd_adaptive(const void* q, const void* k, const void* v, void* out, const S
   int rc = check_args(q, k, v, out, s, elem);
   if (rc != MONARCH_OK) return rc;
   if (!iters_used || std::isnan(tol)) return MONARCH_EINVAL;
-  size_t fprev_off = 0;
-  const size_t need = adaptive_bytes(s, elem, &fprev_off);
+  size_t fprev_off = 0, nstop_off = 0;
+  const size_t need = adaptive_bytes(s, elem, &fprev_off, &nstop_off);
   if (!workspace || workspace_bytes < need) return MONARCH_ENOMEM;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return MONARCH_EINVAL;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const Workspace w = layout(s, elem, true);
-  Adaptive ad{iters_used, reinterpret_cast<double*>(ws + fprev_off), tol};
+  int* nstop_upto = reinterpret_cast<int*>(ws + nstop_off);
+  Adaptive ad{iters_used, nstop_upto, reinterpret_cast<double*>(ws + fprev_off), tol};
   hipError_t e = hipSuccess;
   clear_stale_error();
+  // fill kernels, not memsets: the call can be captured in a HIP graph
   k_fill_int<><<<static_cast<unsigned>((s.BH + 255) / 256), 256, 0, st>>>(iters_used, static_cast<int>(s.BH), 0);
+  k_fill_int<><<<static_cast<unsigned>((s.T + 1 + 255) / 256), 256, 0, st>>>(nstop_upto, s.T + 1, 0);
   e = hipGetLastError();
   auto go = [&](auto tag) {
     using T = decltype(tag);

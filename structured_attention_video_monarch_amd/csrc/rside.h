@@ -47,7 +47,7 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
                                            T* qhat,   // [BH][t][b1][b2][D]; U written over it when LAST
                                            T* __restrict__ ktil, float* __restrict__ hent,
                                            T* uout,   // U goes here instead when not NULL
-                                           const RGeom& p) {
+                                           const RGeom& p, int item) {  // item = bh*b1 + c1
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -59,7 +59,6 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
   T* sK = reinterpret_cast<T*>(smem_raw);
   T* sV = sK + p.b2p * DK;
 
-  const int item = xcd_remap(blockIdx.x, gridDim.x);  // bh*b1 + c1
   const int c1 = item % p.b1;
   const int bh = item / p.b1;
   const long long blk = static_cast<long long>(item) * p.b2 * D;  // first element of block c1
@@ -233,25 +232,32 @@ template <typename T, int D, bool LAST>
 __global__ __launch_bounds__(512) void k_rstep(const T* __restrict__ k, const T* __restrict__ v, T* qhat,
                                                T* __restrict__ ktil, float* __restrict__ hent, T* uout,
                                                RGeom p) {
-  rstep_body<T, D, LAST>(k, v, qhat, ktil, hent, uout, p);
+  rstep_body<T, D, LAST>(k, v, qhat, ktil, hent, uout, p, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // Iteration `it` of a run that stops each head on its own: stop_at[bh] is the
-// iteration after which head bh stops (0 = not decided).  Heads that stopped
-// earlier are skipped; a head that stops now gets R V (the last R-step), the
-// others the next L-step's keys and entropies.  Dynamic LDS as for the last
-// R-step.
-template <typename T, int D>
+// iteration after which head bh stops (0 = not decided).  Two launches per
+// iteration: LAST = true gives R V (the last R-step) to the heads that stop
+// now (stop_at == it), LAST = false the next L-step's keys and entropies to
+// the heads that go on (stop_at == 0); heads that stopped earlier are skipped
+// by both.  Each launch has the LDS of its own form and one workgroup per
+// key block (a workgroup that looped over several key blocks would wait for
+// the stores of one before the loads of the next: measured 20% slower), and
+// every workgroup returns at once when no head is left for the launch:
+// nstop_upto[i] counts the heads stopped after iteration <= i, so
+// nstop_upto[it] - nstop_upto[it - 1] heads stop now and BH - nstop_upto[it]
+// go on.
+template <typename T, int D, bool LAST>
 __global__ __launch_bounds__(512) void k_rstep_adaptive(const T* __restrict__ k, const T* __restrict__ v,
                                                         T* qhat, T* __restrict__ ktil, float* __restrict__ hent,
-                                                        const int* __restrict__ stop_at, int it, RGeom p) {
-  const int bh = xcd_remap(blockIdx.x, gridDim.x) / p.b1;
-  const int sa = stop_at[bh];
-  if (sa != 0 && sa < it) return;
-  if (sa == it)
-    rstep_body<T, D, true>(k, v, qhat, nullptr, nullptr, nullptr, p);
-  else
-    rstep_body<T, D, false>(k, v, qhat, ktil, hent, nullptr, p);
+                                                        const int* __restrict__ stop_at, int it, RGeom p,
+                                                        const int* __restrict__ nstop_upto) {
+  const int done_before = nstop_upto[it - 1], done_now = nstop_upto[it];
+  if (LAST ? done_now == done_before : done_now >= p.BH) return;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int sa = stop_at[item / p.b1];
+  if (LAST ? sa != it : sa != 0) return;
+  rstep_body<T, D, LAST>(k, v, qhat, LAST ? nullptr : ktil, LAST ? nullptr : hent, nullptr, p, item);
 }
 
 }  // namespace monarch

@@ -201,23 +201,30 @@ __global__ __launch_bounds__(NW * kWave) void k_rstep_long(const T* __restrict__
 
 // Iteration `it` of a run that stops each head on its own (stop_at as for
 // k_rstep_adaptive): heads that stopped earlier are skipped, a head that stops
-// now gets R V, the others the next L-step's keys and entropies.
+// now gets R V, the others the next L-step's keys and entropies.  The
+// workgroups loop over nitems work items and return at once when every head
+// has stopped (nstop).
 template <typename T, int D, int RW, int NW>
 __global__ __launch_bounds__(NW * kWave) void k_rstep_long_adaptive(const T* __restrict__ k, const T* __restrict__ v,
                                                                     T* qhat, T* __restrict__ ktil,
                                                                     float* __restrict__ hent,
                                                                     const int* __restrict__ stop_at, int it,
-                                                                    RLGeom p) {
+                                                                    RLGeom p, const int* __restrict__ nstop,
+                                                                    int nitems) {
   MONARCH_RSTEP_LONG_LDS(T, (D < 32 ? 32 : D), true)
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = item / (p.nrb * p.t * p.b1);
-  const int sa = stop_at[bh];
-  if (sa != 0 && sa < it) return;
-  if (sa == it)
-    rstep_long_body<T, D, RW, NW, true>(k, v, qhat, nullptr, nullptr, nullptr, nullptr, p, item, sK0, sK1, sV0,
-                                        sV1);
-  else
-    rstep_long_body<T, D, RW, NW, false>(k, v, qhat, ktil, hent, nullptr, nullptr, p, item, sK0, sK1, sV0, sV1);
+  if (*nstop >= p.BH) return;
+  for (int wi = blockIdx.x; wi < nitems; wi += gridDim.x) {
+    if (wi != static_cast<int>(blockIdx.x)) __syncthreads();
+    const int item = xcd_remap(wi, nitems);
+    const int bh = item / (p.nrb * p.t * p.b1);
+    const int sa = stop_at[bh];
+    if (sa != 0 && sa < it) continue;
+    if (sa == it)
+      rstep_long_body<T, D, RW, NW, true>(k, v, qhat, nullptr, nullptr, nullptr, nullptr, p, item, sK0, sK1, sV0,
+                                          sV1);
+    else
+      rstep_long_body<T, D, RW, NW, false>(k, v, qhat, ktil, hent, nullptr, nullptr, p, item, sK0, sK1, sV0, sV1);
+  }
 }
 
 #undef MONARCH_RSTEP_LONG_LDS

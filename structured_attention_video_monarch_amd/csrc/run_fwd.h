@@ -82,8 +82,11 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
 
   const int* sa = ad ? ad->stop_at : nullptr;
   if (ad && r_lds_last > 65536)
-    ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rstep_adaptive<T, D>),
+    ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rstep_adaptive<T, D, true>),
                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds_last)));
+  if (ad && r_lds_mid > 65536)
+    ok(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rstep_adaptive<T, D, false>),
+                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(r_lds_mid)));
   for (int it = 1; it <= s.T; ++it) {
     const bool first = it == 1, last = it == s.T;
     float* lse = bf.lse_of(it);
@@ -94,6 +97,12 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     const float* hent = first ? nullptr : bf.hent_of(it - 1);
     T* ktil_out = last ? nullptr : bf.ktil_of(it);
     float* hent_out = last ? nullptr : bf.hent_of(it);
+    // early stopping, iterations after the first: the iteration's kernels
+    // loop over their work items with as many workgroups as the chip holds,
+    // skip the heads that stopped before, and return at once when every head
+    // has (ns: heads stopped after iteration <= it - 1)
+    const bool persist = ad && !first;
+    const int* ns = ad ? ad->nstop_upto + (it - 1) : nullptr;
     if (first) {
       ok(timed(1, st, [&] {
         if constexpr (sizeof(T) == 2) {
@@ -106,6 +115,13 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
         k_lse<T, D, kLseRW, kLseNW, true, true><<<lse_contig_grid, kLseNW * kWave, 0, st>>>(q, kbar, nullptr, lse, lse_contig,
                                                                                           nullptr, 0, bf.knorm);
       }));
+    } else if (persist) {
+      auto kern = &k_lse<T, D, kLseRW, kLseNW, false, false>;
+      const unsigned grid = persistent_grid(reinterpret_cast<const void*>(kern), kLseNW * kWave, 0, lse_col_grid);
+      ok(timed(1, st, [&] {
+        kern<<<grid, kLseNW * kWave, 0, st>>>(q, ktil, hent, lse, lse_col, sa, it, nullptr, ns,
+                                              static_cast<int>(lse_col_grid));
+      }));
     } else {
       ok(timed(1, st, [&] {
         k_lse<T, D, kLseRW, kLseNW, false, false><<<lse_col_grid, kLseNW * kWave, 0, st>>>(q, ktil, hent, lse, lse_col,
@@ -114,8 +130,8 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     }
     if (ad) {
       ok(timed(11, st, [&] {
-        k_objective<><<<static_cast<unsigned>(s.BH), 256, 0, st>>>(lse, Nq, s.b2, ad->fprev, ad->stop_at, it, s.T,
-                                                                  ad->tol);
+        k_objective<><<<static_cast<unsigned>(s.BH), kObjThreads, 0, st>>>(lse, Nq, s.b2, ad->fprev, ad->stop_at, it,
+                                                                          s.T, ad->tol, ad->nstop_upto);
       }));
     }
     if (cols) {
@@ -123,7 +139,12 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
         if (first)
           k_aggregate_cols<T, D, cols_nw, true><<<cols_grid, cols_nw * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat,
                                                                                      beta, base);
-        else
+        else if (persist) {
+          auto kern = &k_aggregate_cols<T, D, cols_nw, false>;
+          const unsigned grid = persistent_grid(reinterpret_cast<const void*>(kern), cols_nw * kWave, 0, cols_grid);
+          kern<<<grid, cols_nw * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, base, sa, it, ns,
+                                                 static_cast<int>(cols_grid));
+        } else
           k_aggregate_cols<T, D, cols_nw, false><<<cols_grid, cols_nw * kWave, 0, st>>>(q, ktil, hent, lse, qhat,
                                                                                       beta, base, sa, it);
       }));
@@ -141,6 +162,20 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
         else
           k_aggregate<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
       }));
+    } else if (persist) {
+      ok(timed(2, st, [&] {
+        if (col_fits) {
+          auto kern = &k_aggregate_col<T, D, kAggRW, kAggNW, false>;
+          const unsigned grid = persistent_grid(reinterpret_cast<const void*>(kern), kAggNW * kWave, 0, agg_grid);
+          kern<<<grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg, sa, it, ns,
+                                                static_cast<int>(agg_grid));
+        } else {
+          auto kern = &k_aggregate<T, D, kAggRW, kAggNW, false>;
+          const unsigned grid = persistent_grid(reinterpret_cast<const void*>(kern), kAggNW * kWave, 0, agg_grid);
+          kern<<<grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg, sa, it, ns,
+                                                static_cast<int>(agg_grid));
+        }
+      }));
     } else {
       ok(timed(2, st, [&] {
         if (col_fits)
@@ -153,9 +188,13 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     }
     if (long_blocks) {
       ok(timed(3, st, [&] {
-        if (ad)
-          k_rstep_long_adaptive<T, D, kRlRW, kRlNW><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, bf.ktil, bf.hent,
-                                                                                      ad->stop_at, it, rl);
+        if (ad) {
+          auto kern = &k_rstep_long_adaptive<T, D, kRlRW, kRlNW>;
+          const unsigned grid =
+              persist ? persistent_grid(reinterpret_cast<const void*>(kern), kRlNW * kWave, 0, rl_grid) : rl_grid;
+          kern<<<grid, kRlNW * kWave, 0, st>>>(k, v, qhat, bf.ktil, bf.hent, ad->stop_at, it, rl,
+                                               ad->nstop_upto + (it - 1), static_cast<int>(rl_grid));
+        }
         else if (last)
           k_rstep_long<T, D, kRlRW, kRlNW, true><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, nullptr, nullptr,
                                                                                    uout, bf.rlse_of(it), rl);
@@ -165,8 +204,11 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
       }));
     } else if (ad) {
       ok(timed(3, st, [&] {
-        k_rstep_adaptive<T, D><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, bf.ktil, bf.hent, ad->stop_at, it,
-                                                                       rg);
+        // the heads that go on (next keys and entropies), then those that stop now (R V)
+        k_rstep_adaptive<T, D, false><<<r_grid, r_threads, r_lds_mid, st>>>(k, v, qhat, bf.ktil, bf.hent, ad->stop_at,
+                                                                            it, rg, ad->nstop_upto);
+        k_rstep_adaptive<T, D, true><<<r_grid, r_threads, r_lds_last, st>>>(k, v, qhat, bf.ktil, bf.hent, ad->stop_at,
+                                                                           it, rg, ad->nstop_upto);
       }));
     } else if (last) {
       ok(timed(3, st, [&] {

@@ -203,7 +203,9 @@ def test_kv_workspace_bytes():
 def test_adaptive_workspace_and_bad_arguments():
     shape = (1, 40, 21, 45, 80, 128, 945, 80, 4, 10, 0)
     nb = M.monarch_attn_adaptive_workspace_bytes(*shape)
-    assert nb == M.monarch_attn_workspace_bytes(*shape) + _align(40 * 8)
+    # the forward's workspace, then the previous objective per head (double)
+    # and the counts of heads stopped after each iteration (max_iters + 1 ints)
+    assert nb == M.monarch_attn_workspace_bytes(*shape) + _align(40 * 8) + _align(11 * 4)
     p = _train_ptrs(6)  # q k v out iters_used workspace
     base = (1, 2, 3, 30, 52, 128, 90, 52, 1, 10)
     lib = M.lib()
@@ -255,7 +257,7 @@ def test_kv_bwd_bad_arguments_rejected_before_any_gpu_call(kw, status):
 def test_adaptive_kv_workspace_and_bad_arguments():
     shape = (1, 40, 3, 21, 45, 80, 128, 945, 80, 1, 10, 0)
     nb = M.monarch_attn_adaptive_kv_workspace_bytes(*shape)
-    assert nb == M.monarch_attn_kv_workspace_bytes(*shape) + _align(40 * 8)
+    assert nb == M.monarch_attn_kv_workspace_bytes(*shape) + _align(40 * 8) + _align(11 * 4)
     p = _train_ptrs(6)  # q k v out iters_used workspace
     base = (1, 2, 1, 4, 3, 5, 64, 12, 5, 1, 10)
     lib = M.lib()
