@@ -54,6 +54,7 @@ constexpr int kAppRW = MONARCH_APP_RW, kAppNW = MONARCH_APP_NW;
 #define MONARCH_AGG_COL 1
 #endif
 
+
 // the R-step of long key blocks (b2 > kShortB2): rows a2 per workgroup
 #ifndef MONARCH_RL_RW
 #define MONARCH_RL_RW 2

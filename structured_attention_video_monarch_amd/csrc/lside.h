@@ -679,6 +679,9 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
   }
   const typename E::frag ones = E::ones();
   __syncthreads();
+  // a wave whose key tiles all lie past b1 has nothing to compute or store
+  // (it took its share of the column's DMA above)
+  if (cb * CB + wave * RW * 16 >= p.b1) return;
 
   const int nblk = (nrows + 31) / 32;
   for (int blk = 0; blk < nblk; ++blk) {
