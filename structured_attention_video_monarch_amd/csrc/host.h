@@ -53,6 +53,15 @@ constexpr int kAppRW = MONARCH_APP_RW, kAppNW = MONARCH_APP_NW;
 #ifndef MONARCH_AGG_COL
 #define MONARCH_AGG_COL 1
 #endif
+#ifndef MONARCH_AGG_SCHED_BARRIER
+#define MONARCH_AGG_SCHED_BARRIER 1
+#endif
+#ifndef MONARCH_APP_SCHED_BARRIER
+#define MONARCH_APP_SCHED_BARRIER 1
+#endif
+#ifndef MONARCH_LSE_SCHED_BARRIER
+#define MONARCH_LSE_SCHED_BARRIER 1
+#endif
 
 
 // the R-step of long key blocks (b2 > kShortB2): rows a2 per workgroup

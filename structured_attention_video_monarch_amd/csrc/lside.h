@@ -381,7 +381,9 @@ __device__ __forceinline__ void k_lse_item(const T* __restrict__ q,
 #pragma unroll
         for (int j = 0; j < 8; ++j) bias[j] = sH[cur][k0 + 8 * G + j];
       }
+#if MONARCH_LSE_SCHED_BARRIER
       __builtin_amdgcn_sched_barrier(0);
+#endif
       f32x4 S[2][RW];
       logits<T, KS, RW>(S, a, bq);
 #pragma unroll
@@ -664,6 +666,14 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
     for (int s = 0; s < KS; ++s) {
       const int col = s * 32 + 8 * G;
       bk[rt][s] = (c1 < p.b1 && col < D) ? E::load(ks.k + c1 * ks.kstride + col) : E::zero();
+      // PRE: the keys negated (a sign flip of each bf16), so that the product
+      // starts from +lse and ends at lse - x: the exponent's negation is then
+      // a free input modifier of v_exp_f32, not one instruction per lse value
+      if constexpr (PRE) {
+        uint4 u = __builtin_bit_cast(uint4, bk[rt][s]);
+        u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+        bk[rt][s] = __builtin_bit_cast(typename E::frag, u);
+      }
     }
     bias[rt] = BCAST ? 0.0f : (c1 < p.b1 ? ks.bias(c1, p.b1) : 0.0f);
   }
@@ -683,8 +693,14 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
   // (it took its share of the column's DMA above)
   if (cb * CB + wave * RW * 16 >= p.b1) return;
 
+  // the column's 32-row blocks, unrolled: every LDS address is a per-lane
+  // offset plus an immediate, the accumulators start from the first block's
+  // products, and only the last block masks rows
   const int nblk = (nrows + 31) / 32;
-  for (int blk = 0; blk < nblk; ++blk) {
+  constexpr int kMaxBlk = kColRows / 32;
+#pragma unroll
+  for (int blk = 0; blk < kMaxBlk; ++blk) {
+    if (blk >= nblk) break;
     const int st = blk / kHalves, k0 = 32 * (blk % kHalves);
     const int r0 = 32 * blk;
     const bool tail = r0 + 32 > nrows;
@@ -695,15 +711,17 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
     float lr[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) lr[j] = sL[st][k0 + 8 * G + j];
+#if MONARCH_AGG_SCHED_BARRIER
     __builtin_amdgcn_sched_barrier(0);
+#endif
     f32x4 S[2][RW];
     if constexpr (PRE) {
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
-        S[0][rt] = f32x4{-lr[0], -lr[1], -lr[2], -lr[3]};
-        S[1][rt] = f32x4{-lr[4], -lr[5], -lr[6], -lr[7]};
+        S[0][rt] = f32x4{lr[0], lr[1], lr[2], lr[3]};
+        S[1][rt] = f32x4{lr[4], lr[5], lr[6], lr[7]};
       }
-      logits_onto<T, KS, RW>(S, a, bk);
+      logits_onto<T, KS, RW>(S, a, bk);  // lse - x (negated keys)
     } else {
       logits<T, KS, RW>(S, a, bk);
     }
@@ -713,11 +731,12 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
       float w[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        w[j] = PRE ? fast_exp2(S[j >> 2][rt][j & 3])
+        w[j] = PRE ? fast_exp2(-S[j >> 2][rt][j & 3])
                    : fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? -lr[j] : bias[rt] - lr[j]));
       if (tail) {
+        const int lim = nrows - r0 - 8 * G;  // rows of this lane group still in the tile
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = r0 + 8 * G + j < nrows ? w[j] : 0.0f;
+        for (int j = 0; j < 8; ++j) w[j] = j < lim ? w[j] : 0.0f;
       }
       pf[rt] = E::pack(w);
       accb[rt] = E::mma(ones, pf[rt], accb[rt]);
@@ -852,7 +871,9 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
 #pragma unroll
         for (int j = 0; j < 8; ++j) bias[j] = cH[k0 + 8 * G + j];
       }
+#if MONARCH_APP_SCHED_BARRIER
       __builtin_amdgcn_sched_barrier(0);
+#endif
       f32x4 S[2][RW];
       if constexpr (PRE) {
 #pragma unroll
