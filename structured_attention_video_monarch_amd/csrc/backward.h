@@ -431,6 +431,25 @@ constexpr int kRbSingle = 0, kRbLast = 1, kRbMid = 2, kRbFirst = 3;
 #define MONARCH_BRB_RW 1
 #endif
 
+// Row j0 + r (0 <= r < 64; past `total`, the last row) of the sequence of
+// t*b2 rows (g, a2) of one key block: rbase + (j / b2) * tstride + j % b2.
+// j0 is the same for the whole wave, so its split into (g, a2) is scalar
+// work; the lane's offset r then wraps past b2 at most twice when b2 >= 32
+// (a division per lane only for shorter key blocks).
+__device__ inline long long seq_row(long long rbase, long long tstride, int j0, int r, int total, int b2) {
+  if (j0 + r >= total) r = total - 1 - j0;
+  const int g0 = j0 / b2;
+  int a = j0 - g0 * b2 + r, g = g0;
+  if (b2 >= 32) {
+    if (a >= b2) { a -= b2; ++g; }
+    if (a >= b2) { a -= b2; ++g; }
+  } else {
+    g += a / b2;
+    a %= b2;
+  }
+  return rbase + static_cast<long long>(g) * tstride + a;
+}
+
 // Global -> LDS DMA of 32 rows j0 .. j0+31 of the sequence of t*b2 rows
 // (g, a2) of one key block: row j lives at rbase + (j / b2) * tstride + j % b2
 // (rows past `total` repeat the last row).
@@ -447,9 +466,7 @@ __device__ inline void dma_rows32(T* tile, const T* src, long long rbase, int j0
     const int c = ((byte % ROWB) / 16) ^ Tile<T, DK>::swz(r);
     int col = c * V;
     if (col >= D) col -= D;
-    int j = j0 + r;
-    if (j >= total) j = total - 1;
-    const long long row = rbase + static_cast<long long>(j / b2) * tstride + j % b2;
+    const long long row = seq_row(rbase, tstride, j0, r, total, b2);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row * D + col),
                                      (__attribute__((address_space(3))) void*)(tile + ci * (1024 / static_cast<int>(sizeof(T)))),
                                      16, 0, 0);
@@ -459,9 +476,7 @@ __device__ inline void dma_rows32(T* tile, const T* src, long long rbase, int j0
 // The same for one float per row (64 lanes, rows j0 .. j0+63).
 __device__ inline void dma_rowstat(float* dst, const float* src, long long rbase, int j0, int total, int b2,
                                    long long tstride) {
-  int j = j0 + lane_id();
-  if (j >= total) j = total - 1;
-  const long long row = rbase + static_cast<long long>(j / b2) * tstride + j % b2;
+  const long long row = seq_row(rbase, tstride, j0, lane_id(), total, b2);
   __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row),
                                    (__attribute__((address_space(3))) void*)(dst), 4, 0, 0);
 }
@@ -560,18 +575,26 @@ __global__ __launch_bounds__(RWK == 1 || RWK != MONARCH_BRB_RW ? 512 : 256) void
       else
         logits<T, KS, RW>(DR, a, bv2);  // <dU, v>
       typename E::frag rf[RW], zf[RW];
+      const bool tail = j0 + 32 > total;  // rows past the sequence repeat the last row: weight 0
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         float r[8], z[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const bool ok = j0 + 8 * G + jj < total;  // rows past the sequence repeat the last row: weight 0
           const float xl = Z[jj >> 2][rt][jj & 3] * p.c - sLR[cur][j][8 * G + jj];  // log2 R
           const float rr = fast_exp2(xl);
           float dr = DR[jj >> 2][rt][jj & 3];
           if (MID) dr -= sDh[MID ? cur : 0][MID ? j : 0][8 * G + jj] * kLn2 * xl;
-          r[jj] = ok ? rr : 0.0f;
-          z[jj] = ok ? rr * (dr - sRh[cur][j][8 * G + jj]) : 0.0f;
+          r[jj] = rr;
+          z[jj] = rr * (dr - sRh[cur][j][8 * G + jj]);
+        }
+        if (tail) {
+          const int lim = total - j0 - 8 * G;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            r[jj] = jj < lim ? r[jj] : 0.0f;
+            z[jj] = jj < lim ? z[jj] : 0.0f;
+          }
         }
         rf[rt] = E::pack(r);
         zf[rt] = E::pack(z);
