@@ -608,11 +608,18 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate(cons
 // Same result as k_aggregate for tiles of at most kColRows rows: the whole q
 // column of the tile and its log-sum-exps are copied to LDS once (DMA), then
 // all its 32-row blocks run with no further barrier or wait.
+// ALLK: one work item is the whole tile column (bh, g, a2) and each wave takes
+// the key tiles wave, wave + NW, ... of all b1 key blocks, so the column is
+// copied once for every key block instead of once per 128 keys; otherwise an
+// item is (bh, g, a2, 128 key blocks), one key tile per wave.
 constexpr int kColRows = 256;
+#ifndef MONARCH_AGG_ALLK
+#define MONARCH_AGG_ALLK 1
+#endif
 
 // PRE: block-mean keys pre-scaled by c (see k_lse); each logit product starts
 // from -lse of its row.
-template <typename T, int D, int RW, int NW, bool BCAST, bool PRE = false>
+template <typename T, int D, int RW, int NW, bool BCAST, bool PRE = false, bool ALLK = false>
 __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
                                                                                 const T* __restrict__ kt,
                                                                                 const float* __restrict__ h2,
@@ -624,7 +631,6 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
-  constexpr int CB = NW * RW * 16;
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
   using Dma = TileDma<T, D, DK, kStep, NW>;
@@ -657,108 +663,113 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
     if (wave == NW - 1) dma_floats64(sL[st], lh + n_first, p.b2, nvalid);
   }
 
-  typename E::frag bk[RW][KS];
-  float bias[RW];
-#pragma unroll
-  for (int rt = 0; rt < RW; ++rt) {
-    const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int col = s * 32 + 8 * G;
-      bk[rt][s] = (c1 < p.b1 && col < D) ? E::load(ks.k + c1 * ks.kstride + col) : E::zero();
-      // PRE: the keys negated (a sign flip of each bf16), so that the product
-      // starts from +lse and ends at lse - x: the exponent's negation is then
-      // a free input modifier of v_exp_f32, not one instruction per lse value
-      if constexpr (PRE) {
-        uint4 u = __builtin_bit_cast(uint4, bk[rt][s]);
-        u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
-        bk[rt][s] = __builtin_bit_cast(typename E::frag, u);
-      }
-    }
-    bias[rt] = BCAST ? 0.0f : (c1 < p.b1 ? ks.bias(c1, p.b1) : 0.0f);
-  }
-  f32x4 acc[NACC][2][RW];
-  f32x4 accb[RW];
-#pragma unroll
-  for (int rt = 0; rt < RW; ++rt) {
-    accb[rt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int dp = 0; dp < NACC; ++dp)
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
-  }
   const typename E::frag ones = E::ones();
   __syncthreads();
-  // a wave whose key tiles all lie past b1 has nothing to compute or store
-  // (it took its share of the column's DMA above)
-  if (cb * CB + wave * RW * 16 >= p.b1) return;
-
-  // the column's 32-row blocks, unrolled: every LDS address is a per-lane
-  // offset plus an immediate, the accumulators start from the first block's
-  // products, and only the last block masks rows
+  // key tiles of RW*16 key blocks: this wave's one (cb * NW + wave), or with
+  // ALLK every NW-th; a wave whose key tiles all lie past b1 has nothing to
+  // compute or store (it took its share of the column's DMA above)
+  const int nkt = (p.b1 + RW * 16 - 1) / (RW * 16);
+  const int kt0 = ALLK ? wave : cb * NW + wave;
+  const int kt_end = ALLK ? nkt : (kt0 + 1 < nkt ? kt0 + 1 : nkt);
   const int nblk = (nrows + 31) / 32;
   constexpr int kMaxBlk = kColRows / 32;
-#pragma unroll
-  for (int blk = 0; blk < kMaxBlk; ++blk) {
-    if (blk >= nblk) break;
-    const int st = blk / kHalves, k0 = 32 * (blk % kHalves);
-    const int r0 = 32 * blk;
-    const bool tail = r0 + 32 > nrows;
-    typename E::frag a[KS][2];
-    typename E::frag v[NACC][2];
-    load_rows<T, DK, KS>(a, sQ[st], k0, l16, G);
-    load_cols<T, D, DK, NACC>(v, sQ[st], k0);
-    float lr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lr[j] = sL[st][k0 + 8 * G + j];
-#if MONARCH_AGG_SCHED_BARRIER
-    __builtin_amdgcn_sched_barrier(0);
-#endif
-    f32x4 S[2][RW];
-    if constexpr (PRE) {
-#pragma unroll
-      for (int rt = 0; rt < RW; ++rt) {
-        S[0][rt] = f32x4{lr[0], lr[1], lr[2], lr[3]};
-        S[1][rt] = f32x4{lr[4], lr[5], lr[6], lr[7]};
-      }
-      logits_onto<T, KS, RW>(S, a, bk);  // lse - x (negated keys)
-    } else {
-      logits<T, KS, RW>(S, a, bk);
-    }
-    typename E::frag pf[RW];
+  for (int ktile = kt0; ktile < kt_end; ktile += NW) {
+    const int c1base = ktile * RW * 16;
+    typename E::frag bk[RW][KS];
+    float bias[RW];
 #pragma unroll
     for (int rt = 0; rt < RW; ++rt) {
-      float w[8];
+      const int c1 = c1base + rt * 16 + l16;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        w[j] = PRE ? fast_exp2(-S[j >> 2][rt][j & 3])
-                   : fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? -lr[j] : bias[rt] - lr[j]));
-      if (tail) {
-        const int lim = nrows - r0 - 8 * G;  // rows of this lane group still in the tile
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = j < lim ? w[j] : 0.0f;
+      for (int s = 0; s < KS; ++s) {
+        const int col = s * 32 + 8 * G;
+        bk[rt][s] = (c1 < p.b1 && col < D) ? E::load(ks.k + c1 * ks.kstride + col) : E::zero();
+        // PRE: the keys negated (a sign flip of each bf16), so that the product
+        // starts from +lse and ends at lse - x: the exponent's negation is then
+        // a free input modifier of v_exp_f32, not one instruction per lse value
+        if constexpr (PRE) {
+          uint4 u = __builtin_bit_cast(uint4, bk[rt][s]);
+          u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+          bk[rt][s] = __builtin_bit_cast(typename E::frag, u);
+        }
       }
-      pf[rt] = E::pack(w);
-      accb[rt] = E::mma(ones, pf[rt], accb[rt]);
+      bias[rt] = BCAST ? 0.0f : (c1 < p.b1 ? ks.bias(c1, p.b1) : 0.0f);
     }
-    weighted_sum<T, D, NACC, RW>(acc, v, pf);
-  }
+    f32x4 acc[NACC][2][RW];
+    f32x4 accb[RW];
+#pragma unroll
+    for (int rt = 0; rt < RW; ++rt) {
+      accb[rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
+    }
+
+    // the column's 32-row blocks, unrolled: every LDS address is a per-lane
+    // offset plus an immediate, and only the last block masks rows
+#pragma unroll
+    for (int blk = 0; blk < kMaxBlk; ++blk) {
+      if (blk >= nblk) break;
+      const int st = blk / kHalves, k0 = 32 * (blk % kHalves);
+      const int r0 = 32 * blk;
+      const bool tail = r0 + 32 > nrows;
+      typename E::frag a[KS][2];
+      typename E::frag v[NACC][2];
+      load_rows<T, DK, KS>(a, sQ[st], k0, l16, G);
+      load_cols<T, D, DK, NACC>(v, sQ[st], k0);
+      float lr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lr[j] = sL[st][k0 + 8 * G + j];
+#if MONARCH_AGG_SCHED_BARRIER
+      __builtin_amdgcn_sched_barrier(0);
+#endif
+      f32x4 S[2][RW];
+      if constexpr (PRE) {
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) {
+          S[0][rt] = f32x4{lr[0], lr[1], lr[2], lr[3]};
+          S[1][rt] = f32x4{lr[4], lr[5], lr[6], lr[7]};
+        }
+        logits_onto<T, KS, RW>(S, a, bk);  // lse - x (negated keys)
+      } else {
+        logits<T, KS, RW>(S, a, bk);
+      }
+      typename E::frag pf[RW];
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          w[j] = PRE ? fast_exp2(-S[j >> 2][rt][j & 3])
+                     : fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? -lr[j] : bias[rt] - lr[j]));
+        if (tail) {
+          const int lim = nrows - r0 - 8 * G;  // rows of this lane group still in the tile
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = j < lim ? w[j] : 0.0f;
+        }
+        pf[rt] = E::pack(w);
+        accb[rt] = E::mma(ones, pf[rt], accb[rt]);
+      }
+      weighted_sum<T, D, NACC, RW>(acc, v, pf);
+    }
 
 #pragma unroll
-  for (int rt = 0; rt < RW; ++rt) {
-    const float b = accb[rt][0];
-    const float inv = b > 0.0f ? 1.0f / b : 0.0f;
-    const int c1 = cb * CB + (wave * RW + rt) * 16 + l16;
-    if (c1 >= p.b1) continue;
-    const long long row = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
-    store_rows<T, D, NACC, RW>(qhat + row * D, acc, rt, inv, G);
-    if (beta_out && G == 0) beta_out[row] = b;
+    for (int rt = 0; rt < RW; ++rt) {
+      const float b = accb[rt][0];
+      const float inv = b > 0.0f ? 1.0f / b : 0.0f;
+      const int c1 = c1base + rt * 16 + l16;
+      if (c1 >= p.b1) continue;
+      const long long row = ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
+      store_rows<T, D, NACC, RW>(qhat + row * D, acc, rt, inv, G);
+      if (beta_out && G == 0) beta_out[row] = b;
+    }
   }
 }
 
 // Work items k_aggregate_col_item, one per workgroup, or looped over by fewer workgroups
 // (nitems > 0); nothing runs once every head has stopped iterating (nstop).
-template <typename T, int D, int RW, int NW, bool BCAST, bool PRE = false>
+template <typename T, int D, int RW, int NW, bool BCAST, bool PRE = false, bool ALLK = MONARCH_AGG_ALLK>
 __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(const T* __restrict__ q,
                                                                                 const T* __restrict__ kt,
                                                                                 const float* __restrict__ h2,
@@ -772,7 +783,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_AGG_MINW) void k_aggregate_col(
   const int wn = nitems > 0 ? nitems : static_cast<int>(gridDim.x);
   for (int wi = blockIdx.x; wi < wn; wi += gridDim.x) {
     if (wi != static_cast<int>(blockIdx.x)) __syncthreads();
-    k_aggregate_col_item<T, D, RW, NW, BCAST, PRE>(q, kt, h2, lse, qhat, beta_out, p, stop_at, it, wi, wn);
+    k_aggregate_col_item<T, D, RW, NW, BCAST, PRE, ALLK>(q, kt, h2, lse, qhat, beta_out, p, stop_at, it, wi, wn);
   }
 }
 

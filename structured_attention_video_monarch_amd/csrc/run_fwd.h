@@ -53,6 +53,10 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
   const unsigned lse_contig_grid = static_cast<unsigned>(s.BH * lse_contig.nrb);
   const unsigned app_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * app.nrb);
   const unsigned agg_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * agg.nrb);
+  // k_aggregate_col: a whole tile column per work item (every key tile)
+  LGeom aggc = agg;
+  if (MONARCH_AGG_ALLK) aggc.nrb = 1;
+  const unsigned aggc_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * aggc.nrb);
   // whole tile column resident in LDS when it is short enough (bf16 only:
   // the f32 column would not fit)
   const bool col_fits = MONARCH_AGG_COL && sizeof(T) == 2 && ngmax <= kColRows;
@@ -152,13 +156,13 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
       ok(timed(2, st, [&] {
         if constexpr (sizeof(T) == 2) {
           if (pre) {
-            k_aggregate_col<T, D, kAggRW, kAggNW, true, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse,
-                                                                                                qhat, beta, agg);
+            k_aggregate_col<T, D, kAggRW, kAggNW, true, true><<<aggc_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse,
+                                                                                                 qhat, beta, aggc);
             return;
           }
         }
         if (col_fits)
-          k_aggregate_col<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
+          k_aggregate_col<T, D, kAggRW, kAggNW, true><<<aggc_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, aggc);
         else
           k_aggregate<T, D, kAggRW, kAggNW, true><<<agg_grid, kAggNW * kWave, 0, st>>>(q, kbar, nullptr, lse, qhat, beta, agg);
       }));
@@ -166,9 +170,9 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
       ok(timed(2, st, [&] {
         if (col_fits) {
           auto kern = &k_aggregate_col<T, D, kAggRW, kAggNW, false>;
-          const unsigned grid = persistent_grid(reinterpret_cast<const void*>(kern), kAggNW * kWave, 0, agg_grid);
-          kern<<<grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg, sa, it, ns,
-                                                static_cast<int>(agg_grid));
+          const unsigned grid = persistent_grid(reinterpret_cast<const void*>(kern), kAggNW * kWave, 0, aggc_grid);
+          kern<<<grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, aggc, sa, it, ns,
+                                                static_cast<int>(aggc_grid));
         } else {
           auto kern = &k_aggregate<T, D, kAggRW, kAggNW, false>;
           const unsigned grid = persistent_grid(reinterpret_cast<const void*>(kern), kAggNW * kWave, 0, agg_grid);
@@ -179,8 +183,8 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
     } else {
       ok(timed(2, st, [&] {
         if (col_fits)
-          k_aggregate_col<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg,
-                                                                                          sa, it);
+          k_aggregate_col<T, D, kAggRW, kAggNW, false><<<aggc_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta,
+                                                                                           aggc, sa, it);
         else
           k_aggregate<T, D, kAggRW, kAggNW, false><<<agg_grid, kAggNW * kWave, 0, st>>>(q, ktil, hent, lse, qhat, beta, agg,
                                                                                       sa, it);
