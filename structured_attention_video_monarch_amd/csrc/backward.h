@@ -219,6 +219,115 @@ __global__ __launch_bounds__(NW * kWave) void kb_du(const T* __restrict__ q, con
   }
 }
 
+// ------------------------------------------------------------- kb_du_col --
+// Same result as kb_du for tiles of at most kColRows rows (bf16): one
+// workgroup owns the whole tile column (bh, g, a2); its q and dy rows and
+// log-sum-exps are copied to LDS once, and each wave then takes the key tiles
+// wave, wave + NW, ... (RW*16 key blocks each) of all b1 key blocks with no
+// further barrier: the column is read once for every key block instead of
+// once per CB of them.
+template <typename T, int D, int RW, int NW, bool BCAST = true>
+__global__ __launch_bounds__(NW * kWave) void kb_du_col(const T* __restrict__ q, const T* __restrict__ dy,
+                                                        const T* __restrict__ kt, const float* __restrict__ h2,
+                                                        const float* __restrict__ lse, T* __restrict__ du, LGeom p) {
+  using E = Elem<T>;
+  constexpr int DK = D < 32 ? 32 : D;
+  constexpr int KS = DK / 32;
+  constexpr int NDP = D / 32;
+  constexpr int NACC = NDP > 0 ? NDP : 1;
+  using Dma = TileDma<T, D, DK, kStep, NW>;
+  constexpr int NSTEP = kColRows / kStep;
+  __shared__ __align__(16) T sQ[NSTEP][kStep * DK];
+  __shared__ __align__(16) T sY[NSTEP][kStep * DK];
+  __shared__ __align__(16) float sL[NSTEP][kStep];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int a2 = logical % p.b2;
+  const int rest = logical / p.b2;
+  const int g = rest % p.t;
+  const int bh = rest / p.t;
+  const int lo = tile_lo(g, p.b1r, p.t), hi = tile_lo(g + 1, p.b1r, p.t);
+  const int nrows = hi - lo;
+  const int nst = (nrows + kStep - 1) / kStep;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int l16 = lane & 15, G = lane >> 4;
+  const long long hoff = static_cast<long long>(bh) * p.N;
+  const long long qstride = static_cast<long long>(p.b2) * D;
+  const long long gbase = (static_cast<long long>(bh) * p.t + g) * p.b1;  // (bh, g, c1 = 0)
+
+  for (int st = 0; st < nst; ++st) {
+    const long long n_first = hoff + static_cast<long long>(lo + st * kStep) * p.b2 + a2;
+    const int nvalid = nrows - st * kStep;
+    Dma::issue(sQ[st], q + n_first * D, qstride, nvalid);
+    Dma::issue(sY[st], dy + n_first * D, qstride, nvalid);
+    if (wave == NW - 1) dma_floats64(sL[st], lse + n_first, p.b2, nvalid);
+  }
+  __syncthreads();
+
+  const int nkt = (p.b1 + RW * 16 - 1) / (RW * 16);
+  const int nblk = (nrows + 31) / 32;
+  constexpr int kMaxBlk = kColRows / 32;
+  for (int ktile = wave; ktile < nkt; ktile += NW) {
+    const int c1base = ktile * RW * 16;
+    typename E::frag bk[RW][KS];
+    float hb[RW];  // entropy bias of the lane's key block
+#pragma unroll
+    for (int rt = 0; rt < RW; ++rt) {
+      const int c1 = c1base + rt * 16 + l16;
+      const long long krow = BCAST ? static_cast<long long>(bh) * p.b1 + c1 : (gbase + c1) * p.b2 + a2;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int col = s * 32 + 8 * G;
+        bk[rt][s] = (c1 < p.b1 && col < D) ? E::load(kt + krow * D + col) : E::zero();
+      }
+      hb[rt] = (BCAST || c1 >= p.b1) ? 0.0f : h2[krow];
+    }
+    f32x4 acc[NACC][2][RW];
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) acc[dp][0][rt] = acc[dp][1][rt] = f32x4{0, 0, 0, 0};
+
+#pragma unroll
+    for (int blk = 0; blk < kMaxBlk; ++blk) {
+      if (blk >= nblk) break;
+      const int st = blk / kHalves, k0 = 32 * (blk % kHalves);
+      const int r0 = 32 * blk;
+      const bool tail = r0 + 32 > nrows;
+      typename E::frag a[KS][2];
+      load_rows<T, DK, KS>(a, sQ[st], k0, l16, G);
+      float lr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lr[j] = sL[st][k0 + 8 * G + j];
+      f32x4 S[2][RW];
+      logits<T, KS, RW>(S, a, bk);
+      typename E::frag pf[RW];
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, hb[rt] - lr[j]));
+        if (tail) {
+          const int lim = nrows - r0 - 8 * G;  // rows of this lane group still in the tile
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = j < lim ? w[j] : 0.0f;
+        }
+        pf[rt] = E::pack(w);
+      }
+      typename E::frag vv[NACC][2];
+      load_cols<T, D, DK, NACC>(vv, sY[st], k0);
+      weighted_sum<T, D, NACC, RW>(acc, vv, pf);
+    }
+
+#pragma unroll
+    for (int rt = 0; rt < RW; ++rt) {
+      const int c1 = c1base + rt * 16 + l16;
+      if (c1 >= p.b1) continue;
+      store_rows<T, D, NACC, RW>(du + ((gbase + c1) * p.b2 + a2) * D, acc, rt, 1.0f, G);
+    }
+  }
+}
+
 // ------------------------------------------------------------- kb_rside_a --
 // Key-block pass, part 1 (as the forward R-step): one workgroup per (bh, c1)
 // with ceil(b2/16) waves; K and V of the block are copied to LDS once, each

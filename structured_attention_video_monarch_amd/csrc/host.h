@@ -394,6 +394,17 @@ template <typename T> struct BwdCfg;
 #ifndef MONARCH_BDU_NW
 #define MONARCH_BDU_NW 8
 #endif
+// kb_du with the whole tile column in LDS (bf16, at most kColRows rows per
+// tile): rows per wave / 16 and waves per workgroup
+#ifndef MONARCH_BDU_COL
+#define MONARCH_BDU_COL 1
+#endif
+#ifndef MONARCH_BDUC_RW
+#define MONARCH_BDUC_RW 2
+#endif
+#ifndef MONARCH_BDUC_NW
+#define MONARCH_BDUC_NW 8
+#endif
 #ifndef MONARCH_BGM_RW
 #define MONARCH_BGM_RW 4
 #endif

@@ -54,8 +54,22 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   constexpr int cols_nw = 4;
   const bool cols = s.b1 <= kColsRows && ngmax <= kColsRows;
   const unsigned cols_grid = static_cast<unsigned>(s.BH * s.t * ((s.b2 + cols_nw - 1) / cols_nw));
-  // dU = L^T dy per tile column (L of the last L-step)
+  // dU = L^T dy per tile column (L of the last L-step); bf16 tiles of at
+  // most kColRows rows: the whole column resident in LDS, one workgroup each
+  const bool du_col = MONARCH_BDU_COL && sizeof(T) == 2 && !cols && ngmax <= kColRows;
+  const unsigned du_col_grid = static_cast<unsigned>(s.BH * s.t * s.b2);
   ok(timed(5, st, [&] {
+    if constexpr (sizeof(T) == 2) {
+      if (du_col) {
+        if (T_ == 1)
+          kb_du_col<T, D, MONARCH_BDUC_RW, MONARCH_BDUC_NW, true><<<du_col_grid, MONARCH_BDUC_NW * kWave, 0, st>>>(
+              q, dout, bf.kbar, nullptr, bf.lse_of(1), du, col_geom);
+        else
+          kb_du_col<T, D, MONARCH_BDUC_RW, MONARCH_BDUC_NW, false><<<du_col_grid, MONARCH_BDUC_NW * kWave, 0, st>>>(
+              q, dout, keys_of(T_), ent_of(T_), bf.lse_of(T_), du, col_geom);
+        return;
+      }
+    }
     if (cols && T_ == 1)
       kb_du_cols<T, D, cols_nw, true><<<cols_grid, cols_nw * kWave, 0, st>>>(q, dout, bf.kbar, nullptr, bf.lse_of(1),
                                                                              du, col_geom);
