@@ -371,9 +371,16 @@ __device__ inline void dma_block(T* tile, const T* src, int rows, int nvalid, in
 #ifndef MONARCH_BRA_TB
 #define MONARCH_BRA_TB 2
 #endif
+// minimum waves per SIMD the register allocator must allow
+#ifndef MONARCH_BRA_MINW
+#define MONARCH_BRA_MINW 1
+#endif
+#ifndef MONARCH_BRB_MINW
+#define MONARCH_BRB_MINW 1
+#endif
 
 template <typename T, int D, int NCP, bool MID = false>
-__global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const T* __restrict__ v,
+__global__ __launch_bounds__(512, MONARCH_BRA_MINW) void kb_rside_a(const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ qhat, const T* __restrict__ du,
                                                   const float* __restrict__ dh,
                                                   const float* __restrict__ beta, T* __restrict__ gq,
@@ -499,8 +506,13 @@ __global__ __launch_bounds__(512) void kb_rside_a(const T* __restrict__ k, const
         acc[dp][0][0] *= sc;
         acc[dp][1][0] *= sc;
       }
-      // e = <G, Qh> with the rounded Qh the forward used
-      float e = dot_acc_row<T, D, NACC, 1>(qhat + (row_ok ? row : 0) * D, acc, 0, G);
+      // e = <G, Qh> with the rounded Qh the forward used (held in bq: its
+      // lane slots are the accumulator's d positions)
+      float e;
+      if constexpr (D >= 32)
+        e = dot_acc_frags<T, NACC, 1>(bq[gi], acc, 0);
+      else
+        e = dot_acc_row<T, D, NACC, 1>(qhat + (row_ok ? row : 0) * D, acc, 0, G);
       e += __shfl_xor(e, 16);
       e += __shfl_xor(e, 32);
       if (row_ok) {
@@ -591,7 +603,7 @@ __device__ inline void dma_rowstat(float* dst, const float* src, long long rbase
 }
 
 template <typename T, int D, int MODE = kRbSingle, int RWK = MONARCH_BRB_RW>
-__global__ __launch_bounds__(RWK == 1 || RWK != MONARCH_BRB_RW ? 512 : 256) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
+__global__ __launch_bounds__(RWK == 1 || RWK != MONARCH_BRB_RW ? 512 : 256, MONARCH_BRB_MINW) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ qhat, const T* __restrict__ du,
                                                   const float* __restrict__ lser, const float* __restrict__ rho,
                                                   const float* __restrict__ dh,
