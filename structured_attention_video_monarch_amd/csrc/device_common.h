@@ -240,17 +240,27 @@ struct TileDma {
   static constexpr int ROWB = DK * static_cast<int>(sizeof(T));
   static constexpr int NINS = ROWS * ROWB / 1024;
   static_assert(NINS * 1024 == ROWS * ROWB, "tile must be a whole number of KiB");
+  // The source offset of a lane within the tile fits 32 bits (ROWS rows of
+  // at most kMaxB2 * 128 elements), so it is formed in 32-bit arithmetic and
+  // added to the wave-uniform base once: the load then takes a scalar base
+  // and a 32-bit lane offset, with no 64-bit multiply per lane.
   __device__ static inline void issue(T* tile, const T* g, long long rstride, int nvalid) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const unsigned rs = static_cast<unsigned>(rstride);
+    const char* gb = reinterpret_cast<const char*>(g);
 #pragma unroll
-    for (int ci = wave; ci < NINS; ci += NW) {
+    for (int i = 0; i < (NINS + NW - 1) / NW; ++i) {
+      const int ci = wave + i * NW;
+      if (NINS % NW != 0 && ci >= NINS) break;
       const int byte = ci * 1024 + 16 * lane;
       const int r = byte / ROWB;
       const int c = ((byte % ROWB) / 16) ^ Tile<T, DK>::swz(r);  // logical chunk at this position
       int col = c * V;
       if (col >= D) col -= D;
-      const int rr = r < nvalid ? r : nvalid - 1;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g + rr * rstride + col),
+      const unsigned rr = static_cast<unsigned>(r < nvalid ? r : nvalid - 1);
+      const unsigned off = (rr * rs + static_cast<unsigned>(col)) * static_cast<unsigned>(sizeof(T));
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(gb + off),
                                        (__attribute__((address_space(3))) void*)(tile + ci * (1024 / static_cast<int>(sizeof(T)))),
                                        16, 0, 0);
     }
@@ -261,8 +271,9 @@ struct TileDma {
 // dst[l] = src[min(l, nvalid - 1) * stride].
 __device__ inline void dma_floats64(float* dst, const float* src, long long stride, int nvalid) {
   const int lane = threadIdx.x & 63;
-  const int rr = lane < nvalid ? lane : nvalid - 1;
-  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + rr * stride),
+  const unsigned rr = static_cast<unsigned>(lane < nvalid ? lane : nvalid - 1);
+  const unsigned off = rr * static_cast<unsigned>(stride) * 4u;  // < 2^32: 64 rows of a stride <= kMaxB2
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(reinterpret_cast<const char*>(src) + off),
                                    (__attribute__((address_space(3))) void*)(dst), 4, 0, 0);
 }
 
