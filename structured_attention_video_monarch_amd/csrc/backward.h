@@ -557,7 +557,9 @@ constexpr int kRbSingle = 0, kRbLast = 1, kRbMid = 2, kRbFirst = 3;
 // j0 is the same for the whole wave, so its split into (g, a2) is scalar
 // work; the lane's offset r then wraps past b2 at most twice when b2 >= 32
 // (a division per lane only for shorter key blocks).
-__device__ inline long long seq_row(long long rbase, long long tstride, int j0, int r, int total, int b2) {
+// Row of the sequence position j0 + r relative to rbase: g * tstride + a,
+// below t*N < 2^31 (the shape envelope).
+__device__ inline unsigned seq_row_rel(long long tstride, int j0, int r, int total, int b2) {
   if (j0 + r >= total) r = total - 1 - j0;
   const int g0 = j0 / b2;
   int a = j0 - g0 * b2 + r, g = g0;
@@ -568,7 +570,7 @@ __device__ inline long long seq_row(long long rbase, long long tstride, int j0, 
     g += a / b2;
     a %= b2;
   }
-  return rbase + static_cast<long long>(g) * tstride + a;
+  return static_cast<unsigned>(g) * static_cast<unsigned>(tstride) + static_cast<unsigned>(a);
 }
 
 // Global -> LDS DMA of 32 rows j0 .. j0+31 of the sequence of t*b2 rows
@@ -580,15 +582,20 @@ __device__ inline void dma_rows32(T* tile, const T* src, long long rbase, int j0
   constexpr int V = Elem<T>::kVec;
   constexpr int ROWB = DK * static_cast<int>(sizeof(T));
   constexpr int NINS = 32 * ROWB / 1024;
-  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave)), lane = lane_id();
   for (int ci = wave; ci < NINS; ci += nw) {
     const int byte = ci * 1024 + 16 * lane;
     const int r = byte / ROWB;
     const int c = ((byte % ROWB) / 16) ^ Tile<T, DK>::swz(r);
     int col = c * V;
     if (col >= D) col -= D;
-    const long long row = seq_row(rbase, tstride, j0, r, total, b2);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row * D + col),
+    const unsigned rel = seq_row_rel(tstride, j0, r, total, b2);
+    // bf16: the byte offset from the block's first row fits 32 bits (t*N*d <
+    // 2^31 elements), so it is a lane offset on a wave-uniform base
+    const void* a = sizeof(T) == 2
+        ? static_cast<const void*>(reinterpret_cast<const char*>(src + rbase * D) + (rel * D + col) * 2u)
+        : static_cast<const void*>(src + (rbase + rel) * D + col);
+    __builtin_amdgcn_global_load_lds(a,
                                      (__attribute__((address_space(3))) void*)(tile + ci * (1024 / static_cast<int>(sizeof(T)))),
                                      16, 0, 0);
   }
@@ -597,8 +604,8 @@ __device__ inline void dma_rows32(T* tile, const T* src, long long rbase, int j0
 // The same for one float per row (64 lanes, rows j0 .. j0+63).
 __device__ inline void dma_rowstat(float* dst, const float* src, long long rbase, int j0, int total, int b2,
                                    long long tstride) {
-  const long long row = seq_row(rbase, tstride, j0, lane_id(), total, b2);
-  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row),
+  const unsigned rel = seq_row_rel(tstride, j0, lane_id(), total, b2);
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(reinterpret_cast<const char*>(src + rbase) + rel * 4u),
                                    (__attribute__((address_space(3))) void*)(dst), 4, 0, 0);
 }
 

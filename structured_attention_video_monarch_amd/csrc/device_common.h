@@ -265,6 +265,47 @@ struct TileDma {
                                        16, 0, 0);
     }
   }
+
+  // The lane's byte offsets for a whole tile of row stride `rstride`, formed
+  // once per kernel: a streaming loop then issues each whole tile with no
+  // per-lane address arithmetic (only the last, partial tile clamps rows).
+  static constexpr int PER = (NINS + NW - 1) / NW;
+  struct Plan {
+    unsigned off[PER];
+  };
+  __device__ static inline Plan plan(long long rstride) {
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    Plan pl;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ci = wave + i * NW;
+      const int byte = ci * 1024 + 16 * lane;
+      const int r = byte / ROWB;
+      const int c = ((byte % ROWB) / 16) ^ Tile<T, DK>::swz(r);
+      int col = c * V;
+      if (col >= D) col -= D;
+      pl.off[i] = (static_cast<unsigned>(r) * static_cast<unsigned>(rstride) + static_cast<unsigned>(col)) *
+                  static_cast<unsigned>(sizeof(T));
+    }
+    return pl;
+  }
+  __device__ static inline void issue(T* tile, const T* g, const Plan& pl, long long rstride, int nvalid) {
+    if (nvalid < ROWS) {
+      issue(tile, g, rstride, nvalid);
+      return;
+    }
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const char* gb = reinterpret_cast<const char*>(g);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ci = wave + i * NW;
+      if (NINS % NW != 0 && ci >= NINS) break;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(gb + pl.off[i]),
+                                       (__attribute__((address_space(3))) void*)(tile + ci * (1024 / static_cast<int>(sizeof(T)))),
+                                       16, 0, 0);
+    }
+  }
 };
 
 // Global -> LDS DMA of 64 floats, one per lane of the calling wave:

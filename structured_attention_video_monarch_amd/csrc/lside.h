@@ -831,12 +831,13 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
   const float* lh = lse + static_cast<long long>(bh) * p.N;
   const T* ucol = u + ((static_cast<long long>(bh) * p.t + g) * p.b1 * p.b2 + a2) * D;
   const long long ustride = static_cast<long long>(p.b2) * D;
+  const typename Dma::Plan plk = Dma::plan(ks.kstride), plu = Dma::plan(ustride);
 
   const int nst = (p.b1 + kStep - 1) / kStep;
   auto fetch = [&](int st, T* tK, T* tU, float* tH) {
     const int c1 = st * kStep;
-    Dma::issue(tK, ks.k + c1 * ks.kstride, ks.kstride, p.b1 - c1);
-    Dma::issue(tU, ucol + c1 * ustride, ustride, p.b1 - c1);
+    Dma::issue(tK, ks.k + c1 * ks.kstride, plk, ks.kstride, p.b1 - c1);
+    Dma::issue(tU, ucol + c1 * ustride, plu, ustride, p.b1 - c1);
     if (!BCAST && wave == NW - 1) dma_floats64(tH, ks.h + static_cast<long long>(c1) * ks.hstride, ks.hstride, p.b1 - c1);
   };
   fetch(0, sK0, sU0, sH0);
