@@ -93,6 +93,10 @@ static_assert(kStep == 64, "one 64-lane float DMA stages the log-sum-exps / entr
 #ifndef MONARCH_LSE_MINW
 #define MONARCH_LSE_MINW 1
 #endif
+// the first L-step's form (keys shared by all columns)
+#ifndef MONARCH_LSE_MINW_BCAST
+#define MONARCH_LSE_MINW_BCAST 4
+#endif
 #ifndef MONARCH_AGG_MINW
 #define MONARCH_AGG_MINW 1
 #endif
@@ -430,7 +434,7 @@ __device__ __forceinline__ void k_lse_item(const T* __restrict__ q,
 // Work items k_lse_item, one per workgroup, or looped over by fewer workgroups
 // (nitems > 0); nothing runs once every head has stopped iterating (nstop).
 template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG, bool PRE = false>
-__global__ __launch_bounds__(NW * kWave, MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
+__global__ __launch_bounds__(NW * kWave, BCAST ? MONARCH_LSE_MINW_BCAST : MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
                                                                       const T* __restrict__ kt,
                                                                       const float* __restrict__ h2,
                                                                       float* __restrict__ lse, LGeom p,
