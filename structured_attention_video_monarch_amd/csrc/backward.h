@@ -956,6 +956,9 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   __syncthreads();
 
   // ---------------- pass 2: dl and dq
+  float nls[RW];
+#pragma unroll
+  for (int rt = 0; rt < RW; ++rt) nls[rt] = nl[rt] + log2f(sc);
   auto stage2 = [&](int st, const Stage& c, const Stage& n) {
     if (NB == 2 && st + 1 < nst) fetch(st + 1, n, true);
 #pragma unroll
@@ -966,31 +969,35 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
       const bool tail = c1_0 + 32 > p.b1;
       typename E::frag a[KS][2];
       f32x4 S[2][RW], X[2][RW];
-      load_rows<T, DK, KS>(a, c.K, k0, l16, G);
-      logits<T, KS, RW>(S, a, bq);
-      if (HAS_DY) {
-        load_rows<T, DK, KS>(a, c.U, k0, l16, G);
-        logits<T, KS, RW>(X, a, bdy);  // <U, dy>
-        load_rows<T, DK, KS>(a, c.G, k0, l16, G);
-        products<T, KS, RW>(X, a, bq);  // + <G, q>
-      } else {
-        load_rows<T, DK, KS>(a, c.G, k0, l16, G);
-        logits<T, KS, RW>(X, a, bq);  // <G, q>
-      }
       float e8[8], hb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         e8[j] = c.E[k0 + 8 * G + j];
         hb[j] = BCAST ? 0.0f : c.H[k0 + 8 * G + j];
       }
+      // X = dL - delta accumulates onto -(e + delta): the products start
+      // from it, so no subtraction is left per weight
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        X[0][rt] = f32x4{-(e8[0] + dlt[rt]), -(e8[1] + dlt[rt]), -(e8[2] + dlt[rt]), -(e8[3] + dlt[rt])};
+        X[1][rt] = f32x4{-(e8[4] + dlt[rt]), -(e8[5] + dlt[rt]), -(e8[6] + dlt[rt]), -(e8[7] + dlt[rt])};
+      }
+      load_rows<T, DK, KS>(a, c.K, k0, l16, G);
+      logits<T, KS, RW>(S, a, bq);
+      if (HAS_DY) {
+        load_rows<T, DK, KS>(a, c.U, k0, l16, G);
+        products<T, KS, RW>(X, a, bdy);  // + <U, dy>
+      }
+      load_rows<T, DK, KS>(a, c.G, k0, l16, G);
+      products<T, KS, RW>(X, a, bq);  // + <G, q>
       typename E::frag pf[RW];
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         float w[8];
+        // s * L: the scale s = 2^lsc rides in the exponent
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          w[j] = sc * fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, nl[rt] + hb[j])) *
-                 (X[j >> 2][rt][j & 3] - e8[j] - dlt[rt]);
+          w[j] = fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, nls[rt] + hb[j])) * X[j >> 2][rt][j & 3];
         if (tail) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) w[j] = c1_0 + 8 * G + j < p.b1 ? w[j] : 0.0f;

@@ -91,7 +91,7 @@ constexpr int kHalves = kStep / 32;
 static_assert(kStep == 64, "one 64-lane float DMA stages the log-sum-exps / entropies of a step");
 // Minimum waves per SIMD the register allocator must allow (launch bounds).
 #ifndef MONARCH_LSE_MINW
-#define MONARCH_LSE_MINW 1
+#define MONARCH_LSE_MINW 4
 #endif
 // the first L-step's form (keys shared by all columns)
 #ifndef MONARCH_LSE_MINW_BCAST
