@@ -84,23 +84,33 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
     }
   }
   f32x4 acc[NACC][2][RW];
-  float m[RW], l[RW], sx[RW];
+  // m: the reference maximum of the row (log2 units); accl: the row sum of
+  // the rounded weights, summed by an MFMA against a ones fragment (every
+  // lane holds its row's whole sum); sx: the lane's share of sum w (x - m)
+  f32x4 accl[RW];
+  float m[RW], sx[RW];
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
     m[rt] = kMaskLogit;
-    l[rt] = 0.0f;
     sx[rt] = 0.0f;
+    accl[rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int dp = 0; dp < NACC; ++dp) acc[dp][0][rt] = acc[dp][1][rt] = f32x4{0, 0, 0, 0};
   }
+  const typename E::frag ones = E::ones();
   __syncthreads();
 
-  // one step of 64 keys: prefetch the next into (nK, nV), products on (cK, cV)
+  // one step of 64 keys: prefetch the next into (nK, nV), products on (cK, cV).
+  // The reference maximum moves only when the step's maximum exceeds it by
+  // more than kRescale (log2 units), so weights stay below 2^kRescale and the
+  // accumulators are rescaled only on those rare steps (one branch for the
+  // wave); the logit scale c rides in the exponent's multiply-add.
+  constexpr float kRescale = 8.0f;
   auto stage = [&](int st, const T* cK, const T* cV, T* nK, T* nV) {
     if (st + 1 < nst) fetch(st + 1, nK, nV);
     const int c2s = st * kStep;
-    // logits of both 32-key halves (lane: keys 8G + j of each half, row l16
-    // of each row tile), in log2 units, keys past b2 masked
+    // raw logits of both 32-key halves (lane: keys 8G + j of each half, row
+    // l16 of each row tile), keys past b2 masked
     f32x4 S[kHalves][2][RW];
 #pragma unroll
     for (int h = 0; h < kHalves; ++h) {
@@ -109,6 +119,8 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
       logits<T, KS, RW>(S[h], a, bq);
     }
     const bool tail = c2s + kStep > p.b2;
+    bool jump = false;
+    float mstep[RW];
 #pragma unroll
     for (int rt = 0; rt < RW; ++rt) {
       float mx = kMaskLogit;
@@ -116,22 +128,29 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
       for (int h = 0; h < kHalves; ++h)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float x = S[h][j >> 2][rt][j & 3] * p.c;
-          if (tail && c2s + 32 * h + 8 * G + j >= p.b2) x = kMaskLogit;
-          S[h][j >> 2][rt][j & 3] = x;
-          mx = fmaxf(mx, x);
+          if (tail && c2s + 32 * h + 8 * G + j >= p.b2) S[h][j >> 2][rt][j & 3] = kMaskLogit;
+          mx = fmaxf(mx, S[h][j >> 2][rt][j & 3]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[rt], mx);
-      const float a = fast_exp2(m[rt] - mnew);
-      if (!LAST) sx[rt] = a * (sx[rt] - (mnew - m[rt]) * l[rt]);
-      l[rt] *= a;
-      m[rt] = mnew;
+      mstep[rt] = mx * p.c;  // c > 0: the maximum of the scaled logits
+      jump = jump || mstep[rt] > m[rt] + kRescale;
+    }
+    if (__any(jump)) {
 #pragma unroll
-      for (int dp = 0; dp < NACC; ++dp) {
-        acc[dp][0][rt] *= a;
-        acc[dp][1][rt] *= a;
+      for (int rt = 0; rt < RW; ++rt) {
+        const float mnew = mstep[rt] > m[rt] + kRescale ? mstep[rt] : m[rt];
+        const float a = fast_exp2(m[rt] - mnew);
+        // the row sum is shared by the row's four lane groups: each takes a
+        // quarter of the correction of the lane-split entropy sum
+        if (!LAST) sx[rt] = a * (sx[rt] - (mnew - m[rt]) * 0.25f * accl[rt][0]);
+        accl[rt] *= a;
+        m[rt] = mnew;
+#pragma unroll
+        for (int dp = 0; dp < NACC; ++dp) {
+          acc[dp][0][rt] *= a;
+          acc[dp][1][rt] *= a;
+        }
       }
     }
 #pragma unroll
@@ -142,12 +161,12 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
         float w[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float dx = S[h][j >> 2][rt][j & 3] - m[rt];
+          const float dx = __builtin_fmaf(S[h][j >> 2][rt][j & 3], p.c, -m[rt]);
           w[j] = fast_exp2(dx);
-          l[rt] += w[j];
           if (!LAST) sx[rt] = __builtin_fmaf(w[j], dx, sx[rt]);
         }
         pf[rt] = E::pack(w);
+        accl[rt] = E::mma(ones, pf[rt], accl[rt]);
       }
       // X^T P^T (X = V, or K for the next keys): rows d, columns a2
       typename E::frag vv[NACC][2];
@@ -163,12 +182,10 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
 
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
-    // the row's sums over its four lane groups (all lanes take part)
-    float lt = l[rt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = accl[rt][0];
     float st = sx[rt];
     if (!LAST) {
+      // the entropy sum over the row's four lane groups (all lanes take part)
       st += __shfl_xor(st, 16);
       st += __shfl_xor(st, 32);
     }
