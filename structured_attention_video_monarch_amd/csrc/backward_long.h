@@ -113,25 +113,33 @@ __global__ __launch_bounds__(NW * kWave) void kb_rside_a_long(const T* __restric
       if (c2s + 32 * h >= p.b2) break;
       typename E::frag a[KS][2];
       f32x4 S[2][RW], DR[2][RW];
+      // dR - rho: the products start from -rho
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) DR[0][rt] = DR[1][rt] = f32x4{-rh[rt], -rh[rt], -rh[rt], -rh[rt]};
       load_rows<T, DK, KS>(a, cK, 32 * h, l16, G);
       logits<T, KS, RW>(S, a, bq);
       if (MID) {
-        logits<T, KS, RW>(DR, a, bd);  // <dKt, k>
+        products<T, KS, RW>(DR, a, bd);  // + <dKt, k>
       } else {
         load_rows<T, DK, KS>(a, cV, 32 * h, l16, G);
-        logits<T, KS, RW>(DR, a, bd);  // <dU, v>
+        products<T, KS, RW>(DR, a, bd);  // + <dU, v>
       }
+      // keys past b2 exist only in the block's last 32-key half
+      const bool tail = c2s + 32 * h + 32 > p.b2;
       typename E::frag zf[RW];
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         float z[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const bool valid = c2s + 32 * h + 8 * G + j < p.b2;
-          const float xl = S[j >> 2][rt][j & 3] * p.c - lse2[rt];  // log2 R
+          const float xl = __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, -lse2[rt]);  // log2 R
           float dr = DR[j >> 2][rt][j & 3];
-          if (MID) dr -= dhl[rt] * xl;
-          z[j] = valid ? fast_exp2(xl) * (dr - rh[rt]) : 0.0f;
+          if (MID) dr = __builtin_fmaf(-dhl[rt], xl, dr);
+          z[j] = fast_exp2(xl) * dr;
+        }
+        if (tail) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) z[j] = c2s + 32 * h + 8 * G + j < p.b2 ? z[j] : 0.0f;
         }
         zf[rt] = E::pack(z);
       }
@@ -156,8 +164,13 @@ __global__ __launch_bounds__(NW * kWave) void kb_rside_a_long(const T* __restric
       acc[dp][0][rt] *= sc;
       acc[dp][1][rt] *= sc;
     }
-    // e = <G, Qh> with the rounded Qh the forward used
-    float e = dot_acc_row<T, D, NACC, RW>(qhat + row[rt] * D, acc, rt, G);
+    // e = <G, Qh> with the rounded Qh the forward used (held in bq: its
+    // lane slots are the accumulator's d positions)
+    float e;
+    if constexpr (D >= 32)
+      e = dot_acc_frags<T, NACC, RW>(bq[rt], acc, rt);
+    else
+      e = dot_acc_row<T, D, NACC, RW>(qhat + row[rt] * D, acc, rt, G);
     e += __shfl_xor(e, 16);
     e += __shfl_xor(e, 32);
     if (row_ok[rt]) {
