@@ -33,7 +33,11 @@ struct RLGeom {
   float c;  // log2(e) / sqrt(d)
 };
 
-template <typename T, int D, int RW, int NW, bool LAST>
+// F32SUM (the training forward, which keeps each row's log-sum-exp for the
+// backward): the row sum l is taken in fp32 over the unrounded weights, so
+// that the backward's recomputed R = 2^(x - lse) sums to 1; otherwise it is
+// the MFMA sum of the rounded weights the products use.
+template <typename T, int D, int RW, int NW, bool LAST, bool F32SUM = false>
 __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T* __restrict__ v,
                                                 T* qhat,  // [BH][t][b1][b2][D]; U written over it when LAST
                                                 T* __restrict__ ktil, float* __restrict__ hent,
@@ -88,11 +92,12 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
   // the rounded weights, summed by an MFMA against a ones fragment (every
   // lane holds its row's whole sum); sx: the lane's share of sum w (x - m)
   f32x4 accl[RW];
-  float m[RW], sx[RW];
+  float m[RW], sx[RW], l32[RW];  // l32: F32SUM's lane share of the row sum
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
     m[rt] = kMaskLogit;
     sx[rt] = 0.0f;
+    l32[rt] = 0.0f;
     accl[rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int dp = 0; dp < NACC; ++dp) acc[dp][0][rt] = acc[dp][1][rt] = f32x4{0, 0, 0, 0};
@@ -143,8 +148,11 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
         const float a = fast_exp2(m[rt] - mnew);
         // the row sum is shared by the row's four lane groups: each takes a
         // quarter of the correction of the lane-split entropy sum
-        if (!LAST) sx[rt] = a * (sx[rt] - (mnew - m[rt]) * 0.25f * accl[rt][0]);
-        accl[rt] *= a;
+        if (!LAST) sx[rt] = a * (sx[rt] - (mnew - m[rt]) * (F32SUM ? l32[rt] : 0.25f * accl[rt][0]));
+        if (F32SUM)
+          l32[rt] *= a;
+        else
+          accl[rt] *= a;
         m[rt] = mnew;
 #pragma unroll
         for (int dp = 0; dp < NACC; ++dp) {
@@ -163,10 +171,11 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
         for (int j = 0; j < 8; ++j) {
           const float dx = __builtin_fmaf(S[h][j >> 2][rt][j & 3], p.c, -m[rt]);
           w[j] = fast_exp2(dx);
+          if (F32SUM) l32[rt] += w[j];
           if (!LAST) sx[rt] = __builtin_fmaf(w[j], dx, sx[rt]);
         }
         pf[rt] = E::pack(w);
-        accl[rt] = E::mma(ones, pf[rt], accl[rt]);
+        if (!F32SUM) accl[rt] = E::mma(ones, pf[rt], accl[rt]);
       }
       // X^T P^T (X = V, or K for the next keys): rows d, columns a2
       typename E::frag vv[NACC][2];
@@ -182,7 +191,12 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
 
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
-    const float lt = accl[rt][0];
+    float lt = accl[rt][0];
+    if (F32SUM) {
+      lt = l32[rt];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+    }
     float st = sx[rt];
     if (!LAST) {
       // the entropy sum over the row's four lane groups (all lanes take part)
@@ -207,12 +221,12 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
   __shared__ __align__(16) T sV0[(WITH_V) ? kStep * (DK) : 8]; \
   __shared__ __align__(16) T sV1[(WITH_V) ? kStep * (DK) : 8];
 
-template <typename T, int D, int RW, int NW, bool LAST>
+template <typename T, int D, int RW, int NW, bool LAST, bool F32SUM = false>
 __global__ __launch_bounds__(NW * kWave) void k_rstep_long(const T* __restrict__ k, const T* __restrict__ v, T* qhat,
                                                            T* __restrict__ ktil, float* __restrict__ hent, T* uout,
                                                            float* __restrict__ rlse, RLGeom p) {
   MONARCH_RSTEP_LONG_LDS(T, (D < 32 ? 32 : D), LAST)
-  rstep_long_body<T, D, RW, NW, LAST>(k, v, qhat, ktil, hent, uout, rlse, p, xcd_remap(blockIdx.x, gridDim.x), sK0,
+  rstep_long_body<T, D, RW, NW, LAST, F32SUM>(k, v, qhat, ktil, hent, uout, rlse, p, xcd_remap(blockIdx.x, gridDim.x), sK0,
                                       sK1, sV0, sV1);
 }
 

@@ -199,12 +199,19 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
           kern<<<grid, kRlNW * kWave, 0, st>>>(k, v, qhat, bf.ktil, bf.hent, ad->stop_at, it, rl,
                                                ad->nstop_upto + (it - 1), static_cast<int>(rl_grid));
         }
-        else if (last)
+        else if (bf.rlse) {  // the training forward: fp32 row sums, log-sum-exps kept
+          if (last)
+            k_rstep_long<T, D, kRlRW, kRlNW, true, true><<<rl_grid, kRlNW * kWave, 0, st>>>(
+                k, v, qhat, nullptr, nullptr, uout, bf.rlse_of(it), rl);
+          else
+            k_rstep_long<T, D, kRlRW, kRlNW, false, true><<<rl_grid, kRlNW * kWave, 0, st>>>(
+                k, v, qhat, ktil_out, hent_out, nullptr, bf.rlse_of(it), rl);
+        } else if (last)
           k_rstep_long<T, D, kRlRW, kRlNW, true><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, nullptr, nullptr,
-                                                                                   uout, bf.rlse_of(it), rl);
+                                                                                   uout, nullptr, rl);
         else
           k_rstep_long<T, D, kRlRW, kRlNW, false><<<rl_grid, kRlNW * kWave, 0, st>>>(k, v, qhat, ktil_out, hent_out,
-                                                                                    nullptr, bf.rlse_of(it), rl);
+                                                                                    nullptr, nullptr, rl);
       }));
     } else if (ad) {
       ok(timed(3, st, [&] {

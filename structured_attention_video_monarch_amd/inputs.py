@@ -38,7 +38,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "positional_term",
     "round_to_bf16_bits", "bf16_bits_to_f32", "make_head", "make_inputs",
-    "make_cotangent", "make_underflow_head",
+    "make_cotangent", "make_underflow_head", "make_late_spike_head",
 ]
 
 
@@ -282,6 +282,37 @@ def make_underflow_head(seed: int, b1: int, b2: int, d: int, cstar: int, dtype: 
     q[:, 0] = 2.0
     k[cstar * b2:(cstar + 1) * b2, 0] = -2400.0
     k[cstar * b2, 0] = 64.0
+    if dtype == "bf16":
+        bits = [round_to_bf16_bits(x) for x in (q, k, v)]
+        q, k, v = (bf16_bits_to_f32(x) for x in bits)
+        return q, k, v, bits
+    return q, k, v
+
+
+def make_late_spike_head(seed: int, N: int, d: int, spikes=((300, 16.0), (590, 28.0)), dtype: str = "f32"):
+    """A head whose best key for every query sits late in the key order.
+
+    Standard normal q, k, v (``default_rng([seed, 11])``, drawn in that
+    order), then a unit vector ``u`` along channel 0: every query gets
+    ``+4 u`` and each spike key ``j`` of ``spikes`` (pairs ``(j, b)``) is set
+    to ``b u`` in channel 0 only.  At scale ``1/sqrt(d)`` spike ``j``'s logit
+    is about ``b (4 + z) / sqrt(d)`` nats for a query with ``z ~ N(0, 1)`` in
+    channel 0 (14 nats for b = 28, d = 64), well above the few nats of the
+    other keys, so a streaming softmax over the keys in order meets a new row
+    maximum several log2 units higher at each spike.  ``dtype == "bf16"``
+    rounds to bf16 as :func:`make_inputs` does.  Returns float32 ``(q, k,
+    v)`` of shape ``[N, d]`` and, for bf16, their bit patterns as a 4th item.
+    """
+    rng = np.random.default_rng([seed, 11])
+    q = rng.standard_normal((N, d), dtype=np.float32)
+    k = rng.standard_normal((N, d), dtype=np.float32)
+    v = rng.standard_normal((N, d), dtype=np.float32)
+    q[:, 0] += 4.0
+    for j, b in spikes:
+        if not 0 <= j < N:
+            raise ValueError("spike key out of range")
+        k[j, :] = 0.0
+        k[j, 0] = b
     if dtype == "bf16":
         bits = [round_to_bf16_bits(x) for x in (q, k, v)]
         q, k, v = (bf16_bits_to_f32(x) for x in bits)

@@ -263,3 +263,51 @@ def test_one_key_block_gradients_are_attention_gradients(dtype, b2, T):
                 assert mx <= F32_REL_MAX, (name, hh, mx)
     say(f"[ok] one key block gradients {dtype} N={wl.N} T={T}: " + ", ".join(
         f"{n} {'max-abs' if n == 'y' else 'rel-max'} {wv[0]:.2e}" for n, wv in worst.items()))
+
+
+@pytest.mark.parametrize("dtype,T", [("f32", 1), ("f32", 2), ("bf16", 1), ("bf16", 2)])
+def test_late_spikes_move_the_streaming_maximum(dtype, T):
+    """One key block of 600 keys (exact softmax attention) whose best key for
+    every query comes late: keys 300 and 590 of the stream lift many rows'
+    maxima by more than 8 log2 units in the middle and in the last 64-key
+    step, so the online R-step moves its reference maximum and rescales the
+    accumulators mid-stream for those rows, and keeps it for the others of the
+    same wave.  The output and its gradients against scaled dot-product
+    attention (and autograd through it) in float64 on the CPU: fp32 with the
+    usual bars for the outputs and every gradient (the gradients run through
+    the log-sum-exps the rescaled forward keeps).  bf16: the outputs with the
+    usual bars; its gradients are reported, not held to the bf16 gradient
+    bars, because the input is as ill-conditioned for them as the peaked
+    softmaxes of test_gpu_backward: where a row's softmax is one-hot, dz =
+    R (dR - rho) cancels almost exactly (dR ~ rho), and the spike keys'
+    gradients (norms 16 and 28) sum such terms, so the bf16 roundings of dU,
+    U and R leave a few per cent there (measured: relative max 1.5-4.5e-2,
+    dq relative mean 4.4e-2)."""
+    from test_gpu_backward import F32_REL_MAX, rel_errors, run_train
+    N, d = 600, 64
+    heads = [I.make_late_spike_head(s, N, d, dtype=dtype) for s in (0, 1)]
+    wl = I.Workload("late_spikes", 1, len(heads), d, 2, 6, 50, 1, N, 1, T, dtype, pos_amp=0.0)
+    say(f"[case] late spikes in one key block of {N} keys, {dtype}, T={T}")
+    x = {n: np.stack([hd[i] for hd in heads])[None] for i, n in enumerate("qkv")}
+    if dtype == "bf16":
+        for i, n in enumerate("qkv"):
+            x[n + "_bits"] = np.stack([hd[3][i] for hd in heads])[None]
+    dyx = I.make_cotangent(wl, 2)
+    y = run_gpu(wl, x)
+    yg, dq, dk, dv = run_train(wl, x, dyx)
+    for h in range(wl.H):
+        q, k, v = (torch.from_numpy(x[n][0, h]).to(torch.float64).requires_grad_() for n in "qkv")
+        ref = torch.nn.functional.scaled_dot_product_attention(q[None, None], k[None, None], v[None, None])[0, 0]
+        for label, got in (("forward", y), ("training forward", yg)):
+            mx, mean = errors(got[0, h], ref.detach().numpy())
+            say(f"[ok] late spikes {label} head {h}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+            if dtype == "bf16":
+                assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (label, h, mx, mean)
+            else:
+                assert mx <= F32_MAX_ABS, (label, h, mx)
+        ref.backward(torch.from_numpy(dyx["dy"][0, h]).to(torch.float64))
+        for name, got, gref in zip(("dq", "dk", "dv"), (dq, dk, dv), (q.grad, k.grad, v.grad)):
+            mx, mean = rel_errors(got[0, h], gref.numpy())
+            say(f"[ok] late spikes {name} head {h}: relative max {mx:.3e} mean {mean:.3e}")
+            if dtype == "f32":
+                assert mx <= F32_REL_MAX, (name, h, mx)
