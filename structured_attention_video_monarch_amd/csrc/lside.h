@@ -434,7 +434,7 @@ __device__ __forceinline__ void k_lse_item(const T* __restrict__ q,
 // Work items k_lse_item, one per workgroup, or looped over by fewer workgroups
 // (nitems > 0); nothing runs once every head has stopped iterating (nstop).
 template <typename T, int D, int RW, int NW, bool BCAST, bool CONTIG, bool PRE = false>
-__global__ __launch_bounds__(NW * kWave, BCAST ? MONARCH_LSE_MINW_BCAST : MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
+__global__ __launch_bounds__(NW * kWave, sizeof(T) != 2 ? 1 : BCAST ? MONARCH_LSE_MINW_BCAST : MONARCH_LSE_MINW) void k_lse(const T* __restrict__ q,
                                                                       const T* __restrict__ kt,
                                                                       const float* __restrict__ h2,
                                                                       float* __restrict__ lse, LGeom p,
