@@ -548,9 +548,6 @@ constexpr int kRbSingle = 0, kRbLast = 1, kRbMid = 2, kRbFirst = 3;
 #ifndef MONARCH_BRB_BPS
 #define MONARCH_BRB_BPS 4
 #endif
-#ifndef MONARCH_BRBL_NW
-#define MONARCH_BRBL_NW 8  // waves per workgroup of kb_rside_b for key blocks over 128
-#endif
 #ifndef MONARCH_BRB_RW
 #define MONARCH_BRB_RW 1
 #endif
@@ -613,7 +610,7 @@ __device__ inline void dma_rowstat(float* dst, const float* src, long long rbase
 }
 
 template <typename T, int D, int MODE = kRbSingle, int RWK = MONARCH_BRB_RW>
-__global__ __launch_bounds__(RWK != MONARCH_BRB_RW ? MONARCH_BRBL_NW * kWave : RWK == 1 ? 512 : 256, MONARCH_BRB_MINW) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
+__global__ __launch_bounds__(RWK == 1 || RWK != MONARCH_BRB_RW ? 512 : 256, MONARCH_BRB_MINW) void kb_rside_b(const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ qhat, const T* __restrict__ du,
                                                   const float* __restrict__ lser, const float* __restrict__ rho,
                                                   const float* __restrict__ dh,

@@ -90,13 +90,12 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   const bool long_blocks = s.b2 > kShortB2;
   constexpr int rb_keys = 16 * MONARCH_BRB_RW;  // keys c2 per wave of kb_rside_b
   constexpr int rbl_keys = 16 * MONARCH_BRBL_RW;  // keys per wave of kb_rside_b for long blocks
-  constexpr int rbl_nw = MONARCH_BRBL_NW;  // waves per workgroup of kb_rside_b for long blocks
-  const int nks = long_blocks ? (s.b2 + rbl_nw * rbl_keys - 1) / (rbl_nw * rbl_keys) : 1;
-  const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc, nks, rbl_nw * rbl_keys};
+  const int nks = long_blocks ? (s.b2 + 8 * rbl_keys - 1) / (8 * rbl_keys) : 1;
+  const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc, nks, 8 * rbl_keys};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
   const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
   const unsigned rb_threads =
-      static_cast<unsigned>(kWave * (long_blocks ? rbl_nw : (s.b2 + rb_keys - 1) / rb_keys));
+      static_cast<unsigned>(kWave * (long_blocks ? 8 : (s.b2 + rb_keys - 1) / rb_keys));
   const unsigned rb_grid = static_cast<unsigned>(s.BH * s.b1 * nks);
   const size_t ra_lds = long_blocks ? 0 : rside_bwd_lds_bytes<T, D>(bg.b2p);
   constexpr int ral_nw = 4;
