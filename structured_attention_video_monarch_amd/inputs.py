@@ -31,6 +31,8 @@ Token order is ``n = (fi*h + hi)*w + wi`` (column fastest); arrays are
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -186,6 +188,15 @@ def make_head(wl: Workload, seed: int, b: int, h: int, pos: np.ndarray | None = 
     return q, k, v
 
 
+def _input_workers() -> int:
+    """Threads for making inputs: the cores this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def make_inputs(wl: Workload, seed: int = 0, heads=None, want_f32: bool = True,
                 want_bits: bool = True):
     """Seeded inputs for a workload.
@@ -213,19 +224,32 @@ def make_inputs(wl: Workload, seed: int = 0, heads=None, want_f32: bool = True,
         if bf16 and want_bits:
             out[name + "_bits"] = np.empty(shp, dtype=np.uint16)
     pos = positional_term(wl.f, wl.h, wl.w, d, wl.pos_amp) if wl.pos_amp else None
-    for b in range(wl.B):
-        for j, hh in enumerate(heads):
-            tensors = list(make_head(wl, seed, b, hh, pos))
-            tensors[0] = tensors[0][N - wl.Nq:]
-            for name, x in zip("qkv", tensors):
-                if bf16:
-                    bits = round_to_bf16_bits(x)
-                    if want_bits:
-                        out[name + "_bits"][b, j] = bits
-                    if want_f32:
-                        out[name][b, j] = bf16_bits_to_f32(bits)
-                elif want_f32:
-                    out[name][b, j] = x
+
+    def one(item):
+        b, j, hh = item
+        tensors = list(make_head(wl, seed, b, hh, pos))
+        tensors[0] = tensors[0][N - wl.Nq:]
+        for name, x in zip("qkv", tensors):
+            if bf16:
+                bits = round_to_bf16_bits(x)
+                if want_bits:
+                    out[name + "_bits"][b, j] = bits
+                if want_f32:
+                    out[name][b, j] = bf16_bits_to_f32(bits)
+            elif want_f32:
+                out[name][b, j] = x
+
+    # heads are drawn from generators of their own and written to disjoint
+    # slices, so they can be made concurrently (numpy releases the GIL in
+    # the draws and array arithmetic); the values do not depend on the order
+    items = [(b, j, hh) for b in range(wl.B) for j, hh in enumerate(heads)]
+    workers = min(len(items), _input_workers())
+    if workers > 1:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, items))
+    else:
+        for it in items:
+            one(it)
     return out
 
 
@@ -242,17 +266,26 @@ def make_cotangent(wl: Workload, seed: int = 0, heads=None, want_f32: bool = Tru
         out["dy"] = np.empty(shape, dtype=np.float32)
     if bf16 and want_bits:
         out["dy_bits"] = np.empty(shape, dtype=np.uint16)
-    for b in range(wl.B):
-        for j, hh in enumerate(heads):
-            x = np.random.default_rng([seed, b, hh, 1]).standard_normal((wl.Nq, wl.d), dtype=np.float32)
-            if bf16:
-                bits = round_to_bf16_bits(x)
-                if want_bits:
-                    out["dy_bits"][b, j] = bits
-                if want_f32:
-                    out["dy"][b, j] = bf16_bits_to_f32(bits)
-            elif want_f32:
-                out["dy"][b, j] = x
+    def one(item):
+        b, j, hh = item
+        x = np.random.default_rng([seed, b, hh, 1]).standard_normal((wl.Nq, wl.d), dtype=np.float32)
+        if bf16:
+            bits = round_to_bf16_bits(x)
+            if want_bits:
+                out["dy_bits"][b, j] = bits
+            if want_f32:
+                out["dy"][b, j] = bf16_bits_to_f32(bits)
+        elif want_f32:
+            out["dy"][b, j] = x
+
+    items = [(b, j, hh) for b in range(wl.B) for j, hh in enumerate(heads)]
+    workers = min(len(items), _input_workers())
+    if workers > 1:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, items))
+    else:
+        for it in items:
+            one(it)
     return out
 
 
