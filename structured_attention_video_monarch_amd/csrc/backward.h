@@ -796,7 +796,8 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
                                                     const T* __restrict__ gq, const float* __restrict__ ev,
                                                     T* __restrict__ dq,
                                                     float* __restrict__ dq_acc,
-                                                    T* __restrict__ dlout, int ldl, LGeom p, float sc) {
+                                                    T* __restrict__ dlout, int ldl, LGeom p, float sc,
+                                                    float kscale = 1.0f) {
   using E = Elem<T>;
   constexpr int DK = D < 32 ? 32 : D;
   constexpr int KS = DK / 32;
@@ -955,6 +956,19 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   }
   __syncthreads();
 
+  // keys stored pre-scaled (c Kbar, kscale = c): the products of pass 2 with
+  // them are c times the dq term, so ghat is scaled to match here and the
+  // sum is divided by c at the end
+  if (kscale != 1.0f) {
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        acc[dp][0][rt] *= kscale;
+        acc[dp][1][rt] *= kscale;
+      }
+  }
+
   // ---------------- pass 2: dl and dq
   float nls[RW];
 #pragma unroll
@@ -1027,6 +1041,16 @@ __global__ __launch_bounds__(NW * kWave) void kb_dq(const T* __restrict__ q, con
   for (int st = 0; st < nst; st += 2) {
     stage2(st, B0, B1);
     if (st + 1 < nst) stage2(st + 1, B1, B0);
+  }
+  if (kscale != 1.0f) {
+    const float ik = 1.0f / kscale;
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        acc[dp][0][rt] *= ik;
+        acc[dp][1][rt] *= ik;
+      }
   }
 
 #pragma unroll

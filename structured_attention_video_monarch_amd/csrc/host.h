@@ -267,8 +267,8 @@ struct Bufs {
   T* u;
   float* beta;
   float* rlse;  // training with key blocks over 128: the R rows' log-sum-exps
-  // the inference forward may store the block means pre-scaled to log2 units
-  // (c Kbar); the training forward keeps Kbar itself, as its backward reads it
+  // the block means may be stored pre-scaled to log2 units (c Kbar); the
+  // backward reads them in the same form (prescaled_keys)
   bool prescale;
   long long lse_it, qhat_it, beta_it, ktil_it, hent_it;
   // views of iteration it (1-based); keys/entropies: those the R-step of
@@ -295,6 +295,18 @@ Bufs<T> bufs_of(const Shape& s, unsigned char* ws, const Workspace& w) {
   b.rlse = nullptr;
   b.prescale = true;
   return b;
+}
+
+// Whether the first L-step runs on block means pre-scaled by c = log2(e)/sqrt(d)
+// (stored so by k_kbar; one multiply-add less per logit): bf16, when the
+// buffers allow it and the first L-step's aggregation holds whole tile
+// columns (k_aggregate_col); the forward and the backward take the same
+// decision from the shape.
+template <typename T>
+inline bool prescaled_keys(const Shape& s, const Bufs<T>& bf) {
+  const long long ngmax0 = (s.b1q + s.t - 1) / s.t;
+  return sizeof(T) == 2 && bf.prescale && !(s.b1 <= kColsRows && ngmax0 <= kColsRows) &&
+         ngmax0 <= kColRows && MONARCH_AGG_COL;
 }
 
 // Early stopping (iterations until the objective stops improving): per-head
@@ -364,7 +376,7 @@ Bufs<T> train_bufs(unsigned char* st, const TrainState& t, int iters) {
   b.u = reinterpret_cast<T*>(st + t.u);
   b.beta = reinterpret_cast<float*>(st + t.beta);
   b.rlse = t.rlse < t.total ? reinterpret_cast<float*>(st + t.rlse) : nullptr;
-  b.prescale = false;
+  b.prescale = true;
   b.lse_it = static_cast<long long>(t.lse_blk / sizeof(float));
   b.beta_it = static_cast<long long>(t.beta_blk / sizeof(float));
   b.qhat_it = static_cast<long long>(t.qhat_blk / sizeof(T));

@@ -48,6 +48,11 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
 
   constexpr int du_cb = C::kDuRW * C::kDuNW * 16;
   const LGeom col_geom{BH, Nq, s.b1, s.b1q, s.b2, s.t, (s.b1 + du_cb - 1) / du_cb, c};
+  // the first L-step's keys: block means, stored pre-scaled by c when the
+  // forward ran on them so (their logits are then in log2 units already)
+  const bool pre = prescaled_keys(s, bf);
+  LGeom col_geom1 = col_geom;
+  if (pre) col_geom1.c = 1.0f;
   const unsigned col_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * col_geom.nrb);
   // short tile columns (few key blocks, few rows per tile): one column per
   // wave in kb_du and kb_dq
@@ -63,7 +68,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
       if (du_col) {
         if (T_ == 1)
           kb_du_col<T, D, MONARCH_BDUC_RW, MONARCH_BDUC_NW, true><<<du_col_grid, MONARCH_BDUC_NW * kWave, 0, st>>>(
-              q, dout, bf.kbar, nullptr, bf.lse_of(1), du, col_geom);
+              q, dout, bf.kbar, nullptr, bf.lse_of(1), du, col_geom1);
         else
           kb_du_col<T, D, MONARCH_BDUC_RW, MONARCH_BDUC_NW, false><<<du_col_grid, MONARCH_BDUC_NW * kWave, 0, st>>>(
               q, dout, keys_of(T_), ent_of(T_), bf.lse_of(T_), du, col_geom);
@@ -78,7 +83,7 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
                                                                               bf.lse_of(T_), du, col_geom);
     else if (T_ == 1)
       kb_du<T, D, C::kDuRW, C::kDuNW, true><<<col_grid, C::kDuNW * kWave, 0, st>>>(q, dout, bf.kbar, nullptr,
-                                                                                  bf.lse_of(1), du, col_geom);
+                                                                                  bf.lse_of(1), du, col_geom1);
     else
       kb_du<T, D, C::kDuRW, C::kDuNW, false><<<col_grid, C::kDuNW * kWave, 0, st>>>(
           q, dout, keys_of(T_), ent_of(T_), bf.lse_of(T_), du, col_geom);
@@ -103,6 +108,8 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   const unsigned ral_grid = static_cast<unsigned>(s.BH * s.b1 * s.t * ral.nrb);
   constexpr int dq_rows = C::kDqRW * C::kDqNW * 16;
   const LGeom row_geom{BH, Nq, s.b1, s.b1q, s.b2, s.t, (ngmax + dq_rows - 1) / dq_rows, c};
+  LGeom row_geom1 = row_geom;
+  if (pre) row_geom1.c = 1.0f;
   const unsigned row_grid = static_cast<unsigned>(s.BH * s.t * s.b2 * row_geom.nrb);
 
   for (int i = T_; i >= 1; --i) {
@@ -170,7 +177,8 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
       auto launch = [&](auto kern) {
         ok(timed(7, st, [&] {
           kern<<<row_grid, C::kDqNW * kWave, 0, st>>>(q, dout, out, keys_of(i), ent_of(i), bf.lse_of(i), bf.u, gq,
-                                                        ev, dq, dqacc, dl, w.ldl, row_geom, sc);
+                                                        ev, dq, dqacc, dl, w.ldl, first ? row_geom1 : row_geom, sc,
+                                                        pre && first ? c : 1.0f);
         }));
       };
       constexpr int RW = C::kDqRW, NW = C::kDqNW, SP = C::kDqStep;

@@ -21,12 +21,9 @@ hipError_t run_pass(const T* q, const T* k, const T* v, T* out, const Shape& s, 
   };
 
   // The first L-step's kernels take the block means pre-scaled by c (one
-  // multiply-add less per logit) in the inference forward, where k_lse,
-  // k_aggregate_col and k_apply run them; the training forward keeps Kbar
-  // for its backward.
-  const int ngmax0 = (s.b1q + s.t - 1) / s.t;
-  const bool pre = sizeof(T) == 2 && bf.prescale && !(s.b1 <= kColsRows && ngmax0 <= kColsRows) &&
-                   ngmax0 <= kColRows && MONARCH_AGG_COL;
+  // multiply-add less per logit) where k_lse, k_aggregate_col and k_apply
+  // run them; the training state keeps them in that form for the backward.
+  const bool pre = prescaled_keys(s, bf);
   const float cscale = pre ? c : 1.0f;
 
   // block means of K
