@@ -267,6 +267,11 @@ __global__ __launch_bounds__(NW * kWave) void kb_du_col(const T* __restrict__ q,
   const int nkt = (p.b1 + RW * 16 - 1) / (RW * 16);
   const int nblk = (nrows + 31) / 32;
   constexpr int kMaxBlk = kColRows / 32;
+  // a last block of at most 16 rows takes half the logits and exponentials
+  // (as in k_aggregate_col)
+  constexpr bool kHalfOk = MONARCH_AGG_HALF && BCAST && sizeof(T) == 2 && D >= 32;
+  const bool half_last = kHalfOk && nrows - 32 * (nblk - 1) <= 16;
+  const int nfull = half_last ? nblk - 1 : nblk;
   for (int ktile = wave; ktile < nkt; ktile += NW) {
     const int c1base = ktile * RW * 16;
     typename E::frag bk[RW][KS];
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(NW * kWave) void kb_du_col(const T* __restrict__ q,
 
 #pragma unroll
     for (int blk = 0; blk < kMaxBlk; ++blk) {
-      if (blk >= nblk) break;
+      if (blk >= nfull) break;
       const int st = blk / kHalves, k0 = 32 * (blk % kHalves);
       const int r0 = 32 * blk;
       const bool tail = r0 + 32 > nrows;
@@ -317,6 +322,43 @@ __global__ __launch_bounds__(NW * kWave) void kb_du_col(const T* __restrict__ q,
       typename E::frag vv[NACC][2];
       load_cols<T, D, DK, NACC>(vv, sY[st], k0);
       weighted_sum<T, D, NACC, RW>(acc, vv, pf);
+    }
+    if constexpr (kHalfOk) {
+      if (half_last) {
+        // rows r0 .. r0+15 in natural order: logit slot 4G+i is row 4G+i and
+        // lands in contraction slot 8G+i; slots 8G+4..7 get weight 0 (and
+        // zero values)
+        const int st = nfull / kHalves, k0 = 32 * (nfull % kHalves);
+        const int r0 = 32 * nfull;
+        typename E::frag a[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = Tile<T, DK>::load8(sQ[st], k0 + l16, s * 32 + 8 * G);
+        float lr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lr[i] = sL[st][k0 + 4 * G + i];
+        const int lim = nrows - r0 - 4 * G;
+        typename E::frag pf[RW];
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) {
+          f32x4 S0 = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) S0 = E::mma(a[s], bk[rt][s], S0);
+          float w[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = fast_exp2(__builtin_fmaf(S0[i], p.c, hb[rt] - lr[i]));
+            w[i] = i < lim ? x : 0.0f;
+            w[4 + i] = 0.0f;
+          }
+          pf[rt] = E::pack(w);
+        }
+        typename E::frag vv[NACC][2];
+#pragma unroll
+        for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) vv[dp][dt] = Tile<T, DK>::load_tr_half(sY[st], k0, 32 * dp + 4 * dt, 8);
+        weighted_sum<T, D, NACC, RW>(acc, vv, pf);
+      }
     }
 
 #pragma unroll

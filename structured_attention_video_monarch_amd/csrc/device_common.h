@@ -168,6 +168,23 @@ struct Tile {
       return f;
     }
   }
+  // Half of it for a 16-row block (2-byte elements): lane (G, i) gets
+  // t[k0 + 4G + j][cbase + cstride*(i/4) + i%4] in slot j = 0..3 and zeros
+  // in slots 4..7, so contraction slot 8G + j holds row 4G + j.
+  __device__ static inline typename Elem<T>::frag load_tr_half(const T* t, int k0, int cbase, int cstride) {
+    static_assert(V == 8, "2-byte elements only");
+    const int l = threadIdx.x & 63;
+    const int i = l & 15, G = l >> 4;
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int r = k0 + 4 * G + (i >> 2);
+    const int col = cbase + cstride * (i & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + off(r, col)));
+    const v4i16 zero = {0, 0, 0, 0};
+    const v8i16 v = __builtin_shufflevector(lo, zero, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename Elem<T>::frag, v);
+  }
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

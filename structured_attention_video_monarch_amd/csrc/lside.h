@@ -103,6 +103,12 @@ static_assert(kStep == 64, "one 64-lane float DMA stages the log-sum-exps / entr
 #ifndef MONARCH_APP_MINW
 #define MONARCH_APP_MINW 1
 #endif
+#ifndef MONARCH_ROWSKIP
+#define MONARCH_ROWSKIP 1
+#endif
+#ifndef MONARCH_AGG_HALF
+#define MONARCH_AGG_HALF 1
+#endif
 
 // Fragment of a transposed tile for output columns of d-tile pair dp, half dt
 // (pair mode: the product leaves 8 consecutive d per lane) or the single
@@ -155,26 +161,27 @@ __device__ inline void load_cols(typename Elem<T>::frag (&v)[NACC][2], const T* 
 }
 
 // S tiles with rows from `a` (a 32-row block) and columns from the wave's RW
-// tiles of B fragments.
-template <typename T, int KS, int RW>
+// tiles of B fragments; only the first NR tiles are formed (a wave whose
+// last tiles lie wholly past the rows it owns skips them).
+template <typename T, int KS, int RW, int NR = RW>
 __device__ inline void logits(f32x4 (&S)[2][RW], const typename Elem<T>::frag (&a)[KS][2],
                               const typename Elem<T>::frag (&b)[RW][KS]) {
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-    for (int rt = 0; rt < RW; ++rt) S[ct][rt] = f32x4{0, 0, 0, 0};
+    for (int rt = 0; rt < NR; ++rt) S[ct][rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int rt = 0; rt < RW; ++rt) S[ct][rt] = Elem<T>::mma(a[s][ct], b[rt][s], S[ct][rt]);
+      for (int rt = 0; rt < NR; ++rt) S[ct][rt] = Elem<T>::mma(a[s][ct], b[rt][s], S[ct][rt]);
 }
 
 // The same products accumulated onto S as given (S holds a bias per logit:
 // with keys pre-scaled to log2 units the first MFMA then starts from the
 // bias, and no multiply-add is left for the exponent).
-template <typename T, int KS, int RW>
+template <typename T, int KS, int RW, int NR = RW>
 __device__ inline void logits_onto(f32x4 (&S)[2][RW], const typename Elem<T>::frag (&a)[KS][2],
                                    const typename Elem<T>::frag (&b)[RW][KS]) {
 #pragma unroll
@@ -182,11 +189,11 @@ __device__ inline void logits_onto(f32x4 (&S)[2][RW], const typename Elem<T>::fr
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int rt = 0; rt < RW; ++rt) S[ct][rt] = Elem<T>::mma(a[s][ct], b[rt][s], S[ct][rt]);
+      for (int rt = 0; rt < NR; ++rt) S[ct][rt] = Elem<T>::mma(a[s][ct], b[rt][s], S[ct][rt]);
 }
 
-// acc[dp][dt][rt] += v[dp][dt] * pf[rt]
-template <typename T, int D, int NACC, int RW>
+// acc[dp][dt][rt] += v[dp][dt] * pf[rt], rt < NR
+template <typename T, int D, int NACC, int RW, int NR = RW>
 __device__ inline void weighted_sum(f32x4 (&acc)[NACC][2][RW], const typename Elem<T>::frag (&v)[NACC][2],
                                     const typename Elem<T>::frag (&pf)[RW]) {
 #pragma unroll
@@ -194,7 +201,36 @@ __device__ inline void weighted_sum(f32x4 (&acc)[NACC][2][RW], const typename El
 #pragma unroll
     for (int dt = 0; dt < (D >= 32 ? 2 : 1); ++dt)
 #pragma unroll
-      for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = Elem<T>::mma(v[dp][dt], pf[rt], acc[dp][dt][rt]);
+      for (int rt = 0; rt < NR; ++rt) acc[dp][dt][rt] = Elem<T>::mma(v[dp][dt], pf[rt], acc[dp][dt][rt]);
+}
+
+// Row tiles of 16 a wave has to form: those that hold at least one of the
+// item's nrows rows (wave-uniform).
+template <int RW>
+__device__ inline int live_row_tiles(int nrows, int wave) {
+  const int n = (nrows - wave * RW * 16 + 15) / 16;
+  return n < 0 ? 0 : n > RW ? RW : n;
+}
+
+// Call f with the compile-time number of row tiles to form: none when no
+// tile holds rows, else all RW, or (ONE) a single tile when only the first
+// holds rows.  Without ONE the kernel has one copy of its products: the
+// second copy costs k_apply about 70 registers.  (RW > 2 with 1 < n < RW
+// forms all RW: padded rows are zero and never stored.)
+template <int RW, bool ONE, typename F>
+__device__ inline void with_live_tiles(int n, F&& f) {
+#if MONARCH_ROWSKIP
+  if (n == RW) {
+    f(std::integral_constant<int, RW>{});
+  } else if (ONE && n == 1) {
+    f(std::integral_constant<int, 1>{});
+  } else if (n > 0) {
+    f(std::integral_constant<int, RW>{});
+  }
+#else
+  (void)n;
+  f(std::integral_constant<int, RW>{});
+#endif
 }
 
 // ------------------------------------------------------------------ k_lse --
@@ -254,6 +290,7 @@ __device__ __forceinline__ void k_lse_item(const T* __restrict__ q,
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
   const T* qh = q + static_cast<long long>(bh) * p.N * D;
+  const int nlive = live_row_tiles<RW>(nrows, wave);  // row tiles past the item's rows are skipped
 
   const int nst = (p.b1 + kStep - 1) / kStep;
   auto fetch = [&](int st, int buf) {
@@ -303,21 +340,23 @@ __device__ __forceinline__ void k_lse_item(const T* __restrict__ q,
         mrow[rt] = (PRE ? 1.0f : p.c) * sqrtf(sq) * km * 1.00390625f + 0.00390625f;
         ls[rt] = 0.0f;
       }
-      // one 32-key block: masked only where keys run past b1
-      auto block = [&](const T* tile, int k0, int c1_0, auto masked) {
+      // one 32-key block for the first NR row tiles: masked only where keys
+      // run past b1
+      auto block = [&](const T* tile, int k0, int c1_0, auto masked, auto nr) {
+        constexpr int NR = decltype(nr)::value;
         typename E::frag a[KS][2];
         load_rows<T, DK, KS>(a, tile, k0, l16, G);
         f32x4 S[2][RW];
         if constexpr (PRE) {
 #pragma unroll
-          for (int rt = 0; rt < RW; ++rt)
+          for (int rt = 0; rt < NR; ++rt)
             S[0][rt] = S[1][rt] = f32x4{-mrow[rt], -mrow[rt], -mrow[rt], -mrow[rt]};
-          logits_onto<T, KS, RW>(S, a, bq);
+          logits_onto<T, KS, RW, NR>(S, a, bq);
         } else {
-          logits<T, KS, RW>(S, a, bq);
+          logits<T, KS, RW, NR>(S, a, bq);
         }
 #pragma unroll
-        for (int rt = 0; rt < RW; ++rt)
+        for (int rt = 0; rt < NR; ++rt)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float w = PRE ? fast_exp2(S[j >> 2][rt][j & 3])
@@ -331,16 +370,18 @@ __device__ __forceinline__ void k_lse_item(const T* __restrict__ q,
       for (int st = 0; st < nst; ++st) {
         const int cur = st & 1;
         if (st + 1 < nst) fetch(st + 1, cur ^ 1);
+        with_live_tiles<RW, false>(nlive, [&](auto nr) {
 #pragma unroll
-        for (int half = 0; half < kHalves; ++half) {
-          const int k0 = 32 * half;
-          const int c1_0 = st * kStep + k0;
-          if (c1_0 >= p.b1) break;
-          if (c1_0 + 32 > p.b1)
-            block(sK[cur], k0, c1_0, std::true_type{});
-          else
-            block(sK[cur], k0, c1_0, std::false_type{});
-        }
+          for (int half = 0; half < kHalves; ++half) {
+            const int k0 = 32 * half;
+            const int c1_0 = st * kStep + k0;
+            if (c1_0 >= p.b1) break;
+            if (c1_0 + 32 > p.b1)
+              block(sK[cur], k0, c1_0, std::true_type{}, nr);
+            else
+              block(sK[cur], k0, c1_0, std::false_type{}, nr);
+          }
+        });
         __syncthreads();
       }
       bool loose = false;
@@ -371,47 +412,50 @@ __device__ __forceinline__ void k_lse_item(const T* __restrict__ q,
   for (int st = 0; st < nst; ++st) {
     const int cur = st & 1;
     if (st + 1 < nst) fetch(st + 1, cur ^ 1);
+    with_live_tiles<RW, true>(nlive, [&](auto nr) {
+      constexpr int NR = decltype(nr)::value;
 #pragma unroll
-    for (int half = 0; half < kHalves; ++half) {
-      const int k0 = 32 * half;
-      const int c1_0 = st * kStep + k0;  // first key of this 32-key block
-      if (c1_0 >= p.b1) break;
-      // keys past b1 only exist in the last block
-      const bool tail = c1_0 + 32 > p.b1;
-      typename E::frag a[KS][2];
-      load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
-      float bias[8];
-      if (!BCAST) {
+      for (int half = 0; half < kHalves; ++half) {
+        const int k0 = 32 * half;
+        const int c1_0 = st * kStep + k0;  // first key of this 32-key block
+        if (c1_0 >= p.b1) break;
+        // keys past b1 only exist in the last block
+        const bool tail = c1_0 + 32 > p.b1;
+        typename E::frag a[KS][2];
+        load_rows<T, DK, KS>(a, sK[cur], k0, l16, G);
+        float bias[8];
+        if (!BCAST) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bias[j] = sH[cur][k0 + 8 * G + j];
-      }
-#if MONARCH_LSE_SCHED_BARRIER
-      __builtin_amdgcn_sched_barrier(0);
-#endif
-      f32x4 S[2][RW];
-      logits<T, KS, RW>(S, a, bq);
-#pragma unroll
-      for (int rt = 0; rt < RW; ++rt) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          x[j] = PRE ? S[j >> 2][rt][j & 3]
-                     : BCAST ? S[j >> 2][rt][j & 3] * p.c : __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
-        if (tail) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = c1_0 + 8 * G + j < p.b1 ? x[j] : kNegInf;
+          for (int j = 0; j < 8; ++j) bias[j] = sH[cur][k0 + 8 * G + j];
         }
-        float cm = x[0];
+#if MONARCH_LSE_SCHED_BARRIER
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+        f32x4 S[2][RW];
+        logits<T, KS, RW, NR>(S, a, bq);
 #pragma unroll
-        for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
-        const float mn = fmaxf(m[rt], cm);
-        float acc = l[rt] * fast_exp2(m[rt] - mn);
+        for (int rt = 0; rt < NR; ++rt) {
+          float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc += fast_exp2(x[j] - mn);
-        l[rt] = acc;
-        m[rt] = mn;
+          for (int j = 0; j < 8; ++j)
+            x[j] = PRE ? S[j >> 2][rt][j & 3]
+                       : BCAST ? S[j >> 2][rt][j & 3] * p.c : __builtin_fmaf(S[j >> 2][rt][j & 3], p.c, bias[j]);
+          if (tail) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = c1_0 + 8 * G + j < p.b1 ? x[j] : kNegInf;
+          }
+          float cm = x[0];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
+          const float mn = fmaxf(m[rt], cm);
+          float acc = l[rt] * fast_exp2(m[rt] - mn);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc += fast_exp2(x[j] - mn);
+          l[rt] = acc;
+          m[rt] = mn;
+        }
       }
-    }
+    });
     __syncthreads();
   }
 
@@ -677,6 +721,11 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
   const int kt_end = ALLK ? nkt : (kt0 + 1 < nkt ? kt0 + 1 : nkt);
   const int nblk = (nrows + 31) / 32;
   constexpr int kMaxBlk = kColRows / 32;
+  // a last block of at most 16 rows takes half the logits and exponentials
+  // (bf16): its rows sit in the contraction slots of the first logit half
+  constexpr bool kHalfOk = MONARCH_AGG_HALF && PRE && sizeof(T) == 2 && D >= 32;
+  const bool half_last = kHalfOk && nrows - 32 * (nblk - 1) <= 16;
+  const int nfull = half_last ? nblk - 1 : nblk;
   for (int ktile = kt0; ktile < kt_end; ktile += NW) {
     const int c1base = ktile * RW * 16;
     typename E::frag bk[RW][KS];
@@ -714,7 +763,7 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
     // offset plus an immediate, and only the last block masks rows
 #pragma unroll
     for (int blk = 0; blk < kMaxBlk; ++blk) {
-      if (blk >= nblk) break;
+      if (blk >= nfull) break;
       const int st = blk / kHalves, k0 = 32 * (blk % kHalves);
       const int r0 = 32 * blk;
       const bool tail = r0 + 32 > nrows;
@@ -756,6 +805,46 @@ __device__ __forceinline__ void k_aggregate_col_item(const T* __restrict__ q,
         accb[rt] = E::mma(ones, pf[rt], accb[rt]);
       }
       weighted_sum<T, D, NACC, RW>(acc, v, pf);
+    }
+    if constexpr (kHalfOk) {
+      if (half_last) {
+        // rows r0 .. r0+15 in natural order: logit slot 4G+i is row 4G+i and
+        // lands in contraction slot 8G+i; slots 8G+4..7 get weight 0 (and
+        // zero values)
+        const int st = nfull / kHalves, k0 = 32 * (nfull % kHalves);
+        const int r0 = 32 * nfull;
+        const T* tile = sQ[st];
+        typename E::frag a[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = Tile<T, DK>::load8(tile, k0 + l16, s * 32 + 8 * G);
+        typename E::frag v[NACC][2];
+#pragma unroll
+        for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) v[dp][dt] = Tile<T, DK>::load_tr_half(tile, k0, 32 * dp + 4 * dt, 8);
+        float lr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lr[i] = sL[st][k0 + 4 * G + i];
+        const int lim = nrows - r0 - 4 * G;
+        typename E::frag pf[RW];
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) {
+          f32x4 S0 = PRE ? f32x4{lr[0], lr[1], lr[2], lr[3]} : f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) S0 = E::mma(a[s], bk[rt][s], S0);
+          float w[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = PRE ? fast_exp2(-S0[i])
+                                : fast_exp2(__builtin_fmaf(S0[i], p.c, BCAST ? -lr[i] : bias[rt] - lr[i]));
+            w[i] = i < lim ? x : 0.0f;
+            w[4 + i] = 0.0f;
+          }
+          pf[rt] = E::pack(w);
+          accb[rt] = E::mma(ones, pf[rt], accb[rt]);
+        }
+        weighted_sum<T, D, NACC, RW>(acc, v, pf);
+      }
     }
 
 #pragma unroll
@@ -868,9 +957,11 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
       for (int rt = 0; rt < RW; ++rt) acc[dp][dt][rt] = f32x4{0, 0, 0, 0};
   __syncthreads();
 
-  // one step: prefetch the next into (nK, nU, nH), products on (cK, cU, cH)
-  auto stage = [&](int st, const T* cK, const T* cU, const float* cH, T* nK, T* nU, float* nH) {
-    if (st + 1 < nst) fetch(st + 1, nK, nU, nH);
+  // row tiles of this wave that hold rows of the item: the others are skipped
+  const int nlive = live_row_tiles<RW>(it.nrows, wave);
+  // one step's products on (cK, cU, cH) for the first NR row tiles
+  auto products_of = [&](int st, const T* cK, const T* cU, const float* cH, auto nr) {
+    constexpr int NR = decltype(nr)::value;
 #pragma unroll
     for (int half = 0; half < kHalves; ++half) {
       const int k0 = 32 * half;
@@ -893,15 +984,15 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
       f32x4 S[2][RW];
       if constexpr (PRE) {
 #pragma unroll
-        for (int rt = 0; rt < RW; ++rt)
+        for (int rt = 0; rt < NR; ++rt)
           S[0][rt] = S[1][rt] = f32x4{nlrow[rt], nlrow[rt], nlrow[rt], nlrow[rt]};
-        logits_onto<T, KS, RW>(S, a, bq);
+        logits_onto<T, KS, RW, NR>(S, a, bq);
       } else {
-        logits<T, KS, RW>(S, a, bq);
+        logits<T, KS, RW, NR>(S, a, bq);
       }
       typename E::frag pf[RW];
 #pragma unroll
-      for (int rt = 0; rt < RW; ++rt) {
+      for (int rt = 0; rt < NR; ++rt) {
         float w[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -913,8 +1004,13 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
         }
         pf[rt] = E::pack(w);
       }
-      weighted_sum<T, D, NACC, RW>(acc, v, pf);
+      weighted_sum<T, D, NACC, RW, NR>(acc, v, pf);
     }
+  };
+  // one step: prefetch the next into (nK, nU, nH), products on (cK, cU, cH)
+  auto stage = [&](int st, const T* cK, const T* cU, const float* cH, T* nK, T* nU, float* nH) {
+    if (st + 1 < nst) fetch(st + 1, nK, nU, nH);
+    with_live_tiles<RW, false>(nlive, [&](auto nr) { products_of(st, cK, cU, cH, nr); });
     __syncthreads();
   };
   for (int st = 0; st < nst; st += 2) {
