@@ -371,10 +371,13 @@ __global__ __launch_bounds__(NW * kWave) void kb_du_col(const T* __restrict__ q,
 }
 
 // ------------------------------------------------------------- kb_rside_a --
-// Key-block pass, part 1 (as the forward R-step): one workgroup per (bh, c1)
-// with ceil(b2/16) waves; K and V of the block are copied to LDS once, each
-// wave owns 16 rows a2 and loops over the tiles g with the aggregated
-// queries Qh and dU of TB tiles in flight (no barrier inside the loop).
+// Key-block pass, part 1 (as the forward R-step): one workgroup per (bh, c1);
+// K and V of the block are copied to LDS once, and the waves share out the
+// tasks (tile g, 16 rows a2) of the block, each task's rows of the
+// aggregated queries Qh and of dU loaded by its wave (no barrier inside the
+// loop).  With ceil(b2/16) waves a wave keeps one row tile through all
+// tiles g; with four waves (bf16, at most 168 registers) three workgroups
+// share a CU, twelve waves where one workgroup of five waves did before.
 // Per (g, c1, a2), from the transposed logits (rows c2, columns a2):
 //   R = softmax_c2(s<Qh, k>), dR = <dU, v>, rho = <R, dR>, dz = R (dR - rho),
 //   G = s (K^T dz) / beta, e = <G, Qh>; stored: G, e and the row statistics
@@ -410,8 +413,9 @@ __device__ inline void dma_block(T* tile, const T* src, int rows, int nvalid, in
   }
 }
 
-#ifndef MONARCH_BRA_TB
-#define MONARCH_BRA_TB 2
+// waves per kb_rside_a workgroup when a block has at least 2 tasks per wave
+#ifndef MONARCH_BRA_NW
+#define MONARCH_BRA_NW 4
 #endif
 // minimum waves per SIMD the register allocator must allow
 #ifndef MONARCH_BRA_MINW
@@ -433,7 +437,6 @@ __global__ __launch_bounds__(512, MONARCH_BRA_MINW) void kb_rside_a(const T* __r
   constexpr int KS = DK / 32;
   constexpr int NDP = D / 32;
   constexpr int NACC = NDP > 0 ? NDP : 1;
-  constexpr int TB = sizeof(T) == 2 ? MONARCH_BRA_TB : 1;
   using TL = Tile<T, DK>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int b2p = p.b2p;
@@ -447,125 +450,144 @@ __global__ __launch_bounds__(512, MONARCH_BRA_MINW) void kb_rside_a(const T* __r
   const int nw = blockDim.x / kWave;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
-  const int a2 = wave * 16 + l16;
-  const bool row_ok = a2 < p.b2;
-  auto qrow = [&](int g) { return ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2; };
+  // tasks: (tile g, 16 rows a2) pairs, task = g * ntr + row tile; wave w
+  // takes tasks w, w + nw, ...
+  const int ntr = (p.b2 + 15) / 16;
+  const int ntask = p.t * ntr;
 
   dma_block<T, D, DK>(sK, k + blk * D, b2p, p.b2, nw);
   if (!MID) dma_block<T, D, DK>(sV, v + blk * D, b2p, p.b2, nw);
-  typename E::frag bq[TB][KS], bd[TB][KS];
-  auto load_rows_g = [&](int g0) {
-#pragma unroll
-    for (int i = 0; i < TB; ++i)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int col = s * 32 + 8 * G;
-        const bool ok = g0 + i < p.t && row_ok && col < D;
-        bq[i][s] = ok ? E::load(qhat + qrow(g0 + i) * D + col) : E::zero();
-        bd[i][s] = ok ? E::load(du + qrow(g0 + i) * D + col) : E::zero();
-      }
-  };
-  load_rows_g(0);
-  __syncthreads();
 
-  for (int g0 = 0; g0 < p.t; g0 += TB) {
-    if (g0 > 0) load_rows_g(g0);
+  // a task's operands: its rows of Qh and dU (B fragments), beta and dH
+  struct Ops {
+    typename E::frag q[KS], d[KS];
+    float bt, dhv;
+  };
+  auto row_of = [&](int task, bool& row_ok) {
+    const int g = task / ntr;
+    const int a2 = (task - g * ntr) * 16 + l16;
+    row_ok = a2 < p.b2;
+    return ((static_cast<long long>(bh) * p.t + g) * p.b1 + c1) * p.b2 + a2;
+  };
+  auto load_ops = [&](int task, Ops& o) {
+    bool row_ok;
+    const long long row = row_of(task, row_ok);
 #pragma unroll
-    for (int gi = 0; gi < TB; ++gi) {
-      const int g = g0 + gi;
-      if (g >= p.t) break;
-      const long long row = qrow(g);
-      f32x4 S[NCP][2], DR[NCP][2];
+    for (int s = 0; s < KS; ++s) {
+      const int col = s * 32 + 8 * G;
+      const bool ok = row_ok && col < D;
+      o.q[s] = ok ? E::load(qhat + row * D + col) : E::zero();
+      o.d[s] = ok ? E::load(du + row * D + col) : E::zero();
+    }
+    o.bt = row_ok ? beta[row] : 0.0f;
+    // MID: dH of this row in nats per log2 unit of the logit
+    o.dhv = MID && row_ok ? dh[row] * kLn2 : 0.0f;
+  };
+  auto run_task = [&](int task, const Ops& o) {
+    // K and V never change in LDS during the loop: without this fence the
+    // compiler hoists every fragment read of them out of the task loop
+    // (about 190 registers) and spills
+    asm volatile("" ::: "memory");
+    bool row_ok;
+    const long long row = row_of(task, row_ok);
+    f32x4 S[NCP][2], DR[NCP][2];
 #pragma unroll
-      for (int cp = 0; cp < NCP; ++cp) {
-        S[cp][0] = S[cp][1] = DR[cp][0] = DR[cp][1] = f32x4{0, 0, 0, 0};
+    for (int cp = 0; cp < NCP; ++cp) {
+      S[cp][0] = S[cp][1] = DR[cp][0] = DR[cp][1] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            const int r = 32 * cp + perm_row(ct, l16);
-            S[cp][ct] = E::mma(TL::load8(sK, r, 32 * s + 8 * G), bq[gi][s], S[cp][ct]);
-            DR[cp][ct] = E::mma(TL::load8(sV, r, 32 * s + 8 * G), bd[gi][s], DR[cp][ct]);
-          }
-      }
-      // softmax over c2 = 32cp + 8G + j for column a2 (keys past b2 masked)
-      float x[NCP][8];
-      float mx = -1e30f;
-#pragma unroll
-      for (int cp = 0; cp < NCP; ++cp)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c2 = 32 * cp + 8 * G + j;
-          x[cp][j] = c2 < p.b2 ? S[cp][j >> 2][j & 3] * p.c : kNegInf;
-          mx = fmaxf(mx, x[cp][j]);
+        for (int ct = 0; ct < 2; ++ct) {
+          const int r = 32 * cp + perm_row(ct, l16);
+          S[cp][ct] = E::mma(TL::load8(sK, r, 32 * s + 8 * G), o.q[s], S[cp][ct]);
+          DR[cp][ct] = E::mma(TL::load8(sV, r, 32 * s + 8 * G), o.d[s], DR[cp][ct]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float sum = 0.0f;
+    }
+    // softmax over c2 = 32cp + 8G + j for column a2 (keys past b2 masked)
+    float x[NCP][8];
+    float mx = -1e30f;
 #pragma unroll
-      for (int cp = 0; cp < NCP; ++cp)
+    for (int cp = 0; cp < NCP; ++cp)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sum += fast_exp2(x[cp][j] - mx);
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      const float lse2 = mx + log2f(sum);
-      // MID: dH of this row in nats per log2 unit of the logit
-      const float dhl = MID ? (row_ok ? dh[row] * kLn2 : 0.0f) : 0.0f;
-      float rh = 0.0f;
-#pragma unroll
-      for (int cp = 0; cp < NCP; ++cp)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (MID) {
-            const bool valid = 32 * cp + 8 * G + j < p.b2;
-            DR[cp][j >> 2][j & 3] = valid ? DR[cp][j >> 2][j & 3] - dhl * (x[cp][j] - lse2) : 0.0f;
-          }
-          x[cp][j] = fast_exp2(x[cp][j] - lse2);  // now R
-          rh += x[cp][j] * DR[cp][j >> 2][j & 3];
-        }
-      rh += __shfl_xor(rh, 16);
-      rh += __shfl_xor(rh, 32);
-      // dQh^T = K^T dz^T: rows d, columns a2
-      f32x4 acc[NACC][2][1];
-#pragma unroll
-      for (int dp = 0; dp < NACC; ++dp) acc[dp][0][0] = acc[dp][1][0] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int cp = 0; cp < NCP; ++cp) {
-        float z[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) z[j] = x[cp][j] * (DR[cp][j >> 2][j & 3] - rh);
-        const typename E::frag zf = E::pack(z);
-#pragma unroll
-        for (int dp = 0; dp < NACC; ++dp)
-#pragma unroll
-          for (int dt = 0; dt < (NDP > 0 ? 2 : 1); ++dt)
-            acc[dp][dt][0] = E::mma(load_vals_tr<T, D, DK>(sK, 32 * cp, dp, dt), zf, acc[dp][dt][0]);
+      for (int j = 0; j < 8; ++j) {
+        const int c2 = 32 * cp + 8 * G + j;
+        x[cp][j] = c2 < p.b2 ? S[cp][j >> 2][j & 3] * p.c : kNegInf;
+        mx = fmaxf(mx, x[cp][j]);
       }
-      const float bt = row_ok ? beta[row] : 0.0f;
-      const float sc = bt > 0.0f ? p.s / bt : 0.0f;
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float sum = 0.0f;
 #pragma unroll
-      for (int dp = 0; dp < NACC; ++dp) {
-        acc[dp][0][0] *= sc;
-        acc[dp][1][0] *= sc;
-      }
-      // e = <G, Qh> with the rounded Qh the forward used (held in bq: its
-      // lane slots are the accumulator's d positions)
-      float e;
-      if constexpr (D >= 32)
-        e = dot_acc_frags<T, NACC, 1>(bq[gi], acc, 0);
-      else
-        e = dot_acc_row<T, D, NACC, 1>(qhat + (row_ok ? row : 0) * D, acc, 0, G);
-      e += __shfl_xor(e, 16);
-      e += __shfl_xor(e, 32);
-      if (row_ok) {
-        store_rows<T, D, NACC, 1>(gq + row * D, acc, 0, 1.0f, G);
-        if (G == 0) {
-          ev[row] = e;
-          lser[row] = lse2;
-          rho[row] = rh;
+    for (int cp = 0; cp < NCP; ++cp)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += fast_exp2(x[cp][j] - mx);
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    const float lse2 = mx + log2f(sum);
+    // MID: dH of this row in nats per log2 unit of the logit
+    const float dhl = o.dhv;
+    float rh = 0.0f;
+#pragma unroll
+    for (int cp = 0; cp < NCP; ++cp)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (MID) {
+          const bool valid = 32 * cp + 8 * G + j < p.b2;
+          DR[cp][j >> 2][j & 3] = valid ? DR[cp][j >> 2][j & 3] - dhl * (x[cp][j] - lse2) : 0.0f;
         }
+        x[cp][j] = fast_exp2(x[cp][j] - lse2);  // now R
+        rh += x[cp][j] * DR[cp][j >> 2][j & 3];
+      }
+    rh += __shfl_xor(rh, 16);
+    rh += __shfl_xor(rh, 32);
+    // dQh^T = K^T dz^T: rows d, columns a2
+    f32x4 acc[NACC][2][1];
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp) acc[dp][0][0] = acc[dp][1][0] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int cp = 0; cp < NCP; ++cp) {
+      float z[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z[j] = x[cp][j] * (DR[cp][j >> 2][j & 3] - rh);
+      const typename E::frag zf = E::pack(z);
+#pragma unroll
+      for (int dp = 0; dp < NACC; ++dp)
+#pragma unroll
+        for (int dt = 0; dt < (NDP > 0 ? 2 : 1); ++dt)
+          acc[dp][dt][0] = E::mma(load_vals_tr<T, D, DK>(sK, 32 * cp, dp, dt), zf, acc[dp][dt][0]);
+    }
+    const float bt = o.bt;
+    const float sc = bt > 0.0f ? p.s / bt : 0.0f;
+#pragma unroll
+    for (int dp = 0; dp < NACC; ++dp) {
+      acc[dp][0][0] *= sc;
+      acc[dp][1][0] *= sc;
+    }
+    // e = <G, Qh> with the rounded Qh the forward used (held in o.q: its
+    // lane slots are the accumulator's d positions)
+    float e;
+    if constexpr (D >= 32)
+      e = dot_acc_frags<T, NACC, 1>(o.q, acc, 0);
+    else
+      e = dot_acc_row<T, D, NACC, 1>(qhat + (row_ok ? row : 0) * D, acc, 0, G);
+    e += __shfl_xor(e, 16);
+    e += __shfl_xor(e, 32);
+    if (row_ok) {
+      store_rows<T, D, NACC, 1>(gq + row * D, acc, 0, 1.0f, G);
+      if (G == 0) {
+        ev[row] = e;
+        lser[row] = lse2;
+        rho[row] = rh;
       }
     }
+  };
+
+  Ops o;
+  if (wave < ntask) load_ops(wave, o);
+  __syncthreads();
+  for (int task = wave; task < ntask; task += nw) {
+    if (task != wave) load_ops(task, o);
+    run_task(task, o);
   }
 }
 

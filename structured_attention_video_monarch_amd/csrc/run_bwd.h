@@ -98,7 +98,11 @@ hipError_t run_bwd(const T* q, const T* k, const T* v, const T* out, const T* do
   const int nks = long_blocks ? (s.b2 + 8 * rbl_keys - 1) / (8 * rbl_keys) : 1;
   const BGeom bg{BH, N, s.b1, s.b2, s.t, (s.b2 + 31) / 32 * 32, c, sc, nks, 8 * rbl_keys};
   const unsigned r_grid = static_cast<unsigned>(s.BH * s.b1);
-  const unsigned r_threads = static_cast<unsigned>(kWave * ((s.b2 + 15) / 16));
+  // kb_rside_a: four waves when each has at least two (tile, row tile) tasks
+  // (bf16: three workgroups per CU), else one wave per row tile
+  const int ra_ntr = (s.b2 + 15) / 16;
+  const int ra_nw = sizeof(T) == 2 && s.t * ra_ntr >= 2 * MONARCH_BRA_NW ? MONARCH_BRA_NW : ra_ntr;
+  const unsigned r_threads = static_cast<unsigned>(kWave * ra_nw);
   const unsigned rb_threads =
       static_cast<unsigned>(kWave * (long_blocks ? 8 : (s.b2 + rb_keys - 1) / rb_keys));
   const unsigned rb_grid = static_cast<unsigned>(s.BH * s.b1 * nks);
