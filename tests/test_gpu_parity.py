@@ -98,6 +98,12 @@ EDGE = [
     ("d32_f32", 1, 2, 32, 2, 9, 20, 18, 20, 2, 1, "f32"),
     ("d128_f32_T3", 1, 1, 128, 3, 5, 24, 15, 24, 3, 3, "f32"),
     ("b1_big_ragged", 1, 1, 128, 7, 37, 3, 259, 3, 3, 1, "bf16"),
+    # tile columns whose last 32-row block holds 1, 16 or 17 rows (the first
+    # two take the 16-row form of the aggregation), and key blocks whose
+    # (tile, 16-row) tasks do not divide evenly over the R-side waves
+    ("tail_1_row", 1, 2, 128, 3, 11, 12, 33, 12, 1, 1, "bf16"),
+    ("tail_16_rows_uneven_tasks", 1, 2, 64, 5, 48, 20, 240, 20, 5, 2, "bf16"),
+    ("tail_17_rows", 1, 2, 32, 7, 7, 16, 49, 16, 1, 1, "bf16"),
 ]
 
 
