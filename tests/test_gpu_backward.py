@@ -109,7 +109,7 @@ def test_bwd_chunk480p_bf16():
     compare_grad(I.get_workload("chunk480p"), heads=[0, 5, 11])
 
 
-@pytest.mark.parametrize("t", [1, 4])
+@pytest.mark.parametrize("t", [1, 4, 8])
 def test_bwd_clip480p_spikes_bf16(t):
     compare_grad(I.get_workload(f"clip480p_spikes_t{t}_T1"), heads=[0, 11])
 
@@ -194,8 +194,9 @@ def test_bwd_iters_chunk480p_bf16(T):
     compare_grad(I.get_workload("chunk480p"), heads=[0, 11], iters=T)
 
 
-def test_bwd_iters_clip480p_spikes_bf16():
-    compare_grad(I.get_workload("clip480p_spikes_t4_T1"), heads=[0, 11], iters=2)
+@pytest.mark.parametrize("t", [4, 8])
+def test_bwd_iters_clip480p_spikes_bf16(t):
+    compare_grad(I.get_workload(f"clip480p_spikes_t{t}_T1"), heads=[0, 11], iters=2)
 
 
 def test_bwd_iters_latent720p_bf16():
