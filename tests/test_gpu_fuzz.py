@@ -50,25 +50,25 @@ def draw(kind, seed):
     return I.Workload(f"fuzz-{kind}{seed}", B, H, d, f, h, w, b1, b2, t, T, dtype, fq=fq)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_fuzz_forward(seed):
     wl = draw("fwd", seed)
     compare(wl, seed=seed, label=f"{wl.name} f,h,w=({wl.f},{wl.h},{wl.w})")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(32))
 def test_fuzz_chunk_against_cached_keys(seed):
     wl = draw("kv", seed)
     compare_kv(wl, seed=seed, label=f"{wl.name} fq/f={wl.fq}/{wl.f} h,w=({wl.h},{wl.w})")
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(64))
 def test_fuzz_backward(seed):
     wl = draw("bwd", seed)
     compare_grad(wl, seed=seed, label=f"{wl.name} f,h,w=({wl.f},{wl.h},{wl.w})", iters=wl.iters)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(24))
 def test_fuzz_backward_chunk(seed):
     wl = draw("bwdkv", seed)
     compare_grad(wl, seed=seed, label=f"{wl.name} fq/f={wl.fq}/{wl.f} h,w=({wl.h},{wl.w})", iters=wl.iters)
