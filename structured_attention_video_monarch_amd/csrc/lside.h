@@ -999,6 +999,7 @@ __global__ __launch_bounds__(NW * kWave, MONARCH_APP_MINW) void k_apply(const T*
           w[j] = PRE ? fast_exp2(S[j >> 2][rt][j & 3])
                      : fast_exp2(__builtin_fmaf(S[j >> 2][rt][j & 3], p.c, BCAST ? nlrow[rt] : bias[j] + nlrow[rt]));
         if (tail) {
+          asm volatile("");  // keeps the tail a (wave-uniform) branch: no selects in the other key blocks
 #pragma unroll
           for (int j = 0; j < 8; ++j) w[j] = c1_0 + 8 * G + j < p.b1 ? w[j] : 0.0f;
         }

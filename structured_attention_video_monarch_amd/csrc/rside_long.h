@@ -69,10 +69,13 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int l16 = lane & 15, G = lane >> 4;
   const int nst = (p.b2 + kStep - 1) / kStep;
+  // the lanes' DMA offsets within a 64-key tile, formed once (K and V tiles
+  // have the same layout): only the last, partial tile clamps rows per lane
+  const typename Dma::Plan plan = Dma::plan(D);
   auto fetch = [&](int st, T* tK, T* tV) {
     const int c2 = st * kStep;
-    Dma::issue(tK, k + kblk + static_cast<long long>(c2) * D, D, p.b2 - c2);
-    if (LAST) Dma::issue(tV, v + kblk + static_cast<long long>(c2) * D, D, p.b2 - c2);
+    Dma::issue(tK, k + kblk + static_cast<long long>(c2) * D, plan, D, p.b2 - c2);
+    if (LAST) Dma::issue(tV, v + kblk + static_cast<long long>(c2) * D, plan, D, p.b2 - c2);
   };
   fetch(0, sK0, sV0);
 
@@ -87,6 +90,23 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
       bq[rt][s] = (ok && col < D) ? E::load(qhat + (qbase + r) * D + col) : E::zero();
     }
   }
+  // PRES (the bf16 forms without F32SUM): the queries are held pre-scaled by
+  // c and every logit product starts from -m, so the products give
+  // x' = c<q,k> - m, the exponent's argument itself: no multiply-add per
+  // weight.  The training forward (F32SUM) keeps the plain products, the
+  // form from which the backward recomputes R.
+  constexpr bool PRES = sizeof(T) == 2 && !F32SUM;
+  if constexpr (PRES) {
+#pragma unroll
+    for (int rt = 0; rt < RW; ++rt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = p.c * E::slot(bq[rt][s], j);
+        bq[rt][s] = E::pack(w);
+      }
+  }
   f32x4 acc[NACC][2][RW];
   // m: the reference maximum of the row (log2 units); accl: the row sum of
   // the rounded weights, summed by an MFMA against a ones fragment (every
@@ -95,7 +115,7 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
   float m[RW], sx[RW], l32[RW];  // l32: F32SUM's lane share of the row sum
 #pragma unroll
   for (int rt = 0; rt < RW; ++rt) {
-    m[rt] = kMaskLogit;
+    m[rt] = PRES ? 0.0f : kMaskLogit;  // PRES: the first step sets it
     sx[rt] = 0.0f;
     l32[rt] = 0.0f;
     accl[rt] = f32x4{0, 0, 0, 0};
@@ -109,22 +129,42 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
   // The reference maximum moves only when the step's maximum exceeds it by
   // more than kRescale (log2 units), so weights stay below 2^kRescale and the
   // accumulators are rescaled only on those rare steps (one branch for the
-  // wave); the logit scale c rides in the exponent's multiply-add.
+  // wave); the logit scale c rides in the exponent's multiply-add (or, with
+  // PRES, in the queries).
   constexpr float kRescale = 8.0f;
   auto stage = [&](int st, const T* cK, const T* cV, T* nK, T* nV) {
     if (st + 1 < nst) fetch(st + 1, nK, nV);
     const int c2s = st * kStep;
-    // raw logits of both 32-key halves (lane: keys 8G + j of each half, row
-    // l16 of each row tile), keys past b2 masked
+    // logits of both 32-key halves (lane: keys 8G + j of each half, row l16
+    // of each row tile): raw, or with PRES c<q,k> - m; keys past b2 masked
     f32x4 S[kHalves][2][RW];
 #pragma unroll
     for (int h = 0; h < kHalves; ++h) {
       typename E::frag a[KS][2];
       load_rows<T, DK, KS>(a, cK, 32 * h, l16, G);
-      logits<T, KS, RW>(S[h], a, bq);
+      if constexpr (PRES) {
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) S[h][0][rt] = S[h][1][rt] = f32x4{-m[rt], -m[rt], -m[rt], -m[rt]};
+        logits_onto<T, KS, RW>(S[h], a, bq);
+      } else {
+        logits<T, KS, RW>(S[h], a, bq);
+      }
     }
-    const bool tail = c2s + kStep > p.b2;
-    bool jump = false;
+    if (c2s + kStep > p.b2) {
+      // only the last step holds keys past b2; the empty asm keeps this a
+      // (wave-uniform) branch instead of selects in every step
+      asm volatile("");
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt)
+#pragma unroll
+        for (int h = 0; h < kHalves; ++h)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c2s + 32 * h + 8 * G + j >= p.b2) S[h][j >> 2][rt][j & 3] = kMaskLogit;
+    }
+    // PRES: the first step always sets the reference (m starts at 0)
+    const bool first = PRES && st == 0;
+    bool jump = first;
     float mstep[RW];
 #pragma unroll
     for (int rt = 0; rt < RW; ++rt) {
@@ -132,16 +172,40 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
 #pragma unroll
       for (int h = 0; h < kHalves; ++h)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (tail && c2s + 32 * h + 8 * G + j >= p.b2) S[h][j >> 2][rt][j & 3] = kMaskLogit;
-          mx = fmaxf(mx, S[h][j >> 2][rt][j & 3]);
-        }
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, S[h][j >> 2][rt][j & 3]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mstep[rt] = mx * p.c;  // c > 0: the maximum of the scaled logits
-      jump = jump || mstep[rt] > m[rt] + kRescale;
+      if constexpr (PRES) {
+        mstep[rt] = mx;  // relative to m
+        jump = jump || mx > kRescale;
+      } else {
+        mstep[rt] = mx * p.c;  // c > 0: the maximum of the scaled logits
+        jump = jump || mstep[rt] > m[rt] + kRescale;
+      }
     }
-    if (__any(jump)) {
+    if (PRES && __any(jump)) {
+#pragma unroll
+      for (int rt = 0; rt < RW; ++rt) {
+        // dm: the rise of the reference (the step's maximum above m)
+        const float dm = first || mstep[rt] > kRescale ? mstep[rt] : 0.0f;
+        if (!first) {  // the sums are still zero in the first step
+          const float a = fast_exp2(-dm);
+          if (!LAST) sx[rt] = a * (sx[rt] - dm * 0.25f * accl[rt][0]);
+          accl[rt] *= a;
+#pragma unroll
+          for (int dp = 0; dp < NACC; ++dp) {
+            acc[dp][0][rt] *= a;
+            acc[dp][1][rt] *= a;
+          }
+        }
+        m[rt] += dm;
+#pragma unroll
+        for (int h = 0; h < kHalves; ++h) {
+          S[h][0][rt] -= dm;
+          S[h][1][rt] -= dm;
+        }
+      }
+    } else if (!PRES && __any(jump)) {
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         const float mnew = mstep[rt] > m[rt] + kRescale ? mstep[rt] : m[rt];
@@ -169,7 +233,7 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
         float w[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float dx = __builtin_fmaf(S[h][j >> 2][rt][j & 3], p.c, -m[rt]);
+          const float dx = PRES ? S[h][j >> 2][rt][j & 3] : __builtin_fmaf(S[h][j >> 2][rt][j & 3], p.c, -m[rt]);
           w[j] = fast_exp2(dx);
           if (F32SUM) l32[rt] += w[j];
           if (!LAST) sx[rt] = __builtin_fmaf(w[j], dx, sx[rt]);
