@@ -132,6 +132,7 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
   // wave); the logit scale c rides in the exponent's multiply-add (or, with
   // PRES, in the queries).
   constexpr float kRescale = 8.0f;
+  constexpr float kBig = 18446744073709551616.0f;  // 2^64, the PRES forms' bound on a half's row sum
   auto stage = [&](int st, const T* cK, const T* cV, T* nK, T* nV) {
     if (st + 1 < nst) fetch(st + 1, nK, nV);
     const int c2s = st * kStep;
@@ -162,9 +163,92 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
           for (int j = 0; j < 8; ++j)
             if (c2s + 32 * h + 8 * G + j >= p.b2) S[h][j >> 2][rt][j & 3] = kMaskLogit;
     }
-    // PRES: the first step always sets the reference (m starts at 0)
-    const bool first = PRES && st == 0;
-    bool jump = first;
+    if constexpr (PRES) {
+      // The reference starts at the first step's maximum (m = 0 before it)
+      // and afterwards moves only when a 32-key half's row sum exceeds 2^64
+      // (kBig): the sums come from the MFMA the row sums need anyway, and an
+      // overflowed weight makes them infinite, so no later step takes a
+      // maximum unless its half trips that test.  Weights up to 2^64 lose
+      // nothing in bf16 or in the fp32 sums (both keep fp32's exponent
+      // range), and the sums of a row stay far below fp32's limit.
+      if (st == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) {
+          float mx = kMaskLogit;
+#pragma unroll
+          for (int h = 0; h < kHalves; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mx = fmaxf(mx, S[h][j >> 2][rt][j & 3]);
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          m[rt] = mx;
+#pragma unroll
+          for (int h = 0; h < kHalves; ++h) {
+            S[h][0][rt] -= mx;
+            S[h][1][rt] -= mx;
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < kHalves; ++h) {
+        typename E::frag pf[RW];
+        float w[RW][8];
+        f32x4 hs[RW];
+        auto weights = [&](int rt) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[rt][j] = fast_exp2(S[h][j >> 2][rt][j & 3]);
+          pf[rt] = E::pack(w[rt]);
+          hs[rt] = E::mma(ones, pf[rt], f32x4{0, 0, 0, 0});
+        };
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) weights(rt);
+        bool big = false;
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) big = big || !(hs[rt][0] <= kBig);
+        if (__any(big)) {
+          // rare: the rows whose half sum tripped move the reference up to
+          // the half's maximum; their sums and accumulators are rescaled and
+          // the half's weights made again
+#pragma unroll
+          for (int rt = 0; rt < RW; ++rt) {
+            float mx = kMaskLogit;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mx = fmaxf(mx, S[h][j >> 2][rt][j & 3]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float dm = !(hs[rt][0] <= kBig) ? mx : 0.0f;
+            const float a = fast_exp2(-dm);
+            if (!LAST) sx[rt] = a * (sx[rt] - dm * 0.25f * accl[rt][0]);
+            accl[rt] *= a;
+#pragma unroll
+            for (int dp = 0; dp < NACC; ++dp) {
+              acc[dp][0][rt] *= a;
+              acc[dp][1][rt] *= a;
+            }
+            m[rt] += dm;
+#pragma unroll
+            for (int h2 = h; h2 < kHalves; ++h2) {
+              S[h2][0][rt] -= dm;
+              S[h2][1][rt] -= dm;
+            }
+            weights(rt);
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RW; ++rt) {
+          accl[rt] += hs[rt];
+          if (!LAST) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sx[rt] = __builtin_fmaf(w[rt][j], S[h][j >> 2][rt][j & 3], sx[rt]);
+          }
+        }
+        // X^T P^T (X = V, or K for the next keys): rows d, columns a2
+        typename E::frag vv[NACC][2];
+        load_cols<T, D, DK, NACC>(vv, LAST ? cV : cK, 32 * h);
+        weighted_sum<T, D, NACC, RW>(acc, vv, pf);
+      }
+    } else {
+    bool jump = false;
     float mstep[RW];
 #pragma unroll
     for (int rt = 0; rt < RW; ++rt) {
@@ -175,37 +259,10 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
         for (int j = 0; j < 8; ++j) mx = fmaxf(mx, S[h][j >> 2][rt][j & 3]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if constexpr (PRES) {
-        mstep[rt] = mx;  // relative to m
-        jump = jump || mx > kRescale;
-      } else {
-        mstep[rt] = mx * p.c;  // c > 0: the maximum of the scaled logits
-        jump = jump || mstep[rt] > m[rt] + kRescale;
-      }
+      mstep[rt] = mx * p.c;  // c > 0: the maximum of the scaled logits
+      jump = jump || mstep[rt] > m[rt] + kRescale;
     }
-    if (PRES && __any(jump)) {
-#pragma unroll
-      for (int rt = 0; rt < RW; ++rt) {
-        // dm: the rise of the reference (the step's maximum above m)
-        const float dm = first || mstep[rt] > kRescale ? mstep[rt] : 0.0f;
-        if (!first) {  // the sums are still zero in the first step
-          const float a = fast_exp2(-dm);
-          if (!LAST) sx[rt] = a * (sx[rt] - dm * 0.25f * accl[rt][0]);
-          accl[rt] *= a;
-#pragma unroll
-          for (int dp = 0; dp < NACC; ++dp) {
-            acc[dp][0][rt] *= a;
-            acc[dp][1][rt] *= a;
-          }
-        }
-        m[rt] += dm;
-#pragma unroll
-        for (int h = 0; h < kHalves; ++h) {
-          S[h][0][rt] -= dm;
-          S[h][1][rt] -= dm;
-        }
-      }
-    } else if (!PRES && __any(jump)) {
+    if (__any(jump)) {
 #pragma unroll
       for (int rt = 0; rt < RW; ++rt) {
         const float mnew = mstep[rt] > m[rt] + kRescale ? mstep[rt] : m[rt];
@@ -233,7 +290,7 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
         float w[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float dx = PRES ? S[h][j >> 2][rt][j & 3] : __builtin_fmaf(S[h][j >> 2][rt][j & 3], p.c, -m[rt]);
+          const float dx = __builtin_fmaf(S[h][j >> 2][rt][j & 3], p.c, -m[rt]);
           w[j] = fast_exp2(dx);
           if (F32SUM) l32[rt] += w[j];
           if (!LAST) sx[rt] = __builtin_fmaf(w[j], dx, sx[rt]);
@@ -245,6 +302,7 @@ __device__ __forceinline__ void rstep_long_body(const T* __restrict__ k, const T
       typename E::frag vv[NACC][2];
       load_cols<T, D, DK, NACC>(vv, LAST ? cV : cK, 32 * h);
       weighted_sum<T, D, NACC, RW>(acc, vv, pf);
+    }
     }
     __syncthreads();
   };

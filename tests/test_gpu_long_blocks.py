@@ -265,6 +265,38 @@ def test_one_key_block_gradients_are_attention_gradients(dtype, b2, T):
         f"{n} {'max-abs' if n == 'y' else 'rel-max'} {wv[0]:.2e}" for n, wv in worst.items()))
 
 
+@pytest.mark.parametrize("dtype,T", [("bf16", 1), ("bf16", 2), ("f32", 1)])
+def test_late_spikes_beyond_the_weight_range(dtype, T):
+    """As the late-spike case below, with spikes so strong that their weight
+    would overflow fp32 against the reference the stream started from: key
+    300 lifts rows by about 70 log2 units and key 590 by about 140 (logits of
+    about 50 and 100 nats).  The bf16 inference forward keeps its reference
+    until a 32-key half's row sum passes 2^64, which these halves do (the
+    second one by an infinite weight), so it takes its rescaling branch
+    mid-stream for those rows only; fp32 takes its own (the step maximum).
+    Outputs against scaled dot-product attention in float64 on the CPU with
+    the usual bars."""
+    N, d = 600, 64
+    heads = [I.make_late_spike_head(s, N, d, spikes=((300, 100.0), (590, 200.0)), dtype=dtype) for s in (0, 1)]
+    wl = I.Workload("late_spikes_big", 1, len(heads), d, 2, 6, 50, 1, N, 1, T, dtype, pos_amp=0.0)
+    say(f"[case] overflowing late spikes in one key block of {N} keys, {dtype}, T={T}")
+    x = {n: np.stack([hd[i] for hd in heads])[None] for i, n in enumerate("qkv")}
+    if dtype == "bf16":
+        for i, n in enumerate("qkv"):
+            x[n + "_bits"] = np.stack([hd[3][i] for hd in heads])[None]
+    y = run_gpu(wl, x)
+    assert np.isfinite(y).all()
+    for h in range(wl.H):
+        q, k, v = (torch.from_numpy(x[n][0, h]).to(torch.float64) for n in "qkv")
+        ref = torch.nn.functional.scaled_dot_product_attention(q[None, None], k[None, None], v[None, None])[0, 0]
+        mx, mean = errors(y[0, h], ref.numpy())
+        say(f"[ok] overflowing late spikes head {h}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+        if dtype == "bf16":
+            assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
+        else:
+            assert mx <= F32_MAX_ABS, (h, mx)
+
+
 @pytest.mark.parametrize("dtype,T", [("f32", 1), ("f32", 2), ("bf16", 1), ("bf16", 2)])
 def test_late_spikes_move_the_streaming_maximum(dtype, T):
     """One key block of 600 keys (exact softmax attention) whose best key for
