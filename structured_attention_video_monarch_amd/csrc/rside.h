@@ -95,21 +95,19 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
   // aggregated queries of up to TB tiles in flight at once
   constexpr int TB = sizeof(T) == 2 ? (LAST ? MONARCH_RSTEP_TB : MONARCH_RSTEP_TB_MID) : 1;
   typename E::frag bq[TB][KS];
-  auto load_queries = [&](int g0) {
+  auto load_query = [&](int i, int g) {
 #pragma unroll
-    for (int i = 0; i < TB; ++i)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int col = s * 32 + 8 * G;
-        bq[i][s] = (g0 + i < p.t && row_ok && col < D) ? E::load(qhat + qrow(g0 + i) * D + col) : E::zero();
-      }
+    for (int s = 0; s < KS; ++s) {
+      const int col = s * 32 + 8 * G;
+      bq[i][s] = (g < p.t && row_ok && col < D) ? E::load(qhat + qrow(g) * D + col) : E::zero();
+    }
   };
-  load_queries(0);
+#pragma unroll
+  for (int i = 0; i < TB; ++i) load_query(i, i);
   __syncthreads();
   const T* sX = LAST ? sV : sK;
 
   for (int g0 = 0; g0 < p.t; g0 += TB) {
-    if (g0 > 0) load_queries(g0);
 #pragma unroll
   for (int gi = 0; gi < TB; ++gi) {
     const int g = g0 + gi;
@@ -131,6 +129,10 @@ __device__ __forceinline__ void rstep_body(const T* __restrict__ k, const T* __r
           }
       }
     }
+    // this slot's queries are consumed: load the tile TB further on into it,
+    // so that the loads run under this tile's softmax, products and stores
+    // (U is written over Q-hat only for the rows of tile g itself)
+    if (g + TB < p.t) load_query(gi, g + TB);
     // softmax over c2 for column a2: lane holds c2 = 32cp + 8G + j.  Keys
     // past b2 get the finite logit kMaskLogit: 2^(x - m) is exactly 0 for
     // them and x * 0 stays 0 in the entropy sum below.
