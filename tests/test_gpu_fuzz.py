@@ -50,7 +50,7 @@ def draw(kind, seed):
     return I.Workload(f"fuzz-{kind}{seed}", B, H, d, f, h, w, b1, b2, t, T, dtype, fq=fq)
 
 
-@pytest.mark.parametrize("seed", range(96))
+@pytest.mark.parametrize("seed", range(300))
 def test_fuzz_forward(seed):
     wl = draw("fwd", seed)
     compare(wl, seed=seed, label=f"{wl.name} f,h,w=({wl.f},{wl.h},{wl.w})")

@@ -156,13 +156,13 @@ def draw_long(seed):
     return I.Workload(f"fuzz-long{seed}", 1, int(rng.integers(1, 3)), d, f, h, w, b1, b2, t, T, dtype)
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(128))
 def test_fuzz_long_blocks(seed):
     wl = draw_long(seed)
     compare_long(wl, seed=seed, label=f"{wl.name} f,h,w=({wl.f},{wl.h},{wl.w})")
 
 
-@pytest.mark.parametrize("seed", range(100, 116))
+@pytest.mark.parametrize("seed", range(100, 160))
 def test_fuzz_long_blocks_backward(seed):
     """dq, dk and dv through every iteration of seeded long-block shapes
     against the gradient oracle (the bars of the hand-picked cases)."""
